@@ -1,0 +1,540 @@
+// C ABI of libflashovl: argument checks, per-device state, emulated arrivals and the launch.
+//
+// Flash-AG / Flash-RS as described on the FlashOverlap page (gist.science paper 2604.24013),
+// technical summary section 2: collectives split into point-to-point transfers, slices computed
+// in an order that hides them (local slice first for AG, own chunk last for RS), with per-slice
+// synchronisation instead of step barriers (section 3). On one GPU a transfer is emulated by a
+// device-to-device copy from a "peer" buffer on the copy stream, followed by a write of the call's
+// epoch into that slice's arrival flag; the GEMM kernel's tiles of that slice wait for the flag.
+#include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "fo_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+void set_error(const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+}
+
+fo_status invalid(const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return FO_ERR_INVALID_ARG;
+}
+
+#define FO_HIP(call)                                                              \
+  do {                                                                            \
+    hipError_t e_ = (call);                                                       \
+    if (e_ != hipSuccess) {                                                       \
+      set_error("%s failed: %s", #call, hipGetErrorString(e_));                   \
+      return FO_ERR_HIP;                                                          \
+    }                                                                             \
+  } while (0)
+
+constexpr int kMaxDevices = 64;
+constexpr uint32_t kDefaultTimeoutUs = 2000000u;
+
+// Library-owned objects of one device. Flags live in uncached device memory (written by the copy
+// stream, polled by kernels); release flags live in signal memory (written by kernels, waited on
+// by the copy stream). Both are allocated once and kept for the life of the process.
+struct DevState {
+  std::mutex mu;
+  bool ready = false;
+  int n_cu = 0;
+  int wall_khz = 100000;     // wall-clock counter rate read by the kernels' bounded waits
+  uint32_t* arr = nullptr;   // [FO_MAX_P] arrival flags, then [1] timeout record
+  uint32_t* err = nullptr;
+  uint32_t* done = nullptr;  // [FO_MAX_P] completed-tile counters
+  uint32_t* rel[FO_MAX_P] = {};
+  uint32_t epoch = 0;
+  hipStream_t copy_stream = nullptr;
+  hipEvent_t ev_start = nullptr, ev_copy = nullptr, ev_last = nullptr;
+  bool have_last = false;
+};
+
+DevState g_dev[kMaxDevices];
+
+fo_status ensure_ready(int dev, DevState& st) {
+  if (st.ready) return FO_OK;
+  FO_HIP(hipDeviceGetAttribute(&st.n_cu, hipDeviceAttributeMultiprocessorCount, dev));
+  int khz = 0;
+  FO_HIP(hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev));
+  if (khz > 0) st.wall_khz = khz;
+  void* p = nullptr;
+  FO_HIP(hipExtMallocWithFlags(&p, 4096, hipDeviceMallocUncached));
+  st.arr = (uint32_t*)p;
+  st.err = st.arr + FO_MAX_P;
+  FO_HIP(hipMemset(st.arr, 0, 4096));
+  FO_HIP(hipMalloc(&p, FO_MAX_P * sizeof(uint32_t)));
+  st.done = (uint32_t*)p;
+  FO_HIP(hipMemset(st.done, 0, FO_MAX_P * sizeof(uint32_t)));
+  for (int i = 0; i < FO_MAX_P; ++i) {
+    FO_HIP(hipExtMallocWithFlags(&p, 8, hipMallocSignalMemory));
+    st.rel[i] = (uint32_t*)p;
+    FO_HIP(hipMemset(st.rel[i], 0, 8));
+  }
+  FO_HIP(hipStreamCreateWithFlags(&st.copy_stream, hipStreamNonBlocking));
+  FO_HIP(hipEventCreateWithFlags(&st.ev_start, hipEventDisableTiming));
+  FO_HIP(hipEventCreateWithFlags(&st.ev_copy, hipEventDisableTiming));
+  FO_HIP(hipEventCreateWithFlags(&st.ev_last, hipEventDisableTiming));
+  FO_HIP(hipDeviceSynchronize());
+  st.ready = true;
+  return FO_OK;
+}
+
+fo_status current_state(DevState** out, int* dev_out) {
+  int dev = 0;
+  FO_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) {
+    set_error("device %d beyond the library's limit of %d", dev, kMaxDevices);
+    return FO_ERR_UNSUPPORTED;
+  }
+  *out = &g_dev[dev];
+  if (dev_out) *dev_out = dev;
+  return FO_OK;
+}
+
+size_t dt_size(int dt) { return dt == FO_DT_BF16 ? 2 : 4; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range rng(const void* p, size_t bytes) { return {(uintptr_t)p, (uintptr_t)p + bytes}; }
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo < a.hi && b.lo < b.hi; }
+
+fo_status check_opts(const fo_opts* o, fo_opts* out) {
+  fo_opts_init(out);
+  if (!o) return FO_OK;
+  if (o->order != FO_ORDER_FLASH && o->order != FO_ORDER_NATURAL)
+    return invalid("opts.order %d is not a fo_order", o->order);
+  if (o->arrival < FO_ARR_DEFAULT || o->arrival > FO_ARR_LOCKSTEP)
+    return invalid("opts.arrival %d is not a fo_arrival", o->arrival);
+  if (o->copy_engine != FO_COPY_SDMA && o->copy_engine != FO_COPY_BLIT)
+    return invalid("opts.copy_engine %d is not a fo_copy_engine", o->copy_engine);
+  if (o->tile < FO_TILE_AUTO || o->tile > FO_TILE_64x64)
+    return invalid("opts.tile %d is not a fo_tile", o->tile);
+  if (o->reserved[0] || o->reserved[1] || o->reserved[2])
+    return invalid("opts.reserved must be zero");
+  *out = *o;
+  if (out->spin_timeout_us == 0) out->spin_timeout_us = kDefaultTimeoutUs;
+  return FO_OK;
+}
+
+fo_status check_common(int P, int rank, int64_t m, int64_t K, int64_t N, int in_dt) {
+  if (P < 1 || P > FO_MAX_P) return invalid("P = %d outside [1, %d]", P, FO_MAX_P);
+  if (rank < 0 || rank >= P) return invalid("rank = %d outside [0, P = %d)", rank, P);
+  if (m < 0 || K < 0 || N < 0) return invalid("negative size (m %lld, K %lld, N %lld)",
+                                              (long long)m, (long long)K, (long long)N);
+  if (in_dt != FO_DT_BF16 && in_dt != FO_DT_F32) return invalid("in_dt %d is not a fo_dtype", in_dt);
+  const int64_t lim = (int64_t)1 << 40;
+  if (m > lim || K > lim || N > lim || (double)P * m * std::max<int64_t>(K, N) > 4.0e15)
+    return invalid("sizes too large");
+  if (in_dt == FO_DT_BF16 && (K % 8 || N % 8))
+    return invalid("bf16 operands need K and N to be multiples of 8 (K %lld, N %lld)",
+                   (long long)K, (long long)N);
+  return FO_OK;
+}
+
+int resolve_tile(const fo_opts& o, int in_dt, int P, int64_t m, int64_t N, int n_cu) {
+  if (in_dt == FO_DT_F32) return 0;
+  if (o.tile != FO_TILE_AUTO) return o.tile;
+  return fo::choose_tile(P, m, N, n_cu);
+}
+
+fo_status tiles_for(int in_dt, int tile, int64_t m, int64_t N, int P, fo::Plan& p) {
+  int bm = 64, bn = 64;
+  if (in_dt == FO_DT_BF16) {
+    const fo::TileShape ts = fo::tile_shape(tile);
+    bm = ts.bm;
+    bn = ts.bn;
+  }
+  const int64_t tm = (m + bm - 1) / bm, tn = (N + bn - 1) / bn;
+  if (tm * tn * P > 0x7fffffffLL) return invalid("too many tiles");
+  p.tiles_m = (int32_t)tm;
+  p.tiles_n = (int32_t)tn;
+  return FO_OK;
+}
+
+uint32_t next_epoch(DevState& st) {
+  if (++st.epoch == 0) ++st.epoch;
+  return st.epoch;
+}
+
+uint64_t spin_ticks(const DevState& st, uint32_t us) { return (uint64_t)us * st.wall_khz / 1000u; }
+
+hipMemcpyKind copy_kind(const fo_opts& o) {
+  return o.copy_engine == FO_COPY_BLIT ? hipMemcpyDeviceToDevice : hipMemcpyDeviceToDeviceNoCU;
+}
+
+}  // namespace
+
+extern "C" {
+
+void fo_opts_init(fo_opts* o) {
+  if (!o) return;
+  memset(o, 0, sizeof *o);
+  o->order = FO_ORDER_FLASH;
+  o->arrival = FO_ARR_DEFAULT;
+  o->copy_engine = FO_COPY_SDMA;
+  o->tile = FO_TILE_AUTO;
+  o->spin_timeout_us = kDefaultTimeoutUs;
+}
+
+const char* fo_status_str(fo_status s) {
+  switch (s) {
+    case FO_OK: return "FO_OK";
+    case FO_ERR_INVALID_ARG: return "FO_ERR_INVALID_ARG";
+    case FO_ERR_UNSUPPORTED: return "FO_ERR_UNSUPPORTED";
+    case FO_ERR_HIP: return "FO_ERR_HIP";
+    case FO_ERR_TIMEOUT: return "FO_ERR_TIMEOUT";
+  }
+  return "FO_ERR_UNKNOWN";
+}
+
+const char* fo_last_error(void) { return g_last_error.c_str(); }
+
+int32_t fo_version(void) { return FO_VERSION; }
+
+fo_status fo_slice_order(int32_t kind, int32_t order, int32_t P, int32_t rank, int32_t* out) {
+  if (kind != 0 && kind != 1) return invalid("kind %d is neither 0 (AG) nor 1 (RS)", kind);
+  if (!out) return invalid("out is NULL");
+  if (order != FO_ORDER_FLASH && order != FO_ORDER_NATURAL) return invalid("bad order %d", order);
+  if (P < 1 || P > FO_MAX_P || rank < 0 || rank >= P) return invalid("bad P %d / rank %d", P, rank);
+  fo::slice_order(kind, order, P, rank, out);
+  return FO_OK;
+}
+
+fo_status fo_tile_info(int32_t P, int64_t m, int64_t K, int64_t N, int32_t in_dt, int32_t tile,
+                       int32_t* bm, int32_t* bn, int64_t* workgroups) {
+  fo_status s = check_common(P, 0, m, K, N, in_dt);
+  if (s != FO_OK) return s;
+  if (tile < FO_TILE_AUTO || tile > FO_TILE_64x64) return invalid("bad tile %d", tile);
+  // the CU count only matters for AUTO; use the device's when one is present
+  int n_cu = 256, dev = 0;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int c = 0;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && c > 0)
+      n_cu = c;
+  }
+  fo_opts o;
+  fo_opts_init(&o);
+  o.tile = tile;
+  const int t = resolve_tile(o, in_dt, P, m, N, n_cu);
+  fo::Plan p{};
+  s = tiles_for(in_dt, t, m, N, P, p);
+  if (s != FO_OK) return s;
+  int vbm = 64, vbn = 64;
+  if (in_dt == FO_DT_BF16) {
+    vbm = fo::tile_shape(t).bm;
+    vbn = fo::tile_shape(t).bn;
+  }
+  if (bm) *bm = vbm;
+  if (bn) *bn = vbn;
+  if (workgroups) *workgroups = (int64_t)P * p.tiles_m * p.tiles_n;
+  return FO_OK;
+}
+
+fo_status fo_ag_gemm(const void* x_local, const void* const* x_peer, void* x_recv, const void* w,
+                     void* y, int32_t P, int32_t rank, int64_t m, int64_t K, int64_t N,
+                     int32_t in_dt, int32_t out_dt, void* compute_stream, void* copy_stream,
+                     const fo_opts* opts) {
+  fo_opts o;
+  fo_status s = check_opts(opts, &o);
+  if (s != FO_OK) return s;
+  s = check_common(P, rank, m, K, N, in_dt);
+  if (s != FO_OK) return s;
+  if (out_dt != FO_DT_BF16 && out_dt != FO_DT_F32) return invalid("out_dt %d is not a fo_dtype", out_dt);
+  if (o.arrival == FO_ARR_LOCKSTEP) return invalid("LOCKSTEP arrivals apply to fo_gemm_rs only");
+  const bool arrivals = x_peer != nullptr && o.arrival != FO_ARR_NONE && P > 1;
+  const size_t es = dt_size(in_dt), os = dt_size(out_dt);
+  const size_t align = in_dt == FO_DT_BF16 ? 16 : 4;
+  if (!x_local || !w || !y || (P > 1 && !x_recv)) return invalid("NULL buffer");
+  if (!aligned(x_local, align) || !aligned(w, align) || (x_recv && !aligned(x_recv, align)) ||
+      !aligned(y, os))
+    return invalid("misaligned buffer (inputs need %zu-byte alignment)", align);
+  const size_t slice_b = (size_t)m * K * es;
+  const Range r_y = rng(y, (size_t)P * m * N * os);
+  const Range r_recv = rng(x_recv, x_recv ? (size_t)P * slice_b : 0);
+  if (overlap(r_y, rng(x_local, slice_b)) || overlap(r_y, rng(w, (size_t)K * N * es)) ||
+      overlap(r_y, r_recv))
+    return invalid("y overlaps an input");
+  if (arrivals) {
+    for (int q = 0; q < P; ++q) {
+      if (q == rank) continue;
+      if (!x_peer[q]) return invalid("x_peer[%d] is NULL", q);
+      if (!aligned(x_peer[q], align)) return invalid("x_peer[%d] misaligned", q);
+      const Range rp = rng(x_peer[q], slice_b);
+      if (overlap(rp, r_recv) || overlap(rp, r_y)) return invalid("x_peer[%d] overlaps x_recv or y", q);
+    }
+  }
+  if (m == 0 || N == 0) return FO_OK;
+
+  DevState* st = nullptr;
+  s = current_state(&st, nullptr);
+  if (s != FO_OK) return s;
+  std::lock_guard<std::mutex> lk(st->mu);
+  int dev = 0;
+  FO_HIP(hipGetDevice(&dev));
+  s = ensure_ready(dev, *st);
+  if (s != FO_OK) return s;
+
+  const int tile = resolve_tile(o, in_dt, P, m, N, st->n_cu);
+  fo::Plan p{};
+  s = tiles_for(in_dt, tile, m, N, P, p);
+  if (s != FO_OK) return s;
+  int32_t order[FO_MAX_P];
+  fo::slice_order(0, o.order, P, rank, order);
+  const uint32_t epoch = next_epoch(*st);
+  for (int pos = 0; pos < P; ++pos) {
+    const int sl = order[pos];
+    p.a_pos[pos] = sl == rank ? x_local : (const uint8_t*)x_recv + (size_t)sl * slice_b;
+    p.c_pos[pos] = (uint8_t*)y + (size_t)sl * m * N * os;
+    p.gate[pos] = (arrivals && sl != rank) ? sl : -1;
+  }
+  p.b = w;
+  p.arr = st->arr;
+  p.done = st->done;
+  p.err = st->err;
+  p.spin_limit = spin_ticks(*st, o.spin_timeout_us);
+  p.m = m;
+  p.K = K;
+  p.N = N;
+  p.npos = P;
+  p.n_recv = 0;
+  p.accum_pos = -1;
+  p.out_f32 = out_dt == FO_DT_F32;
+  p.epoch = epoch;
+
+  hipStream_t cs = (hipStream_t)compute_stream;
+  hipStream_t ks = copy_stream ? (hipStream_t)copy_stream : st->copy_stream;
+  if (st->have_last) FO_HIP(hipStreamWaitEvent(cs, st->ev_last, 0));
+  if (arrivals) {
+    FO_HIP(hipEventRecord(st->ev_start, cs));
+    FO_HIP(hipStreamWaitEvent(ks, st->ev_start, 0));
+    const hipMemcpyKind kind = copy_kind(o);
+    for (int pos = 0; pos < P; ++pos) {
+      const int sl = order[pos];
+      if (sl == rank) continue;
+      FO_HIP(hipMemcpyAsync((uint8_t*)x_recv + (size_t)sl * slice_b, x_peer[sl], slice_b, kind, ks));
+      FO_HIP(hipStreamWriteValue32(ks, st->arr + sl, epoch, 0));
+    }
+  }
+  FO_HIP(fo::launch_gemm(p, in_dt, tile, cs));
+  if (arrivals) {
+    FO_HIP(hipEventRecord(st->ev_copy, ks));
+    FO_HIP(hipStreamWaitEvent(cs, st->ev_copy, 0));
+  }
+  FO_HIP(hipEventRecord(st->ev_last, cs));
+  st->have_last = true;
+  return FO_OK;
+}
+
+fo_status fo_gemm_rs(const void* x_shard, const void* w, float* send_buf, float* out,
+                     const float* const* peer_partial, float* recv_buf, int32_t P, int32_t rank,
+                     int64_t m, int64_t K, int64_t N, int32_t in_dt, void* compute_stream,
+                     void* copy_stream, const fo_opts* opts) {
+  fo_opts o;
+  fo_status s = check_opts(opts, &o);
+  if (s != FO_OK) return s;
+  s = check_common(P, rank, m, K, N, in_dt);
+  if (s != FO_OK) return s;
+  if (o.order != FO_ORDER_FLASH) {
+    set_error("fo_gemm_rs implements the Flash-RS order only");
+    return FO_ERR_UNSUPPORTED;
+  }
+  const int arrival = o.arrival == FO_ARR_DEFAULT ? FO_ARR_LOCKSTEP : o.arrival;
+  const bool arrivals = peer_partial != nullptr && arrival != FO_ARR_NONE && P > 1;
+  const size_t es = dt_size(in_dt);
+  const size_t align = in_dt == FO_DT_BF16 ? 16 : 4;
+  if (!x_shard || !w || !out || (P > 1 && (!send_buf || !recv_buf))) return invalid("NULL buffer");
+  if (!aligned(x_shard, align) || !aligned(w, align) || !aligned(out, 4) ||
+      (send_buf && !aligned(send_buf, 4)) || (recv_buf && !aligned(recv_buf, 4)))
+    return invalid("misaligned buffer (inputs need %zu-byte alignment)", align);
+  const size_t chunk_b = (size_t)m * N * 4;
+  const Range r_x = rng(x_shard, (size_t)P * m * K * es), r_w = rng(w, (size_t)K * N * es);
+  const Range r_out = rng(out, chunk_b);
+  const Range r_send = rng(send_buf, send_buf ? (size_t)P * chunk_b : 0);
+  const Range r_recv = rng(recv_buf, recv_buf ? (size_t)P * chunk_b : 0);
+  for (Range o1 : {r_out, r_send}) {
+    if (overlap(o1, r_x) || overlap(o1, r_w) || overlap(o1, r_recv))
+      return invalid("an output overlaps an input");
+  }
+  if (overlap(r_out, r_send)) return invalid("out overlaps send_buf");
+  if (arrivals) {
+    for (int q = 0; q < P; ++q) {
+      if (q == rank) continue;
+      if (!peer_partial[q]) return invalid("peer_partial[%d] is NULL", q);
+      if (!aligned(peer_partial[q], 4)) return invalid("peer_partial[%d] misaligned", q);
+      const Range rp = rng(peer_partial[q], chunk_b);
+      if (overlap(rp, r_recv) || overlap(rp, r_out) || overlap(rp, r_send))
+        return invalid("peer_partial[%d] overlaps recv_buf or an output", q);
+    }
+  }
+  if (m == 0 || N == 0) return FO_OK;
+
+  DevState* st = nullptr;
+  s = current_state(&st, nullptr);
+  if (s != FO_OK) return s;
+  std::lock_guard<std::mutex> lk(st->mu);
+  int dev = 0;
+  FO_HIP(hipGetDevice(&dev));
+  s = ensure_ready(dev, *st);
+  if (s != FO_OK) return s;
+
+  const int tile = resolve_tile(o, in_dt, P, m, N, st->n_cu);
+  fo::Plan p{};
+  s = tiles_for(in_dt, tile, m, N, P, p);
+  if (s != FO_OK) return s;
+  int32_t order[FO_MAX_P];
+  fo::slice_order(1, FO_ORDER_FLASH, P, rank, order);
+  const uint32_t epoch = next_epoch(*st);
+  const bool lockstep = arrivals && arrival == FO_ARR_LOCKSTEP;
+  for (int pos = 0; pos < P; ++pos) {
+    const int d = order[pos];
+    p.a_pos[pos] = (const uint8_t*)x_shard + (size_t)d * m * K * es;
+    p.c_pos[pos] = d == rank ? (void*)out : (void*)((uint8_t*)send_buf + (size_t)d * chunk_b);
+    p.gate[pos] = -1;
+    p.rel[pos] = (lockstep && d != rank) ? st->rel[pos] : nullptr;
+    if (d == rank) p.accum_pos = pos;
+  }
+  // partials arrive from rank-1, rank-2, ... (mod P) and are added in that order
+  for (int i = 1; i < P; ++i) {
+    const int q = ((rank - i) % P + P) % P;
+    p.recv[i - 1] = (const float*)((const uint8_t*)recv_buf + (size_t)q * chunk_b);
+    p.recv_flag[i - 1] = arrivals ? q : -1;
+  }
+  p.n_recv = P - 1;
+  p.b = w;
+  p.arr = st->arr;
+  p.done = st->done;
+  p.err = st->err;
+  p.spin_limit = spin_ticks(*st, o.spin_timeout_us);
+  p.m = m;
+  p.K = K;
+  p.N = N;
+  p.npos = P;
+  p.out_f32 = 1;
+  p.epoch = epoch;
+
+  hipStream_t cs = (hipStream_t)compute_stream;
+  hipStream_t ks = copy_stream ? (hipStream_t)copy_stream : st->copy_stream;
+  if (st->have_last) FO_HIP(hipStreamWaitEvent(cs, st->ev_last, 0));
+  if (arrivals) FO_HIP(hipEventRecord(st->ev_start, cs));
+  // the kernel is enqueued before the copy stream's waits on its release flags, so a failed
+  // launch never leaves the copy stream waiting for a flag that nobody raises
+  FO_HIP(fo::launch_gemm(p, in_dt, tile, cs));
+  if (arrivals) {
+    FO_HIP(hipStreamWaitEvent(ks, st->ev_start, 0));
+    const hipMemcpyKind kind = copy_kind(o);
+    for (int i = 1; i < P; ++i) {
+      const int q = ((rank - i) % P + P) % P;
+      // lockstep: peer q's partial for this rank is sent at its step i-1, which ends when this
+      // rank finishes its own step i-1
+      if (lockstep) FO_HIP(hipStreamWaitValue32(ks, st->rel[i - 1], epoch, hipStreamWaitValueEq, 0xffffffffu));
+      FO_HIP(hipMemcpyAsync((uint8_t*)recv_buf + (size_t)q * chunk_b, peer_partial[q], chunk_b, kind, ks));
+      FO_HIP(hipStreamWriteValue32(ks, st->arr + q, epoch, 0));
+    }
+  }
+  if (arrivals) {
+    FO_HIP(hipEventRecord(st->ev_copy, ks));
+    FO_HIP(hipStreamWaitEvent(cs, st->ev_copy, 0));
+  }
+  FO_HIP(hipEventRecord(st->ev_last, cs));
+  st->have_last = true;
+  return FO_OK;
+}
+
+fo_status fo_gemm_ref(const void* a, const void* b, void* c, int64_t M, int64_t K, int64_t N,
+                      int32_t in_dt, int32_t out_dt, int32_t tile, void* stream) {
+  fo_status s = check_common(1, 0, M, K, N, in_dt);
+  if (s != FO_OK) return s;
+  if (out_dt != FO_DT_BF16 && out_dt != FO_DT_F32) return invalid("out_dt %d is not a fo_dtype", out_dt);
+  if (tile < FO_TILE_AUTO || tile > FO_TILE_64x64) return invalid("tile %d is not a fo_tile", tile);
+  const size_t es = dt_size(in_dt), os = dt_size(out_dt);
+  const size_t align = in_dt == FO_DT_BF16 ? 16 : 4;
+  if (!a || !b || !c) return invalid("NULL buffer");
+  if (!aligned(a, align) || !aligned(b, align) || !aligned(c, os)) return invalid("misaligned buffer");
+  const Range rc = rng(c, (size_t)M * N * os);
+  if (overlap(rc, rng(a, (size_t)M * K * es)) || overlap(rc, rng(b, (size_t)K * N * es)))
+    return invalid("c overlaps an input");
+  if (M == 0 || N == 0) return FO_OK;
+
+  DevState* st = nullptr;
+  s = current_state(&st, nullptr);
+  if (s != FO_OK) return s;
+  std::lock_guard<std::mutex> lk(st->mu);
+  int dev = 0;
+  FO_HIP(hipGetDevice(&dev));
+  s = ensure_ready(dev, *st);
+  if (s != FO_OK) return s;
+  fo_opts o;
+  fo_opts_init(&o);
+  o.tile = tile;
+  const int t = resolve_tile(o, in_dt, 1, M, N, st->n_cu);
+  fo::Plan p{};
+  s = tiles_for(in_dt, t, M, N, 1, p);
+  if (s != FO_OK) return s;
+  p.a_pos[0] = a;
+  p.c_pos[0] = c;
+  p.gate[0] = -1;
+  p.b = b;
+  p.arr = st->arr;
+  p.done = st->done;
+  p.err = st->err;
+  p.spin_limit = spin_ticks(*st, kDefaultTimeoutUs);
+  p.m = M;
+  p.K = K;
+  p.N = N;
+  p.npos = 1;
+  p.accum_pos = -1;
+  p.out_f32 = out_dt == FO_DT_F32;
+  p.epoch = st->epoch;
+  hipStream_t cs = (hipStream_t)stream;
+  FO_HIP(fo::launch_gemm(p, in_dt, t, cs));
+  return FO_OK;
+}
+
+fo_status fo_check(void* stream) {
+  DevState* st = nullptr;
+  int dev = 0;
+  fo_status s = current_state(&st, &dev);
+  if (s != FO_OK) return s;
+  FO_HIP(hipStreamSynchronize((hipStream_t)stream));
+  std::lock_guard<std::mutex> lk(st->mu);
+  if (!st->ready) return FO_OK;
+  FO_HIP(hipStreamSynchronize(st->copy_stream));
+  uint32_t e = 0;
+  FO_HIP(hipMemcpy(&e, st->err, sizeof e, hipMemcpyDeviceToHost));
+  if (e) {
+    const uint32_t zero = 0;
+    FO_HIP(hipMemcpy(st->err, &zero, sizeof zero, hipMemcpyHostToDevice));
+    set_error("an in-kernel arrival wait ran past its bound");
+    return FO_ERR_TIMEOUT;
+  }
+  return FO_OK;
+}
+
+}  // extern "C"

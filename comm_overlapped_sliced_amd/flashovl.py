@@ -1,0 +1,213 @@
+"""ctypes binding of libflashovl (argument marshalling only).
+
+Every entry point of ``include/flashovl.h`` is exposed under the same name without the ``fo_``
+prefix. Tensors are torch device tensors (torch provides device memory and streams only); the
+computation runs entirely in the library's HIP kernels. If the library is missing this module
+raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libflashovl.so")
+
+FO_OK, FO_ERR_INVALID_ARG, FO_ERR_UNSUPPORTED, FO_ERR_HIP, FO_ERR_TIMEOUT = range(5)
+BF16, F32 = 0, 1
+ORDER_FLASH, ORDER_NATURAL = 0, 1
+ARR_DEFAULT, ARR_NONE, ARR_EAGER, ARR_LOCKSTEP = 0, 1, 2, 3
+COPY_SDMA, COPY_BLIT = 0, 1
+TILE_AUTO, TILE_256x256, TILE_256x128, TILE_128x256, TILE_128x128, TILE_64x64 = range(6)
+MAX_P = 32
+
+EXPORTS = ("fo_opts_init", "fo_ag_gemm", "fo_gemm_rs", "fo_gemm_ref", "fo_check",
+           "fo_slice_order", "fo_tile_info", "fo_status_str", "fo_last_error", "fo_version")
+
+
+class FoError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__(f"{where}: {_status_name(status)}: {detail}")
+
+
+class Opts(ctypes.Structure):
+    _fields_ = [("order", ctypes.c_int32), ("arrival", ctypes.c_int32),
+                ("copy_engine", ctypes.c_int32), ("tile", ctypes.c_int32),
+                ("spin_timeout_us", ctypes.c_uint32), ("reserved", ctypes.c_int32 * 3)]
+
+
+_lib = None
+
+
+def load():
+    """Open libflashovl.so (after torch, so that both use the same HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+    try:
+        import torch  # noqa: F401  (load torch's HIP runtime first so there is only one)
+    except ImportError:
+        pass
+    lib = ctypes.CDLL(LIB_PATH)
+    i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+    op = ctypes.POINTER(Opts)
+    lib.fo_opts_init.argtypes = [op]
+    lib.fo_opts_init.restype = None
+    lib.fo_ag_gemm.argtypes = [vp, vp, vp, vp, vp, i32, i32, i64, i64, i64, i32, i32, vp, vp, op]
+    lib.fo_gemm_rs.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i64, i64, i64, i32, vp, vp, op]
+    lib.fo_gemm_ref.argtypes = [vp, vp, vp, i64, i64, i64, i32, i32, i32, vp]
+    lib.fo_check.argtypes = [vp]
+    lib.fo_slice_order.argtypes = [i32, i32, i32, i32, ctypes.POINTER(i32)]
+    lib.fo_tile_info.argtypes = [i32, i64, i64, i64, i32, i32, ctypes.POINTER(i32),
+                                 ctypes.POINTER(i32), ctypes.POINTER(i64)]
+    lib.fo_status_str.argtypes = [i32]
+    lib.fo_status_str.restype = ctypes.c_char_p
+    lib.fo_last_error.argtypes = []
+    lib.fo_last_error.restype = ctypes.c_char_p
+    lib.fo_version.argtypes = []
+    for f in ("fo_ag_gemm", "fo_gemm_rs", "fo_gemm_ref", "fo_check", "fo_slice_order",
+              "fo_tile_info", "fo_version"):
+        getattr(lib, f).restype = ctypes.c_int32
+    _lib = lib
+    return lib
+
+
+def _status_name(s: int) -> str:
+    try:
+        return load().fo_status_str(s).decode()
+    except Exception:  # noqa: BLE001
+        return str(s)
+
+
+def _raise_on(status: int, where: str) -> None:
+    if status != FO_OK:
+        raise FoError(status, where, load().fo_last_error().decode())
+
+
+def opts(order=ORDER_FLASH, arrival=ARR_DEFAULT, copy_engine=COPY_SDMA, tile=TILE_AUTO,
+         spin_timeout_us=0) -> Opts:
+    o = Opts()
+    load().fo_opts_init(ctypes.byref(o))
+    o.order, o.arrival, o.copy_engine, o.tile = order, arrival, copy_engine, tile
+    if spin_timeout_us:
+        o.spin_timeout_us = spin_timeout_us
+    return o
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(s) -> int | None:
+    if s is None:
+        return None
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _dt(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr_array(ptrs):
+    arr = (ctypes.c_void_p * len(ptrs))()
+    for i, p in enumerate(ptrs):
+        arr[i] = _ptr(p)
+    return arr
+
+
+def ag_gemm(x_local, x_peer, x_recv, w, y, P: int, rank: int, compute_stream=None,
+            copy_stream=None, o: Opts | None = None, raw: bool = False):
+    """Flash-AG (fo_ag_gemm). x_local [m, K], x_peer list of P tensors (or None), x_recv
+    [P*m, K], w [K, N], y [P*m, N]. Returns the status when raw=True, else raises on error."""
+    m, K = x_local.shape
+    N = w.shape[1]
+    peers = None if x_peer is None else _ptr_array(x_peer)
+    st = load().fo_ag_gemm(_ptr(x_local), ctypes.cast(peers, ctypes.c_void_p) if peers else None,
+                           _ptr(x_recv), _ptr(w), _ptr(y), P, rank, m, K, N, _dt(x_local),
+                           _dt(y), _stream(compute_stream), _stream(copy_stream),
+                           ctypes.byref(o) if o is not None else None)
+    if raw:
+        return st
+    _raise_on(st, "fo_ag_gemm")
+    return st
+
+
+def gemm_rs(x_shard, w, send_buf, out, peer_partial, recv_buf, P: int, rank: int,
+            compute_stream=None, copy_stream=None, o: Opts | None = None, raw: bool = False):
+    """Flash-RS (fo_gemm_rs). x_shard [P*m, K], w [K, N], send_buf [P*m, N] fp32, out [m, N]
+    fp32, peer_partial list of P fp32 [m, N] tensors (or None), recv_buf [P*m, N] fp32."""
+    M, K = x_shard.shape
+    N = w.shape[1]
+    m = M // P
+    peers = None if peer_partial is None else _ptr_array(peer_partial)
+    st = load().fo_gemm_rs(_ptr(x_shard), _ptr(w), _ptr(send_buf), _ptr(out),
+                           ctypes.cast(peers, ctypes.c_void_p) if peers else None,
+                           _ptr(recv_buf), P, rank, m, K, N, _dt(x_shard),
+                           _stream(compute_stream), _stream(copy_stream),
+                           ctypes.byref(o) if o is not None else None)
+    if raw:
+        return st
+    _raise_on(st, "fo_gemm_rs")
+    return st
+
+
+def gemm_ref(a, b, c, tile: int = TILE_AUTO, stream=None, raw: bool = False):
+    """Monolithic C = A . B (fo_gemm_ref)."""
+    M, K = a.shape
+    N = b.shape[1]
+    st = load().fo_gemm_ref(_ptr(a), _ptr(b), _ptr(c), M, K, N, _dt(a), _dt(c), tile,
+                            _stream(stream))
+    if raw:
+        return st
+    _raise_on(st, "fo_gemm_ref")
+    return st
+
+
+def check(stream=None) -> int:
+    """fo_check: synchronize and report in-kernel wait timeouts (raises FoError on timeout)."""
+    st = load().fo_check(_stream(stream))
+    _raise_on(st, "fo_check")
+    return st
+
+
+def slice_order(kind: str, P: int, rank: int, order: int = ORDER_FLASH) -> list:
+    out = (ctypes.c_int32 * P)()
+    st = load().fo_slice_order(0 if kind == "ag" else 1, order, P, rank, out)
+    _raise_on(st, "fo_slice_order")
+    return list(out)
+
+
+def tile_info(P: int, m: int, K: int, N: int, in_dt: int = BF16, tile: int = TILE_AUTO):
+    bm, bn, wg = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()
+    st = load().fo_tile_info(P, m, K, N, in_dt, tile, ctypes.byref(bm), ctypes.byref(bn),
+                             ctypes.byref(wg))
+    _raise_on(st, "fo_tile_info")
+    return bm.value, bn.value, wg.value
+
+
+def version() -> int:
+    return int(load().fo_version())
+
+
+def hip_runtimes_mapped() -> set:
+    """Paths of libamdhip64 mapped into this process (one expected)."""
+    paths = set()
+    with open("/proc/self/maps") as f:
+        for line in f:
+            if "libamdhip64" in line:
+                paths.add(os.path.realpath(line.split()[-1]))
+    return paths

@@ -1,0 +1,177 @@
+/*
+ * libflashovl — the Flash-Overlap hot path on AMD MI355X (gfx950): one tensor-parallel rank's
+ * share of the MLP projections, computed slice by slice while the other slices are in flight.
+ *
+ * What is computed follows the FlashOverlap page (gist.science, paper 2604.24013), technical
+ * summary section 2 "Methodology (Flash-Overlap)":
+ *   - Flash-AG (Flash-All-Gather): All-Gather split into ring point-to-point transfers; the rank
+ *     multiplies the slice it already holds first and each received slice after it arrives.
+ *   - Flash-RS (Flash-Reduce-Scatter): Reduce-Scatter split into point-to-point transfers;
+ *     rank-adaptive scheduling computes the chunk that stays on the rank last, and the partial
+ *     sums received from the other ranks are added into it.
+ *   - Architectural instantiations: the column-parallel projection (All-Gather, then GEMM) and
+ *     the row-parallel projection (GEMM, then Reduce-Scatter) of MLP and attention layers.
+ * Section 3 ("Key contributions") states the algorithm is exact: every result equals the plain
+ * product, whatever the slice order.
+ *
+ * On one GPU the peer ranks are emulated: a "peer" buffer holds what the peer would send and the
+ * library copies it into the receive buffer on a copy stream (SDMA copy engine by default), then
+ * raises a per-slice arrival flag. Kernels wait on those flags per slice; there is no global
+ * barrier.
+ *
+ * Conventions for every entry point:
+ *   - All matrices are dense and row-major. X is [rows, K], W is [K, N] (N contiguous), outputs
+ *     are [rows, N]. bf16 is the IEEE binary32 upper half; accumulation is fp32.
+ *   - Device pointers are device memory on the current HIP device. Arrays "of P pointers" are
+ *     host arrays of device pointers. The caller owns every buffer; the library never frees
+ *     caller memory. Device pointers must be 16-byte aligned; K and N must be multiples of 8
+ *     (bf16) or 4 (fp32); the slice height m may be any positive value.
+ *   - Streams are hipStream_t passed as void*. NULL compute stream = the null stream; NULL copy
+ *     stream = a library-owned stream. Calls are stream-ordered and return after enqueueing; the
+ *     copy stream is joined back into the compute stream, so synchronizing the compute stream is
+ *     enough. Calls on one device are serialized by the library (they share its flags).
+ *   - Errors are return codes; nothing is enqueued when an argument is rejected. An in-kernel
+ *     wait that exceeds opts->spin_timeout_us is recorded on the device and reported as
+ *     FO_ERR_TIMEOUT by fo_check(); the kernel still runs to completion (no hang), but its
+ *     results are then unspecified.
+ *   - Thread safety: entry points may be called from several host threads; each call holds a
+ *     per-device lock while it enqueues.
+ */
+#ifndef FLASHOVL_H
+#define FLASHOVL_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FO_VERSION 1
+#define FO_MAX_P 32 /* largest tensor-parallel degree (number of slices) */
+
+typedef enum fo_status {
+  FO_OK = 0,
+  FO_ERR_INVALID_ARG = 1, /* a NULL/misaligned pointer, bad size, rank, dtype or option */
+  FO_ERR_UNSUPPORTED = 2, /* well-formed but not implemented (e.g. a dtype combination) */
+  FO_ERR_HIP = 3,         /* a HIP runtime call failed; fo_last_error() has its message */
+  FO_ERR_TIMEOUT = 4      /* an in-kernel arrival wait ran past its bound */
+} fo_status;
+
+typedef enum fo_dtype { FO_DT_BF16 = 0, FO_DT_F32 = 1 } fo_dtype;
+
+/* Slice order. FLASH: the page's schedule (AG: local slice first, then ring arrivals; RS: chunks
+   for the other ranks first, own chunk last). NATURAL: slices in index order 0..P-1, the
+   data-slicing baseline of the page's problem statement. */
+typedef enum fo_order { FO_ORDER_FLASH = 0, FO_ORDER_NATURAL = 1 } fo_order;
+
+/* How emulated peer data arrives. NONE: the data is already resident in the receive buffer and
+   no slice waits. EAGER: every copy is enqueued at the start of the call. LOCKSTEP (RS only): the
+   partial that rank r receives at step i is released only when rank r has finished its own step
+   i-1, modelling peers that progress in step with this rank. DEFAULT: EAGER for AG, LOCKSTEP for
+   RS. */
+typedef enum fo_arrival {
+  FO_ARR_DEFAULT = 0,
+  FO_ARR_NONE = 1,
+  FO_ARR_EAGER = 2,
+  FO_ARR_LOCKSTEP = 3
+} fo_arrival;
+
+/* Engine that performs the emulated transfers. SDMA: hipMemcpyDeviceToDeviceNoCU, a DMA engine
+   that takes no compute units (stands in for a link's copy engine). BLIT: an ordinary
+   device-to-device copy, run by copy kernels on the compute units (much faster, but competes
+   with the GEMM for CUs and HBM). */
+typedef enum fo_copy_engine { FO_COPY_SDMA = 0, FO_COPY_BLIT = 1 } fo_copy_engine;
+
+/* Tile shape of the bf16 GEMM (rows x columns of one workgroup's output tile). AUTO picks one
+   from the shape. */
+typedef enum fo_tile {
+  FO_TILE_AUTO = 0,
+  FO_TILE_256x256 = 1,
+  FO_TILE_256x128 = 2,
+  FO_TILE_128x256 = 3,
+  FO_TILE_128x128 = 4,
+  FO_TILE_64x64 = 5
+} fo_tile;
+
+typedef struct fo_opts {
+  int32_t order;            /* fo_order */
+  int32_t arrival;          /* fo_arrival */
+  int32_t copy_engine;      /* fo_copy_engine */
+  int32_t tile;             /* fo_tile */
+  uint32_t spin_timeout_us; /* bound of each in-kernel wait; 0 = 2 000 000 us */
+  int32_t reserved[3];      /* must be zero */
+} fo_opts;
+
+/* Fills *o with the defaults (FLASH order, DEFAULT arrival, SDMA, AUTO tile, 2 s bound). */
+void fo_opts_init(fo_opts* o);
+
+/*
+ * Flash-AG: Y = [X_0; X_1; ...; X_{P-1}] . W for rank `rank` (column-parallel projection).
+ *   x_local  device [m, K] in_dt: this rank's slice X_rank.
+ *   x_peer   host array of P device pointers; x_peer[s] ([m, K] in_dt) is what peer s sends.
+ *            Entry [rank] is ignored. NULL: no transfers, the slices are already in x_recv.
+ *   x_recv   device [P*m, K] in_dt receive buffer; slice s arrives at x_recv + s*m*K. The rows of
+ *            slice `rank` are neither read nor written.
+ *   w        device [K, N] in_dt, this rank's column shard of the weight.
+ *   y        device [P*m, N] out_dt; rows s*m .. s*m+m-1 hold X_s . W.
+ * Slices are computed in the Flash-AG order (rank, rank-1, ..., rank-P+1 mod P); slice s != rank
+ * is read only after its arrival flag is raised. in_dt: BF16 or F32 (F32 requires out_dt F32).
+ * out_dt BF16 rounds the fp32 accumulator to nearest-even. No output aliases an input.
+ */
+fo_status fo_ag_gemm(const void* x_local, const void* const* x_peer, void* x_recv, const void* w,
+                     void* y, int32_t P, int32_t rank, int64_t m, int64_t K, int64_t N,
+                     int32_t in_dt, int32_t out_dt, void* compute_stream, void* copy_stream,
+                     const fo_opts* opts);
+
+/*
+ * Flash-RS: the P row-chunks of X_shard . W for rank `rank` (row-parallel projection), own chunk
+ * last, plus the partials received from the other ranks.
+ *   x_shard      device [P*m, K] in_dt: this rank's activation (all tokens, its share of K).
+ *   w            device [K, N] in_dt: this rank's row shard of the weight.
+ *   send_buf     device [P*m, N] fp32; chunk d != rank (rows d*m..) receives X_shard[d rows] . W,
+ *                the partial this rank would send to rank d. Chunk `rank` is not written.
+ *   out          device [m, N] fp32: X_shard[rank rows] . W + sum of the incoming partials, added
+ *                onto the fp32 accumulator in arrival order q = rank-1, rank-2, ... (mod P).
+ *   peer_partial host array of P device pointers; peer_partial[q] ([m, N] fp32) is what peer q
+ *                sends for this rank's chunk. Entry [rank] ignored. NULL: no transfers, the
+ *                partials are already in recv_buf.
+ *   recv_buf     device [P*m, N] fp32; peer q's partial arrives at recv_buf + q*m*N.
+ * Chunks are computed in the Flash-RS order (rank+1, ..., rank+P-1, rank mod P).
+ */
+fo_status fo_gemm_rs(const void* x_shard, const void* w, float* send_buf, float* out,
+                     const float* const* peer_partial, float* recv_buf, int32_t P, int32_t rank,
+                     int64_t m, int64_t K, int64_t N, int32_t in_dt, void* compute_stream,
+                     void* copy_stream, const fo_opts* opts);
+
+/*
+ * Plain monolithic GEMM C[M, N] = A[M, K] . B[K, N] with the same kernels (no slices, no waits):
+ * the "pure GEMM" latency the overlap is measured against, and the unsliced product that the
+ * page's exactness claim compares to. tile: a fo_tile value (AUTO = the choice fo_ag_gemm would
+ * make for a single slice of M rows).
+ */
+fo_status fo_gemm_ref(const void* a, const void* b, void* c, int64_t M, int64_t K, int64_t N,
+                      int32_t in_dt, int32_t out_dt, int32_t tile, void* stream);
+
+/* Synchronizes `stream` (hipStream_t) and reports FO_ERR_TIMEOUT if any in-kernel wait on the
+   current device ran past its bound since the previous fo_check (the record is then cleared). */
+fo_status fo_check(void* stream);
+
+/* Host-side slice scheduler. kind 0 = AG, 1 = RS; order a fo_order. Writes P slice/chunk ids in
+   computation order to out[0..P-1]. */
+fo_status fo_slice_order(int32_t kind, int32_t order, int32_t P, int32_t rank, int32_t* out);
+
+/* The tile shape the bf16 kernel would use for slices of m rows, K, N (tile: fo_tile request).
+   Writes the tile rows/columns and the number of workgroups one call over P slices launches. */
+fo_status fo_tile_info(int32_t P, int64_t m, int64_t K, int64_t N, int32_t in_dt, int32_t tile,
+                       int32_t* bm, int32_t* bn, int64_t* workgroups);
+
+const char* fo_status_str(fo_status s);
+/* Detail of the last failure on the calling thread (empty string if none). */
+const char* fo_last_error(void);
+int32_t fo_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASHOVL_H */

@@ -1,0 +1,175 @@
+"""CPU tests of the C ABI boundary: the library loads without a GPU, exports every entry point
+its header declares, implements the slice schedule of the FlashOverlap page, and rejects bad
+arguments before touching the device."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+from comm_overlapped_sliced_amd import flashovl as fo
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flashovl.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return fo.load()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fo_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(lib):
+    names = header_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in flashovl.h but not exported"
+    assert set(names) == set(fo.EXPORTS)
+
+
+def test_version_and_status_strings(lib):
+    assert fo.version() == 1
+    for s, name in enumerate(["FO_OK", "FO_ERR_INVALID_ARG", "FO_ERR_UNSUPPORTED", "FO_ERR_HIP",
+                              "FO_ERR_TIMEOUT"]):
+        assert lib.fo_status_str(s).decode() == name
+    assert lib.fo_status_str(99).decode() == "FO_ERR_UNKNOWN"
+
+
+def test_opts_defaults():
+    o = fo.opts()
+    assert (o.order, o.arrival, o.copy_engine, o.tile) == (0, 0, 0, 0)
+    assert o.spin_timeout_us == 2_000_000
+    assert list(o.reserved) == [0, 0, 0]
+
+
+@pytest.mark.parametrize("P", list(range(1, 33)))
+def test_slice_orders_follow_the_page(P):
+    for r in range(P):
+        ag = fo.slice_order("ag", P, r)
+        rs = fo.slice_order("rs", P, r)
+        assert ag[0] == r and sorted(ag) == list(range(P))     # local slice first
+        assert rs[-1] == r and sorted(rs) == list(range(P))    # own chunk last
+        assert ag == oracle.ag_order(P, r)
+        assert rs == oracle.rs_order(P, r)
+        assert fo.slice_order("ag", P, r, fo.ORDER_NATURAL) == list(range(P))
+    for i in range(P - 1):  # every RS step is a derangement over the ranks
+        tgt = [fo.slice_order("rs", P, r)[i] for r in range(P)]
+        assert sorted(tgt) == list(range(P)) and all(t != r for r, t in enumerate(tgt))
+
+
+def test_slice_order_rejects(lib):
+    out = (ctypes.c_int32 * 4)()
+    assert lib.fo_slice_order(2, 0, 4, 0, out) == fo.FO_ERR_INVALID_ARG
+    assert lib.fo_slice_order(0, 0, 0, 0, out) == fo.FO_ERR_INVALID_ARG
+    assert lib.fo_slice_order(0, 0, 4, 4, out) == fo.FO_ERR_INVALID_ARG
+    assert lib.fo_slice_order(0, 7, 4, 0, out) == fo.FO_ERR_INVALID_ARG
+    assert lib.fo_slice_order(0, 0, 33, 0, out) == fo.FO_ERR_INVALID_ARG
+
+
+def test_tile_choice_for_the_workloads():
+    # tiles never cross a slice; the 70B and 405B shares use 256x256 tiles
+    assert fo.tile_info(8, 512, 8192, 7168)[:2] == (256, 256)
+    assert fo.tile_info(8, 512, 3584, 8192)[:2] == (256, 256)
+    assert fo.tile_info(8, 1024, 16384, 13312)[:2] == (256, 256)
+    bm, bn, wg = fo.tile_info(8, 128, 8192, 7168)       # M = 1024: slices of 128 rows
+    assert bm == 128 and wg == 8 * (7168 // bn)
+    assert fo.tile_info(4, 64, 256, 512, fo.F32)[:2] == (64, 64)
+    assert fo.tile_info(8, 512, 8192, 7168, fo.BF16, fo.TILE_128x128) == (128, 128, 8 * 4 * 56)
+
+
+# --- argument checks: all rejected before any HIP call (no GPU in this container) ---------
+
+A = 0x10000000   # fake, 16-byte aligned addresses that are never dereferenced
+B = 0x20000000
+C = 0x30000000
+D = 0x40000000
+
+
+def _ag(lib, **kw):
+    args = dict(x_local=A, x_peer=None, x_recv=B, w=C, y=D, P=4, rank=0, m=64, K=256, N=512,
+                in_dt=fo.BF16, out_dt=fo.BF16, cs=None, ks=None, opts=None)
+    args.update(kw)
+    peers = args["x_peer"]
+    if peers is not None:
+        arr = (ctypes.c_void_p * len(peers))(*peers)
+        peers = ctypes.cast(arr, ctypes.c_void_p)
+    return lib.fo_ag_gemm(args["x_local"], peers, args["x_recv"], args["w"], args["y"], args["P"],
+                          args["rank"], args["m"], args["K"], args["N"], args["in_dt"],
+                          args["out_dt"], args["cs"], args["ks"], args["opts"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(P=0), dict(P=33), dict(rank=4), dict(rank=-1), dict(m=-1), dict(K=-8),
+    dict(K=260), dict(N=500), dict(in_dt=5), dict(out_dt=2), dict(x_local=None), dict(w=None),
+    dict(y=None), dict(x_recv=None), dict(x_local=A + 2), dict(w=C + 8), dict(y=D + 1),
+    dict(y=A),                                   # output overlaps the local slice
+    dict(y=B + 4096),                            # output overlaps the receive buffer
+    dict(x_peer=[0x50000000, None, 0x60000000, 0x70000000], rank=0),  # a peer missing
+    dict(x_peer=[0x50000000, B, 0x60000000, 0x70000000], rank=0),     # peer inside x_recv
+])
+def test_ag_rejects(lib, kw):
+    assert _ag(lib, **kw) == fo.FO_ERR_INVALID_ARG
+    assert lib.fo_last_error().decode() != ""
+
+
+def test_ag_rejects_bad_opts(lib):
+    for field, val in [("order", 9), ("arrival", 7), ("copy_engine", 3), ("tile", 11)]:
+        o = fo.opts()
+        setattr(o, field, val)
+        assert _ag(lib, opts=ctypes.byref(o)) == fo.FO_ERR_INVALID_ARG
+    o = fo.opts()
+    o.reserved[1] = 1
+    assert _ag(lib, opts=ctypes.byref(o)) == fo.FO_ERR_INVALID_ARG
+    o = fo.opts(arrival=fo.ARR_LOCKSTEP)
+    assert _ag(lib, opts=ctypes.byref(o)) == fo.FO_ERR_INVALID_ARG
+
+
+def test_ag_empty_is_a_no_op(lib):
+    # m = 0 or N = 0: valid, nothing to compute, nothing enqueued
+    assert _ag(lib, m=0) == fo.FO_OK
+    assert _ag(lib, N=0) == fo.FO_OK
+
+
+def _rs(lib, **kw):
+    args = dict(x=A, w=B, send=C, out=D, peers=None, recv=0x50000000, P=4, rank=1, m=64, K=256,
+                N=512, in_dt=fo.BF16, opts=None)
+    args.update(kw)
+    peers = args["peers"]
+    if peers is not None:
+        arr = (ctypes.c_void_p * len(peers))(*peers)
+        peers = ctypes.cast(arr, ctypes.c_void_p)
+    return lib.fo_gemm_rs(args["x"], args["w"], args["send"], args["out"], peers, args["recv"],
+                          args["P"], args["rank"], args["m"], args["K"], args["N"], args["in_dt"],
+                          None, None, args["opts"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(P=0), dict(rank=4), dict(N=12), dict(K=7), dict(x=None), dict(out=None),
+    dict(send=None), dict(recv=None), dict(out=A), dict(send=B), dict(out=0x50000000),
+    dict(send=D - 4), dict(x=A + 4), dict(out=D + 2),
+    dict(peers=[0x60000000, 0x70000000, None, 0x78000000]),
+    dict(peers=[0x60000000, 0x70000000, 0x50000000, 0x78000000]),  # peer inside recv_buf
+])
+def test_rs_rejects(lib, kw):
+    assert _rs(lib, **kw) == fo.FO_ERR_INVALID_ARG
+
+
+def test_rs_natural_order_unsupported(lib):
+    o = fo.opts(order=fo.ORDER_NATURAL)
+    assert _rs(lib, opts=ctypes.byref(o)) == fo.FO_ERR_UNSUPPORTED
+
+
+def test_ref_rejects(lib):
+    assert lib.fo_gemm_ref(A, B, C, 64, 256, 500, fo.BF16, fo.BF16, 0, None) == fo.FO_ERR_INVALID_ARG
+    assert lib.fo_gemm_ref(A, B, A, 64, 256, 512, fo.BF16, fo.BF16, 0, None) == fo.FO_ERR_INVALID_ARG
+    assert lib.fo_gemm_ref(A, B, C, 64, 256, 512, fo.BF16, fo.BF16, 9, None) == fo.FO_ERR_INVALID_ARG
+    assert lib.fo_gemm_ref(None, B, C, 64, 256, 512, fo.BF16, fo.BF16, 0, None) == fo.FO_ERR_INVALID_ARG
+    assert lib.fo_gemm_ref(A, B, C, 0, 256, 512, fo.BF16, fo.BF16, 0, None) == fo.FO_OK
