@@ -200,11 +200,18 @@ def test_bf16_rs_ragged(dev, tile):
 # ---- degenerate cases ------------------------------------------------------------------------
 
 def test_single_rank_and_tiny_shapes(dev):
+    """Degenerate shapes. The AG output is taken in fp32 here: with only a handful of entries,
+    the bf16 rounding of the output alone can push the relative error past 2e-3 by chance; the
+    rounded output is instead held to half a bf16 ulp (plus fp32 accumulation error) per entry."""
     for (P, m, K, N) in [(1, 64, 128, 64), (2, 1, 8, 8), (1, 1, 8, 8), (5, 3, 16, 24)]:
         x = inputs.normal(7400 + m, (P * m, K), 1.0, "bf16")
         w = inputs.normal(7401 + K, (K, N), 0.02, "bf16")
+        ref = oracle.gemm(x, w)
+        prob32 = AG(x, w, P, dev, out_dt="f32")
+        assert rel_frobenius(prob32.run(P - 1), ref) <= 1e-5
         prob = AG(x, w, P, dev)
-        assert rel_frobenius(prob.run(P - 1), oracle.gemm(x, w)) <= TOL_BF16
+        got = prob.run(P - 1)
+        assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6)
         parts = [inputs.normal(7410 + q, (m, N), 1.0, "f32") for q in range(P)]
         rs = RS(x, w, parts, P, dev)
         out, _ = rs.run(0)
