@@ -1,0 +1,304 @@
+"""Benchmark of the Flash-Overlap hot path on one MI355X.
+
+One step is one pass of the whole path for one tensor-parallel rank (rank 0 of TP8) of the
+Llama-3.1-70B MLP: the gate+up projection as Flash-AG (fo_ag_gemm, M=4096 tokens in 8 slices,
+K=8192, N=7168, bf16) and the down projection as Flash-RS (fo_gemm_rs, M=4096, K=3584, N=8192,
+seven incoming fp32 partials), each with its emulated peer arrivals. Inputs are synthetic and
+seeded, resident in HBM before timing starts.
+
+Prints one JSON line: throughput (TFLOP/s of the step), the roofline of the dominant kernel
+(measured with HIP events around each GEMM kernel launch on its own stream), the
+exposed-transfer decomposition, and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """Raw hipEvent_t handles from the HIP runtime torch loaded (the library records them itself,
+    which torch.cuda.Event would not see)."""
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so.7")  # the copy already in the process
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+
+    def create(self) -> int:
+        e = self.ct.c_void_p()
+        if self.hip.hipEventCreate(self.ct.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return e.value
+
+    def record(self, e: int, stream: int) -> None:
+        if self.hip.hipEventRecord(e, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = self.ct.c_float()
+        if self.hip.hipEventElapsedTime(self.ct.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--rank", type=int, default=0)
+    ap.add_argument("--engine", choices=["sdma", "blit"], default="sdma")
+    ap.add_argument("--lanes", type=int, default=0, help="copy lanes (0: library default)")
+    ap.add_argument("--exposure-reps", type=int, default=15)
+    ap.add_argument("--no-exposure", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample (0 disables)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: every box of this setup has a single MI355X, so "
+              "--gpus must be 1 (the multi-GPU sharding is described in DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from comm_overlapped_sliced_amd import configs, flashovl as fo
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    fo.load()
+    stream = torch.cuda.current_stream()
+    copy_stream = torch.cuda.Stream()
+
+    ag_case, rs_case = configs.L70B_AG, configs.L70B_RS
+    P, r = ag_case.P, args.rank
+
+    def dev_of(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    t0 = time.time()
+    xa = ag_case.x()
+    ag_slices = [dev_of(np.ascontiguousarray(xa[s * ag_case.m:(s + 1) * ag_case.m]))
+                 for s in range(P)]
+    ag_full = dev_of(xa)
+    del xa
+    ag_w = dev_of(ag_case.w())
+    ag_recv = torch.empty((ag_case.M, ag_case.K), dtype=torch.bfloat16, device=dev)
+    ag_y = torch.empty((ag_case.M, ag_case.N), dtype=torch.bfloat16, device=dev)
+    rs_x = dev_of(rs_case.x())
+    rs_w = dev_of(rs_case.w())
+    rs_peer = [dev_of(rs_case.partial(q)) for q in range(P)]
+    rs_send = torch.empty((rs_case.M, rs_case.N), dtype=torch.float32, device=dev)
+    rs_out = torch.empty((rs_case.m, rs_case.N), dtype=torch.float32, device=dev)
+    rs_recv = torch.empty((rs_case.M, rs_case.N), dtype=torch.float32, device=dev)
+    ref_y_ag = torch.empty_like(ag_y)
+    ref_y_rs = torch.empty((rs_case.M, rs_case.N), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.time() - t0:.1f} s")
+
+    engine = fo.COPY_SDMA if args.engine == "sdma" else fo.COPY_BLIT
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def ag_call(evs=None, arrival=fo.ARR_DEFAULT, eng=engine, lanes=args.lanes):
+        o = fo.opts(copy_engine=eng, copy_lanes=lanes, arrival=arrival, kernel_events=evs)
+        peers = None if arrival == fo.ARR_NONE else ag_slices
+        fo.ag_gemm(ag_slices[r], peers, ag_recv, ag_w, ag_y, P, r, compute_stream=stream,
+                   copy_stream=copy_stream, o=o)
+
+    def rs_call(evs=None, arrival=fo.ARR_DEFAULT, eng=engine, lanes=args.lanes):
+        o = fo.opts(copy_engine=eng, copy_lanes=lanes, arrival=arrival, kernel_events=evs)
+        peers = None if arrival == fo.ARR_NONE else rs_peer
+        fo.gemm_rs(rs_x, rs_w, rs_send, rs_out, peers, rs_recv, P, r, compute_stream=stream,
+                   copy_stream=copy_stream, o=o)
+
+    def step(evs=None):
+        ag_call(evs[0] if evs else None)
+        rs_call(evs[1] if evs else None)
+
+    def timed(fn, reps):
+        """Median duration (ms) of fn() on the compute stream."""
+        out = []
+        for _ in range(reps):
+            a, b = ev(), ev()
+            a.record(stream)
+            fn()
+            b.record(stream)
+            b.synchronize()
+            out.append(a.elapsed_time(b))
+        return statistics.median(out)
+
+    for _ in range(args.warmup):
+        step()
+    fo.check(stream)
+
+    # ---- exposed-transfer decomposition (before the timed region) ------------------------
+    exposure = None
+    if not args.no_exposure:
+        exposure = {}
+        reps = args.exposure_reps
+        variants = [("sdma_1lane", fo.COPY_SDMA, 1), ("sdma_4lane", fo.COPY_SDMA, 4),
+                    ("blit", fo.COPY_BLIT, 1)]
+        t_ref_ag = timed(lambda: fo.gemm_ref(ag_full, ag_w, ref_y_ag, stream=stream), reps)
+        t_ref_rs = timed(lambda: fo.gemm_ref(rs_x, rs_w, ref_y_rs, stream=stream), reps)
+        t0_ag = timed(lambda: ag_call(arrival=fo.ARR_NONE), reps)
+        t0_rs = timed(lambda: rs_call(arrival=fo.ARR_NONE), reps)
+        for name, eng, lanes in variants:
+            to = fo.opts(copy_engine=eng, copy_lanes=lanes)
+            tx_ag = timed(lambda: fo.transfer_ref("ag", ag_slices, ag_recv, P, r,
+                                                  ag_case.m * ag_case.K * 2, stream, to), reps)
+            tx_rs = timed(lambda: fo.transfer_ref("rs", rs_peer, rs_recv, P, r,
+                                                  rs_case.m * rs_case.N * 4, stream, to), reps)
+            ts_ag = timed(lambda: ag_call(eng=eng, lanes=lanes), reps)
+            ts_rs = timed(lambda: rs_call(eng=eng, lanes=lanes), reps)
+            exposure[name] = {
+                "ag": {"t_ref_us": t_ref_ag * 1e3, "t_slice0_us": t0_ag * 1e3,
+                       "t_slice_us": ts_ag * 1e3, "t_xfer_us": tx_ag * 1e3,
+                       "exposed_frac": (ts_ag - t_ref_ag) / tx_ag},
+                "rs": {"t_ref_us": t_ref_rs * 1e3, "t_slice0_us": t0_rs * 1e3,
+                       "t_slice_us": ts_rs * 1e3, "t_xfer_us": tx_rs * 1e3,
+                       "exposed_frac": (ts_rs - t_ref_rs) / tx_rs},
+            }
+            log(f"exposure {name}: AG ref {t_ref_ag*1e3:.0f} us slice0 {t0_ag*1e3:.0f} "
+                f"slice {ts_ag*1e3:.0f} xfer {tx_ag*1e3:.0f} -> {exposure[name]['ag']['exposed_frac']:.3f}; "
+                f"RS ref {t_ref_rs*1e3:.0f} slice0 {t0_rs*1e3:.0f} slice {ts_rs*1e3:.0f} "
+                f"xfer {tx_rs*1e3:.0f} -> {exposure[name]['rs']['exposed_frac']:.3f}")
+        fo.check(stream)
+        step()
+        fo.check(stream)
+
+    # ---- timed region -------------------------------------------------------------------
+    he = HipEvents()
+    kevs = [((he.create(), he.create()), (he.create(), he.create())) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    g0, g1 = ev(), ev()
+    h0 = time.perf_counter()
+    g0.record(stream)
+    for i in range(args.steps):
+        step(kevs[i])
+    g1.record(stream)
+    torch.cuda.synchronize()
+    host_s = time.perf_counter() - h0
+    fo.check(stream)
+    total_ms = g0.elapsed_time(g1)
+    ms_per_step = total_ms / args.steps
+    flops = ag_case.flops + rs_case.flops
+    value = flops / (ms_per_step * 1e-3) / 1e12
+
+    k_ag = [he.elapsed_ms(a, b) for (a, b), _ in kevs]
+    k_rs = [he.elapsed_ms(a, b) for _, (a, b) in kevs]
+    mean_ag, mean_rs = statistics.mean(k_ag), statistics.mean(k_rs)
+    if mean_ag * ag_case.flops >= 0 and mean_ag >= mean_rs:
+        dom, dom_ms, dom_flops = "ag", mean_ag, ag_case.flops
+    else:
+        dom, dom_ms, dom_flops = "rs", mean_rs, rs_case.flops
+    bm, bn, wg = fo.tile_info(P, ag_case.m if dom == "ag" else rs_case.m,
+                              ag_case.K if dom == "ag" else rs_case.K,
+                              ag_case.N if dom == "ag" else rs_case.N)
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    roofline = {
+        "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "traffic": traffic_for(dom),
+        "kernel": f"gemm_bf16_kernel<{bm},{bn}> ({'fo_ag_gemm' if dom == 'ag' else 'fo_gemm_rs'})",
+        "kernel_us": round(dom_ms * 1e3, 1), "workgroups": wg,
+        "ag_kernel_us": round(mean_ag * 1e3, 1), "rs_kernel_us": round(mean_rs * 1e3, 1),
+    }
+    log(f"timed: {args.steps} steps {total_ms:.2f} ms (host {host_s*1e3:.2f} ms), "
+        f"{ms_per_step*1e3:.1f} us/step, {value:.1f} TFLOP/s; AG kernel {mean_ag*1e3:.1f} us, "
+        f"RS kernel {mean_rs*1e3:.1f} us")
+
+    cpu = cpu_baseline(ag_case, args.cpu_seconds) if args.cpu_seconds > 0 else None
+
+    line = {
+        "metric": "sliced AG/RS-GEMM TFLOP/s, % bf16 MFMA peak, exposed-transfer % (1 GPU)",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "Llama-3.1-70B MLP, one TP8 rank share (rank %d): Flash-AG "
+                   "gate+up M=4096 K=8192 N=7168 + Flash-RS down M=4096 K=3584 N=8192, "
+                   "P=8 slices" % r,
+                   "copy_engine": args.engine, "copy_lanes": args.lanes or 1,
+                   "ag_arrival": "eager", "rs_arrival": "lockstep"},
+        "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "exposed_transfer": exposure,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def traffic_for(dom: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken on the kernel
+    source as it is now (else null)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    src = os.path.join(ROOT, "comm_overlapped_sliced_amd", "csrc", "fo_gemm.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    ent = data.get(dom)
+    if not ent or ent.get("kernel_source_sha256") != sha:
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(case, target_s: float):
+    """The oracle (plain fp64 C, OpenMP) on a bounded sample of the Flash-AG product: the first
+    R rows of X times the full W, R chosen so the run takes about target_s seconds."""
+    import oracle
+
+    x = case.x()
+    w = case.w()
+    orc = oracle.default()
+    probes = []
+    for n in (16, 64):  # separate the per-call decode of W from the per-row cost
+        t0 = time.perf_counter()
+        orc.gemm(x[:n], w)
+        probes.append(time.perf_counter() - t0)
+    per_row = max((probes[1] - probes[0]) / 48, 1e-6)
+    fixed = max(probes[0] - 16 * per_row, 0.0)
+    rows = int(max(64, min(case.M, (target_s - fixed) / per_row)))
+    t0 = time.perf_counter()
+    orc.gemm(x[:rows], w)
+    secs = time.perf_counter() - t0
+    fl = 2.0 * rows * case.K * case.N
+    return {"value": round(fl / secs / 1e12, 6), "unit": "TFLOP/s", "cores": orc.num_threads(),
+            "kind": "oracle",
+            "sample": f"first {rows} of {case.M} rows of the Flash-AG product "
+                      f"(K={case.K}, N={case.N}), fp64, {secs:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

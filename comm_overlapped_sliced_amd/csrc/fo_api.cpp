@@ -67,6 +67,9 @@ struct DevState {
   uint32_t* rel[FO_MAX_P] = {};
   uint32_t epoch = 0;
   hipStream_t copy_stream = nullptr;
+  hipStream_t lane[FO_MAX_LANES - 1] = {};          // extra copy streams for striped transfers
+  hipEvent_t lane_ev[FO_MAX_P][FO_MAX_LANES] = {};  // piece done (per transfer, per lane)
+  hipEvent_t rel_ev[FO_MAX_P] = {};                 // release observed by the copy stream
   hipEvent_t ev_start = nullptr, ev_copy = nullptr, ev_last = nullptr;
   bool have_last = false;
 };
@@ -93,6 +96,13 @@ fo_status ensure_ready(int dev, DevState& st) {
     FO_HIP(hipMemset(st.rel[i], 0, 8));
   }
   FO_HIP(hipStreamCreateWithFlags(&st.copy_stream, hipStreamNonBlocking));
+  for (int l = 0; l < FO_MAX_LANES - 1; ++l)
+    FO_HIP(hipStreamCreateWithFlags(&st.lane[l], hipStreamNonBlocking));
+  for (int t = 0; t < FO_MAX_P; ++t) {
+    FO_HIP(hipEventCreateWithFlags(&st.rel_ev[t], hipEventDisableTiming));
+    for (int l = 0; l < FO_MAX_LANES; ++l)
+      FO_HIP(hipEventCreateWithFlags(&st.lane_ev[t][l], hipEventDisableTiming));
+  }
   FO_HIP(hipEventCreateWithFlags(&st.ev_start, hipEventDisableTiming));
   FO_HIP(hipEventCreateWithFlags(&st.ev_copy, hipEventDisableTiming));
   FO_HIP(hipEventCreateWithFlags(&st.ev_last, hipEventDisableTiming));
@@ -136,10 +146,12 @@ fo_status check_opts(const fo_opts* o, fo_opts* out) {
     return invalid("opts.copy_engine %d is not a fo_copy_engine", o->copy_engine);
   if (o->tile < FO_TILE_AUTO || o->tile > FO_TILE_64x64)
     return invalid("opts.tile %d is not a fo_tile", o->tile);
-  if (o->reserved[0] || o->reserved[1] || o->reserved[2])
-    return invalid("opts.reserved must be zero");
+  if (o->copy_lanes < 0 || o->copy_lanes > FO_MAX_LANES)
+    return invalid("opts.copy_lanes %d outside [0, %d]", o->copy_lanes, FO_MAX_LANES);
+  if (o->reserved[0] || o->reserved[1]) return invalid("opts.reserved must be zero");
   *out = *o;
   if (out->spin_timeout_us == 0) out->spin_timeout_us = kDefaultTimeoutUs;
+  if (out->copy_lanes == 0) out->copy_lanes = 1;
   return FO_OK;
 }
 
@@ -187,6 +199,67 @@ uint64_t spin_ticks(const DevState& st, uint32_t us) { return (uint64_t)us * st.
 
 hipMemcpyKind copy_kind(const fo_opts& o) {
   return o.copy_engine == FO_COPY_BLIT ? hipMemcpyDeviceToDevice : hipMemcpyDeviceToDeviceNoCU;
+}
+
+// One emulated transfer sequence: for each slice seq[t] (t = 0..n-1), copy src[seq[t]] into
+// dst + seq[t]*bytes on `ks`, striped over `lanes` streams, then (when flags) write the call's
+// epoch into that slice's arrival flag. With `rel`, transfer t first waits until the kernel has
+// raised rel[t] (lockstep release). `start` is the event the lanes wait on before their first
+// piece (already waited on by ks). Everything the lanes do is joined back into ks per transfer.
+fo_status enqueue_transfers(DevState& st, hipStream_t ks, hipEvent_t start, const int* seq, int n,
+                            const void* const* src, void* dst, size_t bytes, int lanes,
+                            hipMemcpyKind kind, uint32_t epoch, bool flags, bool rel) {
+  lanes = std::max(1, std::min(lanes, FO_MAX_LANES));
+  // pieces are 256-byte aligned; fewer lanes when a transfer is small
+  const size_t unit = 256;
+  size_t piece = ((bytes + lanes - 1) / lanes + unit - 1) / unit * unit;
+  if (piece == 0) piece = unit;
+  const int used = (int)std::min<size_t>((size_t)lanes, (bytes + piece - 1) / piece);
+  for (int l = 1; l < used; ++l) FO_HIP(hipStreamWaitEvent(st.lane[l - 1], start, 0));
+  for (int t = 0; t < n; ++t) {
+    const int sl = seq[t];
+    uint8_t* d = (uint8_t*)dst + (size_t)sl * bytes;
+    const uint8_t* sp = (const uint8_t*)src[sl];
+    if (rel) {
+      FO_HIP(hipStreamWaitValue32(ks, st.rel[t], epoch, hipStreamWaitValueEq, 0xffffffffu));
+      if (used > 1) {
+        FO_HIP(hipEventRecord(st.rel_ev[t], ks));
+        for (int l = 1; l < used; ++l) FO_HIP(hipStreamWaitEvent(st.lane[l - 1], st.rel_ev[t], 0));
+      }
+    }
+    for (int l = 1; l < used; ++l) {
+      const size_t off = (size_t)l * piece;
+      const size_t len = std::min(piece, bytes - off);
+      FO_HIP(hipMemcpyAsync(d + off, sp + off, len, kind, st.lane[l - 1]));
+      FO_HIP(hipEventRecord(st.lane_ev[t][l], st.lane[l - 1]));
+    }
+    FO_HIP(hipMemcpyAsync(d, sp, std::min(piece, bytes), kind, ks));
+    for (int l = 1; l < used; ++l) FO_HIP(hipStreamWaitEvent(ks, st.lane_ev[t][l], 0));
+    if (flags) FO_HIP(hipStreamWriteValue32(ks, st.arr + sl, epoch, 0));
+  }
+  return FO_OK;
+}
+
+// Arrival order of the slices a rank receives: for FLASH (and for RS always) the ring delivers
+// rank-1, rank-2, ... (mod P); for the NATURAL AG order the slices are needed, and so sent, in
+// index order.
+int arrival_sequence(int kind, int order, int P, int rank, int* seq) {
+  int n = 0;
+  if (kind == 0 && order == FO_ORDER_NATURAL) {
+    for (int s = 0; s < P; ++s)
+      if (s != rank) seq[n++] = s;
+  } else {
+    for (int i = 1; i < P; ++i) seq[n++] = ((rank - i) % P + P) % P;
+  }
+  return n;
+}
+
+fo_status launch_with_events(const fo::Plan& p, int in_dt, int tile, hipStream_t cs,
+                             const fo_opts& o) {
+  if (o.kernel_events[0]) FO_HIP(hipEventRecord((hipEvent_t)o.kernel_events[0], cs));
+  FO_HIP(fo::launch_gemm(p, in_dt, tile, cs));
+  if (o.kernel_events[1]) FO_HIP(hipEventRecord((hipEvent_t)o.kernel_events[1], cs));
+  return FO_OK;
 }
 
 }  // namespace
@@ -332,17 +405,17 @@ fo_status fo_ag_gemm(const void* x_local, const void* const* x_peer, void* x_rec
   hipStream_t ks = copy_stream ? (hipStream_t)copy_stream : st->copy_stream;
   if (st->have_last) FO_HIP(hipStreamWaitEvent(cs, st->ev_last, 0));
   if (arrivals) {
+    // the copies are enqueued before the kernel so that they start together with it
     FO_HIP(hipEventRecord(st->ev_start, cs));
     FO_HIP(hipStreamWaitEvent(ks, st->ev_start, 0));
-    const hipMemcpyKind kind = copy_kind(o);
-    for (int pos = 0; pos < P; ++pos) {
-      const int sl = order[pos];
-      if (sl == rank) continue;
-      FO_HIP(hipMemcpyAsync((uint8_t*)x_recv + (size_t)sl * slice_b, x_peer[sl], slice_b, kind, ks));
-      FO_HIP(hipStreamWriteValue32(ks, st->arr + sl, epoch, 0));
-    }
+    int seq[FO_MAX_P];
+    const int n = arrival_sequence(0, o.order, P, rank, seq);
+    s = enqueue_transfers(*st, ks, st->ev_start, seq, n, x_peer, x_recv, slice_b, o.copy_lanes,
+                          copy_kind(o), epoch, true, false);
+    if (s != FO_OK) return s;
   }
-  FO_HIP(fo::launch_gemm(p, in_dt, tile, cs));
+  s = launch_with_events(p, in_dt, tile, cs, o);
+  if (s != FO_OK) return s;
   if (arrivals) {
     FO_HIP(hipEventRecord(st->ev_copy, ks));
     FO_HIP(hipStreamWaitEvent(cs, st->ev_copy, 0));
@@ -445,18 +518,17 @@ fo_status fo_gemm_rs(const void* x_shard, const void* w, float* send_buf, float*
   if (arrivals) FO_HIP(hipEventRecord(st->ev_start, cs));
   // the kernel is enqueued before the copy stream's waits on its release flags, so a failed
   // launch never leaves the copy stream waiting for a flag that nobody raises
-  FO_HIP(fo::launch_gemm(p, in_dt, tile, cs));
+  s = launch_with_events(p, in_dt, tile, cs, o);
+  if (s != FO_OK) return s;
   if (arrivals) {
     FO_HIP(hipStreamWaitEvent(ks, st->ev_start, 0));
-    const hipMemcpyKind kind = copy_kind(o);
-    for (int i = 1; i < P; ++i) {
-      const int q = ((rank - i) % P + P) % P;
-      // lockstep: peer q's partial for this rank is sent at its step i-1, which ends when this
-      // rank finishes its own step i-1
-      if (lockstep) FO_HIP(hipStreamWaitValue32(ks, st->rel[i - 1], epoch, hipStreamWaitValueEq, 0xffffffffu));
-      FO_HIP(hipMemcpyAsync((uint8_t*)recv_buf + (size_t)q * chunk_b, peer_partial[q], chunk_b, kind, ks));
-      FO_HIP(hipStreamWriteValue32(ks, st->arr + q, epoch, 0));
-    }
+    // lockstep: peer q = rank-i sends its partial for this rank at its step i-1, which (peers
+    // progressing together) ends when this rank finishes its own step i-1
+    int seq[FO_MAX_P];
+    const int n = arrival_sequence(1, FO_ORDER_FLASH, P, rank, seq);
+    s = enqueue_transfers(*st, ks, st->ev_start, seq, n, (const void* const*)peer_partial, recv_buf,
+                          chunk_b, o.copy_lanes, copy_kind(o), epoch, true, lockstep);
+    if (s != FO_OK) return s;
   }
   if (arrivals) {
     FO_HIP(hipEventRecord(st->ev_copy, ks));
@@ -514,6 +586,43 @@ fo_status fo_gemm_ref(const void* a, const void* b, void* c, int64_t M, int64_t 
   p.epoch = st->epoch;
   hipStream_t cs = (hipStream_t)stream;
   FO_HIP(fo::launch_gemm(p, in_dt, t, cs));
+  return FO_OK;
+}
+
+fo_status fo_transfer_ref(int32_t kind, const void* const* src, void* dst, int32_t P,
+                          int32_t rank, int64_t slice_bytes, void* stream, const fo_opts* opts) {
+  fo_opts o;
+  fo_status s = check_opts(opts, &o);
+  if (s != FO_OK) return s;
+  if (kind != 0 && kind != 1) return invalid("kind %d is neither 0 (AG) nor 1 (RS)", kind);
+  if (P < 1 || P > FO_MAX_P || rank < 0 || rank >= P) return invalid("bad P %d / rank %d", P, rank);
+  if (slice_bytes < 0 || slice_bytes % 4) return invalid("slice_bytes must be a multiple of 4");
+  if (!src || !dst) return invalid("NULL buffer");
+  const Range rd = rng(dst, (size_t)P * slice_bytes);
+  for (int q = 0; q < P; ++q) {
+    if (q == rank) continue;
+    if (!src[q]) return invalid("src[%d] is NULL", q);
+    if (overlap(rng(src[q], slice_bytes), rd)) return invalid("src[%d] overlaps dst", q);
+  }
+  if (P == 1 || slice_bytes == 0) return FO_OK;
+  DevState* st = nullptr;
+  s = current_state(&st, nullptr);
+  if (s != FO_OK) return s;
+  std::lock_guard<std::mutex> lk(st->mu);
+  int dev = 0;
+  FO_HIP(hipGetDevice(&dev));
+  s = ensure_ready(dev, *st);
+  if (s != FO_OK) return s;
+  hipStream_t ks = (hipStream_t)stream;
+  if (st->have_last) FO_HIP(hipStreamWaitEvent(ks, st->ev_last, 0));
+  FO_HIP(hipEventRecord(st->ev_start, ks));
+  int seq[FO_MAX_P];
+  const int n = arrival_sequence(kind, o.order, P, rank, seq);
+  s = enqueue_transfers(*st, ks, st->ev_start, seq, n, src, dst, (size_t)slice_bytes,
+                        o.copy_lanes, copy_kind(o), 0, false, false);
+  if (s != FO_OK) return s;
+  FO_HIP(hipEventRecord(st->ev_last, ks));
+  st->have_last = true;
   return FO_OK;
 }
 

@@ -17,6 +17,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fo_internal.h"
 
 namespace fo {
@@ -26,7 +28,7 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 constexpr int kThreads = 256;
-constexpr int kBK = 64;  // K step (one 128-byte LDS row per operand row)
+constexpr int kBK = 32;  // K step
 
 // ---------------------------------------------------------------- waits and flags -----------
 
@@ -80,15 +82,21 @@ __device__ __forceinline__ uint16_t to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// Tile order inside one position. Workgroup b runs on XCD b % 8; when a position has a multiple
-// of 8 tiles, XCD x is given the x-th contiguous run of tiles (column-major over the tile grid),
-// so every XCD reuses the same W column blocks across slices in its own L2.
-__device__ __forceinline__ int remap_tile(int u, int T) {
-  if (T % 8) return u;
-  return (u % 8) * (T / 8) + u / 8;
+// Tile order inside one position. Workgroup b runs on XCD b % 8 (round-robin dispatch). When a
+// position has a multiple of 8 tiles, XCD x is given the x-th contiguous run of tile ids, and
+// ids walk the tile grid in groups of up to 8 tile rows, column by column inside a group: the
+// ~32 tiles an XCD runs at once then form an 8 x 4 block that shares its A row blocks and W
+// column blocks in that XCD's L2.
+__device__ __forceinline__ void tile_coords(int u, int T, int tiles_m, int tiles_n, int& tm,
+                                            int& tn) {
+  const int id = (T % 8) ? u : (u % 8) * (T / 8) + u / 8;
+  const int gm = tiles_m < 8 ? tiles_m : 8;
+  const int gsize = gm * tiles_n;
+  const int g = id / gsize, r = id % gsize;
+  const int rows = tiles_m - g * gm < gm ? tiles_m - g * gm : gm;
+  tm = g * gm + r % rows;
+  tn = r / rows;
 }
-
-__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
 // Writes one 32x32 accumulator fragment: lane (lr, lh) holds column lr and rows
 // 8*(v/4) + 4*lh + v%4 of the fragment in element v. The accumulate epilogue adds the received
@@ -97,69 +105,203 @@ __device__ __forceinline__ void store_fragment(const Plan& p, int pos, const f32
                                                int64_t row0, int64_t rbase, int64_t rows_valid,
                                                int64_t col, bool accum) {
   if (col >= p.N) return;
+  float x[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) x[v] = a[v];
+  if (accum) {
+    // all 16 loads of one partial are issued before any add, one partial after the other, so the
+    // sums keep the arrival order while the loads overlap
+    for (int q = 0; q < p.n_recv; ++q) {
+      const float* __restrict__ src = p.recv[q];
+      float t[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t r = rbase + 8 * (v >> 2) + (v & 3);
+        t[v] = r < rows_valid ? __builtin_nontemporal_load(src + (row0 + r) * p.N + col) : 0.f;
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) x[v] += t[v];
+    }
+  }
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     const int64_t r = rbase + 8 * (v >> 2) + (v & 3);
     if (r >= rows_valid) continue;
     const int64_t off = (row0 + r) * p.N + col;
-    float x = a[v];
-    if (accum)
-      for (int q = 0; q < p.n_recv; ++q) x += p.recv[q][off];
     if (p.out_f32)
-      ((float*)p.c_pos[pos])[off] = x;
+      ((float*)p.c_pos[pos])[off] = x[v];
     else
-      ((uint16_t*)p.c_pos[pos])[off] = to_bf16_rne(x);
+      ((uint16_t*)p.c_pos[pos])[off] = to_bf16_rne(x[v]);
   }
 }
 
 // ---------------------------------------------------------------- bf16 MFMA kernel ----------
+//
+// A ring of kStages LDS stages; stage s holds the A tile [BM rows][kBK k] (64-byte rows) and the
+// W tile [kBK rows][BN cols] (2*BN-byte rows). Both are filled straight from HBM by buffer loads
+// that write LDS (16 bytes per lane, no VGPR staging); a load outside the matrix reads zero
+// through the buffer's range check, so ragged edges need no branches. The 16-byte chunks of a
+// row are XOR-swizzled by the row index so that the MFMA operand reads spread over the banks.
+// A fragments are read with ds_read_b128 (K-contiguous); W fragments with two
+// ds_read_b64_tr_b16 transpose reads, which turn 4 rows x 16 columns of the row-major W tile
+// into 4 K-values per lane.
+
+constexpr int kStages = 4;
+constexpr uint32_t kOOB = 0x80000000u;          // offset past every range: the load reads 0
+constexpr int kRsrcWord3 = 0x00020000;          // raw buffer, 32-bit data format
+
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 template <int BM, int BN>
 struct Cfg {
-  static constexpr int WTM = BM / 2, WTN = BN / 2;  // wave tile (2 x 2 waves)
+  static constexpr int WTM = BM / 2, WTN = BN / 2;   // wave tile (2 x 2 waves)
   static constexpr int FM = WTM / 32, FN = WTN / 32;  // 32x32 fragments per wave
-  static constexpr int A_CH = BM * kBK / 8 / kThreads;  // 16-byte A chunks per thread
-  static constexpr int KB = BN / 32;                   // W rows per thread in the transposer
-  static constexpr int NBLK = BN / 8;                  // 8-column blocks of a W tile row
-  static constexpr int LDS_A = BM * kBK * 2;
-  static constexpr int LDS_B = BN * kBK * 2;
-  static constexpr int LDS_STAGE = LDS_A + LDS_B;
-  static_assert(A_CH >= 1 && KB >= 2 && KB <= 8 && FM >= 1 && FN >= 1, "tile");
+  static constexpr int A_BYTES = BM * kBK * 2;        // 64-byte rows
+  static constexpr int B_ROW = BN * 2;
+  static constexpr int B_BYTES = kBK * B_ROW;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int A_LOADS = A_BYTES / 1024 / 4;  // 1 KB loads per wave per stage
+  static constexpr int B_LOADS = B_BYTES / 1024 / 4;
+  static constexpr int LOADS = A_LOADS + B_LOADS;
+  static_assert(A_LOADS >= 1 && B_LOADS >= 1 && FM >= 1 && FN >= 1, "tile");
 };
 
-template <int KB>
-struct WRegs {
-  uint4 r[KB];
-};
+// swizzle of the 4 chunks of an A row and of the chunks of a W row
+__device__ __forceinline__ int swz_a(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+__device__ __forceinline__ int swz_b(int krow) { return (krow & 3) << 1; }
 
-__device__ __forceinline__ uint32_t dword_of(const uint4& v, int d) {
-  return d == 0 ? v.x : d == 1 ? v.y : d == 2 ? v.z : v.w;
+// Values the compiler cannot prove wave-uniform (they come out of VALU integer division) are
+// moved to scalar registers explicitly: buffer descriptors must live in SGPRs.
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ const void* uni_ptr(const void* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = (uint32_t)uni((int)(uint32_t)v), hi = (uint32_t)uni((int)(uint32_t)(v >> 32));
+  return (const void*)(((uint64_t)hi << 32) | lo);
+}
+
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+
+// Raw buffer descriptor (base, stride 0, num_records bytes, 32-bit data format); every field is
+// wave-uniform so it lives in SGPRs.
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t v = (uint64_t)uni_ptr(base);
+  i32x4 r;
+  r.x = uni((int)(uint32_t)v);
+  r.y = uni((int)(uint32_t)(v >> 32));  // stride 0
+  r.z = uni((int)bytes);
+  r.w = kRsrcWord3;
+  return r;
+}
+
+// 16 bytes per lane from the buffer at byte offset voff into LDS at lds_base + 16 * lane (an
+// offset past num_records reads zeros). Issued as inline assembly so that the compiler neither
+// orders later LDS reads behind it nor drains it at barriers: completion is tracked by hand with
+// wait_vmcnt, which counts these loads.
+__device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t lds_base, uint32_t voff,
+                                           uint32_t soff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds"
+      :
+      : "s"(lds_base), "v"(voff), "s"(rsrc), "s"(soff)
+      : "m0");
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
 template <int BM, int BN>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(Plan p) {
   using C = Cfg<BM, BN>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::LDS_STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t st2[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t st3[C::STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // wave-uniform (scalar) so that the LDS destination of the LDS-writing loads is uniform
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
   const int T = p.tiles_m * p.tiles_n;
-  const int pos = blockIdx.x / T;
-  const int t = remap_tile(blockIdx.x - pos * T, T);
-  const int tm = t % p.tiles_m, tn = t / p.tiles_m;
+  const int pos = uni(blockIdx.x / T);
+  int tm_, tn_;
+  tile_coords(blockIdx.x - pos * T, T, p.tiles_m, p.tiles_n, tm_, tn_);
+  const int tm = uni(tm_), tn = uni(tn_);
 
   const int64_t K = p.K, N = p.N;
-  const int64_t row0 = (int64_t)tm * BM;   // first row of the tile inside the slice
+  const int64_t row0 = (int64_t)tm * BM;
   const int64_t col0 = (int64_t)tn * BN;
-  const int64_t rows_valid = p.m - row0;   // >= 1
-  const uint16_t* A = (const uint16_t*)p.a_pos[pos] + row0 * K;
-  const uint16_t* B = (const uint16_t*)p.b + col0;
+  const int64_t rows_valid = p.m - row0;  // >= 1
+  const int a_rows = uni((int)(rows_valid < BM ? rows_valid : BM));
+  const uint16_t* A = (const uint16_t*)uni_ptr((const uint16_t*)p.a_pos[pos] + row0 * K);
+  const uint16_t* W = (const uint16_t*)uni_ptr((const uint16_t*)p.b + col0);
 
   // Flash-AG: a received slice is read only after its arrival flag.
   if (p.gate[pos] >= 0) wait_flags_wg(p, p.gate + pos, 1);
+
+  // ---- loads. Per-lane offsets are fixed for the whole K loop: the K step enters A's loads as
+  // the scalar offset and W's through a descriptor re-based on the step's first row (whose
+  // num_records also cuts off rows past K). Lanes outside the tile carry kOOB and read zeros.
+  const i32x4 rsrc_a = buffer_rsrc(A, (uint32_t)(a_rows * K * 2));
+  uint32_t a_voff[C::A_LOADS];
+  int a_kel[C::A_LOADS];
+#pragma unroll
+  for (int j = 0; j < C::A_LOADS; ++j) {
+    const int row = (wave * C::A_LOADS + j) * 16 + (lane >> 2);
+    a_kel[j] = ((lane & 3) ^ swz_a(row)) * 8;
+    a_voff[j] = row < a_rows ? (uint32_t)(((int64_t)row * K + a_kel[j]) * 2) : kOOB;
+  }
+  uint32_t b_voff[C::B_LOADS];
+#pragma unroll
+  for (int j = 0; j < C::B_LOADS; ++j) {
+    const int P = (wave * C::B_LOADS + j) * 1024 + lane * 16;
+    const int kr = P / C::B_ROW;
+    const int n = ((((P % C::B_ROW) >> 4) ^ swz_b(kr))) * 8;
+    b_voff[j] = col0 + n < N ? (uint32_t)(((int64_t)kr * N + n) * 2) : kOOB;
+  }
+
+  // load number l (A loads first, then W loads) of K step kt into the stage at LDS address lds;
+  // rb is W's descriptor for that step (from w_rsrc). TAIL: the step runs past K, so A columns
+  // beyond K are redirected to kOOB (W rows beyond K fall outside rb's range by themselves).
+  auto w_rsrc = [&](int kt) {
+    const int64_t k0 = (int64_t)kt * kBK;
+    const int64_t rows = K - k0 < kBK ? K - k0 : kBK;
+    return buffer_rsrc(W + k0 * N, (uint32_t)(rows * N * 2));
+  };
+  auto issue_one = [&](auto tail, int kt, uint32_t lds, const i32x4& rb, int l) {
+    const int64_t k0 = (int64_t)kt * kBK;
+    if (l < C::A_LOADS) {
+      uint32_t v = a_voff[l];
+      if constexpr (decltype(tail)::value) {
+        if (k0 + a_kel[l] >= K) v = kOOB;
+      }
+      load_lds16(rsrc_a, lds + (wave * C::A_LOADS + l) * 1024, v, (uint32_t)(k0 * 2));
+    } else {
+      const int j = l - C::A_LOADS;
+      load_lds16(rb, lds + C::A_BYTES + (wave * C::B_LOADS + j) * 1024, b_voff[j], 0u);
+    }
+  };
+  auto issue_step = [&](int kt, uint32_t lds) {
+    const i32x4 rb = w_rsrc(kt);
+    if ((int64_t)(kt + 1) * kBK > K) {
+#pragma unroll
+      for (int l = 0; l < C::LOADS; ++l) issue_one(std::true_type{}, kt, lds, rb, l);
+    } else {
+#pragma unroll
+      for (int l = 0; l < C::LOADS; ++l) issue_one(std::false_type{}, kt, lds, rb, l);
+    }
+  };
+  auto lds_addr = [](const uint8_t* stage) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)stage;
+  };
 
   f32x16 acc[C::FM][C::FN];
 #pragma unroll
@@ -169,109 +311,148 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(Plan p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  uint4 ra[C::A_CH];
-  WRegs<C::KB> rb;
-  const int a_c = tid & 7;            // A: 16-byte chunk of the 128-byte K run
-  const int a_r = tid >> 3;           // A: first row (then +32 per chunk)
-  const int b_nb = tid % C::NBLK;     // W: 8-column block
-  const int b_kg = tid / C::NBLK;     // W: group of KB consecutive k rows
+  const int lr = lane & 31, lh = lane >> 5;
+  const int g16 = lane >> 4, i16 = lane & 15;
 
-  auto load_global = [&](int kt) {
-    const int64_t k0 = (int64_t)kt * kBK;
-#pragma unroll
-    for (int i = 0; i < C::A_CH; ++i) {
-      const int r = a_r + 32 * i;
-      const int64_t k = k0 + a_c * 8;
-      if (r < rows_valid && k < K)
-        ra[i] = *(const uint4*)(A + (int64_t)r * K + k);
-      else
-        ra[i] = make_uint4(0, 0, 0, 0);
-    }
-    const int64_t n = col0 + b_nb * 8;
-#pragma unroll
-    for (int j = 0; j < C::KB; ++j) {
-      const int64_t k = k0 + b_kg * C::KB + j;
-      if (k < K && n < N)
-        rb.r[j] = *(const uint4*)(B + k * N + b_nb * 8);
-      else
-        rb.r[j] = make_uint4(0, 0, 0, 0);
-    }
+  struct Frags {
+    bf16x8 a[C::FM], b[C::FN];
+  };
+  // fragment i of A / j of W for K-substep kk (16 values of k) of a stage
+  auto rd_a = [&](const uint8_t* stage, int kk, int i) {
+    const int r = wm * C::WTM + i * 32 + lr;
+    const int c = 2 * kk + lh;
+    return __builtin_bit_cast(bf16x8, *(const uint4*)(stage + r * 64 + ((c ^ swz_a(r)) << 4)));
+  };
+  auto rd_b = [&](const uint8_t* stage, int kk, int j) {
+    const uint8_t* sb = stage + C::A_BYTES;
+    const int kr = 16 * kk + 8 * (g16 >> 1) + (i16 >> 2);
+    const int n = wn * C::WTN + j * 32 + 16 * (g16 & 1) + 4 * (i16 & 3);
+    const int off = ((n >> 3) ^ swz_b(kr)) * 16 + ((n >> 2) & 1) * 8;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sb + kr * C::B_ROW + off));
+    const s16x4 hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sb + (kr + 4) * C::B_ROW + off));
+    const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+    return __builtin_bit_cast(bf16x8, make_uint4(l2.x, l2.y, h2.x, h2.y));
+  };
+  // fragment read number q of a Frags set (A fragments first)
+  auto rd_frag = [&](const uint8_t* stage, int kk, Frags& f, int q) {
+    if (q < C::FM)
+      f.a[q] = rd_a(stage, kk, q);
+    else
+      f.b[q - C::FM] = rd_b(stage, kk, q - C::FM);
+  };
+  auto mfma = [&](const Frags& f, int idx) {
+    const int i = idx / C::FN, j = idx % C::FN;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+  };
+  // this wave's loads of the oldest pending stage have landed when at most n later stages'
+  // loads are still in flight
+  auto wait_stages = [&](int n) {
+    if (n >= 3)
+      wait_vmcnt<3 * C::LOADS>();
+    else if (n == 2)
+      wait_vmcnt<2 * C::LOADS>();
+    else if (n == 1)
+      wait_vmcnt<C::LOADS>();
+    else
+      wait_vmcnt<0>();
+  };
+  // The workgroup barrier proper: no memory fence, so the prefetches issued before it stay in
+  // flight (every wave has already waited for its own loads of the stage it needs).
+  auto barrier = [&]() {
+    // lgkmcnt(0): this wave's LDS reads are done; the "memory" clobber keeps the compiler from
+    // moving LDS accesses across the barrier
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
 
-  auto store_lds = [&](int stage) {
-    uint8_t* sa = smem + stage * C::LDS_STAGE;
-    uint8_t* sb = sa + C::LDS_A;
+  constexpr int NMFMA = C::FM * C::FN, NREAD = C::FM + C::FN;
+  // Software pipeline over K steps of kBK; stage kt % 4 holds step kt. A step runs its MFMAs in
+  // two halves (K-substeps 0 and 1). The first half's fragments are already in registers; while
+  // its MFMAs issue, the second half's fragments are read. Then, once every wave holds the next
+  // stage and nobody reads this one any more (barrier), the second half's MFMAs issue
+  // interleaved with the loads that refill this stage with step kt + 4 and with the reads of the
+  // next step's first-half fragments. The order inside each half is pinned with scheduling
+  // barriers so that memory instructions issue under running MFMAs.
+  const int KT = uni((int)((K + kBK - 1) / kBK));
+  const int KFULL = uni((int)(K / kBK));  // steps that lie entirely inside K
+  Frags f0, f1;
+  if (KT > 0) {
+    issue_step(0, lds_addr(st0));
+    if (1 < KT) issue_step(1, lds_addr(st1));
+    if (2 < KT) issue_step(2, lds_addr(st2));
+    if (3 < KT) issue_step(3, lds_addr(st3));
+    wait_stages(KT - 1 < 3 ? KT - 1 : 3);
+    barrier();
 #pragma unroll
-    for (int i = 0; i < C::A_CH; ++i) {
-      const int r = a_r + 32 * i;
-      *(uint4*)(sa + r * 128 + ((a_c ^ swz(r)) << 4)) = ra[i];
-    }
-    // transpose the KB x 8 block of W: column e of the block becomes a K-run of row n.
-    // dword d of row j holds columns 2d (low half) and 2d+1 (high half)
-    const int kbyte = b_kg * C::KB * 2;         // byte offset of this K-run in the 128-byte row
-    const int chunk = kbyte >> 4, intra = kbyte & 15;
+    for (int q = 0; q < NREAD; ++q) rd_frag(st0, 0, f0, q);
+  }
+  constexpr int NX1 = NMFMA > NREAD ? NMFMA : NREAD;
+  constexpr int NX2 = NMFMA > C::LOADS ? (NMFMA > NREAD ? NMFMA : NREAD)
+                                       : (C::LOADS > NREAD ? C::LOADS : NREAD);
+  // first half of step kt: MFMAs of f0 with the reads of f1 under them
+  auto first_half = [&](const uint8_t* cur) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int n = b_nb * 8 + e;
-      uint32_t o[C::KB / 2];
-#pragma unroll
-      for (int q = 0; q < C::KB / 2; ++q) {
-        const uint32_t lo = dword_of(rb.r[2 * q], e >> 1);
-        const uint32_t hi = dword_of(rb.r[2 * q + 1], e >> 1);
-        o[q] = (e & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-      }
-      uint8_t* dst = sb + n * 128 + ((chunk ^ swz(n)) << 4) + intra;
-      if constexpr (C::KB == 8)
-        *(uint4*)dst = make_uint4(o[0], o[1], o[2], o[3]);
-      else if constexpr (C::KB == 4)
-        *(uint2*)dst = make_uint2(o[0], o[1]);
-      else
-        *(uint32_t*)dst = o[0];
-    }
-  };
-
-  auto compute = [&](int stage) {
-    const uint8_t* sa = smem + stage * C::LDS_STAGE;
-    const uint8_t* sb = sa + C::LDS_A;
-    const int lr = lane & 31, lh = lane >> 5;
-#pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      const int c = 2 * kk + lh;
-      bf16x8 af[C::FM], bfr[C::FN];
-#pragma unroll
-      for (int i = 0; i < C::FM; ++i) {
-        const int r = wm * C::WTM + i * 32 + lr;
-        af[i] = __builtin_bit_cast(bf16x8, *(const uint4*)(sa + r * 128 + ((c ^ swz(r)) << 4)));
-      }
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j) {
-        const int n = wn * C::WTN + j * 32 + lr;
-        bfr[j] = __builtin_bit_cast(bf16x8, *(const uint4*)(sb + n * 128 + ((c ^ swz(n)) << 4)));
-      }
-#pragma unroll
-      for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    for (int x = 0; x < NX1; ++x) {
+      if (x < NMFMA) mfma(f0, x);
+      if (x < NREAD) rd_frag(cur, 1, f1, x);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
-
-  const int KT = (int)((K + kBK - 1) / kBK);
-  load_global(0);
-  store_lds(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) load_global(kt + 1);
-    compute(cur);
-    if (kt + 1 < KT) store_lds(cur ^ 1);
-    __syncthreads();
+  // Steady-state step: stage kt is refilled with step kt + 4, which lies entirely inside K.
+  auto step_main = [&](int kt, const uint8_t* cur, const uint8_t* nxt) {
+    first_half(cur);
+    wait_stages(2);
+    barrier();
+    const uint32_t cur_lds = lds_addr(cur);
+    const i32x4 rb = w_rsrc(kt + 4);
+#pragma unroll
+    for (int x = 0; x < NX2; ++x) {
+      if (x < NMFMA) mfma(f1, x);
+      if (x < C::LOADS) issue_one(std::false_type{}, kt + 4, cur_lds, rb, x);
+      if (x < NREAD) rd_frag(nxt, 0, f0, x);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // Any step (start-up, last steps, K tail), with the conditions checked at run time.
+  auto step_any = [&](int kt, const uint8_t* cur, const uint8_t* nxt) {
+    first_half(cur);
+    const int later = KT - 2 - kt;  // steps issued beyond kt + 1 (at most 2 at this point)
+    wait_stages(later < 0 ? 0 : (later > 2 ? 2 : later));
+    barrier();
+    const bool refill = kt + 4 < KT, tail = kt + 4 >= KFULL, more = kt + 1 < KT;
+    const uint32_t cur_lds = lds_addr(cur);
+    i32x4 rb{};
+    if (refill) rb = w_rsrc(kt + 4);
+#pragma unroll
+    for (int x = 0; x < NX2; ++x) {
+      if (x < NMFMA) mfma(f1, x);
+      if (x < C::LOADS && refill) {
+        if (tail)
+          issue_one(std::true_type{}, kt + 4, cur_lds, rb, x);
+        else
+          issue_one(std::false_type{}, kt + 4, cur_lds, rb, x);
+      }
+      if (x < NREAD && more) rd_frag(nxt, 0, f0, x);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  int kt = 0;
+  for (; kt + 8 <= KFULL; kt += 4) {
+    step_main(kt, st0, st1);
+    step_main(kt + 1, st1, st2);
+    step_main(kt + 2, st2, st3);
+    step_main(kt + 3, st3, st0);
+  }
+  for (; kt < KT; kt += 4) {
+    step_any(kt, st0, st1);
+    if (kt + 1 < KT) step_any(kt + 1, st1, st2);
+    if (kt + 2 < KT) step_any(kt + 2, st2, st3);
+    if (kt + 3 < KT) step_any(kt + 3, st3, st0);
   }
 
   // ---- epilogue -------------------------------------------------------------------------
   const bool accum = (pos == p.accum_pos);
   if (accum) wait_flags_wg(p, p.recv_flag, p.n_recv);
-  const int lr = lane & 31, lh = lane >> 5;
 #pragma unroll
   for (int i = 0; i < C::FM; ++i) {
 #pragma unroll

@@ -31,33 +31,23 @@ int slice_order(int kind, int order, int P, int rank, int32_t* out) {
   return 1;
 }
 
-TileShape tile_shape(int tile);
-
-// Estimated relative cost of one call: rounds of workgroups over the CUs times the work of one
-// tile, divided by how efficiently that tile shape feeds the MFMAs (larger wave tiles reuse each
-// LDS fragment more often). Rows of a tile never cross a slice.
+// AUTO tile choice. 256x256 tiles need the fewest operand bytes per MFMA and win when the grid
+// covers the CUs several times over. When it is at most a few rounds and the last round is only
+// partly filled, 128x256 tiles (half the rounds' granularity) finish sooner. Slices shorter than
+// 256 rows use 128-row tiles, and very small problems fall back to 64x64. Rows of a tile never
+// cross a slice.
 int choose_tile(int P, int64_t m, int64_t N, int n_cu) {
-  struct Cand {
-    int tile;
-    double eff;
+  auto tiles = [&](int bm, int bn) {
+    return (double)P * (double)((m + bm - 1) / bm) * (double)((N + bn - 1) / bn);
   };
-  static const Cand cands[] = {
-      {FO_TILE_256x256, 1.00}, {FO_TILE_256x128, 0.85}, {FO_TILE_128x256, 0.85},
-      {FO_TILE_128x128, 0.60}, {FO_TILE_64x64, 0.20}};
-  int best = FO_TILE_64x64;
-  double best_cost = 1e300;
-  for (const Cand& c : cands) {
-    const TileShape ts = tile_shape(c.tile);
-    const int64_t tm = (m + ts.bm - 1) / ts.bm, tn = (N + ts.bn - 1) / ts.bn;
-    const int64_t tiles = (int64_t)P * tm * tn;
-    const int64_t rounds = (tiles + n_cu - 1) / n_cu;
-    const double cost = (double)rounds * ts.bm * ts.bn / c.eff;
-    if (cost < best_cost * 0.999) {
-      best_cost = cost;
-      best = c.tile;
-    }
-  }
-  return best;
+  if (m <= 64 || N <= 64) return FO_TILE_64x64;
+  if (m <= 128) return N >= 256 ? FO_TILE_128x256 : FO_TILE_128x128;
+  if (N < 256) return FO_TILE_256x128;
+  const double r256 = tiles(256, 256) / n_cu;
+  if (r256 >= 3.0) return FO_TILE_256x256;
+  const double partial = (double)(int64_t)(r256 + 0.999999) - r256;
+  if (partial > 0.1) return FO_TILE_128x256;
+  return FO_TILE_256x256;
 }
 
 }  // namespace fo

@@ -20,9 +20,11 @@ ARR_DEFAULT, ARR_NONE, ARR_EAGER, ARR_LOCKSTEP = 0, 1, 2, 3
 COPY_SDMA, COPY_BLIT = 0, 1
 TILE_AUTO, TILE_256x256, TILE_256x128, TILE_128x256, TILE_128x128, TILE_64x64 = range(6)
 MAX_P = 32
+MAX_LANES = 8
 
-EXPORTS = ("fo_opts_init", "fo_ag_gemm", "fo_gemm_rs", "fo_gemm_ref", "fo_check",
-           "fo_slice_order", "fo_tile_info", "fo_status_str", "fo_last_error", "fo_version")
+EXPORTS = ("fo_opts_init", "fo_ag_gemm", "fo_gemm_rs", "fo_gemm_ref", "fo_transfer_ref",
+           "fo_check", "fo_slice_order", "fo_tile_info", "fo_status_str", "fo_last_error",
+           "fo_version")
 
 
 class FoError(RuntimeError):
@@ -34,7 +36,8 @@ class FoError(RuntimeError):
 class Opts(ctypes.Structure):
     _fields_ = [("order", ctypes.c_int32), ("arrival", ctypes.c_int32),
                 ("copy_engine", ctypes.c_int32), ("tile", ctypes.c_int32),
-                ("spin_timeout_us", ctypes.c_uint32), ("reserved", ctypes.c_int32 * 3)]
+                ("spin_timeout_us", ctypes.c_uint32), ("copy_lanes", ctypes.c_int32),
+                ("kernel_events", ctypes.c_void_p * 2), ("reserved", ctypes.c_int32 * 2)]
 
 
 _lib = None
@@ -59,6 +62,7 @@ def load():
     lib.fo_ag_gemm.argtypes = [vp, vp, vp, vp, vp, i32, i32, i64, i64, i64, i32, i32, vp, vp, op]
     lib.fo_gemm_rs.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i64, i64, i64, i32, vp, vp, op]
     lib.fo_gemm_ref.argtypes = [vp, vp, vp, i64, i64, i64, i32, i32, i32, vp]
+    lib.fo_transfer_ref.argtypes = [i32, vp, vp, i32, i32, i64, vp, op]
     lib.fo_check.argtypes = [vp]
     lib.fo_slice_order.argtypes = [i32, i32, i32, i32, ctypes.POINTER(i32)]
     lib.fo_tile_info.argtypes = [i32, i64, i64, i64, i32, i32, ctypes.POINTER(i32),
@@ -68,7 +72,8 @@ def load():
     lib.fo_last_error.argtypes = []
     lib.fo_last_error.restype = ctypes.c_char_p
     lib.fo_version.argtypes = []
-    for f in ("fo_ag_gemm", "fo_gemm_rs", "fo_gemm_ref", "fo_check", "fo_slice_order",
+    for f in ("fo_ag_gemm", "fo_gemm_rs", "fo_gemm_ref", "fo_transfer_ref", "fo_check",
+              "fo_slice_order",
               "fo_tile_info", "fo_version"):
         getattr(lib, f).restype = ctypes.c_int32
     _lib = lib
@@ -88,13 +93,24 @@ def _raise_on(status: int, where: str) -> None:
 
 
 def opts(order=ORDER_FLASH, arrival=ARR_DEFAULT, copy_engine=COPY_SDMA, tile=TILE_AUTO,
-         spin_timeout_us=0) -> Opts:
+         spin_timeout_us=0, copy_lanes=0, kernel_events=None) -> Opts:
     o = Opts()
     load().fo_opts_init(ctypes.byref(o))
     o.order, o.arrival, o.copy_engine, o.tile = order, arrival, copy_engine, tile
+    o.copy_lanes = copy_lanes
     if spin_timeout_us:
         o.spin_timeout_us = spin_timeout_us
+    if kernel_events is not None:
+        o.kernel_events[0] = _event(kernel_events[0])
+        o.kernel_events[1] = _event(kernel_events[1])
     return o
+
+
+def _event(e) -> int | None:
+    """hipEvent_t of a torch.cuda.Event (or a raw handle)."""
+    if e is None or isinstance(e, int):
+        return e
+    return e.cuda_event
 
 
 def _ptr(t) -> int | None:
@@ -174,6 +190,19 @@ def gemm_ref(a, b, c, tile: int = TILE_AUTO, stream=None, raw: bool = False):
     if raw:
         return st
     _raise_on(st, "fo_gemm_ref")
+    return st
+
+
+def transfer_ref(kind: str, src, dst, P: int, rank: int, slice_bytes: int, stream=None,
+                 o: Opts | None = None, raw: bool = False):
+    """The emulated transfers of one call alone (fo_transfer_ref)."""
+    arr = _ptr_array(src)
+    st = load().fo_transfer_ref(0 if kind == "ag" else 1, ctypes.cast(arr, ctypes.c_void_p),
+                                _ptr(dst), P, rank, slice_bytes, _stream(stream),
+                                ctypes.byref(o) if o is not None else None)
+    if raw:
+        return st
+    _raise_on(st, "fo_transfer_ref")
     return st
 
 

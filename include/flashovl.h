@@ -24,8 +24,9 @@
  *     are [rows, N]. bf16 is the IEEE binary32 upper half; accumulation is fp32.
  *   - Device pointers are device memory on the current HIP device. Arrays "of P pointers" are
  *     host arrays of device pointers. The caller owns every buffer; the library never frees
- *     caller memory. Device pointers must be 16-byte aligned; K and N must be multiples of 8
- *     (bf16) or 4 (fp32); the slice height m may be any positive value.
+ *     caller memory. bf16 operands must be 16-byte aligned with K and N multiples of 8; fp32
+ *     buffers must be 4-byte aligned; the slice height m may be any value >= 0 (0: nothing to
+ *     do) and K may be 0 (empty sums).
  *   - Streams are hipStream_t passed as void*. NULL compute stream = the null stream; NULL copy
  *     stream = a library-owned stream. Calls are stream-ordered and return after enqueueing; the
  *     copy stream is joined back into the compute stream, so synchronizing the compute stream is
@@ -93,16 +94,24 @@ typedef enum fo_tile {
   FO_TILE_64x64 = 5
 } fo_tile;
 
+#define FO_MAX_LANES 8 /* most copy streams one emulated transfer is striped over */
+
 typedef struct fo_opts {
   int32_t order;            /* fo_order */
   int32_t arrival;          /* fo_arrival */
   int32_t copy_engine;      /* fo_copy_engine */
   int32_t tile;             /* fo_tile */
   uint32_t spin_timeout_us; /* bound of each in-kernel wait; 0 = 2 000 000 us */
-  int32_t reserved[3];      /* must be zero */
+  int32_t copy_lanes;       /* 1..FO_MAX_LANES: each transfer is split into this many contiguous
+                               pieces copied concurrently on separate streams (several copy
+                               engines, like several links); 0 = 1 */
+  void* kernel_events[2];   /* optional hipEvent_t pair recorded on the compute stream right
+                               before and right after the GEMM kernel launch (profiling) */
+  int32_t reserved[2];      /* must be zero */
 } fo_opts;
 
-/* Fills *o with the defaults (FLASH order, DEFAULT arrival, SDMA, AUTO tile, 2 s bound). */
+/* Fills *o with the defaults (FLASH order, DEFAULT arrival, SDMA, AUTO tile, 2 s bound, one
+   lane, no events). */
 void fo_opts_init(fo_opts* o);
 
 /*
@@ -115,8 +124,8 @@ void fo_opts_init(fo_opts* o);
  *   w        device [K, N] in_dt, this rank's column shard of the weight.
  *   y        device [P*m, N] out_dt; rows s*m .. s*m+m-1 hold X_s . W.
  * Slices are computed in the Flash-AG order (rank, rank-1, ..., rank-P+1 mod P); slice s != rank
- * is read only after its arrival flag is raised. in_dt: BF16 or F32 (F32 requires out_dt F32).
- * out_dt BF16 rounds the fp32 accumulator to nearest-even. No output aliases an input.
+ * is read only after its arrival flag is raised. in_dt and out_dt: BF16 or F32; out_dt BF16
+ * rounds the fp32 accumulator to nearest-even. No output may overlap an input.
  */
 fo_status fo_ag_gemm(const void* x_local, const void* const* x_peer, void* x_recv, const void* w,
                      void* y, int32_t P, int32_t rank, int64_t m, int64_t K, int64_t N,
@@ -151,6 +160,19 @@ fo_status fo_gemm_rs(const void* x_shard, const void* w, float* send_buf, float*
  */
 fo_status fo_gemm_ref(const void* a, const void* b, void* c, int64_t M, int64_t K, int64_t N,
                       int32_t in_dt, int32_t out_dt, int32_t tile, void* stream);
+
+/*
+ * The emulated transfers of one fo_ag_gemm (kind 0) or fo_gemm_rs (kind 1) call on their own,
+ * without the GEMM: the same copies, engine, lanes and arrival order, issued back to back on
+ * `stream` (RS releases are not awaited, no flag is raised). Its duration is the transfer time
+ * of the exposed-transfer fraction (sliced latency minus pure-GEMM latency, over transfer time).
+ *   src    host array of P device pointers; src[s] is slice s (slice_bytes bytes). Entry [rank]
+ *          is ignored.
+ *   dst    device buffer of P*slice_bytes bytes; slice s lands at dst + s*slice_bytes.
+ * opts: order, copy_engine and copy_lanes are used. slice_bytes must be a multiple of 4.
+ */
+fo_status fo_transfer_ref(int32_t kind, const void* const* src, void* dst, int32_t P,
+                          int32_t rank, int64_t slice_bytes, void* stream, const fo_opts* opts);
 
 /* Synchronizes `stream` (hipStream_t) and reports FO_ERR_TIMEOUT if any in-kernel wait on the
    current device ran past its bound since the previous fo_check (the record is then cleared). */

@@ -47,7 +47,9 @@ def test_opts_defaults():
     o = fo.opts()
     assert (o.order, o.arrival, o.copy_engine, o.tile) == (0, 0, 0, 0)
     assert o.spin_timeout_us == 2_000_000
-    assert list(o.reserved) == [0, 0, 0]
+    assert o.copy_lanes == 0 and list(o.kernel_events) == [None, None]
+    assert list(o.reserved) == [0, 0]
+    assert ctypes.sizeof(fo.Opts) == 48
 
 
 @pytest.mark.parametrize("P", list(range(1, 33)))
@@ -75,10 +77,12 @@ def test_slice_order_rejects(lib):
 
 
 def test_tile_choice_for_the_workloads():
-    # tiles never cross a slice; the 70B and 405B shares use 256x256 tiles
-    assert fo.tile_info(8, 512, 8192, 7168)[:2] == (256, 256)
+    # tiles never cross a slice. 70B gate+up: 448 tiles of 256x256 leave the second round a
+    # quarter empty, so 128x256; 70B down: exactly two rounds of 256x256; 405B: many rounds
+    assert fo.tile_info(8, 512, 8192, 7168)[:2] == (128, 256)
     assert fo.tile_info(8, 512, 3584, 8192)[:2] == (256, 256)
     assert fo.tile_info(8, 1024, 16384, 13312)[:2] == (256, 256)
+    assert fo.tile_info(8, 1024, 6656, 16384)[:2] == (256, 256)
     bm, bn, wg = fo.tile_info(8, 128, 8192, 7168)       # M = 1024: slices of 128 rows
     assert bm == 128 and wg == 8 * (7168 // bn)
     assert fo.tile_info(4, 64, 256, 512, fo.F32)[:2] == (64, 64)
@@ -121,7 +125,8 @@ def test_ag_rejects(lib, kw):
 
 
 def test_ag_rejects_bad_opts(lib):
-    for field, val in [("order", 9), ("arrival", 7), ("copy_engine", 3), ("tile", 11)]:
+    for field, val in [("order", 9), ("arrival", 7), ("copy_engine", 3), ("tile", 11),
+                       ("copy_lanes", 9), ("copy_lanes", -1)]:
         o = fo.opts()
         setattr(o, field, val)
         assert _ag(lib, opts=ctypes.byref(o)) == fo.FO_ERR_INVALID_ARG
@@ -165,6 +170,17 @@ def test_rs_rejects(lib, kw):
 def test_rs_natural_order_unsupported(lib):
     o = fo.opts(order=fo.ORDER_NATURAL)
     assert _rs(lib, opts=ctypes.byref(o)) == fo.FO_ERR_UNSUPPORTED
+
+
+def test_transfer_ref_rejects(lib):
+    src = (ctypes.c_void_p * 4)(0x50000000, 0x60000000, 0x70000000, 0x78000000)
+    ps = ctypes.cast(src, ctypes.c_void_p)
+    assert lib.fo_transfer_ref(2, ps, B, 4, 0, 4096, None, None) == fo.FO_ERR_INVALID_ARG
+    assert lib.fo_transfer_ref(0, ps, B, 4, 4, 4096, None, None) == fo.FO_ERR_INVALID_ARG
+    assert lib.fo_transfer_ref(0, ps, B, 4, 0, 4098, None, None) == fo.FO_ERR_INVALID_ARG
+    assert lib.fo_transfer_ref(0, None, B, 4, 0, 4096, None, None) == fo.FO_ERR_INVALID_ARG
+    assert lib.fo_transfer_ref(0, ps, 0x60000000 - 8192, 4, 0, 4096, None, None) == fo.FO_ERR_INVALID_ARG
+    assert lib.fo_transfer_ref(0, ps, B, 4, 0, 0, None, None) == fo.FO_OK
 
 
 def test_ref_rejects(lib):
