@@ -53,16 +53,20 @@ fo_status invalid(const char* fmt, ...) {
 constexpr int kMaxDevices = 64;
 constexpr uint32_t kDefaultTimeoutUs = 2000000u;
 
-// Library-owned objects of one device. Flags live in uncached device memory (written by the copy
-// stream, polled by kernels); release flags live in signal memory (written by kernels, waited on
-// by the copy stream). Both are allocated once and kept for the life of the process.
+// Library-owned objects of one device. Arrival flags live in uncached device memory, one 64 KiB
+// block per slice (flag = first word): the copy engine raises a flag by copying the `esrc`
+// block, which a one-workgroup kernel on the compute stream has filled with the call's epoch
+// before anything waits, so that no part of an arrival needs a compute unit (the waiting GEMM
+// may hold all of them). Release flags live in signal memory (written by kernels, waited on by
+// the copy stream). All are allocated once and kept for the life of the process.
 struct DevState {
   std::mutex mu;
   bool ready = false;
   int n_cu = 0;
   int wall_khz = 100000;     // wall-clock counter rate read by the kernels' bounded waits
-  uint32_t* arr = nullptr;   // [FO_MAX_P] arrival flags, then [1] timeout record
-  uint32_t* err = nullptr;
+  uint32_t* arr = nullptr;   // FO_MAX_P flag blocks of kFlagBytes
+  uint32_t* esrc = nullptr;  // kFlagBytes block holding the current epoch
+  uint32_t* err = nullptr;   // timeout record
   uint32_t* done = nullptr;  // [FO_MAX_P] completed-tile counters
   uint32_t* rel[FO_MAX_P] = {};
   uint32_t epoch = 0;
@@ -83,10 +87,12 @@ fo_status ensure_ready(int dev, DevState& st) {
   FO_HIP(hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev));
   if (khz > 0) st.wall_khz = khz;
   void* p = nullptr;
-  FO_HIP(hipExtMallocWithFlags(&p, 4096, hipDeviceMallocUncached));
+  const size_t flag_bytes = (size_t)(FO_MAX_P + 1) * fo::kFlagBytes + 4096;
+  FO_HIP(hipExtMallocWithFlags(&p, flag_bytes, hipDeviceMallocUncached));
   st.arr = (uint32_t*)p;
-  st.err = st.arr + FO_MAX_P;
-  FO_HIP(hipMemset(st.arr, 0, 4096));
+  st.esrc = st.arr + (size_t)FO_MAX_P * fo::kFlagStride;
+  st.err = st.esrc + fo::kFlagStride;
+  FO_HIP(hipMemset(p, 0, flag_bytes));
   FO_HIP(hipMalloc(&p, FO_MAX_P * sizeof(uint32_t)));
   st.done = (uint32_t*)p;
   FO_HIP(hipMemset(st.done, 0, FO_MAX_P * sizeof(uint32_t)));
@@ -96,8 +102,6 @@ fo_status ensure_ready(int dev, DevState& st) {
     FO_HIP(hipMemset(st.rel[i], 0, 8));
   }
   FO_HIP(hipStreamCreateWithFlags(&st.copy_stream, hipStreamNonBlocking));
-  for (int l = 0; l < FO_MAX_LANES - 1; ++l)
-    FO_HIP(hipStreamCreateWithFlags(&st.lane[l], hipStreamNonBlocking));
   for (int t = 0; t < FO_MAX_P; ++t) {
     FO_HIP(hipEventCreateWithFlags(&st.rel_ev[t], hipEventDisableTiming));
     for (int l = 0; l < FO_MAX_LANES; ++l)
@@ -206,10 +210,26 @@ hipMemcpyKind copy_kind(const fo_opts& o) {
 // epoch into that slice's arrival flag. With `rel`, transfer t first waits until the kernel has
 // raised rel[t] (lockstep release). `start` is the event the lanes wait on before their first
 // piece (already waited on by ks). Everything the lanes do is joined back into ks per transfer.
+// The extra lane streams are created on first use only: HIP maps streams onto a small number of
+// hardware queues per process, and every stream created beyond that number shares a queue with
+// an existing one, possibly the caller's compute stream, where copy work would then wait behind
+// the very kernel that is waiting for it.
+fo_status ensure_lanes(DevState& st, int lanes) {
+  for (int l = 0; l < lanes - 1; ++l)
+    if (!st.lane[l]) FO_HIP(hipStreamCreateWithFlags(&st.lane[l], hipStreamNonBlocking));
+  return FO_OK;
+}
+
 fo_status enqueue_transfers(DevState& st, hipStream_t ks, hipEvent_t start, const int* seq, int n,
                             const void* const* src, void* dst, size_t bytes, int lanes,
                             hipMemcpyKind kind, uint32_t epoch, bool flags, bool rel) {
+  // flags: raise the slice's arrival flag after its data (the flag takes the epoch from the esrc
+  // block, which the caller has filled with `epoch`)
   lanes = std::max(1, std::min(lanes, FO_MAX_LANES));
+  {
+    const fo_status s = ensure_lanes(st, lanes);
+    if (s != FO_OK) return s;
+  }
   // pieces are 256-byte aligned; fewer lanes when a transfer is small
   const size_t unit = 256;
   size_t piece = ((bytes + lanes - 1) / lanes + unit - 1) / unit * unit;
@@ -235,7 +255,9 @@ fo_status enqueue_transfers(DevState& st, hipStream_t ks, hipEvent_t start, cons
     }
     FO_HIP(hipMemcpyAsync(d, sp, std::min(piece, bytes), kind, ks));
     for (int l = 1; l < used; ++l) FO_HIP(hipStreamWaitEvent(ks, st.lane_ev[t][l], 0));
-    if (flags) FO_HIP(hipStreamWriteValue32(ks, st.arr + sl, epoch, 0));
+    if (flags)
+      FO_HIP(hipMemcpyAsync(st.arr + (size_t)sl * fo::kFlagStride, st.esrc, fo::kFlagBytes,
+                            hipMemcpyDeviceToDeviceNoCU, ks));
   }
   return FO_OK;
 }
@@ -254,10 +276,21 @@ int arrival_sequence(int kind, int order, int P, int rank, int* seq) {
   return n;
 }
 
+// When an arrival needs a compute unit (copy kernels as the transfer engine, or the copy
+// stream's waits on the RS release flags), the GEMM keeps a few CUs free: a persistent grid of
+// n_cu - 8 workgroups (a multiple of 8, so tile-to-XCD placement is kept). Otherwise tiles
+// waiting for a slice could occupy every CU while the work that delivers the slice waits for
+// one. DMA copies and flag copies need no CU, so the SDMA path uses one workgroup per tile.
+int grid_cap(const DevState& st, const fo_opts& o, bool arrivals, bool lockstep) {
+  if (!arrivals || (o.copy_engine != FO_COPY_BLIT && !lockstep)) return 0;
+  const int cap = (st.n_cu - 8) / 8 * 8;
+  return cap > 0 ? cap : 8;
+}
+
 fo_status launch_with_events(const fo::Plan& p, int in_dt, int tile, hipStream_t cs,
-                             const fo_opts& o) {
+                             const fo_opts& o, int max_grid) {
   if (o.kernel_events[0]) FO_HIP(hipEventRecord((hipEvent_t)o.kernel_events[0], cs));
-  FO_HIP(fo::launch_gemm(p, in_dt, tile, cs));
+  FO_HIP(fo::launch_gemm(p, in_dt, tile, max_grid, cs));
   if (o.kernel_events[1]) FO_HIP(hipEventRecord((hipEvent_t)o.kernel_events[1], cs));
   return FO_OK;
 }
@@ -406,6 +439,7 @@ fo_status fo_ag_gemm(const void* x_local, const void* const* x_peer, void* x_rec
   if (st->have_last) FO_HIP(hipStreamWaitEvent(cs, st->ev_last, 0));
   if (arrivals) {
     // the copies are enqueued before the kernel so that they start together with it
+    FO_HIP(fo::launch_stamp(st->esrc, epoch, cs));
     FO_HIP(hipEventRecord(st->ev_start, cs));
     FO_HIP(hipStreamWaitEvent(ks, st->ev_start, 0));
     int seq[FO_MAX_P];
@@ -414,7 +448,7 @@ fo_status fo_ag_gemm(const void* x_local, const void* const* x_peer, void* x_rec
                           copy_kind(o), epoch, true, false);
     if (s != FO_OK) return s;
   }
-  s = launch_with_events(p, in_dt, tile, cs, o);
+  s = launch_with_events(p, in_dt, tile, cs, o, grid_cap(*st, o, arrivals, false));
   if (s != FO_OK) return s;
   if (arrivals) {
     FO_HIP(hipEventRecord(st->ev_copy, ks));
@@ -515,10 +549,13 @@ fo_status fo_gemm_rs(const void* x_shard, const void* w, float* send_buf, float*
   hipStream_t cs = (hipStream_t)compute_stream;
   hipStream_t ks = copy_stream ? (hipStream_t)copy_stream : st->copy_stream;
   if (st->have_last) FO_HIP(hipStreamWaitEvent(cs, st->ev_last, 0));
-  if (arrivals) FO_HIP(hipEventRecord(st->ev_start, cs));
+  if (arrivals) {
+    FO_HIP(fo::launch_stamp(st->esrc, epoch, cs));
+    FO_HIP(hipEventRecord(st->ev_start, cs));
+  }
   // the kernel is enqueued before the copy stream's waits on its release flags, so a failed
   // launch never leaves the copy stream waiting for a flag that nobody raises
-  s = launch_with_events(p, in_dt, tile, cs, o);
+  s = launch_with_events(p, in_dt, tile, cs, o, grid_cap(*st, o, arrivals, lockstep));
   if (s != FO_OK) return s;
   if (arrivals) {
     FO_HIP(hipStreamWaitEvent(ks, st->ev_start, 0));
@@ -585,7 +622,7 @@ fo_status fo_gemm_ref(const void* a, const void* b, void* c, int64_t M, int64_t 
   p.out_f32 = out_dt == FO_DT_F32;
   p.epoch = st->epoch;
   hipStream_t cs = (hipStream_t)stream;
-  FO_HIP(fo::launch_gemm(p, in_dt, t, cs));
+  FO_HIP(fo::launch_gemm(p, in_dt, t, 0, cs));
   return FO_OK;
 }
 

@@ -52,7 +52,7 @@ __device__ __forceinline__ void wait_flag(const uint32_t* flag, uint32_t epoch, 
 __device__ __forceinline__ void wait_flags_wg(const Plan& p, const int32_t* ids, int n) {
   if (threadIdx.x == 0) {
     for (int i = 0; i < n; ++i)
-      if (ids[i] >= 0) wait_flag(p.arr + ids[i], p.epoch, p.spin_limit, p.err);
+      if (ids[i] >= 0) wait_flag(p.arr + (size_t)ids[i] * kFlagStride, p.epoch, p.spin_limit, p.err);
   }
   __syncthreads();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
@@ -133,6 +133,13 @@ __device__ __forceinline__ void store_fragment(const Plan& p, int pos, const f32
     else
       ((uint16_t*)p.c_pos[pos])[off] = to_bf16_rne(x[v]);
   }
+}
+
+// 16-byte streaming load (the partials are read once)
+__device__ __forceinline__ float4 ld_nt4(const float* p) {
+  typedef __attribute__((ext_vector_type(4))) float v4;
+  const v4 v = __builtin_nontemporal_load((const v4*)p);
+  return make_float4(v.x, v.y, v.z, v.w);
 }
 
 // ---------------------------------------------------------------- bf16 MFMA kernel ----------
@@ -217,12 +224,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 template <int BM, int BN>
-__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(Plan p) {
+__device__ __forceinline__ void bf16_tile(const Plan& p, const int tile, uint8_t* const lds_ring) {
   using C = Cfg<BM, BN>;
-  __shared__ __attribute__((aligned(1024))) uint8_t st0[C::STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t st1[C::STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t st2[C::STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t st3[C::STAGE];
+  uint8_t* const st0 = lds_ring;
+  uint8_t* const st1 = lds_ring + C::STAGE;
+  uint8_t* const st2 = lds_ring + 2 * C::STAGE;
+  uint8_t* const st3 = lds_ring + 3 * C::STAGE;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -231,9 +238,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(Plan p) {
   const int wm = wave >> 1, wn = wave & 1;
 
   const int T = p.tiles_m * p.tiles_n;
-  const int pos = uni(blockIdx.x / T);
+  const int pos = uni(tile / T);
   int tm_, tn_;
-  tile_coords(blockIdx.x - pos * T, T, p.tiles_m, p.tiles_n, tm_, tn_);
+  tile_coords(tile - pos * T, T, p.tiles_m, p.tiles_n, tm_, tn_);
   const int tm = uni(tm_), tn = uni(tn_);
 
   const int64_t K = p.K, N = p.N;
@@ -450,34 +457,112 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(Plan p) {
     if (kt + 3 < KT) step_any(kt + 3, st3, st0);
   }
 
-  // ---- epilogue -------------------------------------------------------------------------
+  // ---- epilogue ---------------------------------------------------------------------------
+  // The accumulators go through LDS (free now) in blocks of ER rows so that every global access
+  // is a row-contiguous 16-byte (fp32) or 8-byte (bf16) vector: output stores, and for the chunk
+  // that stays on the rank, the loads of the received partials, which are all issued before any
+  // of them is added (the adds keep the arrival order).
   const bool accum = (pos == p.accum_pos);
   if (accum) wait_flags_wg(p, p.recv_flag, p.n_recv);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // LDS stages no longer read
+  float* const ep = (float*)lds_ring;  // [ER rows][EW floats] over the whole ring
+  constexpr int EW = BN + 8;      // padded row: rows 4 apart land 32 banks apart
+  constexpr int ER = (BM * EW * 4 <= kStages * C::STAGE)         ? BM
+                     : (BM / 2 * EW * 4 <= kStages * C::STAGE)   ? BM / 2
+                                                                : BM / 4;
+  static_assert(ER * EW * 4 <= kStages * C::STAGE && ER % 32 == 0, "epilogue block");
+  constexpr int CPR = BN / 4;                   // 4-float chunks per row
+  constexpr int CPT = ER * CPR / kThreads;      // chunks per thread per block
+  static_assert(CPT >= 1 && (ER * CPR) % kThreads == 0, "epilogue chunks");
+  constexpr int BATCH = CPT < 4 ? CPT : 4;      // chunks whose partial loads are in flight together
 #pragma unroll
-  for (int i = 0; i < C::FM; ++i) {
+  for (int blk = 0; blk < BM / ER; ++blk) {
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j) {
-      const int64_t col = col0 + wn * C::WTN + j * 32 + lr;
-      const int64_t rbase = (int64_t)wm * C::WTM + i * 32 + 4 * lh;
-      store_fragment(p, pos, acc[i][j], row0, rbase, rows_valid, col, accum);
+    for (int i = 0; i < C::FM; ++i) {
+      const int fr = wm * C::WTM + i * 32;  // first tile row of fragment row i
+      if (fr < blk * ER || fr >= (blk + 1) * ER) continue;
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = fr - blk * ER + 8 * (v >> 2) + 4 * lh + (v & 3);
+          ep[r * EW + wn * C::WTN + j * 32 + lr] = acc[i][j][v];
+        }
     }
+    __syncthreads();
+#pragma unroll
+    for (int b0 = 0; b0 < CPT; b0 += BATCH) {
+      float4 x[BATCH];
+      int64_t off[BATCH];
+      bool ok[BATCH];
+#pragma unroll
+      for (int b = 0; b < BATCH; ++b) {
+        const int c = (b0 + b) * kThreads + tid;  // consecutive threads: consecutive chunks
+        const int r = c / CPR, cc = c % CPR;
+        const int64_t grow = row0 + blk * ER + r, gcol = col0 + cc * 4;
+        ok[b] = grow < p.m && gcol < N;
+        off[b] = grow * N + gcol;
+        x[b] = *(const float4*)(ep + r * EW + cc * 4);
+      }
+      if (accum) {
+        for (int q0 = 0; q0 < p.n_recv; q0 += 4) {
+          float4 t[4][BATCH];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int b = 0; b < BATCH; ++b)
+              t[q][b] = (q0 + q < p.n_recv && ok[b])
+                            ? ld_nt4(p.recv[q0 + q] + off[b])
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int b = 0; b < BATCH; ++b) {
+              x[b].x += t[q][b].x;
+              x[b].y += t[q][b].y;
+              x[b].z += t[q][b].z;
+              x[b].w += t[q][b].w;
+            }
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < BATCH; ++b) {
+        if (!ok[b]) continue;
+        if (p.out_f32) {
+          *(float4*)((float*)p.c_pos[pos] + off[b]) = x[b];
+        } else {
+          const uint32_t lo = (uint32_t)to_bf16_rne(x[b].x) | ((uint32_t)to_bf16_rne(x[b].y) << 16);
+          const uint32_t hi = (uint32_t)to_bf16_rne(x[b].z) | ((uint32_t)to_bf16_rne(x[b].w) << 16);
+          *(uint2*)((uint16_t*)p.c_pos[pos] + off[b]) = make_uint2(lo, hi);
+        }
+      }
+    }
+    __syncthreads();
   }
   release_tile(p, pos, T);
+}
+
+// One workgroup per tile, or (grid smaller than the tile count) a persistent grid whose
+// workgroups walk the tiles with a stride of the grid size, in the same order.
+template <int BM, int BN>
+__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(Plan p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_ring[kStages * Cfg<BM, BN>::STAGE];
+  const int total = p.npos * p.tiles_m * p.tiles_n;
+  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) bf16_tile<BM, BN>(p, tile, lds_ring);
 }
 
 // ---------------------------------------------------------------- fp32 kernel ----------------
 
 constexpr int F_BM = 64, F_BN = 64, F_BK = 16;
 
-__global__ __launch_bounds__(kThreads) void gemm_f32_kernel(Plan p) {
-  __shared__ float sa[F_BK][F_BM + 4];  // k-major so a thread's 4 rows are one broadcast read
-  __shared__ float sb[F_BK][F_BN + 4];
+__device__ __forceinline__ void f32_tile(const Plan& p, const int tile, float (*sa)[F_BM + 4],
+                                         float (*sb)[F_BN + 4]) {
   const int tid = threadIdx.x;
   const int tx = tid & 15, ty = tid >> 4;
 
   const int T = p.tiles_m * p.tiles_n;
-  const int pos = blockIdx.x / T;
-  const int t = blockIdx.x - pos * T;
+  const int pos = tile / T;
+  const int t = tile - pos * T;
   const int tm = t % p.tiles_m, tn = t / p.tiles_m;
   const int64_t K = p.K, N = p.N;
   const int64_t row0 = (int64_t)tm * F_BM, col0 = (int64_t)tn * F_BN;
@@ -534,14 +619,35 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(Plan p) {
   release_tile(p, pos, T);
 }
 
+__global__ __launch_bounds__(kThreads) void gemm_f32_kernel(Plan p) {
+  __shared__ float sa[F_BK][F_BM + 4];  // k-major so a thread's 4 rows are one broadcast read
+  __shared__ float sb[F_BK][F_BN + 4];
+  const int total = p.npos * p.tiles_m * p.tiles_n;
+  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+    f32_tile(p, tile, sa, sb);
+    __syncthreads();  // the next tile refills sa / sb
+  }
+}
+
 template <int BM, int BN>
-hipError_t launch_bf16(const Plan& p, hipStream_t s) {
-  const int64_t grid = (int64_t)p.npos * p.tiles_m * p.tiles_n;
+hipError_t launch_bf16(const Plan& p, int64_t grid, hipStream_t s) {
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN>), dim3((unsigned)grid), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
+// Fills the block the copy engine copies into each arrival-flag block with the call's epoch.
+__global__ __launch_bounds__(256) void stamp_kernel(uint32_t* block, uint32_t value) {
+  uint4* b = (uint4*)block;
+  const uint4 v = make_uint4(value, value, value, value);
+  for (int i = threadIdx.x; i < kFlagBytes / 16; i += blockDim.x) b[i] = v;
+}
+
 }  // namespace
+
+hipError_t launch_stamp(uint32_t* block, uint32_t value, hipStream_t s) {
+  hipLaunchKernelGGL(stamp_kernel, dim3(1), dim3(256), 0, s, block, value);
+  return hipGetLastError();
+}
 
 TileShape tile_shape(int tile) {
   switch (tile) {
@@ -554,18 +660,19 @@ TileShape tile_shape(int tile) {
   }
 }
 
-hipError_t launch_gemm(const Plan& p, int in_dt, int tile, hipStream_t s) {
+hipError_t launch_gemm(const Plan& p, int in_dt, int tile, int max_grid, hipStream_t s) {
+  int64_t grid = (int64_t)p.npos * p.tiles_m * p.tiles_n;
+  if (max_grid > 0 && grid > max_grid) grid = max_grid;
   if (in_dt == FO_DT_F32) {
-    const int64_t grid = (int64_t)p.npos * p.tiles_m * p.tiles_n;
     hipLaunchKernelGGL(gemm_f32_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
     return hipGetLastError();
   }
   switch (tile) {
-    case FO_TILE_256x256: return launch_bf16<256, 256>(p, s);
-    case FO_TILE_256x128: return launch_bf16<256, 128>(p, s);
-    case FO_TILE_128x256: return launch_bf16<128, 256>(p, s);
-    case FO_TILE_128x128: return launch_bf16<128, 128>(p, s);
-    case FO_TILE_64x64: return launch_bf16<64, 64>(p, s);
+    case FO_TILE_256x256: return launch_bf16<256, 256>(p, grid, s);
+    case FO_TILE_256x128: return launch_bf16<256, 128>(p, grid, s);
+    case FO_TILE_128x256: return launch_bf16<128, 256>(p, grid, s);
+    case FO_TILE_128x128: return launch_bf16<128, 128>(p, grid, s);
+    case FO_TILE_64x64: return launch_bf16<64, 64>(p, grid, s);
     default: return hipErrorInvalidValue;
   }
 }

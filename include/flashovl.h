@@ -37,6 +37,10 @@
  *     results are then unspecified.
  *   - Thread safety: entry points may be called from several host threads; each call holds a
  *     per-device lock while it enqueues.
+ *   - The copy stream must not share a hardware queue with the compute stream (HIP maps streams
+ *     onto a few hardware queues per process): work queued behind the GEMM kernel could not
+ *     deliver the slices that kernel waits for, and the call would end in FO_ERR_TIMEOUT. The
+ *     library creates one stream of its own at initialization (more only for copy_lanes > 1).
  */
 #ifndef FLASHOVL_H
 #define FLASHOVL_H
