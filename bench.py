@@ -68,8 +68,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--rank", type=int, default=0)
-    ap.add_argument("--engine", choices=["sdma", "blit"], default="sdma")
-    ap.add_argument("--lanes", type=int, default=0, help="copy lanes (0: library default)")
+    ap.add_argument("--links", type=int, default=0,
+                    help="emulated links per call (0: one DMA engine per peer; 1: one link)")
     ap.add_argument("--exposure-reps", type=int, default=15)
     ap.add_argument("--no-exposure", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -95,7 +95,6 @@ def main():
     torch.cuda.set_device(dev)
     fo.load()
     stream = torch.cuda.current_stream()
-    copy_stream = torch.cuda.Stream()
 
     ag_case, rs_case = configs.L70B_AG, configs.L70B_RS
     P, r = ag_case.P, args.rank
@@ -125,22 +124,18 @@ def main():
     torch.cuda.synchronize()
     log(f"inputs ready in {time.time() - t0:.1f} s")
 
-    engine = fo.COPY_SDMA if args.engine == "sdma" else fo.COPY_BLIT
-
     def ev():
         return torch.cuda.Event(enable_timing=True)
 
-    def ag_call(evs=None, arrival=fo.ARR_DEFAULT, eng=engine, lanes=args.lanes):
-        o = fo.opts(copy_engine=eng, copy_lanes=lanes, arrival=arrival, kernel_events=evs)
+    def ag_call(evs=None, arrival=fo.ARR_DEFAULT, links=args.links):
+        o = fo.opts(links=links, arrival=arrival, kernel_events=evs)
         peers = None if arrival == fo.ARR_NONE else ag_slices
-        fo.ag_gemm(ag_slices[r], peers, ag_recv, ag_w, ag_y, P, r, compute_stream=stream,
-                   copy_stream=copy_stream, o=o)
+        fo.ag_gemm(ag_slices[r], peers, ag_recv, ag_w, ag_y, P, r, compute_stream=stream, o=o)
 
-    def rs_call(evs=None, arrival=fo.ARR_DEFAULT, eng=engine, lanes=args.lanes):
-        o = fo.opts(copy_engine=eng, copy_lanes=lanes, arrival=arrival, kernel_events=evs)
+    def rs_call(evs=None, arrival=fo.ARR_DEFAULT, links=args.links):
+        o = fo.opts(links=links, arrival=arrival, kernel_events=evs)
         peers = None if arrival == fo.ARR_NONE else rs_peer
-        fo.gemm_rs(rs_x, rs_w, rs_send, rs_out, peers, rs_recv, P, r, compute_stream=stream,
-                   copy_stream=copy_stream, o=o)
+        fo.gemm_rs(rs_x, rs_w, rs_send, rs_out, peers, rs_recv, P, r, compute_stream=stream, o=o)
 
     def step(evs=None):
         ag_call(evs[0] if evs else None)
@@ -167,20 +162,21 @@ def main():
     if not args.no_exposure:
         exposure = {}
         reps = args.exposure_reps
-        variants = [("sdma_1lane", fo.COPY_SDMA, 1), ("sdma_4lane", fo.COPY_SDMA, 4),
-                    ("blit", fo.COPY_BLIT, 1)]
+        # one DMA engine per peer (the xGMI mesh), and every transfer over one link (the ring of
+        # the page's Flash-AG, where all slices come from one neighbour)
+        variants = [("mesh", 0), ("onelink", 1)]
         t_ref_ag = timed(lambda: fo.gemm_ref(ag_full, ag_w, ref_y_ag, stream=stream), reps)
         t_ref_rs = timed(lambda: fo.gemm_ref(rs_x, rs_w, ref_y_rs, stream=stream), reps)
         t0_ag = timed(lambda: ag_call(arrival=fo.ARR_NONE), reps)
         t0_rs = timed(lambda: rs_call(arrival=fo.ARR_NONE), reps)
-        for name, eng, lanes in variants:
-            to = fo.opts(copy_engine=eng, copy_lanes=lanes)
+        for name, links in variants:
+            to = fo.opts(links=links)
             tx_ag = timed(lambda: fo.transfer_ref("ag", ag_slices, ag_recv, P, r,
                                                   ag_case.m * ag_case.K * 2, stream, to), reps)
             tx_rs = timed(lambda: fo.transfer_ref("rs", rs_peer, rs_recv, P, r,
                                                   rs_case.m * rs_case.N * 4, stream, to), reps)
-            ts_ag = timed(lambda: ag_call(eng=eng, lanes=lanes), reps)
-            ts_rs = timed(lambda: rs_call(eng=eng, lanes=lanes), reps)
+            ts_ag = timed(lambda: ag_call(links=links), reps)
+            ts_rs = timed(lambda: rs_call(links=links), reps)
             exposure[name] = {
                 "ag": {"t_ref_us": t_ref_ag * 1e3, "t_slice0_us": t0_ag * 1e3,
                        "t_slice_us": ts_ag * 1e3, "t_xfer_us": tx_ag * 1e3,
@@ -248,7 +244,8 @@ def main():
         "config": {"workload": "Llama-3.1-70B MLP, one TP8 rank share (rank %d): Flash-AG "
                    "gate+up M=4096 K=8192 N=7168 + Flash-RS down M=4096 K=3584 N=8192, "
                    "P=8 slices" % r,
-                   "copy_engine": args.engine, "copy_lanes": args.lanes or 1,
+                   "transfers": "SDMA engines, %s" % ("one per peer" if args.links == 0
+                                                      else "%d link(s)" % args.links),
                    "ag_arrival": "eager", "rs_arrival": "lockstep"},
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "exposed_transfer": exposure,

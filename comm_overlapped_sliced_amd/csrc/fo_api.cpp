@@ -3,9 +3,12 @@
 // Flash-AG / Flash-RS as described on the FlashOverlap page (gist.science paper 2604.24013),
 // technical summary section 2: collectives split into point-to-point transfers, slices computed
 // in an order that hides them (local slice first for AG, own chunk last for RS), with per-slice
-// synchronisation instead of step barriers (section 3). On one GPU a transfer is emulated by a
-// device-to-device copy from a "peer" buffer on the copy stream, followed by a write of the call's
-// epoch into that slice's arrival flag; the GEMM kernel's tiles of that slice wait for the flag.
+// synchronisation instead of step barriers (section 3). On one GPU a transfer is emulated by an
+// SDMA copy from a "peer" buffer into the receive buffer (fo_dma.cpp); the GEMM kernel's tiles
+// of a slice wait for that copy's completion signal. Every call enqueues, on the compute stream:
+// a one-thread kernel that releases the call's copies, then the GEMM; the copies are issued to
+// the DMA engines after that, gated on the release (and, for Flash-RS in lockstep, on the GEMM's
+// step releases).
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
 
@@ -50,31 +53,31 @@ fo_status invalid(const char* fmt, ...) {
     }                                                                             \
   } while (0)
 
+// a DMA-layer call that reports failure through a message
+#define FO_DMA(call)                                                              \
+  do {                                                                            \
+    std::string e_;                                                               \
+    if (!(call)) {                                                                \
+      set_error("%s", e_.c_str());                                                \
+      return FO_ERR_HIP;                                                          \
+    }                                                                             \
+  } while (0)
+
 constexpr int kMaxDevices = 64;
 constexpr uint32_t kDefaultTimeoutUs = 2000000u;
+constexpr size_t kScratchBytes = 2 * 65536;
 
-// Library-owned objects of one device. Arrival flags live in uncached device memory, one 64 KiB
-// block per slice (flag = first word): the copy engine raises a flag by copying the `esrc`
-// block, which a one-workgroup kernel on the compute stream has filled with the call's epoch
-// before anything waits, so that no part of an arrival needs a compute unit (the waiting GEMM
-// may hold all of them). Release flags live in signal memory (written by kernels, waited on by
-// the copy stream). All are allocated once and kept for the life of the process.
+// Library-owned objects of one device, allocated once and kept for the life of the process.
 struct DevState {
   std::mutex mu;
   bool ready = false;
+  int dev = 0;
   int n_cu = 0;
   int wall_khz = 100000;     // wall-clock counter rate read by the kernels' bounded waits
-  uint32_t* arr = nullptr;   // FO_MAX_P flag blocks of kFlagBytes
-  uint32_t* esrc = nullptr;  // kFlagBytes block holding the current epoch
-  uint32_t* err = nullptr;   // timeout record
+  uint32_t* err = nullptr;   // wait record: 1 timeout, 2 failed copy (uncached memory)
   uint32_t* done = nullptr;  // [FO_MAX_P] completed-tile counters
-  uint32_t* rel[FO_MAX_P] = {};
-  uint32_t epoch = 0;
-  hipStream_t copy_stream = nullptr;
-  hipStream_t lane[FO_MAX_LANES - 1] = {};          // extra copy streams for striped transfers
-  hipEvent_t lane_ev[FO_MAX_P][FO_MAX_LANES] = {};  // piece done (per transfer, per lane)
-  hipEvent_t rel_ev[FO_MAX_P] = {};                 // release observed by the copy stream
-  hipEvent_t ev_start = nullptr, ev_copy = nullptr, ev_last = nullptr;
+  void* scratch = nullptr;   // source and destination of the DMA engines' first copies
+  hipEvent_t ev_last = nullptr;
   bool have_last = false;
 };
 
@@ -82,48 +85,40 @@ DevState g_dev[kMaxDevices];
 
 fo_status ensure_ready(int dev, DevState& st) {
   if (st.ready) return FO_OK;
+  st.dev = dev;
   FO_HIP(hipDeviceGetAttribute(&st.n_cu, hipDeviceAttributeMultiprocessorCount, dev));
   int khz = 0;
   FO_HIP(hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev));
   if (khz > 0) st.wall_khz = khz;
   void* p = nullptr;
-  const size_t flag_bytes = (size_t)(FO_MAX_P + 1) * fo::kFlagBytes + 4096;
-  FO_HIP(hipExtMallocWithFlags(&p, flag_bytes, hipDeviceMallocUncached));
-  st.arr = (uint32_t*)p;
-  st.esrc = st.arr + (size_t)FO_MAX_P * fo::kFlagStride;
-  st.err = st.esrc + fo::kFlagStride;
-  FO_HIP(hipMemset(p, 0, flag_bytes));
+  FO_HIP(hipExtMallocWithFlags(&p, 4096, hipDeviceMallocUncached));
+  st.err = (uint32_t*)p;
+  FO_HIP(hipMemset(p, 0, 4096));
   FO_HIP(hipMalloc(&p, FO_MAX_P * sizeof(uint32_t)));
   st.done = (uint32_t*)p;
   FO_HIP(hipMemset(st.done, 0, FO_MAX_P * sizeof(uint32_t)));
-  for (int i = 0; i < FO_MAX_P; ++i) {
-    FO_HIP(hipExtMallocWithFlags(&p, 8, hipMallocSignalMemory));
-    st.rel[i] = (uint32_t*)p;
-    FO_HIP(hipMemset(st.rel[i], 0, 8));
-  }
-  FO_HIP(hipStreamCreateWithFlags(&st.copy_stream, hipStreamNonBlocking));
-  for (int t = 0; t < FO_MAX_P; ++t) {
-    FO_HIP(hipEventCreateWithFlags(&st.rel_ev[t], hipEventDisableTiming));
-    for (int l = 0; l < FO_MAX_LANES; ++l)
-      FO_HIP(hipEventCreateWithFlags(&st.lane_ev[t][l], hipEventDisableTiming));
-  }
-  FO_HIP(hipEventCreateWithFlags(&st.ev_start, hipEventDisableTiming));
-  FO_HIP(hipEventCreateWithFlags(&st.ev_copy, hipEventDisableTiming));
+  FO_HIP(hipMalloc(&st.scratch, kScratchBytes));
+  FO_HIP(hipMemset(st.scratch, 0, kScratchBytes));
   FO_HIP(hipEventCreateWithFlags(&st.ev_last, hipEventDisableTiming));
   FO_HIP(hipDeviceSynchronize());
+  FO_DMA(fo::dma::init(dev, st.scratch, &e_));
   st.ready = true;
   return FO_OK;
 }
 
-fo_status current_state(DevState** out, int* dev_out) {
+// The state of the current device, initialized on first use, with its lock held by `lk`.
+fo_status current_state(DevState** out, std::unique_lock<std::mutex>* lk) {
   int dev = 0;
   FO_HIP(hipGetDevice(&dev));
   if (dev < 0 || dev >= kMaxDevices) {
     set_error("device %d beyond the library's limit of %d", dev, kMaxDevices);
     return FO_ERR_UNSUPPORTED;
   }
-  *out = &g_dev[dev];
-  if (dev_out) *dev_out = dev;
+  DevState& st = g_dev[dev];
+  *lk = std::unique_lock<std::mutex>(st.mu);
+  const fo_status s = ensure_ready(dev, st);
+  if (s != FO_OK) return s;
+  *out = &st;
   return FO_OK;
 }
 
@@ -146,16 +141,13 @@ fo_status check_opts(const fo_opts* o, fo_opts* out) {
     return invalid("opts.order %d is not a fo_order", o->order);
   if (o->arrival < FO_ARR_DEFAULT || o->arrival > FO_ARR_LOCKSTEP)
     return invalid("opts.arrival %d is not a fo_arrival", o->arrival);
-  if (o->copy_engine != FO_COPY_SDMA && o->copy_engine != FO_COPY_BLIT)
-    return invalid("opts.copy_engine %d is not a fo_copy_engine", o->copy_engine);
   if (o->tile < FO_TILE_AUTO || o->tile > FO_TILE_64x64)
     return invalid("opts.tile %d is not a fo_tile", o->tile);
-  if (o->copy_lanes < 0 || o->copy_lanes > FO_MAX_LANES)
-    return invalid("opts.copy_lanes %d outside [0, %d]", o->copy_lanes, FO_MAX_LANES);
-  if (o->reserved[0] || o->reserved[1]) return invalid("opts.reserved must be zero");
+  if (o->links < 0 || o->links > FO_MAX_P)
+    return invalid("opts.links %d outside [0, %d]", o->links, FO_MAX_P);
+  if (o->reserved0 || o->reserved[0] || o->reserved[1]) return invalid("opts.reserved must be zero");
   *out = *o;
   if (out->spin_timeout_us == 0) out->spin_timeout_us = kDefaultTimeoutUs;
-  if (out->copy_lanes == 0) out->copy_lanes = 1;
   return FO_OK;
 }
 
@@ -194,77 +186,18 @@ fo_status tiles_for(int in_dt, int tile, int64_t m, int64_t N, int P, fo::Plan& 
   return FO_OK;
 }
 
-uint32_t next_epoch(DevState& st) {
-  if (++st.epoch == 0) ++st.epoch;
-  return st.epoch;
-}
-
 uint64_t spin_ticks(const DevState& st, uint32_t us) { return (uint64_t)us * st.wall_khz / 1000u; }
 
-hipMemcpyKind copy_kind(const fo_opts& o) {
-  return o.copy_engine == FO_COPY_BLIT ? hipMemcpyDeviceToDevice : hipMemcpyDeviceToDeviceNoCU;
+// Links (DMA engines) one call's transfers are spread over: transfer t goes over link t mod L.
+// Default: one link per peer.
+int links_for(const fo_opts& o, int P) {
+  const int L = o.links == 0 ? P - 1 : o.links;
+  return std::max(1, std::min(L, P - 1));
 }
 
-// One emulated transfer sequence: for each slice seq[t] (t = 0..n-1), copy src[seq[t]] into
-// dst + seq[t]*bytes on `ks`, striped over `lanes` streams, then (when flags) write the call's
-// epoch into that slice's arrival flag. With `rel`, transfer t first waits until the kernel has
-// raised rel[t] (lockstep release). `start` is the event the lanes wait on before their first
-// piece (already waited on by ks). Everything the lanes do is joined back into ks per transfer.
-// The extra lane streams are created on first use only: HIP maps streams onto a small number of
-// hardware queues per process, and every stream created beyond that number shares a queue with
-// an existing one, possibly the caller's compute stream, where copy work would then wait behind
-// the very kernel that is waiting for it.
-fo_status ensure_lanes(DevState& st, int lanes) {
-  for (int l = 0; l < lanes - 1; ++l)
-    if (!st.lane[l]) FO_HIP(hipStreamCreateWithFlags(&st.lane[l], hipStreamNonBlocking));
-  return FO_OK;
-}
-
-fo_status enqueue_transfers(DevState& st, hipStream_t ks, hipEvent_t start, const int* seq, int n,
-                            const void* const* src, void* dst, size_t bytes, int lanes,
-                            hipMemcpyKind kind, uint32_t epoch, bool flags, bool rel) {
-  // flags: raise the slice's arrival flag after its data (the flag takes the epoch from the esrc
-  // block, which the caller has filled with `epoch`)
-  lanes = std::max(1, std::min(lanes, FO_MAX_LANES));
-  {
-    const fo_status s = ensure_lanes(st, lanes);
-    if (s != FO_OK) return s;
-  }
-  // pieces are 256-byte aligned; fewer lanes when a transfer is small
-  const size_t unit = 256;
-  size_t piece = ((bytes + lanes - 1) / lanes + unit - 1) / unit * unit;
-  if (piece == 0) piece = unit;
-  const int used = (int)std::min<size_t>((size_t)lanes, (bytes + piece - 1) / piece);
-  for (int l = 1; l < used; ++l) FO_HIP(hipStreamWaitEvent(st.lane[l - 1], start, 0));
-  for (int t = 0; t < n; ++t) {
-    const int sl = seq[t];
-    uint8_t* d = (uint8_t*)dst + (size_t)sl * bytes;
-    const uint8_t* sp = (const uint8_t*)src[sl];
-    if (rel) {
-      FO_HIP(hipStreamWaitValue32(ks, st.rel[t], epoch, hipStreamWaitValueEq, 0xffffffffu));
-      if (used > 1) {
-        FO_HIP(hipEventRecord(st.rel_ev[t], ks));
-        for (int l = 1; l < used; ++l) FO_HIP(hipStreamWaitEvent(st.lane[l - 1], st.rel_ev[t], 0));
-      }
-    }
-    for (int l = 1; l < used; ++l) {
-      const size_t off = (size_t)l * piece;
-      const size_t len = std::min(piece, bytes - off);
-      FO_HIP(hipMemcpyAsync(d + off, sp + off, len, kind, st.lane[l - 1]));
-      FO_HIP(hipEventRecord(st.lane_ev[t][l], st.lane[l - 1]));
-    }
-    FO_HIP(hipMemcpyAsync(d, sp, std::min(piece, bytes), kind, ks));
-    for (int l = 1; l < used; ++l) FO_HIP(hipStreamWaitEvent(ks, st.lane_ev[t][l], 0));
-    if (flags)
-      FO_HIP(hipMemcpyAsync(st.arr + (size_t)sl * fo::kFlagStride, st.esrc, fo::kFlagBytes,
-                            hipMemcpyDeviceToDeviceNoCU, ks));
-  }
-  return FO_OK;
-}
-
-// Arrival order of the slices a rank receives: for FLASH (and for RS always) the ring delivers
-// rank-1, rank-2, ... (mod P); for the NATURAL AG order the slices are needed, and so sent, in
-// index order.
+// Arrival order of the slices a rank receives: for FLASH (and for RS always) rank-1, rank-2, ...
+// (mod P), the order in which a ring from rank-1 delivers them; for the NATURAL AG order the
+// slices are needed, and so sent, in index order.
 int arrival_sequence(int kind, int order, int P, int rank, int* seq) {
   int n = 0;
   if (kind == 0 && order == FO_ORDER_NATURAL) {
@@ -276,21 +209,10 @@ int arrival_sequence(int kind, int order, int P, int rank, int* seq) {
   return n;
 }
 
-// When an arrival needs a compute unit (copy kernels as the transfer engine, or the copy
-// stream's waits on the RS release flags), the GEMM keeps a few CUs free: a persistent grid of
-// n_cu - 8 workgroups (a multiple of 8, so tile-to-XCD placement is kept). Otherwise tiles
-// waiting for a slice could occupy every CU while the work that delivers the slice waits for
-// one. DMA copies and flag copies need no CU, so the SDMA path uses one workgroup per tile.
-int grid_cap(const DevState& st, const fo_opts& o, bool arrivals, bool lockstep) {
-  if (!arrivals || (o.copy_engine != FO_COPY_BLIT && !lockstep)) return 0;
-  const int cap = (st.n_cu - 8) / 8 * 8;
-  return cap > 0 ? cap : 8;
-}
-
 fo_status launch_with_events(const fo::Plan& p, int in_dt, int tile, hipStream_t cs,
-                             const fo_opts& o, int max_grid) {
+                             const fo_opts& o) {
   if (o.kernel_events[0]) FO_HIP(hipEventRecord((hipEvent_t)o.kernel_events[0], cs));
-  FO_HIP(fo::launch_gemm(p, in_dt, tile, max_grid, cs));
+  FO_HIP(fo::launch_gemm(p, in_dt, tile, cs));
   if (o.kernel_events[1]) FO_HIP(hipEventRecord((hipEvent_t)o.kernel_events[1], cs));
   return FO_OK;
 }
@@ -304,7 +226,6 @@ void fo_opts_init(fo_opts* o) {
   memset(o, 0, sizeof *o);
   o->order = FO_ORDER_FLASH;
   o->arrival = FO_ARR_DEFAULT;
-  o->copy_engine = FO_COPY_SDMA;
   o->tile = FO_TILE_AUTO;
   o->spin_timeout_us = kDefaultTimeoutUs;
 }
@@ -365,8 +286,7 @@ fo_status fo_tile_info(int32_t P, int64_t m, int64_t K, int64_t N, int32_t in_dt
 
 fo_status fo_ag_gemm(const void* x_local, const void* const* x_peer, void* x_recv, const void* w,
                      void* y, int32_t P, int32_t rank, int64_t m, int64_t K, int64_t N,
-                     int32_t in_dt, int32_t out_dt, void* compute_stream, void* copy_stream,
-                     const fo_opts* opts) {
+                     int32_t in_dt, int32_t out_dt, void* compute_stream, const fo_opts* opts) {
   fo_opts o;
   fo_status s = check_opts(opts, &o);
   if (s != FO_OK) return s;
@@ -399,29 +319,25 @@ fo_status fo_ag_gemm(const void* x_local, const void* const* x_peer, void* x_rec
   if (m == 0 || N == 0) return FO_OK;
 
   DevState* st = nullptr;
-  s = current_state(&st, nullptr);
-  if (s != FO_OK) return s;
-  std::lock_guard<std::mutex> lk(st->mu);
-  int dev = 0;
-  FO_HIP(hipGetDevice(&dev));
-  s = ensure_ready(dev, *st);
+  std::unique_lock<std::mutex> lk;
+  s = current_state(&st, &lk);
   if (s != FO_OK) return s;
 
   const int tile = resolve_tile(o, in_dt, P, m, N, st->n_cu);
   fo::Plan p{};
   s = tiles_for(in_dt, tile, m, N, P, p);
   if (s != FO_OK) return s;
+  fo::dma::Call call{};
+  if (arrivals) FO_DMA(fo::dma::begin(st->dev, P, &call, &e_));
   int32_t order[FO_MAX_P];
   fo::slice_order(0, o.order, P, rank, order);
-  const uint32_t epoch = next_epoch(*st);
   for (int pos = 0; pos < P; ++pos) {
     const int sl = order[pos];
     p.a_pos[pos] = sl == rank ? x_local : (const uint8_t*)x_recv + (size_t)sl * slice_b;
     p.c_pos[pos] = (uint8_t*)y + (size_t)sl * m * N * os;
-    p.gate[pos] = (arrivals && sl != rank) ? sl : -1;
+    p.gate[pos] = (arrivals && sl != rank) ? call.comp[sl] : nullptr;
   }
   p.b = w;
-  p.arr = st->arr;
   p.done = st->done;
   p.err = st->err;
   p.spin_limit = spin_ticks(*st, o.spin_timeout_us);
@@ -432,37 +348,32 @@ fo_status fo_ag_gemm(const void* x_local, const void* const* x_peer, void* x_rec
   p.n_recv = 0;
   p.accum_pos = -1;
   p.out_f32 = out_dt == FO_DT_F32;
-  p.epoch = epoch;
 
   hipStream_t cs = (hipStream_t)compute_stream;
-  hipStream_t ks = copy_stream ? (hipStream_t)copy_stream : st->copy_stream;
   if (st->have_last) FO_HIP(hipStreamWaitEvent(cs, st->ev_last, 0));
-  if (arrivals) {
-    // the copies are enqueued before the kernel so that they start together with it
-    FO_HIP(fo::launch_stamp(st->esrc, epoch, cs));
-    FO_HIP(hipEventRecord(st->ev_start, cs));
-    FO_HIP(hipStreamWaitEvent(ks, st->ev_start, 0));
-    int seq[FO_MAX_P];
-    const int n = arrival_sequence(0, o.order, P, rank, seq);
-    s = enqueue_transfers(*st, ks, st->ev_start, seq, n, x_peer, x_recv, slice_b, o.copy_lanes,
-                          copy_kind(o), epoch, true, false);
-    if (s != FO_OK) return s;
-  }
-  s = launch_with_events(p, in_dt, tile, cs, o, grid_cap(*st, o, arrivals, false));
+  if (arrivals) FO_HIP(fo::launch_release(call.start, cs));
+  s = launch_with_events(p, in_dt, tile, cs, o);
   if (s != FO_OK) return s;
-  if (arrivals) {
-    FO_HIP(hipEventRecord(st->ev_copy, ks));
-    FO_HIP(hipStreamWaitEvent(cs, st->ev_copy, 0));
-  }
+  if (arrivals) FO_DMA(fo::dma::end(st->dev, call, cs, &e_));
   FO_HIP(hipEventRecord(st->ev_last, cs));
   st->have_last = true;
+  if (arrivals) {
+    int seq[FO_MAX_P];
+    const int n = arrival_sequence(0, o.order, P, rank, seq);
+    const int L = links_for(o, P);
+    for (int t = 0; t < n; ++t) {
+      const int sl = seq[t];
+      FO_DMA(fo::dma::copy(st->dev, call, t % L, sl, -1, (uint8_t*)x_recv + (size_t)sl * slice_b,
+                           x_peer[sl], slice_b, &e_));
+    }
+  }
   return FO_OK;
 }
 
 fo_status fo_gemm_rs(const void* x_shard, const void* w, float* send_buf, float* out,
                      const float* const* peer_partial, float* recv_buf, int32_t P, int32_t rank,
                      int64_t m, int64_t K, int64_t N, int32_t in_dt, void* compute_stream,
-                     void* copy_stream, const fo_opts* opts) {
+                     const fo_opts* opts) {
   fo_opts o;
   fo_status s = check_opts(opts, &o);
   if (s != FO_OK) return s;
@@ -503,39 +414,34 @@ fo_status fo_gemm_rs(const void* x_shard, const void* w, float* send_buf, float*
   if (m == 0 || N == 0) return FO_OK;
 
   DevState* st = nullptr;
-  s = current_state(&st, nullptr);
-  if (s != FO_OK) return s;
-  std::lock_guard<std::mutex> lk(st->mu);
-  int dev = 0;
-  FO_HIP(hipGetDevice(&dev));
-  s = ensure_ready(dev, *st);
+  std::unique_lock<std::mutex> lk;
+  s = current_state(&st, &lk);
   if (s != FO_OK) return s;
 
   const int tile = resolve_tile(o, in_dt, P, m, N, st->n_cu);
   fo::Plan p{};
   s = tiles_for(in_dt, tile, m, N, P, p);
   if (s != FO_OK) return s;
+  const bool lockstep = arrivals && arrival == FO_ARR_LOCKSTEP;
+  fo::dma::Call call{};
+  if (arrivals) FO_DMA(fo::dma::begin(st->dev, P, &call, &e_));
   int32_t order[FO_MAX_P];
   fo::slice_order(1, FO_ORDER_FLASH, P, rank, order);
-  const uint32_t epoch = next_epoch(*st);
-  const bool lockstep = arrivals && arrival == FO_ARR_LOCKSTEP;
   for (int pos = 0; pos < P; ++pos) {
     const int d = order[pos];
     p.a_pos[pos] = (const uint8_t*)x_shard + (size_t)d * m * K * es;
     p.c_pos[pos] = d == rank ? (void*)out : (void*)((uint8_t*)send_buf + (size_t)d * chunk_b);
-    p.gate[pos] = -1;
-    p.rel[pos] = (lockstep && d != rank) ? st->rel[pos] : nullptr;
+    p.rel[pos] = (lockstep && d != rank) ? call.rel[pos] : nullptr;
     if (d == rank) p.accum_pos = pos;
   }
   // partials arrive from rank-1, rank-2, ... (mod P) and are added in that order
   for (int i = 1; i < P; ++i) {
     const int q = ((rank - i) % P + P) % P;
     p.recv[i - 1] = (const float*)((const uint8_t*)recv_buf + (size_t)q * chunk_b);
-    p.recv_flag[i - 1] = arrivals ? q : -1;
+    p.recv_sig[i - 1] = arrivals ? call.comp[q] : nullptr;
   }
   p.n_recv = P - 1;
   p.b = w;
-  p.arr = st->arr;
   p.done = st->done;
   p.err = st->err;
   p.spin_limit = spin_ticks(*st, o.spin_timeout_us);
@@ -544,35 +450,28 @@ fo_status fo_gemm_rs(const void* x_shard, const void* w, float* send_buf, float*
   p.N = N;
   p.npos = P;
   p.out_f32 = 1;
-  p.epoch = epoch;
 
   hipStream_t cs = (hipStream_t)compute_stream;
-  hipStream_t ks = copy_stream ? (hipStream_t)copy_stream : st->copy_stream;
   if (st->have_last) FO_HIP(hipStreamWaitEvent(cs, st->ev_last, 0));
-  if (arrivals) {
-    FO_HIP(fo::launch_stamp(st->esrc, epoch, cs));
-    FO_HIP(hipEventRecord(st->ev_start, cs));
-  }
-  // the kernel is enqueued before the copy stream's waits on its release flags, so a failed
-  // launch never leaves the copy stream waiting for a flag that nobody raises
-  s = launch_with_events(p, in_dt, tile, cs, o, grid_cap(*st, o, arrivals, lockstep));
+  if (arrivals) FO_HIP(fo::launch_release(call.start, cs));
+  s = launch_with_events(p, in_dt, tile, cs, o);
   if (s != FO_OK) return s;
-  if (arrivals) {
-    FO_HIP(hipStreamWaitEvent(ks, st->ev_start, 0));
-    // lockstep: peer q = rank-i sends its partial for this rank at its step i-1, which (peers
-    // progressing together) ends when this rank finishes its own step i-1
-    int seq[FO_MAX_P];
-    const int n = arrival_sequence(1, FO_ORDER_FLASH, P, rank, seq);
-    s = enqueue_transfers(*st, ks, st->ev_start, seq, n, (const void* const*)peer_partial, recv_buf,
-                          chunk_b, o.copy_lanes, copy_kind(o), epoch, true, lockstep);
-    if (s != FO_OK) return s;
-  }
-  if (arrivals) {
-    FO_HIP(hipEventRecord(st->ev_copy, ks));
-    FO_HIP(hipStreamWaitEvent(cs, st->ev_copy, 0));
-  }
+  if (arrivals) FO_DMA(fo::dma::end(st->dev, call, cs, &e_));
   FO_HIP(hipEventRecord(st->ev_last, cs));
   st->have_last = true;
+  if (arrivals) {
+    // transfer t brings the partial of peer rank-1-t. In lockstep that peer sends it at its own
+    // step t, which (peers progressing together) ends when this rank ends its step t: the copy
+    // waits for position t's release.
+    int seq[FO_MAX_P];
+    const int n = arrival_sequence(1, FO_ORDER_FLASH, P, rank, seq);
+    const int L = links_for(o, P);
+    for (int t = 0; t < n; ++t) {
+      const int q = seq[t];
+      FO_DMA(fo::dma::copy(st->dev, call, t % L, q, lockstep ? t : -1,
+                           (uint8_t*)recv_buf + (size_t)q * chunk_b, peer_partial[q], chunk_b, &e_));
+    }
+  }
   return FO_OK;
 }
 
@@ -592,12 +491,8 @@ fo_status fo_gemm_ref(const void* a, const void* b, void* c, int64_t M, int64_t 
   if (M == 0 || N == 0) return FO_OK;
 
   DevState* st = nullptr;
-  s = current_state(&st, nullptr);
-  if (s != FO_OK) return s;
-  std::lock_guard<std::mutex> lk(st->mu);
-  int dev = 0;
-  FO_HIP(hipGetDevice(&dev));
-  s = ensure_ready(dev, *st);
+  std::unique_lock<std::mutex> lk;
+  s = current_state(&st, &lk);
   if (s != FO_OK) return s;
   fo_opts o;
   fo_opts_init(&o);
@@ -608,9 +503,7 @@ fo_status fo_gemm_ref(const void* a, const void* b, void* c, int64_t M, int64_t 
   if (s != FO_OK) return s;
   p.a_pos[0] = a;
   p.c_pos[0] = c;
-  p.gate[0] = -1;
   p.b = b;
-  p.arr = st->arr;
   p.done = st->done;
   p.err = st->err;
   p.spin_limit = spin_ticks(*st, kDefaultTimeoutUs);
@@ -620,9 +513,7 @@ fo_status fo_gemm_ref(const void* a, const void* b, void* c, int64_t M, int64_t 
   p.npos = 1;
   p.accum_pos = -1;
   p.out_f32 = out_dt == FO_DT_F32;
-  p.epoch = st->epoch;
-  hipStream_t cs = (hipStream_t)stream;
-  FO_HIP(fo::launch_gemm(p, in_dt, t, 0, cs));
+  FO_HIP(fo::launch_gemm(p, in_dt, t, (hipStream_t)stream));
   return FO_OK;
 }
 
@@ -643,40 +534,56 @@ fo_status fo_transfer_ref(int32_t kind, const void* const* src, void* dst, int32
   }
   if (P == 1 || slice_bytes == 0) return FO_OK;
   DevState* st = nullptr;
-  s = current_state(&st, nullptr);
+  std::unique_lock<std::mutex> lk;
+  s = current_state(&st, &lk);
   if (s != FO_OK) return s;
-  std::lock_guard<std::mutex> lk(st->mu);
-  int dev = 0;
-  FO_HIP(hipGetDevice(&dev));
-  s = ensure_ready(dev, *st);
-  if (s != FO_OK) return s;
-  hipStream_t ks = (hipStream_t)stream;
-  if (st->have_last) FO_HIP(hipStreamWaitEvent(ks, st->ev_last, 0));
-  FO_HIP(hipEventRecord(st->ev_start, ks));
+  fo::dma::Call call{};
+  FO_DMA(fo::dma::begin(st->dev, P, &call, &e_));
   int seq[FO_MAX_P];
   const int n = arrival_sequence(kind, o.order, P, rank, seq);
-  s = enqueue_transfers(*st, ks, st->ev_start, seq, n, src, dst, (size_t)slice_bytes,
-                        o.copy_lanes, copy_kind(o), 0, false, false);
-  if (s != FO_OK) return s;
+  const int64_t* wait[FO_MAX_P];
+  for (int t = 0; t < n; ++t) wait[t] = call.comp[seq[t]];
+  hipStream_t ks = (hipStream_t)stream;
+  if (st->have_last) FO_HIP(hipStreamWaitEvent(ks, st->ev_last, 0));
+  FO_HIP(fo::launch_release(call.start, ks));
+  FO_HIP(fo::launch_wait(wait, n, spin_ticks(*st, o.spin_timeout_us), st->err, ks));
+  FO_DMA(fo::dma::end(st->dev, call, ks, &e_));
   FO_HIP(hipEventRecord(st->ev_last, ks));
   st->have_last = true;
+  const int L = links_for(o, P);
+  for (int t = 0; t < n; ++t) {
+    const int sl = seq[t];
+    FO_DMA(fo::dma::copy(st->dev, call, t % L, sl, -1, (uint8_t*)dst + (size_t)sl * slice_bytes,
+                         src[sl], (size_t)slice_bytes, &e_));
+  }
   return FO_OK;
 }
 
 fo_status fo_check(void* stream) {
-  DevState* st = nullptr;
-  int dev = 0;
-  fo_status s = current_state(&st, &dev);
-  if (s != FO_OK) return s;
   FO_HIP(hipStreamSynchronize((hipStream_t)stream));
-  std::lock_guard<std::mutex> lk(st->mu);
-  if (!st->ready) return FO_OK;
-  FO_HIP(hipStreamSynchronize(st->copy_stream));
+  int dev = 0;
+  FO_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return FO_OK;
+  DevState& st = g_dev[dev];
+  std::lock_guard<std::mutex> lk(st.mu);
+  if (!st.ready) return FO_OK;
+  {
+    std::string e;
+    bool timed_out = false;
+    if (!fo::dma::drain(dev, 30000, &e, &timed_out)) {
+      set_error("%s", e.c_str());
+      return timed_out ? FO_ERR_TIMEOUT : FO_ERR_HIP;
+    }
+  }
   uint32_t e = 0;
-  FO_HIP(hipMemcpy(&e, st->err, sizeof e, hipMemcpyDeviceToHost));
+  FO_HIP(hipMemcpy(&e, st.err, sizeof e, hipMemcpyDeviceToHost));
   if (e) {
     const uint32_t zero = 0;
-    FO_HIP(hipMemcpy(st->err, &zero, sizeof zero, hipMemcpyHostToDevice));
+    FO_HIP(hipMemcpy(st.err, &zero, sizeof zero, hipMemcpyHostToDevice));
+    if (e == 2) {
+      set_error("a DMA transfer reported failure");
+      return FO_ERR_HIP;
+    }
     set_error("an in-kernel arrival wait ran past its bound");
     return FO_ERR_TIMEOUT;
   }

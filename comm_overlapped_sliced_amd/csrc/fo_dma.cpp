@@ -1,0 +1,324 @@
+// DMA transfer layer of libflashovl: emulated point-to-point transfers on the SDMA engines.
+//
+// The FlashOverlap page (gist.science paper 2604.24013, technical summary section 2) splits the
+// collectives into point-to-point transfers that run while the GEMM computes; section 3 credits
+// the method with relaxing the step-wise synchronisation of the collective. On one GPU a transfer
+// is a copy from a "peer" buffer, and what matters is that it neither takes compute units from
+// the GEMM nor needs one to be scheduled: the GEMM may hold every CU while it waits for the very
+// slice being copied. So each transfer is an SDMA copy issued through the HSA runtime with its
+// dependencies given as signals that the engine itself polls (the start of the call, and for
+// Flash-RS in lockstep the release of a GEMM step), and its completion is a signal whose value
+// the kernels poll. One engine stands for one link: transfers on the same link run one after
+// the other in issue order, transfers on different links run concurrently.
+//
+// The HSA entry points are looked up in the HSA runtime already loaded into the process (the
+// one HIP runs on), so the library never brings a second runtime instance into the process.
+#include <dlfcn.h>
+#include <link.h>
+#include <hsa/hsa.h>
+#include <hsa/hsa_ext_amd.h>
+
+#include <chrono>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <thread>
+#include <type_traits>
+#include <vector>
+
+#include "fo_internal.h"
+
+namespace fo {
+namespace dma {
+namespace {
+
+struct Hsa {
+  decltype(&hsa_init) init = nullptr;
+  decltype(&hsa_amd_pointer_info) pointer_info = nullptr;
+  decltype(&hsa_amd_memory_copy_engine_status) engine_status = nullptr;
+  decltype(&hsa_amd_signal_create) signal_create = nullptr;
+  decltype(&hsa_amd_signal_value_pointer) value_pointer = nullptr;
+  decltype(&hsa_signal_store_screlease) store = nullptr;
+  decltype(&hsa_signal_load_scacquire) load = nullptr;
+  decltype(&hsa_amd_memory_async_copy_on_engine) copy = nullptr;
+};
+
+Hsa g_hsa;
+bool g_hsa_ok = false;
+std::once_flag g_hsa_once;
+std::string g_hsa_err;
+
+int collect_hsa(struct dl_phdr_info* info, size_t, void* data) {
+  if (info->dlpi_name && strstr(info->dlpi_name, "libhsa-runtime64.so"))
+    static_cast<std::vector<std::string>*>(data)->push_back(info->dlpi_name);
+  return 0;
+}
+
+void resolve_hsa() {
+  std::vector<std::string> libs;
+  dl_iterate_phdr(collect_hsa, &libs);
+  if (libs.empty()) {
+    g_hsa_err = "no HSA runtime is loaded in the process";
+    return;
+  }
+  if (libs.size() > 1) {
+    g_hsa_err = "more than one HSA runtime is loaded in the process (" + libs[0] + ", " + libs[1] + ")";
+    return;
+  }
+  void* h = dlopen(libs[0].c_str(), RTLD_NOW | RTLD_NOLOAD);
+  if (!h) {
+    g_hsa_err = "cannot open the loaded HSA runtime " + libs[0];
+    return;
+  }
+  bool ok = true;
+  auto get = [&](auto& fn, const char* name) {
+    fn = reinterpret_cast<std::remove_reference_t<decltype(fn)>>(dlsym(h, name));
+    if (!fn) {
+      ok = false;
+      g_hsa_err = std::string("the HSA runtime lacks ") + name;
+    }
+  };
+  get(g_hsa.init, "hsa_init");
+  get(g_hsa.pointer_info, "hsa_amd_pointer_info");
+  get(g_hsa.engine_status, "hsa_amd_memory_copy_engine_status");
+  get(g_hsa.signal_create, "hsa_amd_signal_create");
+  get(g_hsa.value_pointer, "hsa_amd_signal_value_pointer");
+  get(g_hsa.store, "hsa_signal_store_screlease");
+  get(g_hsa.load, "hsa_signal_load_scacquire");
+  get(g_hsa.copy, "hsa_amd_memory_async_copy_on_engine");
+  g_hsa_ok = ok;
+}
+
+struct Slot {
+  hsa_signal_t start{}, rel[FO_MAX_P]{}, comp[FO_MAX_P]{};
+  int64_t* start_v = nullptr;
+  int64_t* rel_v[FO_MAX_P] = {};
+  int64_t* comp_v[FO_MAX_P] = {};
+  hipEvent_t ev = nullptr;  // recorded after the call's last kernel that reads the signals
+  bool pending = false;     // used by a call that may not be complete yet
+  uint32_t issued = 0;      // slices whose completion signal a copy will decrement
+};
+
+struct Dev {
+  bool ready = false;
+  hsa_agent_t agent{};
+  int n_eng = 0;
+  uint32_t eng[32] = {};
+  Slot slot[kSlots];
+  int next = 0;
+};
+
+constexpr int kMaxDevices = 64;
+Dev g_dev[kMaxDevices];
+
+constexpr size_t kWarmBytes = 65536;
+
+const char* hsa_msg(hsa_status_t s) {
+  switch (s) {
+    case HSA_STATUS_SUCCESS: return "success";
+    case HSA_STATUS_ERROR_INVALID_ARGUMENT: return "invalid argument";
+    case HSA_STATUS_ERROR_INVALID_AGENT: return "invalid agent";
+    case HSA_STATUS_ERROR_INVALID_SIGNAL: return "invalid signal";
+    case HSA_STATUS_ERROR_OUT_OF_RESOURCES: return "out of resources";
+    case HSA_STATUS_ERROR_NOT_INITIALIZED: return "runtime not initialized";
+    default: return "error";
+  }
+}
+
+bool fail(std::string* err, const char* what, hsa_status_t s) {
+  char buf[256];
+  snprintf(buf, sizeof buf, "%s failed: %s (0x%x)", what, hsa_msg(s), (unsigned)s);
+  *err = buf;
+  return false;
+}
+
+bool new_signal(hsa_signal_t* sig, int64_t** value, std::string* err) {
+  hsa_status_t s = g_hsa.signal_create(1, 0, nullptr, HSA_AMD_SIGNAL_AMD_GPU_ONLY, sig);
+  if (s != HSA_STATUS_SUCCESS) return fail(err, "hsa_amd_signal_create", s);
+  volatile hsa_signal_value_t* v = nullptr;
+  s = g_hsa.value_pointer(*sig, &v);
+  if (s != HSA_STATUS_SUCCESS) return fail(err, "hsa_amd_signal_value_pointer", s);
+  *value = (int64_t*)v;
+  return true;
+}
+
+// Host wait (bounded) until the completion signal of every issued slice has dropped to zero.
+bool wait_landed(const Slot& sl, uint32_t timeout_ms, std::string* err, bool* timed_out = nullptr) {
+  const auto t0 = std::chrono::steady_clock::now();
+  for (int i = 0; i < FO_MAX_P; ++i) {
+    if (!(sl.issued & (1u << i))) continue;
+    int spins = 0;
+    for (;;) {
+      const int64_t v = g_hsa.load(sl.comp[i]);
+      if (v < 0) {
+        *err = "a DMA transfer reported failure";
+        return false;
+      }
+      if (v == 0) break;
+      if (std::chrono::steady_clock::now() - t0 > std::chrono::milliseconds(timeout_ms)) {
+        *err = "a DMA transfer did not complete within its bound";
+        if (timed_out) *timed_out = true;
+        return false;
+      }
+      if (++spins > 64) std::this_thread::sleep_for(std::chrono::microseconds(50));
+    }
+  }
+  return true;
+}
+
+}  // namespace
+
+bool init(int dev, void* scratch, std::string* err) {
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = "device index beyond the DMA layer's limit";
+    return false;
+  }
+  Dev& d = g_dev[dev];
+  if (d.ready) return true;
+  std::call_once(g_hsa_once, resolve_hsa);
+  if (!g_hsa_ok) {
+    *err = g_hsa_err;
+    return false;
+  }
+  hsa_status_t s = g_hsa.init();  // HIP has initialized the runtime already; this only counts up
+  if (s != HSA_STATUS_SUCCESS) return fail(err, "hsa_init", s);
+  hsa_amd_pointer_info_t info;
+  memset(&info, 0, sizeof info);
+  info.size = sizeof info;
+  s = g_hsa.pointer_info(scratch, &info, nullptr, nullptr, nullptr);
+  if (s != HSA_STATUS_SUCCESS) return fail(err, "hsa_amd_pointer_info", s);
+  if (info.type != HSA_EXT_POINTER_TYPE_HSA) {
+    *err = "the library's scratch buffer is not device memory of the HSA runtime";
+    return false;
+  }
+  d.agent = info.agentOwner;
+  // Engines for device-to-device copies. Runtimes that cannot report them for a copy within one
+  // device get ids 2..15 tried (0 and 1 are left to HIP's own copies, as the runtimes that do
+  // report them leave them out); an id whose first copy the runtime refuses is dropped.
+  uint32_t mask = 0;
+  s = g_hsa.engine_status(d.agent, d.agent, &mask);
+  if (s != HSA_STATUS_SUCCESS || mask == 0) mask = 0xfffcu;
+  d.n_eng = 0;
+  for (int i = 0; i < 32; ++i)
+    if (mask & (1u << i)) d.eng[d.n_eng++] = 1u << i;
+  for (Slot& sl : d.slot) {
+    if (!new_signal(&sl.start, &sl.start_v, err)) return false;
+    for (int i = 0; i < FO_MAX_P; ++i) {
+      if (!new_signal(&sl.rel[i], &sl.rel_v[i], err)) return false;
+      if (!new_signal(&sl.comp[i], &sl.comp_v[i], err)) return false;
+    }
+    if (hipEventCreateWithFlags(&sl.ev, hipEventDisableTiming) != hipSuccess) {
+      *err = "hipEventCreateWithFlags failed";
+      return false;
+    }
+  }
+  // one small copy per engine, one engine at a time
+  Slot& w = d.slot[0];
+  uint8_t* src = (uint8_t*)scratch;
+  int kept = 0;
+  for (int e = 0; e < d.n_eng; ++e) {
+    g_hsa.store(w.comp[0], 1);
+    s = g_hsa.copy(src + kWarmBytes, d.agent, src, d.agent, kWarmBytes, 0, nullptr, w.comp[0],
+                   (hsa_amd_sdma_engine_id_t)d.eng[e], true);
+    if (s != HSA_STATUS_SUCCESS) continue;
+    w.issued = 1u;
+    if (!wait_landed(w, 10000, err)) return false;
+    d.eng[kept++] = d.eng[e];
+  }
+  d.n_eng = kept;
+  if (kept == 0) {
+    *err = "no SDMA engine accepts device-to-device copies on this device";
+    return false;
+  }
+  w.issued = 0;
+  d.ready = true;
+  return true;
+}
+
+int n_engines(int dev) { return (dev >= 0 && dev < kMaxDevices) ? g_dev[dev].n_eng : 0; }
+
+bool begin(int dev, int P, Call* call, std::string* err) {
+  Dev& d = g_dev[dev];
+  if (!d.ready) {
+    *err = "DMA layer not initialized";
+    return false;
+  }
+  const int k = d.next;
+  Slot& sl = d.slot[k];
+  if (sl.pending) {
+    if (hipEventSynchronize(sl.ev) != hipSuccess) {
+      *err = "hipEventSynchronize on a previous call failed";
+      return false;
+    }
+    if (!wait_landed(sl, 30000, err)) return false;
+    sl.pending = false;
+  }
+  g_hsa.store(sl.start, 1);
+  for (int i = 0; i < P; ++i) {
+    g_hsa.store(sl.rel[i], 1);
+    g_hsa.store(sl.comp[i], 1);
+  }
+  sl.issued = 0;
+  sl.pending = true;
+  d.next = (k + 1) % kSlots;
+  call->slot = k;
+  call->start = sl.start_v;
+  for (int i = 0; i < FO_MAX_P; ++i) {
+    call->rel[i] = sl.rel_v[i];
+    call->comp[i] = sl.comp_v[i];
+  }
+  return true;
+}
+
+bool copy(int dev, const Call& call, int link, int slice, int rel_pos, void* dst, const void* src,
+          size_t bytes, std::string* err) {
+  Dev& d = g_dev[dev];
+  Slot& sl = d.slot[call.slot];
+  if (bytes == 0) {
+    g_hsa.store(sl.comp[slice], 0);
+    return true;
+  }
+  hsa_signal_t deps[2] = {sl.start, {}};
+  uint32_t n = 1;
+  if (rel_pos >= 0) deps[n++] = sl.rel[rel_pos];
+  const uint32_t eng = d.eng[(link % d.n_eng + d.n_eng) % d.n_eng];
+  const hsa_status_t s = g_hsa.copy(dst, d.agent, src, d.agent, bytes, n, deps, sl.comp[slice],
+                                    (hsa_amd_sdma_engine_id_t)eng, true);
+  if (s != HSA_STATUS_SUCCESS) {
+    // the kernel must not wait for a copy that was never issued: report it as failed
+    g_hsa.store(sl.comp[slice], -1);
+    return fail(err, "hsa_amd_memory_async_copy_on_engine", s);
+  }
+  sl.issued |= 1u << slice;
+  return true;
+}
+
+bool end(int dev, const Call& call, hipStream_t stream, std::string* err) {
+  if (hipEventRecord(g_dev[dev].slot[call.slot].ev, stream) != hipSuccess) {
+    *err = "hipEventRecord failed";
+    return false;
+  }
+  return true;
+}
+
+bool drain(int dev, uint32_t timeout_ms, std::string* err, bool* timed_out) {
+  *timed_out = false;
+  if (dev < 0 || dev >= kMaxDevices) return true;
+  Dev& d = g_dev[dev];
+  if (!d.ready) return true;
+  for (Slot& sl : d.slot) {
+    if (!sl.pending) continue;
+    if (hipEventSynchronize(sl.ev) != hipSuccess) {
+      *err = "hipEventSynchronize on a previous call failed";
+      return false;
+    }
+    if (!wait_landed(sl, timeout_ms, err, timed_out)) return false;
+    sl.pending = false;
+    sl.issued = 0;
+  }
+  return true;
+}
+
+}  // namespace dma
+}  // namespace fo

@@ -2,16 +2,14 @@
 //
 // One launch computes every slice of a Flash-AG or Flash-RS call (FlashOverlap page, technical
 // summary section 2): workgroups are laid out in schedule order, a tile of a slice that is still
-// in flight waits on that slice's arrival flag before reading it, and the chunk that stays on the
-// rank (Flash-RS) adds the partials received from the peers in its write-back.
+// in flight waits on that slice's arrival signal before reading it, and the chunk that stays on
+// the rank (Flash-RS) adds the partials received from the peers in its write-back.
 //
 // bf16 path: v_mfma_f32_32x32x16_bf16 with fp32 accumulation. Each workgroup is 4 waves (2 x 2);
-// each wave owns a (BM/2) x (BN/2) block of 32x32 MFMA fragments. K advances in steps of 64
-// through two LDS stages: the next step's operands are fetched from HBM into registers with
-// 128-bit loads while the current stage feeds the MFMAs. A (K-contiguous) is stored to LDS as
-// is; W (N-contiguous) is transposed in registers on the way so that both operands are read
-// from LDS as 16-byte K-runs. LDS rows are 128 bytes with an XOR swizzle of the 16-byte chunks
-// so that the fragment reads and the transposed writes are free of bank conflicts.
+// each wave owns a (BM/2) x (BN/2) block of 32x32 fragments. K advances in steps of 32 through a
+// ring of 4 LDS stages that buffer loads fill straight from HBM (the bf16 section below has the
+// layout); the accumulators leave through LDS so that output stores and partial loads are
+// row-contiguous 16-byte accesses.
 //
 // fp32 path: a plain LDS-tiled fp32 FMA kernel (exact fp32 products, fp32 sums in k order).
 #include <hip/hip_runtime.h>
@@ -32,12 +30,18 @@ constexpr int kBK = 32;  // K step
 
 // ---------------------------------------------------------------- waits and flags -----------
 
-// Bounded wait for flag == epoch. Once any wait of the call has run past the bound (err set),
-// later waits give up at once, so a missing arrival costs one bound, not one per workgroup.
-__device__ __forceinline__ void wait_flag(const uint32_t* flag, uint32_t epoch, uint64_t limit,
-                                          uint32_t* err) {
+// Bounded wait until a signal value has dropped to zero (the copy engine decrements it from 1
+// when its transfer has landed; a negative value reports a failed copy, recorded as err = 2).
+// Once any wait of the call has run past the bound (err set), later waits give up at once, so a
+// missing arrival costs one bound, not one per workgroup.
+__device__ __forceinline__ void wait_signal(const int64_t* v, uint64_t limit, uint32_t* err) {
   const uint64_t t0 = wall_clock64();
-  while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != epoch) {
+  for (;;) {
+    const int64_t x = __hip_atomic_load(v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    if (x <= 0) {
+      if (x < 0) __hip_atomic_store(err, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      return;
+    }
     if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != 0u) return;
     if (wall_clock64() - t0 > limit) {
       __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
@@ -47,19 +51,21 @@ __device__ __forceinline__ void wait_flag(const uint32_t* flag, uint32_t epoch, 
   }
 }
 
-// Thread 0 waits for every listed flag; then the whole workgroup acquires at system scope so
-// that data written by the copy engine before the flag is seen (no stale cache lines).
-__device__ __forceinline__ void wait_flags_wg(const Plan& p, const int32_t* ids, int n) {
+// Thread 0 waits for every listed signal (null entries are skipped); then the whole workgroup
+// acquires at system scope so that data the copy engine wrote before the signal is seen (no
+// stale cache lines).
+__device__ __forceinline__ void wait_signals_wg(const Plan& p, const int64_t* const* sigs, int n) {
   if (threadIdx.x == 0) {
     for (int i = 0; i < n; ++i)
-      if (ids[i] >= 0) wait_flag(p.arr + (size_t)ids[i] * kFlagStride, p.epoch, p.spin_limit, p.err);
+      if (sigs[i]) wait_signal(sigs[i], p.spin_limit, p.err);
   }
   __syncthreads();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
 }
 
-// After a tile of position `pos` is stored: count it; the last tile of the position raises the
-// position's release flag (read by the copy stream's wait) and re-arms the counter.
+// After a tile of position `pos` is stored: count it; the last tile of the position stores 0 into
+// the position's release signal (polled by the copy engine that carries the next transfer) and
+// re-arms the counter.
 __device__ __forceinline__ void release_tile(const Plan& p, int pos, int tiles_per_pos) {
   if (p.rel[pos] == nullptr) return;
   __syncthreads();
@@ -69,7 +75,7 @@ __device__ __forceinline__ void release_tile(const Plan& p, int pos, int tiles_p
                                                 __HIP_MEMORY_SCOPE_AGENT);
     if (old + 1 == (uint32_t)tiles_per_pos) {
       __hip_atomic_store(p.done + pos, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(p.rel[pos], p.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+      __hip_atomic_store(p.rel[pos], (int64_t)0, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
     }
   }
 }
@@ -96,43 +102,6 @@ __device__ __forceinline__ void tile_coords(int u, int T, int tiles_m, int tiles
   const int rows = tiles_m - g * gm < gm ? tiles_m - g * gm : gm;
   tm = g * gm + r % rows;
   tn = r / rows;
-}
-
-// Writes one 32x32 accumulator fragment: lane (lr, lh) holds column lr and rows
-// 8*(v/4) + 4*lh + v%4 of the fragment in element v. The accumulate epilogue adds the received
-// partials in arrival order onto the fp32 value before the store.
-__device__ __forceinline__ void store_fragment(const Plan& p, int pos, const f32x16 a,
-                                               int64_t row0, int64_t rbase, int64_t rows_valid,
-                                               int64_t col, bool accum) {
-  if (col >= p.N) return;
-  float x[16];
-#pragma unroll
-  for (int v = 0; v < 16; ++v) x[v] = a[v];
-  if (accum) {
-    // all 16 loads of one partial are issued before any add, one partial after the other, so the
-    // sums keep the arrival order while the loads overlap
-    for (int q = 0; q < p.n_recv; ++q) {
-      const float* __restrict__ src = p.recv[q];
-      float t[16];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t r = rbase + 8 * (v >> 2) + (v & 3);
-        t[v] = r < rows_valid ? __builtin_nontemporal_load(src + (row0 + r) * p.N + col) : 0.f;
-      }
-#pragma unroll
-      for (int v = 0; v < 16; ++v) x[v] += t[v];
-    }
-  }
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int64_t r = rbase + 8 * (v >> 2) + (v & 3);
-    if (r >= rows_valid) continue;
-    const int64_t off = (row0 + r) * p.N + col;
-    if (p.out_f32)
-      ((float*)p.c_pos[pos])[off] = x[v];
-    else
-      ((uint16_t*)p.c_pos[pos])[off] = to_bf16_rne(x[v]);
-  }
 }
 
 // 16-byte streaming load (the partials are read once)
@@ -252,7 +221,7 @@ __device__ __forceinline__ void bf16_tile(const Plan& p, const int tile, uint8_t
   const uint16_t* W = (const uint16_t*)uni_ptr((const uint16_t*)p.b + col0);
 
   // Flash-AG: a received slice is read only after its arrival flag.
-  if (p.gate[pos] >= 0) wait_flags_wg(p, p.gate + pos, 1);
+  if (p.gate[pos]) wait_signals_wg(p, p.gate + pos, 1);
 
   // ---- loads. Per-lane offsets are fixed for the whole K loop: the K step enters A's loads as
   // the scalar offset and W's through a descriptor re-based on the step's first row (whose
@@ -463,7 +432,7 @@ __device__ __forceinline__ void bf16_tile(const Plan& p, const int tile, uint8_t
   // that stays on the rank, the loads of the received partials, which are all issued before any
   // of them is added (the adds keep the arrival order).
   const bool accum = (pos == p.accum_pos);
-  if (accum) wait_flags_wg(p, p.recv_flag, p.n_recv);
+  if (accum) wait_signals_wg(p, p.recv_sig, p.n_recv);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // LDS stages no longer read
   float* const ep = (float*)lds_ring;  // [ER rows][EW floats] over the whole ring
   constexpr int EW = BN + 8;      // padded row: rows 4 apart land 32 banks apart
@@ -570,7 +539,7 @@ __device__ __forceinline__ void f32_tile(const Plan& p, const int tile, float (*
   const float* A = (const float*)p.a_pos[pos] + row0 * K;
   const float* B = (const float*)p.b + col0;
 
-  if (p.gate[pos] >= 0) wait_flags_wg(p, p.gate + pos, 1);
+  if (p.gate[pos]) wait_signals_wg(p, p.gate + pos, 1);
 
   float acc[4][4];
 #pragma unroll
@@ -599,7 +568,7 @@ __device__ __forceinline__ void f32_tile(const Plan& p, const int tile, float (*
   }
 
   const bool accum = (pos == p.accum_pos);
-  if (accum) wait_flags_wg(p, p.recv_flag, p.n_recv);
+  if (accum) wait_signals_wg(p, p.recv_sig, p.n_recv);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -635,17 +604,43 @@ hipError_t launch_bf16(const Plan& p, int64_t grid, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Fills the block the copy engine copies into each arrival-flag block with the call's epoch.
-__global__ __launch_bounds__(256) void stamp_kernel(uint32_t* block, uint32_t value) {
-  uint4* b = (uint4*)block;
-  const uint4 v = make_uint4(value, value, value, value);
-  for (int i = threadIdx.x; i < kFlagBytes / 16; i += blockDim.x) b[i] = v;
+// Releases the copies that depend on a call's start signal: everything enqueued earlier on the
+// stream is complete and, after the system-scope release, visible to the copy engines.
+__global__ __launch_bounds__(64) void release_kernel(int64_t* v) {
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
+    __hip_atomic_store(v, (int64_t)0, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+}
+
+struct SignalList {
+  const int64_t* v[FO_MAX_P];
+  int32_t n;
+};
+
+// Waits until every listed signal has dropped to zero (the transfers alone, without a GEMM).
+__global__ __launch_bounds__(64) void wait_kernel(SignalList l, uint64_t limit, uint32_t* err) {
+  if (threadIdx.x == 0)
+    for (int i = 0; i < l.n; ++i)
+      if (l.v[i]) wait_signal(l.v[i], limit, err);
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
 }
 
 }  // namespace
 
-hipError_t launch_stamp(uint32_t* block, uint32_t value, hipStream_t s) {
-  hipLaunchKernelGGL(stamp_kernel, dim3(1), dim3(256), 0, s, block, value);
+hipError_t launch_release(int64_t* v, hipStream_t s) {
+  hipLaunchKernelGGL(release_kernel, dim3(1), dim3(64), 0, s, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_wait(const int64_t* const* v, int n, uint64_t spin_limit, uint32_t* err,
+                       hipStream_t s) {
+  if (n < 0 || n > FO_MAX_P) return hipErrorInvalidValue;
+  SignalList l{};
+  for (int i = 0; i < n; ++i) l.v[i] = v[i];
+  l.n = n;
+  hipLaunchKernelGGL(wait_kernel, dim3(1), dim3(64), 0, s, l, spin_limit, err);
   return hipGetLastError();
 }
 
@@ -660,9 +655,8 @@ TileShape tile_shape(int tile) {
   }
 }
 
-hipError_t launch_gemm(const Plan& p, int in_dt, int tile, int max_grid, hipStream_t s) {
-  int64_t grid = (int64_t)p.npos * p.tiles_m * p.tiles_n;
-  if (max_grid > 0 && grid > max_grid) grid = max_grid;
+hipError_t launch_gemm(const Plan& p, int in_dt, int tile, hipStream_t s) {
+  const int64_t grid = (int64_t)p.npos * p.tiles_m * p.tiles_n;
   if (in_dt == FO_DT_F32) {
     hipLaunchKernelGGL(gemm_f32_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
     return hipGetLastError();

@@ -1,9 +1,11 @@
-// Internal interfaces of libflashovl: the launch plan the kernels consume, the tile catalogue
-// and the host-side scheduler. Not part of the public C ABI.
+// Internal interfaces of libflashovl: the launch plan the kernels consume, the tile catalogue,
+// the host-side scheduler and the DMA transfer layer. Not part of the public C ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <string>
 
 #include "flashovl.h"
 
@@ -11,33 +13,29 @@ namespace fo {
 
 // One launch of the sliced GEMM. A "position" is one step of the slice schedule: the kernel's
 // workgroups are laid out position-major, so lower positions are dispatched first.
+//
+// Arrival and release flags are the 64-bit values of HSA signals. A copy engine decrements the
+// value of a slice's completion signal from 1 to 0 when the slice has landed (a negative value
+// reports a failed copy); the kernel stores 0 into a position's release signal when the position
+// is complete, and a copy engine waiting on that signal then starts the next transfer.
 struct Plan {
-  const void* a_pos[FO_MAX_P];  // A rows of position p: [m, K], row stride K
-  void* c_pos[FO_MAX_P];        // output rows of position p: [m, N], row stride N
-  const float* recv[FO_MAX_P];  // partials added in the accumulate epilogue, in arrival order
-  uint32_t* rel[FO_MAX_P];      // release flag raised when position p is complete (or null)
-  int32_t gate[FO_MAX_P];       // arrival flag the mainloop of position p waits on (-1: none)
-  int32_t recv_flag[FO_MAX_P];  // arrival flag of recv[i] (-1: resident, no wait)
-  const void* b;                // W [K, N], row stride N
-  const uint32_t* arr;          // arrival flags: flag of slice s at arr[s * kFlagStride]
-  uint32_t* done;               // per-position completed-tile counters (zero between calls)
-  uint32_t* err;                // set to nonzero when a wait runs past spin_limit
-  uint64_t spin_limit;          // bound of each wait, in wall-clock ticks
-  int64_t m, K, N;              // slice rows, reduction length, output columns
-  int32_t npos;                 // positions in this launch
-  int32_t n_recv;               // partials added at accum_pos
-  int32_t accum_pos;            // position whose epilogue adds recv[] (-1: none)
-  int32_t out_f32;              // 1: fp32 output, 0: bf16 (round to nearest even)
-  int32_t tiles_m, tiles_n;     // tiles per position
-  uint32_t epoch;               // value the flags carry for this call
+  const void* a_pos[FO_MAX_P];       // A rows of position p: [m, K], row stride K
+  void* c_pos[FO_MAX_P];             // output rows of position p: [m, N], row stride N
+  const float* recv[FO_MAX_P];       // partials added in the accumulate epilogue, in arrival order
+  const int64_t* gate[FO_MAX_P];     // completion signal the mainloop of position p waits on
+  const int64_t* recv_sig[FO_MAX_P]; // completion signal of recv[i] (null: resident, no wait)
+  int64_t* rel[FO_MAX_P];            // release signal set when position p is complete (or null)
+  const void* b;                     // W [K, N], row stride N
+  uint32_t* done;                    // per-position completed-tile counters (zero between calls)
+  uint32_t* err;                     // 1: a wait ran past spin_limit; 2: a copy reported failure
+  uint64_t spin_limit;               // bound of each wait, in wall-clock ticks
+  int64_t m, K, N;                   // slice rows, reduction length, output columns
+  int32_t npos;                      // positions in this launch
+  int32_t n_recv;                    // partials added at accum_pos
+  int32_t accum_pos;                 // position whose epilogue adds recv[] (-1: none)
+  int32_t out_f32;                   // 1: fp32 output, 0: bf16 (round to nearest even)
+  int32_t tiles_m, tiles_n;          // tiles per position
 };
-
-// Each arrival flag is the first word of its own 64 KiB block. The block is what the copy engine
-// writes to raise the flag: the HIP runtime runs device-to-device copies smaller than this as
-// copy kernels (and its stream write/wait operations as kernels too), and an arrival must never
-// need a compute unit, all of which the waiting GEMM may hold.
-constexpr int kFlagBytes = 65536;
-constexpr int kFlagStride = kFlagBytes / 4;  // in 32-bit words
 
 struct TileShape {
   int bm, bn;
@@ -49,14 +47,62 @@ TileShape tile_shape(int tile);
 int choose_tile(int P, int64_t m, int64_t N, int n_cu);
 
 // Launches the sliced GEMM for `plan` (bf16 MFMA kernel with the given tile, or the fp32
-// kernel when in_dt is FO_DT_F32). max_grid > 0 caps the number of workgroups: they then walk
-// the tiles persistently, and the CUs beyond the cap stay free for other kernels.
-hipError_t launch_gemm(const Plan& plan, int in_dt, int tile, int max_grid, hipStream_t stream);
+// kernel when in_dt is FO_DT_F32).
+hipError_t launch_gemm(const Plan& plan, int in_dt, int tile, hipStream_t stream);
 
-// Fills the kFlagBytes block at `block` with `value` (one workgroup; stream-ordered).
-hipError_t launch_stamp(uint32_t* block, uint32_t value, hipStream_t stream);
+// Stores 0 into the signal value `v` from a one-thread kernel (stream-ordered), after a
+// system-scope release: every copy that depends on the signal starts after the work enqueued
+// before it on `stream`.
+hipError_t launch_release(int64_t* v, hipStream_t stream);
+
+// One-workgroup kernel that waits (bounded by spin_limit ticks) until each of the n signal values
+// has dropped to zero, recording a timeout or a failed copy in *err like the GEMM's waits.
+hipError_t launch_wait(const int64_t* const* v, int n, uint64_t spin_limit, uint32_t* err,
+                       hipStream_t stream);
 
 // Slice schedule: kind 0 = AG, 1 = RS; order = fo_order. Writes P ids.
 int slice_order(int kind, int order, int P, int rank, int32_t* out);
 
+// ------------------------------------------------------------------ DMA transfer layer -------
+//
+// Emulated point-to-point transfers run on the GPU's SDMA engines through the HSA runtime that
+// HIP itself uses: each transfer is an asynchronous copy on one engine (one engine stands for
+// one link), gated by dependency signals that the engine itself polls, so no part of a transfer
+// or of its gating needs a compute unit (the GEMM may hold all of them).
+namespace dma {
+
+constexpr int kSlots = 4;  // calls in flight per device before the host waits for the oldest
+
+// The signals of one call. Values are device-visible addresses of the signals' 64-bit values.
+struct Call {
+  int slot;
+  int64_t* start;              // released by launch_release on the compute stream
+  int64_t* rel[FO_MAX_P];      // per position (RS lockstep)
+  int64_t* comp[FO_MAX_P];     // per slice id: completion of that slice's transfer
+};
+
+// Per-device setup (called once, under the device lock, with the device current): finds the
+// runtime and the device's agent, chooses the engines, creates the signal slots and runs one
+// small copy on every engine (an engine's first copy sets up its queue, which takes
+// milliseconds). `scratch` is device memory of at least 2 * 65536 bytes.
+bool init(int dev, void* scratch, std::string* err);
+int n_engines(int dev);
+
+// Starts a call: takes the device's next slot (first waiting, on the host, until the call that
+// used it last is complete: its event done and its copies landed), re-arms the start, release
+// and completion signals to 1, and returns them.
+bool begin(int dev, int P, Call* call, std::string* err);
+// Copy `bytes` from src to dst on link `link` (engine link mod n_engines), starting once the
+// call's start signal and, when rel_pos >= 0, the release signal of that position are zero.
+// The completion signal of slice `slice` is decremented when the copy has landed.
+bool copy(int dev, const Call& call, int link, int slice, int rel_pos, void* dst, const void* src,
+          size_t bytes, std::string* err);
+// Records, on `stream`, the point after which the call's kernels no longer read its signals
+// (after the call's last kernel).
+bool end(int dev, const Call& call, hipStream_t stream, std::string* err);
+// Waits (host, bounded) until every copy issued on the device has landed. On failure
+// *timed_out tells a copy still in flight at the bound from one the engine reported as failed.
+bool drain(int dev, uint32_t timeout_ms, std::string* err, bool* timed_out);
+
+}  // namespace dma
 }  // namespace fo

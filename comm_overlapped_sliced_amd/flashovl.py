@@ -2,8 +2,8 @@
 
 Every entry point of ``include/flashovl.h`` is exposed under the same name without the ``fo_``
 prefix. Tensors are torch device tensors (torch provides device memory and streams only); the
-computation runs entirely in the library's HIP kernels. If the library is missing this module
-raises: there is no fallback path.
+computation runs entirely in the library's HIP kernels and its DMA transfers. If the library is
+missing this module raises: there is no fallback path.
 """
 from __future__ import annotations
 
@@ -17,10 +17,8 @@ FO_OK, FO_ERR_INVALID_ARG, FO_ERR_UNSUPPORTED, FO_ERR_HIP, FO_ERR_TIMEOUT = rang
 BF16, F32 = 0, 1
 ORDER_FLASH, ORDER_NATURAL = 0, 1
 ARR_DEFAULT, ARR_NONE, ARR_EAGER, ARR_LOCKSTEP = 0, 1, 2, 3
-COPY_SDMA, COPY_BLIT = 0, 1
 TILE_AUTO, TILE_256x256, TILE_256x128, TILE_128x256, TILE_128x128, TILE_64x64 = range(6)
 MAX_P = 32
-MAX_LANES = 8
 
 EXPORTS = ("fo_opts_init", "fo_ag_gemm", "fo_gemm_rs", "fo_gemm_ref", "fo_transfer_ref",
            "fo_check", "fo_slice_order", "fo_tile_info", "fo_status_str", "fo_last_error",
@@ -35,8 +33,8 @@ class FoError(RuntimeError):
 
 class Opts(ctypes.Structure):
     _fields_ = [("order", ctypes.c_int32), ("arrival", ctypes.c_int32),
-                ("copy_engine", ctypes.c_int32), ("tile", ctypes.c_int32),
-                ("spin_timeout_us", ctypes.c_uint32), ("copy_lanes", ctypes.c_int32),
+                ("tile", ctypes.c_int32), ("spin_timeout_us", ctypes.c_uint32),
+                ("links", ctypes.c_int32), ("reserved0", ctypes.c_int32),
                 ("kernel_events", ctypes.c_void_p * 2), ("reserved", ctypes.c_int32 * 2)]
 
 
@@ -59,8 +57,8 @@ def load():
     op = ctypes.POINTER(Opts)
     lib.fo_opts_init.argtypes = [op]
     lib.fo_opts_init.restype = None
-    lib.fo_ag_gemm.argtypes = [vp, vp, vp, vp, vp, i32, i32, i64, i64, i64, i32, i32, vp, vp, op]
-    lib.fo_gemm_rs.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i64, i64, i64, i32, vp, vp, op]
+    lib.fo_ag_gemm.argtypes = [vp, vp, vp, vp, vp, i32, i32, i64, i64, i64, i32, i32, vp, op]
+    lib.fo_gemm_rs.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i64, i64, i64, i32, vp, op]
     lib.fo_gemm_ref.argtypes = [vp, vp, vp, i64, i64, i64, i32, i32, i32, vp]
     lib.fo_transfer_ref.argtypes = [i32, vp, vp, i32, i32, i64, vp, op]
     lib.fo_check.argtypes = [vp]
@@ -92,12 +90,11 @@ def _raise_on(status: int, where: str) -> None:
         raise FoError(status, where, load().fo_last_error().decode())
 
 
-def opts(order=ORDER_FLASH, arrival=ARR_DEFAULT, copy_engine=COPY_SDMA, tile=TILE_AUTO,
-         spin_timeout_us=0, copy_lanes=0, kernel_events=None) -> Opts:
+def opts(order=ORDER_FLASH, arrival=ARR_DEFAULT, tile=TILE_AUTO, spin_timeout_us=0, links=0,
+         kernel_events=None) -> Opts:
     o = Opts()
     load().fo_opts_init(ctypes.byref(o))
-    o.order, o.arrival, o.copy_engine, o.tile = order, arrival, copy_engine, tile
-    o.copy_lanes = copy_lanes
+    o.order, o.arrival, o.tile, o.links = order, arrival, tile, links
     if spin_timeout_us:
         o.spin_timeout_us = spin_timeout_us
     if kernel_events is not None:
@@ -146,7 +143,7 @@ def _ptr_array(ptrs):
 
 
 def ag_gemm(x_local, x_peer, x_recv, w, y, P: int, rank: int, compute_stream=None,
-            copy_stream=None, o: Opts | None = None, raw: bool = False):
+            o: Opts | None = None, raw: bool = False):
     """Flash-AG (fo_ag_gemm). x_local [m, K], x_peer list of P tensors (or None), x_recv
     [P*m, K], w [K, N], y [P*m, N]. Returns the status when raw=True, else raises on error."""
     m, K = x_local.shape
@@ -154,7 +151,7 @@ def ag_gemm(x_local, x_peer, x_recv, w, y, P: int, rank: int, compute_stream=Non
     peers = None if x_peer is None else _ptr_array(x_peer)
     st = load().fo_ag_gemm(_ptr(x_local), ctypes.cast(peers, ctypes.c_void_p) if peers else None,
                            _ptr(x_recv), _ptr(w), _ptr(y), P, rank, m, K, N, _dt(x_local),
-                           _dt(y), _stream(compute_stream), _stream(copy_stream),
+                           _dt(y), _stream(compute_stream),
                            ctypes.byref(o) if o is not None else None)
     if raw:
         return st
@@ -163,7 +160,7 @@ def ag_gemm(x_local, x_peer, x_recv, w, y, P: int, rank: int, compute_stream=Non
 
 
 def gemm_rs(x_shard, w, send_buf, out, peer_partial, recv_buf, P: int, rank: int,
-            compute_stream=None, copy_stream=None, o: Opts | None = None, raw: bool = False):
+            compute_stream=None, o: Opts | None = None, raw: bool = False):
     """Flash-RS (fo_gemm_rs). x_shard [P*m, K], w [K, N], send_buf [P*m, N] fp32, out [m, N]
     fp32, peer_partial list of P fp32 [m, N] tensors (or None), recv_buf [P*m, N] fp32."""
     M, K = x_shard.shape
@@ -173,7 +170,7 @@ def gemm_rs(x_shard, w, send_buf, out, peer_partial, recv_buf, P: int, rank: int
     st = load().fo_gemm_rs(_ptr(x_shard), _ptr(w), _ptr(send_buf), _ptr(out),
                            ctypes.cast(peers, ctypes.c_void_p) if peers else None,
                            _ptr(recv_buf), P, rank, m, K, N, _dt(x_shard),
-                           _stream(compute_stream), _stream(copy_stream),
+                           _stream(compute_stream),
                            ctypes.byref(o) if o is not None else None)
     if raw:
         return st
@@ -207,7 +204,8 @@ def transfer_ref(kind: str, src, dst, P: int, rank: int, slice_bytes: int, strea
 
 
 def check(stream=None) -> int:
-    """fo_check: synchronize and report in-kernel wait timeouts (raises FoError on timeout)."""
+    """fo_check: synchronize, wait for the DMA transfers, report wait timeouts and failed copies
+    (raises FoError)."""
     st = load().fo_check(_stream(stream))
     _raise_on(st, "fo_check")
     return st
@@ -232,11 +230,12 @@ def version() -> int:
     return int(load().fo_version())
 
 
-def hip_runtimes_mapped() -> set:
-    """Paths of libamdhip64 mapped into this process (one expected)."""
+def runtimes_mapped(name: str = "libamdhip64") -> set:
+    """Paths of the runtime library `name` (libamdhip64, libhsa-runtime64) mapped into this
+    process (one of each expected)."""
     paths = set()
     with open("/proc/self/maps") as f:
         for line in f:
-            if "libamdhip64" in line:
+            if name in line:
                 paths.add(os.path.realpath(line.split()[-1]))
     return paths

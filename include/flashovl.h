@@ -14,10 +14,10 @@
  * Section 3 ("Key contributions") states the algorithm is exact: every result equals the plain
  * product, whatever the slice order.
  *
- * On one GPU the peer ranks are emulated: a "peer" buffer holds what the peer would send and the
- * library copies it into the receive buffer on a copy stream (SDMA copy engine by default), then
- * raises a per-slice arrival flag. Kernels wait on those flags per slice; there is no global
- * barrier.
+ * On one GPU the peer ranks are emulated: a "peer" buffer holds what the peer would send, and the
+ * library copies it into the receive buffer with one of the GPU's SDMA engines (one engine
+ * stands for one link). Kernels wait per slice on the copy's completion; there is no global
+ * barrier, and neither a transfer nor its gating takes a compute unit from the GEMM.
  *
  * Conventions for every entry point:
  *   - All matrices are dense and row-major. X is [rows, K], W is [K, N] (N contiguous), outputs
@@ -27,20 +27,18 @@
  *     caller memory. bf16 operands must be 16-byte aligned with K and N multiples of 8; fp32
  *     buffers must be 4-byte aligned; the slice height m may be any value >= 0 (0: nothing to
  *     do) and K may be 0 (empty sums).
- *   - Streams are hipStream_t passed as void*. NULL compute stream = the null stream; NULL copy
- *     stream = a library-owned stream. Calls are stream-ordered and return after enqueueing; the
- *     copy stream is joined back into the compute stream, so synchronizing the compute stream is
- *     enough. Calls on one device are serialized by the library (they share its flags).
+ *   - Streams are hipStream_t passed as void*; NULL = the null stream. Calls are stream-ordered
+ *     and return after enqueueing. The transfers run on DMA engines outside any HIP stream, but a
+ *     call's kernel completes only after every transfer it waits for has landed, so synchronizing
+ *     the compute stream is enough (fo_check() also waits for transfers a timed-out kernel left
+ *     behind). Calls on one device are serialized by the library: each waits for the previous
+ *     call's kernel, whichever stream that was on.
  *   - Errors are return codes; nothing is enqueued when an argument is rejected. An in-kernel
  *     wait that exceeds opts->spin_timeout_us is recorded on the device and reported as
  *     FO_ERR_TIMEOUT by fo_check(); the kernel still runs to completion (no hang), but its
  *     results are then unspecified.
  *   - Thread safety: entry points may be called from several host threads; each call holds a
  *     per-device lock while it enqueues.
- *   - The copy stream must not share a hardware queue with the compute stream (HIP maps streams
- *     onto a few hardware queues per process): work queued behind the GEMM kernel could not
- *     deliver the slices that kernel waits for, and the call would end in FO_ERR_TIMEOUT. The
- *     library creates one stream of its own at initialization (more only for copy_lanes > 1).
  */
 #ifndef FLASHOVL_H
 #define FLASHOVL_H
@@ -58,7 +56,8 @@ typedef enum fo_status {
   FO_OK = 0,
   FO_ERR_INVALID_ARG = 1, /* a NULL/misaligned pointer, bad size, rank, dtype or option */
   FO_ERR_UNSUPPORTED = 2, /* well-formed but not implemented (e.g. a dtype combination) */
-  FO_ERR_HIP = 3,         /* a HIP runtime call failed; fo_last_error() has its message */
+  FO_ERR_HIP = 3,         /* a HIP or HSA runtime call or a DMA transfer failed; fo_last_error()
+                             has the message */
   FO_ERR_TIMEOUT = 4      /* an in-kernel arrival wait ran past its bound */
 } fo_status;
 
@@ -81,12 +80,6 @@ typedef enum fo_arrival {
   FO_ARR_LOCKSTEP = 3
 } fo_arrival;
 
-/* Engine that performs the emulated transfers. SDMA: hipMemcpyDeviceToDeviceNoCU, a DMA engine
-   that takes no compute units (stands in for a link's copy engine). BLIT: an ordinary
-   device-to-device copy, run by copy kernels on the compute units (much faster, but competes
-   with the GEMM for CUs and HBM). */
-typedef enum fo_copy_engine { FO_COPY_SDMA = 0, FO_COPY_BLIT = 1 } fo_copy_engine;
-
 /* Tile shape of the bf16 GEMM (rows x columns of one workgroup's output tile). AUTO picks one
    from the shape. */
 typedef enum fo_tile {
@@ -98,24 +91,24 @@ typedef enum fo_tile {
   FO_TILE_64x64 = 5
 } fo_tile;
 
-#define FO_MAX_LANES 8 /* most copy streams one emulated transfer is striped over */
-
 typedef struct fo_opts {
   int32_t order;            /* fo_order */
   int32_t arrival;          /* fo_arrival */
-  int32_t copy_engine;      /* fo_copy_engine */
   int32_t tile;             /* fo_tile */
   uint32_t spin_timeout_us; /* bound of each in-kernel wait; 0 = 2 000 000 us */
-  int32_t copy_lanes;       /* 1..FO_MAX_LANES: each transfer is split into this many contiguous
-                               pieces copied concurrently on separate streams (several copy
-                               engines, like several links); 0 = 1 */
+  int32_t links;            /* emulated links (DMA engines) the call's transfers use: the t-th
+                               transfer goes over link t mod links, transfers on one link run
+                               one after the other. 0 = P-1 (one link per peer, the full xGMI
+                               mesh of an 8-GPU node); 1 = a single link, as in a ring whose
+                               slices all come from one neighbour */
+  int32_t reserved0;        /* must be zero */
   void* kernel_events[2];   /* optional hipEvent_t pair recorded on the compute stream right
                                before and right after the GEMM kernel launch (profiling) */
   int32_t reserved[2];      /* must be zero */
 } fo_opts;
 
-/* Fills *o with the defaults (FLASH order, DEFAULT arrival, SDMA, AUTO tile, 2 s bound, one
-   lane, no events). */
+/* Fills *o with the defaults (FLASH order, DEFAULT arrival, AUTO tile, 2 s bound, one link per
+   peer, no events). */
 void fo_opts_init(fo_opts* o);
 
 /*
@@ -128,13 +121,12 @@ void fo_opts_init(fo_opts* o);
  *   w        device [K, N] in_dt, this rank's column shard of the weight.
  *   y        device [P*m, N] out_dt; rows s*m .. s*m+m-1 hold X_s . W.
  * Slices are computed in the Flash-AG order (rank, rank-1, ..., rank-P+1 mod P); slice s != rank
- * is read only after its arrival flag is raised. in_dt and out_dt: BF16 or F32; out_dt BF16
+ * is read only after its transfer has landed. in_dt and out_dt: BF16 or F32; out_dt BF16
  * rounds the fp32 accumulator to nearest-even. No output may overlap an input.
  */
 fo_status fo_ag_gemm(const void* x_local, const void* const* x_peer, void* x_recv, const void* w,
                      void* y, int32_t P, int32_t rank, int64_t m, int64_t K, int64_t N,
-                     int32_t in_dt, int32_t out_dt, void* compute_stream, void* copy_stream,
-                     const fo_opts* opts);
+                     int32_t in_dt, int32_t out_dt, void* compute_stream, const fo_opts* opts);
 
 /*
  * Flash-RS: the P row-chunks of X_shard . W for rank `rank` (row-parallel projection), own chunk
@@ -154,7 +146,7 @@ fo_status fo_ag_gemm(const void* x_local, const void* const* x_peer, void* x_rec
 fo_status fo_gemm_rs(const void* x_shard, const void* w, float* send_buf, float* out,
                      const float* const* peer_partial, float* recv_buf, int32_t P, int32_t rank,
                      int64_t m, int64_t K, int64_t N, int32_t in_dt, void* compute_stream,
-                     void* copy_stream, const fo_opts* opts);
+                     const fo_opts* opts);
 
 /*
  * Plain monolithic GEMM C[M, N] = A[M, K] . B[K, N] with the same kernels (no slices, no waits):
@@ -167,19 +159,23 @@ fo_status fo_gemm_ref(const void* a, const void* b, void* c, int64_t M, int64_t 
 
 /*
  * The emulated transfers of one fo_ag_gemm (kind 0) or fo_gemm_rs (kind 1) call on their own,
- * without the GEMM: the same copies, engine, lanes and arrival order, issued back to back on
- * `stream` (RS releases are not awaited, no flag is raised). Its duration is the transfer time
- * of the exposed-transfer fraction (sliced latency minus pure-GEMM latency, over transfer time).
+ * without the GEMM: the same copies, links and arrival order (RS releases are not awaited). On
+ * `stream` it enqueues the release of the copies and a one-workgroup kernel that waits until all
+ * of them have landed, so the stream's time from the release to that kernel's end is the transfer
+ * time of the exposed-transfer fraction (sliced latency minus pure-GEMM latency, over transfer
+ * time).
  *   src    host array of P device pointers; src[s] is slice s (slice_bytes bytes). Entry [rank]
  *          is ignored.
  *   dst    device buffer of P*slice_bytes bytes; slice s lands at dst + s*slice_bytes.
- * opts: order, copy_engine and copy_lanes are used. slice_bytes must be a multiple of 4.
+ * opts: order, links and spin_timeout_us are used. slice_bytes must be a multiple of 4.
  */
 fo_status fo_transfer_ref(int32_t kind, const void* const* src, void* dst, int32_t P,
                           int32_t rank, int64_t slice_bytes, void* stream, const fo_opts* opts);
 
-/* Synchronizes `stream` (hipStream_t) and reports FO_ERR_TIMEOUT if any in-kernel wait on the
-   current device ran past its bound since the previous fo_check (the record is then cleared). */
+/* Synchronizes `stream` (hipStream_t), waits (on the host, at most 30 s) until every transfer the
+   library issued on the current device has landed, and reports what happened since the previous
+   fo_check: FO_ERR_TIMEOUT if an in-kernel wait ran past its bound or a transfer did not land in
+   time, FO_ERR_HIP if a DMA engine reported a failed copy. The record is then cleared. */
 fo_status fo_check(void* stream);
 
 /* Host-side slice scheduler. kind 0 = AG, 1 = RS; order a fo_order. Writes P slice/chunk ids in

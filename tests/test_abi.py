@@ -45,10 +45,10 @@ def test_version_and_status_strings(lib):
 
 def test_opts_defaults():
     o = fo.opts()
-    assert (o.order, o.arrival, o.copy_engine, o.tile) == (0, 0, 0, 0)
+    assert (o.order, o.arrival, o.tile, o.links) == (0, 0, 0, 0)
     assert o.spin_timeout_us == 2_000_000
-    assert o.copy_lanes == 0 and list(o.kernel_events) == [None, None]
-    assert list(o.reserved) == [0, 0]
+    assert list(o.kernel_events) == [None, None]
+    assert o.reserved0 == 0 and list(o.reserved) == [0, 0]
     assert ctypes.sizeof(fo.Opts) == 48
 
 
@@ -99,7 +99,7 @@ D = 0x40000000
 
 def _ag(lib, **kw):
     args = dict(x_local=A, x_peer=None, x_recv=B, w=C, y=D, P=4, rank=0, m=64, K=256, N=512,
-                in_dt=fo.BF16, out_dt=fo.BF16, cs=None, ks=None, opts=None)
+                in_dt=fo.BF16, out_dt=fo.BF16, cs=None, opts=None)
     args.update(kw)
     peers = args["x_peer"]
     if peers is not None:
@@ -107,7 +107,7 @@ def _ag(lib, **kw):
         peers = ctypes.cast(arr, ctypes.c_void_p)
     return lib.fo_ag_gemm(args["x_local"], peers, args["x_recv"], args["w"], args["y"], args["P"],
                           args["rank"], args["m"], args["K"], args["N"], args["in_dt"],
-                          args["out_dt"], args["cs"], args["ks"], args["opts"])
+                          args["out_dt"], args["cs"], args["opts"])
 
 
 @pytest.mark.parametrize("kw", [
@@ -125,8 +125,8 @@ def test_ag_rejects(lib, kw):
 
 
 def test_ag_rejects_bad_opts(lib):
-    for field, val in [("order", 9), ("arrival", 7), ("copy_engine", 3), ("tile", 11),
-                       ("copy_lanes", 9), ("copy_lanes", -1)]:
+    for field, val in [("order", 9), ("arrival", 7), ("tile", 11), ("links", 33), ("links", -1),
+                       ("reserved0", 1)]:
         o = fo.opts()
         setattr(o, field, val)
         assert _ag(lib, opts=ctypes.byref(o)) == fo.FO_ERR_INVALID_ARG
@@ -153,7 +153,7 @@ def _rs(lib, **kw):
         peers = ctypes.cast(arr, ctypes.c_void_p)
     return lib.fo_gemm_rs(args["x"], args["w"], args["send"], args["out"], peers, args["recv"],
                           args["P"], args["rank"], args["m"], args["K"], args["N"], args["in_dt"],
-                          None, None, args["opts"])
+                          None, args["opts"])
 
 
 @pytest.mark.parametrize("kw", [

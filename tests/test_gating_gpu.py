@@ -1,10 +1,11 @@
 """GPU tests of per-slice gating: a slice is read only after it has arrived, stale data in the
-receive buffers is never used, late arrivals only delay the result, and an arrival that never
-comes within the bound is reported as FO_ERR_TIMEOUT while every kernel still finishes.
+receive buffers is never used, late arrivals only delay the result, and an arrival that does not
+come within the bound is reported as FO_ERR_TIMEOUT while every kernel still finishes.
 
-Late and missing arrivals are forced from the host: the caller's copy stream is held by a
-sleeping kernel queued before the call, so the copies start late; the kernels' own bounded waits
-guarantee termination."""
+Late arrivals are forced by the sizes: large slices carried one after the other over a single
+emulated link (one DMA engine) against a GEMM whose N is small, so the GEMM reaches every slice
+long before it lands. A missed arrival is forced from the host with a 1 us bound on the
+kernel's own waits; the transfers still land and fo_check() waits for them."""
 from __future__ import annotations
 
 import numpy as np
@@ -29,27 +30,6 @@ def dev():
     return torch.device("cuda:0")
 
 
-@pytest.fixture(scope="module")
-def cycles_per_ms(dev):
-    """Calibrates torch.cuda._sleep (a one-wave spin kernel) against event time."""
-    s = torch.cuda.Stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(s):
-        torch.cuda._sleep(1000)
-        e0.record(s)
-        torch.cuda._sleep(2_000_000)
-        e1.record(s)
-    s.synchronize()
-    ms = e0.elapsed_time(e1)
-    assert ms > 0
-    return 2_000_000 / ms
-
-
-def _delay(stream, cycles_per_ms, ms):
-    with torch.cuda.stream(stream):
-        torch.cuda._sleep(int(cycles_per_ms * ms))
-
-
 def test_poisoned_rerun_ag(dev):
     """Receive buffer filled with NaN before every call and the peers' data alternated between
     calls: any early or stale read shows up as a wrong or NaN result."""
@@ -64,11 +44,11 @@ def test_poisoned_rerun_ag(dev):
         # share one receive buffer between both problems, poisoned each time
         prob.x_recv = probs[0].x_recv
         prob.x_recv.view(torch.int16).fill_(-1)  # 0xffff: a bf16 NaN
-        for engine in (fo.COPY_SDMA, fo.COPY_BLIT):
+        for links in (0, 1):
             prob.x_recv.view(torch.int16).fill_(-1)
-            got = prob.run(it % P, o=fo.opts(copy_engine=engine))
+            got = prob.run(it % P, o=fo.opts(links=links))
             assert not np.isnan(got).any()
-            assert rel_frobenius(got, refs[i]) <= TOL_BF16, f"iteration {it} engine {engine}"
+            assert rel_frobenius(got, refs[i]) <= TOL_BF16, f"iteration {it} links {links}"
 
 
 def test_poisoned_rerun_rs(dev):
@@ -91,38 +71,43 @@ def test_poisoned_rerun_rs(dev):
             assert rel_frobenius(out, ref) <= TOL_BF16, f"iteration {it}"
 
 
-@pytest.mark.parametrize("engine", [fo.COPY_SDMA, fo.COPY_BLIT], ids=["sdma", "blit"])
-def test_late_arrivals_only_delay(dev, cycles_per_ms, engine):
-    P, m, K, N = 8, 256, 1024, 512
+def test_late_arrivals_only_delay(dev):
+    """Seven 8 MiB slices over one link take about a millisecond; the GEMM (N = 128) needs a few
+    microseconds per slice, so every received slice is waited for."""
+    P, m, K, N = 8, 1024, 4096, 128
     x = inputs.normal(7800, (P * m, K), 1.0, "bf16")
     w = inputs.normal(7801, (K, N), 0.02, "bf16")
     prob = AG(x, w, P, dev)
     ref = oracle.gemm(x, w)
-    copy = torch.cuda.Stream()
-    prob.x_recv.view(torch.int16).fill_(-1)
-    _delay(copy, cycles_per_ms, 5.0)
-    got = prob.run(2, o=fo.opts(copy_engine=engine), copy_stream=copy)
-    assert rel_frobenius(got, ref) <= TOL_BF16
-    parts = [inputs.normal(7810 + q, (m, N), 1.0, "f32") for q in range(P)]
-    rs = RS(x, w, parts, P, dev)
-    rs.recv.fill_(float("nan"))
-    _delay(copy, cycles_per_ms, 5.0)
-    out, _ = rs.run(6, o=fo.opts(copy_engine=engine), copy_stream=copy)
-    assert rel_frobenius(out, oracle.rs(x, w, parts, P, 6)) <= TOL_BF16
+    for r in (2, 5):
+        prob.x_recv.view(torch.int16).fill_(-1)
+        got = prob.run(r, o=fo.opts(links=1))
+        assert not np.isnan(got).any()
+        assert rel_frobenius(got, ref) <= TOL_BF16
+    # Flash-RS: seven 8 MiB partials over one link, K = 64
+    Pr, mr, Kr, Nr = 8, 512, 64, 4096
+    xr = inputs.normal(7802, (Pr * mr, Kr), 1.0, "bf16")
+    wr = inputs.normal(7803, (Kr, Nr), 0.02, "bf16")
+    parts = [inputs.normal(7810 + q, (mr, Nr), 1.0, "f32") for q in range(Pr)]
+    rs = RS(xr, wr, parts, Pr, dev)
+    for r, arrival in ((6, fo.ARR_LOCKSTEP), (1, fo.ARR_EAGER)):
+        rs.recv.fill_(float("nan"))
+        out, _ = rs.run(r, o=fo.opts(links=1, arrival=arrival))
+        assert not np.isnan(out).any()
+        assert rel_frobenius(out, oracle.rs(xr, wr, parts, Pr, r)) <= TOL_BF16
 
 
-def test_withheld_arrival_times_out(dev, cycles_per_ms):
-    """Arrivals held back far beyond a 2 ms bound: the call reports FO_ERR_TIMEOUT, the kernel
-    finishes, and the next call is correct again."""
-    P, m, K, N = 4, 128, 256, 256
+def test_missed_arrival_times_out(dev):
+    """A 1 us bound on the in-kernel waits against transfers that take a millisecond: the call
+    reports FO_ERR_TIMEOUT, the kernel finishes, fo_check() waits for the transfers, and the next
+    call is correct again."""
+    P, m, K, N = 8, 1024, 4096, 128
     x = inputs.normal(7900, (P * m, K), 1.0, "bf16")
     w = inputs.normal(7901, (K, N), 0.02, "bf16")
     prob = AG(x, w, P, dev)
-    copy = torch.cuda.Stream()
-    _delay(copy, cycles_per_ms, 60.0)
     st = fo.ag_gemm(prob.peer[1], prob.peer, prob.x_recv, prob.w_d, prob.y, P, 1,
-                    compute_stream=torch.cuda.current_stream(), copy_stream=copy,
-                    o=fo.opts(spin_timeout_us=2000), raw=True)
+                    compute_stream=torch.cuda.current_stream(),
+                    o=fo.opts(spin_timeout_us=1, links=1), raw=True)
     assert st == fo.FO_OK
     with pytest.raises(fo.FoError) as ei:
         fo.check(torch.cuda.current_stream())

@@ -29,7 +29,8 @@ def dev():
         pytest.skip("no GPU")
     torch.cuda.set_device(0)
     fo.load()
-    assert len(fo.hip_runtimes_mapped()) == 1, fo.hip_runtimes_mapped()
+    for name in ("libamdhip64", "libhsa-runtime64"):
+        assert len(fo.runtimes_mapped(name)) == 1, fo.runtimes_mapped(name)
     return torch.device("cuda:0")
 
 
@@ -55,16 +56,16 @@ class AG:
         self.y = torch.empty((self.M, self.N), dtype=ot, device=dev)
         self.dev = dev
 
-    def run(self, r, o=None, copy_stream=None, resident=False):
+    def run(self, r, o=None, resident=False):
         if resident:  # arrivals NONE: the slices are already in x_recv
             for s in range(self.P):
                 if s != r:
                     self.x_recv[s * self.m:(s + 1) * self.m].copy_(self.peer[s])
             fo.ag_gemm(self.peer[r], None, self.x_recv, self.w_d, self.y, self.P, r,
-                       compute_stream=_stream(), copy_stream=copy_stream, o=o)
+                       compute_stream=_stream(), o=o)
         else:
             fo.ag_gemm(self.peer[r], self.peer, self.x_recv, self.w_d, self.y, self.P, r,
-                       compute_stream=_stream(), copy_stream=copy_stream, o=o)
+                       compute_stream=_stream(), o=o)
         fo.check(_stream())
         return from_dev(self.y)
 
@@ -85,46 +86,47 @@ class RS:
         self.out = torch.empty((self.m, self.N), dtype=torch.float32, device=dev)
         self.recv = torch.empty((self.M, self.N), dtype=torch.float32, device=dev)
 
-    def run(self, r, o=None, copy_stream=None, resident=False):
+    def run(self, r, o=None, resident=False):
         self.send.fill_(float("nan"))
         if resident:
             for q in range(self.P):
                 if q != r:
                     self.recv[q * self.m:(q + 1) * self.m].copy_(self.peer[q])
             fo.gemm_rs(self.x_d, self.w_d, self.send, self.out, None, self.recv, self.P, r,
-                       compute_stream=_stream(), copy_stream=copy_stream, o=o)
+                       compute_stream=_stream(), o=o)
         else:
             fo.gemm_rs(self.x_d, self.w_d, self.send, self.out, self.peer, self.recv, self.P, r,
-                       compute_stream=_stream(), copy_stream=copy_stream, o=o)
+                       compute_stream=_stream(), o=o)
         fo.check(_stream())
         return from_dev(self.out), from_dev(self.send)
 
 
-ENGINES = [("sdma", fo.COPY_SDMA), ("blit", fo.COPY_BLIT)]
+# emulated link topologies: one DMA engine per peer (default), and every transfer over one link
+LINKS = [("mesh", 0), ("onelink", 1)]
 
 
 # ---- config 1: integer-valued fp32, bit-exact ----------------------------------------------
 
-@pytest.mark.parametrize("engine", ENGINES, ids=lambda e: e[0])
+@pytest.mark.parametrize("links", LINKS, ids=lambda e: e[0])
 @pytest.mark.parametrize("mode", ["eager", "resident"])
-def test_tiny_fp32_ag_bit_exact(dev, engine, mode):
+def test_tiny_fp32_ag_bit_exact(dev, links, mode):
     c = configs.TINY_AG
     prob = AG(c.x(), c.w(), c.P, dev, out_dt="f32")
     for r in range(c.P):
-        got = prob.run(r, o=fo.opts(copy_engine=engine[1]), resident=(mode == "resident"))
+        got = prob.run(r, o=fo.opts(links=links[1]), resident=(mode == "resident"))
         ref = oracle.ag(prob.slices, c.w(), c.P, r)
         assert np.array_equal(got, ref), f"rank {r}"
 
 
-@pytest.mark.parametrize("engine", ENGINES, ids=lambda e: e[0])
+@pytest.mark.parametrize("links", LINKS, ids=lambda e: e[0])
 @pytest.mark.parametrize("arrival", [("lockstep", fo.ARR_LOCKSTEP), ("eager", fo.ARR_EAGER),
                                      ("resident", None)], ids=lambda a: a[0])
-def test_tiny_fp32_rs_bit_exact(dev, engine, arrival):
+def test_tiny_fp32_rs_bit_exact(dev, links, arrival):
     c = configs.TINY_RS
     parts = [c.partial(q) for q in range(c.P)]
     prob = RS(c.x(), c.w(), parts, c.P, dev)
     for r in range(c.P):
-        o = fo.opts(copy_engine=engine[1], arrival=arrival[1] or fo.ARR_DEFAULT)
+        o = fo.opts(links=links[1], arrival=arrival[1] or fo.ARR_DEFAULT)
         out, send = prob.run(r, o=o, resident=arrival[1] is None)
         ref_out, ref_send = oracle.rs(c.x(), c.w(), parts, c.P, r, want_send=True)
         assert np.array_equal(out, ref_out), f"rank {r}"
