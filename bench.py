@@ -74,6 +74,9 @@ def parse():
     ap.add_argument("--no-exposure", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample (0 disables)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="also run one plain device copy of BYTES bytes after the warmup: the "
+                         "reference that scales the HBM byte counters of a profiled run")
     return ap.parse_args()
 
 
@@ -156,6 +159,19 @@ def main():
     for _ in range(args.warmup):
         step()
     fo.check(stream)
+    if args.copy_calibration:
+        n = args.copy_calibration
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        # a 512 MiB fill between the writes of src and the copy leaves no src line in the
+        # 256 MB last-level cache
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        flush.fill_(3)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {n} bytes read and written by one copy kernel")
+        del src, dst, flush
 
     # ---- exposed-transfer decomposition (before the timed region) ------------------------
     exposure = None

@@ -11,8 +11,7 @@
 // the kernels poll. One engine stands for one link: transfers on the same link run one after
 // the other in issue order, transfers on different links run concurrently.
 //
-// The HSA entry points are looked up in the HSA runtime already loaded into the process (the
-// one HIP runs on), so the library never brings a second runtime instance into the process.
+// The HSA entry points are those of the HSA runtime instance that HIP itself runs on.
 #include <dlfcn.h>
 #include <link.h>
 #include <hsa/hsa.h>
@@ -34,7 +33,6 @@ namespace dma {
 namespace {
 
 struct Hsa {
-  decltype(&hsa_init) init = nullptr;
   decltype(&hsa_amd_pointer_info) pointer_info = nullptr;
   decltype(&hsa_amd_memory_copy_engine_status) engine_status = nullptr;
   decltype(&hsa_amd_signal_create) signal_create = nullptr;
@@ -46,7 +44,6 @@ struct Hsa {
 
 Hsa g_hsa;
 bool g_hsa_ok = false;
-std::once_flag g_hsa_once;
 std::string g_hsa_err;
 
 int collect_hsa(struct dl_phdr_info* info, size_t, void* data) {
@@ -55,39 +52,51 @@ int collect_hsa(struct dl_phdr_info* info, size_t, void* data) {
   return 0;
 }
 
-void resolve_hsa() {
-  std::vector<std::string> libs;
-  dl_iterate_phdr(collect_hsa, &libs);
-  if (libs.empty()) {
-    g_hsa_err = "no HSA runtime is loaded in the process";
-    return;
-  }
-  if (libs.size() > 1) {
-    g_hsa_err = "more than one HSA runtime is loaded in the process (" + libs[0] + ", " + libs[1] + ")";
-    return;
-  }
-  void* h = dlopen(libs[0].c_str(), RTLD_NOW | RTLD_NOLOAD);
-  if (!h) {
-    g_hsa_err = "cannot open the loaded HSA runtime " + libs[0];
-    return;
-  }
+bool table_of(void* h, Hsa* t, std::string* err) {
   bool ok = true;
   auto get = [&](auto& fn, const char* name) {
     fn = reinterpret_cast<std::remove_reference_t<decltype(fn)>>(dlsym(h, name));
     if (!fn) {
       ok = false;
-      g_hsa_err = std::string("the HSA runtime lacks ") + name;
+      *err = std::string("the HSA runtime lacks ") + name;
     }
   };
-  get(g_hsa.init, "hsa_init");
-  get(g_hsa.pointer_info, "hsa_amd_pointer_info");
-  get(g_hsa.engine_status, "hsa_amd_memory_copy_engine_status");
-  get(g_hsa.signal_create, "hsa_amd_signal_create");
-  get(g_hsa.value_pointer, "hsa_amd_signal_value_pointer");
-  get(g_hsa.store, "hsa_signal_store_screlease");
-  get(g_hsa.load, "hsa_signal_load_scacquire");
-  get(g_hsa.copy, "hsa_amd_memory_async_copy_on_engine");
-  g_hsa_ok = ok;
+  get(t->pointer_info, "hsa_amd_pointer_info");
+  get(t->engine_status, "hsa_amd_memory_copy_engine_status");
+  get(t->signal_create, "hsa_amd_signal_create");
+  get(t->value_pointer, "hsa_amd_signal_value_pointer");
+  get(t->store, "hsa_signal_store_screlease");
+  get(t->load, "hsa_signal_load_scacquire");
+  get(t->copy, "hsa_amd_memory_async_copy_on_engine");
+  return ok;
+}
+
+// Picks the HSA runtime HIP runs on. A process can hold more than one copy of the runtime (a
+// profiler's tool library brings its own), and only the instance HIP initialized knows HIP's
+// allocations: the runtime chosen is the one that recognizes `dev_ptr`, a hipMalloc'ed buffer.
+void resolve_hsa(const void* dev_ptr) {
+  std::vector<std::string> libs;
+  dl_iterate_phdr(collect_hsa, &libs);
+  g_hsa_err = "no HSA runtime in the process knows the library's device allocation";
+  for (const std::string& lib : libs) {
+    void* h = dlopen(lib.c_str(), RTLD_NOW | RTLD_NOLOAD);
+    if (!h) continue;
+    Hsa t;
+    std::string e;
+    if (!table_of(h, &t, &e)) {
+      g_hsa_err = e + " (" + lib + ")";
+      continue;
+    }
+    hsa_amd_pointer_info_t info;
+    memset(&info, 0, sizeof info);
+    info.size = sizeof info;
+    if (t.pointer_info(dev_ptr, &info, nullptr, nullptr, nullptr) == HSA_STATUS_SUCCESS &&
+        info.type == HSA_EXT_POINTER_TYPE_HSA) {
+      g_hsa = t;
+      g_hsa_ok = true;
+      return;
+    }
+  }
 }
 
 struct Slot {
@@ -176,17 +185,20 @@ bool init(int dev, void* scratch, std::string* err) {
   }
   Dev& d = g_dev[dev];
   if (d.ready) return true;
-  std::call_once(g_hsa_once, resolve_hsa);
-  if (!g_hsa_ok) {
-    *err = g_hsa_err;
-    return false;
+  {
+    static std::mutex m;  // devices initialize under their own locks
+    std::lock_guard<std::mutex> lk(m);
+    if (!g_hsa_ok) resolve_hsa(scratch);
+    if (!g_hsa_ok) {
+      *err = g_hsa_err;
+      return false;
+    }
   }
-  hsa_status_t s = g_hsa.init();  // HIP has initialized the runtime already; this only counts up
-  if (s != HSA_STATUS_SUCCESS) return fail(err, "hsa_init", s);
+  // the runtime is up: HIP initialized it before it allocated `scratch`
   hsa_amd_pointer_info_t info;
   memset(&info, 0, sizeof info);
   info.size = sizeof info;
-  s = g_hsa.pointer_info(scratch, &info, nullptr, nullptr, nullptr);
+  hsa_status_t s = g_hsa.pointer_info(scratch, &info, nullptr, nullptr, nullptr);
   if (s != HSA_STATUS_SUCCESS) return fail(err, "hsa_amd_pointer_info", s);
   if (info.type != HSA_EXT_POINTER_TYPE_HSA) {
     *err = "the library's scratch buffer is not device memory of the HSA runtime";
