@@ -70,6 +70,8 @@ def parse():
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--links", type=int, default=0,
                     help="emulated links per call (0: one DMA engine per peer; 1: one link)")
+    ap.add_argument("--row-groups", type=int, default=0,
+                    help="row groups per slice (0: one per tile row; 1: whole slices)")
     ap.add_argument("--exposure-reps", type=int, default=15)
     ap.add_argument("--no-exposure", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -130,13 +132,13 @@ def main():
     def ev():
         return torch.cuda.Event(enable_timing=True)
 
-    def ag_call(evs=None, arrival=fo.ARR_DEFAULT, links=args.links):
-        o = fo.opts(links=links, arrival=arrival, kernel_events=evs)
+    def ag_call(evs=None, arrival=fo.ARR_DEFAULT, links=args.links, groups=args.row_groups):
+        o = fo.opts(links=links, row_groups=groups, arrival=arrival, kernel_events=evs)
         peers = None if arrival == fo.ARR_NONE else ag_slices
         fo.ag_gemm(ag_slices[r], peers, ag_recv, ag_w, ag_y, P, r, compute_stream=stream, o=o)
 
-    def rs_call(evs=None, arrival=fo.ARR_DEFAULT, links=args.links):
-        o = fo.opts(links=links, arrival=arrival, kernel_events=evs)
+    def rs_call(evs=None, arrival=fo.ARR_DEFAULT, links=args.links, groups=args.row_groups):
+        o = fo.opts(links=links, row_groups=groups, arrival=arrival, kernel_events=evs)
         peers = None if arrival == fo.ARR_NONE else rs_peer
         fo.gemm_rs(rs_x, rs_w, rs_send, rs_out, peers, rs_recv, P, r, compute_stream=stream, o=o)
 
@@ -178,21 +180,28 @@ def main():
     if not args.no_exposure:
         exposure = {}
         reps = args.exposure_reps
-        # one DMA engine per peer (the xGMI mesh), and every transfer over one link (the ring of
-        # the page's Flash-AG, where all slices come from one neighbour)
-        variants = [("mesh", 0), ("onelink", 1)]
+        # one DMA engine per peer (the xGMI mesh) with row-group arrivals (the default), the same
+        # with whole slices (the page's granularity), and every transfer over one link (the
+        # ring of the page's Flash-AG, where all slices come from one neighbour)
+        variants = [("mesh_rowgroups", 0, 0), ("mesh_slices", 0, 1), ("onelink_slices", 1, 1)]
+
+        def groups_of(kind, case, req):
+            order = fo.tile_order(kind, P, case.m, case.K, case.N, o=fo.opts(row_groups=req))
+            return max(g for _, g, _, _ in order) + 1
+
         t_ref_ag = timed(lambda: fo.gemm_ref(ag_full, ag_w, ref_y_ag, stream=stream), reps)
         t_ref_rs = timed(lambda: fo.gemm_ref(rs_x, rs_w, ref_y_rs, stream=stream), reps)
         t0_ag = timed(lambda: ag_call(arrival=fo.ARR_NONE), reps)
         t0_rs = timed(lambda: rs_call(arrival=fo.ARR_NONE), reps)
-        for name, links in variants:
-            to = fo.opts(links=links)
+        for name, links, req in variants:
+            to_ag = fo.opts(links=links, row_groups=groups_of("ag", ag_case, req))
+            to_rs = fo.opts(links=links, row_groups=groups_of("rs", rs_case, req))
             tx_ag = timed(lambda: fo.transfer_ref("ag", ag_slices, ag_recv, P, r,
-                                                  ag_case.m * ag_case.K * 2, stream, to), reps)
+                                                  ag_case.m * ag_case.K * 2, stream, to_ag), reps)
             tx_rs = timed(lambda: fo.transfer_ref("rs", rs_peer, rs_recv, P, r,
-                                                  rs_case.m * rs_case.N * 4, stream, to), reps)
-            ts_ag = timed(lambda: ag_call(links=links), reps)
-            ts_rs = timed(lambda: rs_call(links=links), reps)
+                                                  rs_case.m * rs_case.N * 4, stream, to_rs), reps)
+            ts_ag = timed(lambda: ag_call(links=links, groups=req), reps)
+            ts_rs = timed(lambda: rs_call(links=links, groups=req), reps)
             exposure[name] = {
                 "ag": {"t_ref_us": t_ref_ag * 1e3, "t_slice0_us": t0_ag * 1e3,
                        "t_slice_us": ts_ag * 1e3, "t_xfer_us": tx_ag * 1e3,
@@ -262,6 +271,7 @@ def main():
                    "P=8 slices" % r,
                    "transfers": "SDMA engines, %s" % ("one per peer" if args.links == 0
                                                       else "%d link(s)" % args.links),
+                   "row_groups": "one per tile row" if args.row_groups == 0 else args.row_groups,
                    "ag_arrival": "eager", "rs_arrival": "lockstep"},
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "exposed_transfer": exposure,

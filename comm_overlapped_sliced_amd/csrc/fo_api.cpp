@@ -75,7 +75,7 @@ struct DevState {
   int n_cu = 0;
   int wall_khz = 100000;     // wall-clock counter rate read by the kernels' bounded waits
   uint32_t* err = nullptr;   // wait record: 1 timeout, 2 failed copy (uncached memory)
-  uint32_t* done = nullptr;  // [FO_MAX_P] completed-tile counters
+  uint32_t* done = nullptr;  // completed-tile counters [position][group]
   void* scratch = nullptr;   // source and destination of the DMA engines' first copies
   hipEvent_t ev_last = nullptr;
   bool have_last = false;
@@ -94,9 +94,10 @@ fo_status ensure_ready(int dev, DevState& st) {
   FO_HIP(hipExtMallocWithFlags(&p, 4096, hipDeviceMallocUncached));
   st.err = (uint32_t*)p;
   FO_HIP(hipMemset(p, 0, 4096));
-  FO_HIP(hipMalloc(&p, FO_MAX_P * sizeof(uint32_t)));
+  const size_t counters = (size_t)FO_MAX_P * fo::kMaxGroups * sizeof(uint32_t);
+  FO_HIP(hipMalloc(&p, counters));
   st.done = (uint32_t*)p;
-  FO_HIP(hipMemset(st.done, 0, FO_MAX_P * sizeof(uint32_t)));
+  FO_HIP(hipMemset(st.done, 0, counters));
   FO_HIP(hipMalloc(&st.scratch, kScratchBytes));
   FO_HIP(hipMemset(st.scratch, 0, kScratchBytes));
   FO_HIP(hipEventCreateWithFlags(&st.ev_last, hipEventDisableTiming));
@@ -145,7 +146,9 @@ fo_status check_opts(const fo_opts* o, fo_opts* out) {
     return invalid("opts.tile %d is not a fo_tile", o->tile);
   if (o->links < 0 || o->links > FO_MAX_P)
     return invalid("opts.links %d outside [0, %d]", o->links, FO_MAX_P);
-  if (o->reserved0 || o->reserved[0] || o->reserved[1]) return invalid("opts.reserved must be zero");
+  if (o->row_groups < 0 || o->row_groups > fo::kMaxGroups)
+    return invalid("opts.row_groups %d outside [0, %d]", o->row_groups, fo::kMaxGroups);
+  if (o->reserved[0] || o->reserved[1]) return invalid("opts.reserved must be zero");
   *out = *o;
   if (out->spin_timeout_us == 0) out->spin_timeout_us = kDefaultTimeoutUs;
   return FO_OK;
@@ -172,7 +175,8 @@ int resolve_tile(const fo_opts& o, int in_dt, int P, int64_t m, int64_t N, int n
   return fo::choose_tile(P, m, N, n_cu);
 }
 
-fo_status tiles_for(int in_dt, int tile, int64_t m, int64_t N, int P, fo::Plan& p) {
+fo_status tiles_for(int in_dt, int tile, int64_t m, int64_t N, int P, fo::Plan& p,
+                    int* bm_out = nullptr) {
   int bm = 64, bn = 64;
   if (in_dt == FO_DT_BF16) {
     const fo::TileShape ts = fo::tile_shape(tile);
@@ -181,9 +185,35 @@ fo_status tiles_for(int in_dt, int tile, int64_t m, int64_t N, int P, fo::Plan& 
   }
   const int64_t tm = (m + bm - 1) / bm, tn = (N + bn - 1) / bn;
   if (tm * tn * P > 0x7fffffffLL) return invalid("too many tiles");
-  p.tiles_m = (int32_t)tm;
-  p.tiles_n = (int32_t)tn;
+  p.grid.tiles_m = (int32_t)tm;
+  p.grid.tiles_n = (int32_t)tn;
+  if (bm_out) *bm_out = bm;
   return FO_OK;
+}
+
+// Row groups: `req` groups (0 = one per tile row), at most kMaxGroups and at most one per tile
+// row, each a whole number of tile rows.
+void set_groups(int req, fo::Plan& p) {
+  int G = req == 0 ? p.grid.tiles_m : req;
+  G = std::max(1, std::min({G, fo::kMaxGroups, (int)p.grid.tiles_m}));
+  p.grid.group_rows = (p.grid.tiles_m + G - 1) / G;
+  p.grid.groups = (p.grid.tiles_m + p.grid.group_rows - 1) / p.grid.group_rows;
+}
+
+// Dispatch layout of a call of `kind` (0 AG, 1 RS): Flash-AG puts the local slice first, whole,
+// and computes the received slices group by group (NATURAL: every slice group by group in index
+// order); Flash-RS computes the chunks for the other ranks group by group and its own chunk last,
+// whole.
+void set_layout(int kind, const fo_opts& o, fo::Plan& p) {
+  set_groups(o.row_groups, p);
+  p.grid.lead = (kind == 0 && o.order == FO_ORDER_FLASH) ? 1 : 0;
+  p.grid.trail = kind == 1 ? 1 : 0;
+}
+
+// Element rows [*r0, *r1) of row group g of a slice of m rows with tile height bm.
+void group_span(const fo::Plan& p, int bm, int64_t m, int g, int64_t* r0, int64_t* r1) {
+  *r0 = std::min<int64_t>(m, (int64_t)g * p.grid.group_rows * bm);
+  *r1 = std::min<int64_t>(m, (int64_t)(g + 1) * p.grid.group_rows * bm);
 }
 
 uint64_t spin_ticks(const DevState& st, uint32_t us) { return (uint64_t)us * st.wall_khz / 1000u; }
@@ -270,7 +300,7 @@ fo_status fo_tile_info(int32_t P, int64_t m, int64_t K, int64_t N, int32_t in_dt
   fo_opts_init(&o);
   o.tile = tile;
   const int t = resolve_tile(o, in_dt, P, m, N, n_cu);
-  fo::Plan p{};
+  fo::Plan p = fo::empty_plan();
   s = tiles_for(in_dt, t, m, N, P, p);
   if (s != FO_OK) return s;
   int vbm = 64, vbn = 64;
@@ -280,7 +310,45 @@ fo_status fo_tile_info(int32_t P, int64_t m, int64_t K, int64_t N, int32_t in_dt
   }
   if (bm) *bm = vbm;
   if (bn) *bn = vbn;
-  if (workgroups) *workgroups = (int64_t)P * p.tiles_m * p.tiles_n;
+  if (workgroups) *workgroups = (int64_t)P * p.grid.tiles_m * p.grid.tiles_n;
+  return FO_OK;
+}
+
+fo_status fo_tile_order(int32_t kind, int32_t P, int64_t m, int64_t K, int64_t N, int32_t in_dt,
+                        const fo_opts* opts, int32_t* out, int64_t capacity, int64_t* count) {
+  fo_opts o;
+  fo_status s = check_opts(opts, &o);
+  if (s != FO_OK) return s;
+  if (kind != 0 && kind != 1) return invalid("kind %d is neither 0 (AG) nor 1 (RS)", kind);
+  s = check_common(P, 0, m, K, N, in_dt);
+  if (s != FO_OK) return s;
+  if (capacity < 0 || (capacity > 0 && !out)) return invalid("bad output buffer");
+  int n_cu = 256, dev = 0;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int c = 0;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && c > 0)
+      n_cu = c;
+  }
+  if (m == 0 || N == 0) {
+    if (count) *count = 0;
+    return FO_OK;
+  }
+  const int tile = resolve_tile(o, in_dt, P, m, N, n_cu);
+  fo::Plan p = fo::empty_plan();
+  s = tiles_for(in_dt, tile, m, N, P, p);
+  if (s != FO_OK) return s;
+  p.grid.npos = P;
+  set_layout(kind, o, p);
+  const int64_t total = (int64_t)P * p.grid.tiles_m * p.grid.tiles_n;
+  if (count) *count = total;
+  for (int64_t u = 0; u < std::min(total, capacity); ++u) {
+    int pos, grp, tm, tn;
+    fo::locate(p.grid, (int)u, pos, grp, tm, tn);
+    out[4 * u] = pos;
+    out[4 * u + 1] = grp;
+    out[4 * u + 2] = tm;
+    out[4 * u + 3] = tn;
+  }
   return FO_OK;
 }
 
@@ -324,19 +392,22 @@ fo_status fo_ag_gemm(const void* x_local, const void* const* x_peer, void* x_rec
   if (s != FO_OK) return s;
 
   const int tile = resolve_tile(o, in_dt, P, m, N, st->n_cu);
-  fo::Plan p{};
-  s = tiles_for(in_dt, tile, m, N, P, p);
+  fo::Plan p = fo::empty_plan();
+  int bm = 0;
+  s = tiles_for(in_dt, tile, m, N, P, p, &bm);
   if (s != FO_OK) return s;
+  set_layout(0, o, p);
   fo::dma::Call call{};
-  if (arrivals) FO_DMA(fo::dma::begin(st->dev, P, &call, &e_));
+  if (arrivals) FO_DMA(fo::dma::begin(st->dev, P, p.grid.groups, &call, &e_));
   int32_t order[FO_MAX_P];
   fo::slice_order(0, o.order, P, rank, order);
   for (int pos = 0; pos < P; ++pos) {
     const int sl = order[pos];
     p.a_pos[pos] = sl == rank ? x_local : (const uint8_t*)x_recv + (size_t)sl * slice_b;
     p.c_pos[pos] = (uint8_t*)y + (size_t)sl * m * N * os;
-    p.gate[pos] = (arrivals && sl != rank) ? call.comp[sl] : nullptr;
+    p.gate_slice[pos] = (arrivals && sl != rank) ? sl : -1;
   }
+  p.comp_tab = call.comp_tab;
   p.b = w;
   p.done = st->done;
   p.err = st->err;
@@ -344,7 +415,7 @@ fo_status fo_ag_gemm(const void* x_local, const void* const* x_peer, void* x_rec
   p.m = m;
   p.K = K;
   p.N = N;
-  p.npos = P;
+  p.grid.npos = P;
   p.n_recv = 0;
   p.accum_pos = -1;
   p.out_f32 = out_dt == FO_DT_F32;
@@ -358,13 +429,21 @@ fo_status fo_ag_gemm(const void* x_local, const void* const* x_peer, void* x_rec
   FO_HIP(hipEventRecord(st->ev_last, cs));
   st->have_last = true;
   if (arrivals) {
+    // group-major, in arrival order inside a group: the order the kernel consumes them in
     int seq[FO_MAX_P];
     const int n = arrival_sequence(0, o.order, P, rank, seq);
     const int L = links_for(o, P);
-    for (int t = 0; t < n; ++t) {
-      const int sl = seq[t];
-      FO_DMA(fo::dma::copy(st->dev, call, t % L, sl, -1, (uint8_t*)x_recv + (size_t)sl * slice_b,
-                           x_peer[sl], slice_b, &e_));
+    const size_t row_b = (size_t)K * es;
+    for (int g = 0; g < p.grid.groups; ++g) {
+      int64_t r0, r1;
+      group_span(p, bm, m, g, &r0, &r1);
+      for (int t = 0; t < n; ++t) {
+        const int sl = seq[t];
+        const size_t off = (size_t)sl * slice_b + (size_t)r0 * row_b;
+        FO_DMA(fo::dma::copy(st->dev, call, t % L, sl, g, -1, (uint8_t*)x_recv + off,
+                             (const uint8_t*)x_peer[sl] + (size_t)r0 * row_b,
+                             (size_t)(r1 - r0) * row_b, &e_));
+      }
     }
   }
   return FO_OK;
@@ -419,26 +498,30 @@ fo_status fo_gemm_rs(const void* x_shard, const void* w, float* send_buf, float*
   if (s != FO_OK) return s;
 
   const int tile = resolve_tile(o, in_dt, P, m, N, st->n_cu);
-  fo::Plan p{};
-  s = tiles_for(in_dt, tile, m, N, P, p);
+  fo::Plan p = fo::empty_plan();
+  int bm = 0;
+  s = tiles_for(in_dt, tile, m, N, P, p, &bm);
   if (s != FO_OK) return s;
+  set_layout(1, o, p);
   const bool lockstep = arrivals && arrival == FO_ARR_LOCKSTEP;
   fo::dma::Call call{};
-  if (arrivals) FO_DMA(fo::dma::begin(st->dev, P, &call, &e_));
+  if (arrivals) FO_DMA(fo::dma::begin(st->dev, P, p.grid.groups, &call, &e_));
   int32_t order[FO_MAX_P];
   fo::slice_order(1, FO_ORDER_FLASH, P, rank, order);
   for (int pos = 0; pos < P; ++pos) {
     const int d = order[pos];
     p.a_pos[pos] = (const uint8_t*)x_shard + (size_t)d * m * K * es;
     p.c_pos[pos] = d == rank ? (void*)out : (void*)((uint8_t*)send_buf + (size_t)d * chunk_b);
-    p.rel[pos] = (lockstep && d != rank) ? call.rel[pos] : nullptr;
+    p.gate_slice[pos] = -1;
     if (d == rank) p.accum_pos = pos;
   }
+  p.comp_tab = call.comp_tab;
+  p.rel_tab = lockstep ? call.rel_tab : nullptr;
   // partials arrive from rank-1, rank-2, ... (mod P) and are added in that order
   for (int i = 1; i < P; ++i) {
     const int q = ((rank - i) % P + P) % P;
     p.recv[i - 1] = (const float*)((const uint8_t*)recv_buf + (size_t)q * chunk_b);
-    p.recv_sig[i - 1] = arrivals ? call.comp[q] : nullptr;
+    p.recv_slice[i - 1] = arrivals ? q : -1;
   }
   p.n_recv = P - 1;
   p.b = w;
@@ -448,7 +531,7 @@ fo_status fo_gemm_rs(const void* x_shard, const void* w, float* send_buf, float*
   p.m = m;
   p.K = K;
   p.N = N;
-  p.npos = P;
+  p.grid.npos = P;
   p.out_f32 = 1;
 
   hipStream_t cs = (hipStream_t)compute_stream;
@@ -460,16 +543,24 @@ fo_status fo_gemm_rs(const void* x_shard, const void* w, float* send_buf, float*
   FO_HIP(hipEventRecord(st->ev_last, cs));
   st->have_last = true;
   if (arrivals) {
-    // transfer t brings the partial of peer rank-1-t. In lockstep that peer sends it at its own
-    // step t, which (peers progressing together) ends when this rank ends its step t: the copy
-    // waits for position t's release.
+    // transfer t brings the partial of peer rank-1-t. In lockstep that peer sends its group g at
+    // its own unit (t, g), which (peers progressing together) ends when this rank ends its unit
+    // (t, g): the copy waits for that release.
     int seq[FO_MAX_P];
     const int n = arrival_sequence(1, FO_ORDER_FLASH, P, rank, seq);
     const int L = links_for(o, P);
-    for (int t = 0; t < n; ++t) {
-      const int q = seq[t];
-      FO_DMA(fo::dma::copy(st->dev, call, t % L, q, lockstep ? t : -1,
-                           (uint8_t*)recv_buf + (size_t)q * chunk_b, peer_partial[q], chunk_b, &e_));
+    const size_t row_b = (size_t)N * 4;
+    for (int g = 0; g < p.grid.groups; ++g) {
+      int64_t r0, r1;
+      group_span(p, bm, m, g, &r0, &r1);
+      for (int t = 0; t < n; ++t) {
+        const int q = seq[t];
+        const size_t off = (size_t)q * chunk_b + (size_t)r0 * row_b;
+        FO_DMA(fo::dma::copy(st->dev, call, t % L, q, g, lockstep ? t : -1,
+                             (uint8_t*)recv_buf + off,
+                             (const uint8_t*)peer_partial[q] + (size_t)r0 * row_b,
+                             (size_t)(r1 - r0) * row_b, &e_));
+      }
     }
   }
   return FO_OK;
@@ -498,7 +589,7 @@ fo_status fo_gemm_ref(const void* a, const void* b, void* c, int64_t M, int64_t 
   fo_opts_init(&o);
   o.tile = tile;
   const int t = resolve_tile(o, in_dt, 1, M, N, st->n_cu);
-  fo::Plan p{};
+  fo::Plan p = fo::empty_plan();
   s = tiles_for(in_dt, t, M, N, 1, p);
   if (s != FO_OK) return s;
   p.a_pos[0] = a;
@@ -510,9 +601,11 @@ fo_status fo_gemm_ref(const void* a, const void* b, void* c, int64_t M, int64_t 
   p.m = M;
   p.K = K;
   p.N = N;
-  p.npos = 1;
+  p.grid.npos = 1;
   p.accum_pos = -1;
   p.out_f32 = out_dt == FO_DT_F32;
+  set_groups(1, p);
+  p.grid.lead = 1;
   FO_HIP(fo::launch_gemm(p, in_dt, t, (hipStream_t)stream));
   return FO_OK;
 }
@@ -537,24 +630,30 @@ fo_status fo_transfer_ref(int32_t kind, const void* const* src, void* dst, int32
   std::unique_lock<std::mutex> lk;
   s = current_state(&st, &lk);
   if (s != FO_OK) return s;
+  // the slices cut into opts.row_groups equal pieces (0: whole), issued group-major like the calls
+  const int G = std::max(1, o.row_groups);
   fo::dma::Call call{};
-  FO_DMA(fo::dma::begin(st->dev, P, &call, &e_));
+  FO_DMA(fo::dma::begin(st->dev, P, G, &call, &e_));
   int seq[FO_MAX_P];
   const int n = arrival_sequence(kind, o.order, P, rank, seq);
-  const int64_t* wait[FO_MAX_P];
-  for (int t = 0; t < n; ++t) wait[t] = call.comp[seq[t]];
   hipStream_t ks = (hipStream_t)stream;
   if (st->have_last) FO_HIP(hipStreamWaitEvent(ks, st->ev_last, 0));
   FO_HIP(fo::launch_release(call.start, ks));
-  FO_HIP(fo::launch_wait(wait, n, spin_ticks(*st, o.spin_timeout_us), st->err, ks));
+  FO_HIP(fo::launch_wait(call.comp_tab, seq, n, G, spin_ticks(*st, o.spin_timeout_us), st->err, ks));
   FO_DMA(fo::dma::end(st->dev, call, ks, &e_));
   FO_HIP(hipEventRecord(st->ev_last, ks));
   st->have_last = true;
   const int L = links_for(o, P);
-  for (int t = 0; t < n; ++t) {
-    const int sl = seq[t];
-    FO_DMA(fo::dma::copy(st->dev, call, t % L, sl, -1, (uint8_t*)dst + (size_t)sl * slice_bytes,
-                         src[sl], (size_t)slice_bytes, &e_));
+  const size_t piece = ((size_t)slice_bytes / G + 255) / 256 * 256;
+  for (int g = 0; g < G; ++g) {
+    const size_t b0 = std::min((size_t)slice_bytes, (size_t)g * piece);
+    const size_t b1 = std::min((size_t)slice_bytes, (size_t)(g + 1) * piece);
+    for (int t = 0; t < n; ++t) {
+      const int sl = seq[t];
+      FO_DMA(fo::dma::copy(st->dev, call, t % L, sl, g, -1,
+                           (uint8_t*)dst + (size_t)sl * slice_bytes + b0,
+                           (const uint8_t*)src[sl] + b0, b1 - b0, &e_));
+    }
   }
   return FO_OK;
 }

@@ -17,6 +17,7 @@
 #include <hsa/hsa.h>
 #include <hsa/hsa_ext_amd.h>
 
+#include <bitset>
 #include <chrono>
 #include <cstdio>
 #include <cstring>
@@ -99,14 +100,15 @@ void resolve_hsa(const void* dev_ptr) {
   }
 }
 
+constexpr int kSignals = FO_MAX_P * kMaxGroups;  // per kind and slot: [slice or position][group]
+
 struct Slot {
-  hsa_signal_t start{}, rel[FO_MAX_P]{}, comp[FO_MAX_P]{};
+  hsa_signal_t start{}, rel[kSignals]{}, comp[kSignals]{};
   int64_t* start_v = nullptr;
-  int64_t* rel_v[FO_MAX_P] = {};
-  int64_t* comp_v[FO_MAX_P] = {};
+  int64_t** tab = nullptr;  // device: comp values [kSignals], then rel values [kSignals]
   hipEvent_t ev = nullptr;  // recorded after the call's last kernel that reads the signals
   bool pending = false;     // used by a call that may not be complete yet
-  uint32_t issued = 0;      // slices whose completion signal a copy will decrement
+  std::bitset<kSignals> issued;  // completion signals a copy will decrement
 };
 
 struct Dev {
@@ -155,8 +157,8 @@ bool new_signal(hsa_signal_t* sig, int64_t** value, std::string* err) {
 // Host wait (bounded) until the completion signal of every issued slice has dropped to zero.
 bool wait_landed(const Slot& sl, uint32_t timeout_ms, std::string* err, bool* timed_out = nullptr) {
   const auto t0 = std::chrono::steady_clock::now();
-  for (int i = 0; i < FO_MAX_P; ++i) {
-    if (!(sl.issued & (1u << i))) continue;
+  for (int i = 0; i < kSignals; ++i) {
+    if (!sl.issued[i]) continue;
     int spins = 0;
     for (;;) {
       const int64_t v = g_hsa.load(sl.comp[i]);
@@ -214,11 +216,18 @@ bool init(int dev, void* scratch, std::string* err) {
   d.n_eng = 0;
   for (int i = 0; i < 32; ++i)
     if (mask & (1u << i)) d.eng[d.n_eng++] = 1u << i;
+  std::vector<int64_t*> values(2 * kSignals);
   for (Slot& sl : d.slot) {
     if (!new_signal(&sl.start, &sl.start_v, err)) return false;
-    for (int i = 0; i < FO_MAX_P; ++i) {
-      if (!new_signal(&sl.rel[i], &sl.rel_v[i], err)) return false;
-      if (!new_signal(&sl.comp[i], &sl.comp_v[i], err)) return false;
+    for (int i = 0; i < kSignals; ++i) {
+      if (!new_signal(&sl.comp[i], &values[i], err)) return false;
+      if (!new_signal(&sl.rel[i], &values[kSignals + i], err)) return false;
+    }
+    if (hipMalloc((void**)&sl.tab, values.size() * sizeof(int64_t*)) != hipSuccess ||
+        hipMemcpy(sl.tab, values.data(), values.size() * sizeof(int64_t*),
+                  hipMemcpyHostToDevice) != hipSuccess) {
+      *err = "cannot place the signal tables in device memory";
+      return false;
     }
     if (hipEventCreateWithFlags(&sl.ev, hipEventDisableTiming) != hipSuccess) {
       *err = "hipEventCreateWithFlags failed";
@@ -234,7 +243,8 @@ bool init(int dev, void* scratch, std::string* err) {
     s = g_hsa.copy(src + kWarmBytes, d.agent, src, d.agent, kWarmBytes, 0, nullptr, w.comp[0],
                    (hsa_amd_sdma_engine_id_t)d.eng[e], true);
     if (s != HSA_STATUS_SUCCESS) continue;
-    w.issued = 1u;
+    w.issued.reset();
+    w.issued.set(0);
     if (!wait_landed(w, 10000, err)) return false;
     d.eng[kept++] = d.eng[e];
   }
@@ -243,17 +253,21 @@ bool init(int dev, void* scratch, std::string* err) {
     *err = "no SDMA engine accepts device-to-device copies on this device";
     return false;
   }
-  w.issued = 0;
+  w.issued.reset();
   d.ready = true;
   return true;
 }
 
 int n_engines(int dev) { return (dev >= 0 && dev < kMaxDevices) ? g_dev[dev].n_eng : 0; }
 
-bool begin(int dev, int P, Call* call, std::string* err) {
+bool begin(int dev, int P, int groups, Call* call, std::string* err) {
   Dev& d = g_dev[dev];
   if (!d.ready) {
     *err = "DMA layer not initialized";
+    return false;
+  }
+  if (P < 1 || P > FO_MAX_P || groups < 1 || groups > kMaxGroups) {
+    *err = "slice or group count beyond the DMA layer's signal slots";
     return false;
   }
   const int k = d.next;
@@ -267,42 +281,42 @@ bool begin(int dev, int P, Call* call, std::string* err) {
     sl.pending = false;
   }
   g_hsa.store(sl.start, 1);
-  for (int i = 0; i < P; ++i) {
-    g_hsa.store(sl.rel[i], 1);
-    g_hsa.store(sl.comp[i], 1);
-  }
-  sl.issued = 0;
+  for (int i = 0; i < P; ++i)
+    for (int g = 0; g < groups; ++g) {
+      g_hsa.store(sl.rel[i * kMaxGroups + g], 1);
+      g_hsa.store(sl.comp[i * kMaxGroups + g], 1);
+    }
+  sl.issued.reset();
   sl.pending = true;
   d.next = (k + 1) % kSlots;
   call->slot = k;
   call->start = sl.start_v;
-  for (int i = 0; i < FO_MAX_P; ++i) {
-    call->rel[i] = sl.rel_v[i];
-    call->comp[i] = sl.comp_v[i];
-  }
+  call->comp_tab = sl.tab;
+  call->rel_tab = sl.tab + kSignals;
   return true;
 }
 
-bool copy(int dev, const Call& call, int link, int slice, int rel_pos, void* dst, const void* src,
-          size_t bytes, std::string* err) {
+bool copy(int dev, const Call& call, int link, int slice, int group, int rel_pos, void* dst,
+          const void* src, size_t bytes, std::string* err) {
   Dev& d = g_dev[dev];
   Slot& sl = d.slot[call.slot];
+  const int ci = slice * kMaxGroups + group;
   if (bytes == 0) {
-    g_hsa.store(sl.comp[slice], 0);
+    g_hsa.store(sl.comp[ci], 0);
     return true;
   }
   hsa_signal_t deps[2] = {sl.start, {}};
   uint32_t n = 1;
-  if (rel_pos >= 0) deps[n++] = sl.rel[rel_pos];
+  if (rel_pos >= 0) deps[n++] = sl.rel[rel_pos * kMaxGroups + group];
   const uint32_t eng = d.eng[(link % d.n_eng + d.n_eng) % d.n_eng];
-  const hsa_status_t s = g_hsa.copy(dst, d.agent, src, d.agent, bytes, n, deps, sl.comp[slice],
+  const hsa_status_t s = g_hsa.copy(dst, d.agent, src, d.agent, bytes, n, deps, sl.comp[ci],
                                     (hsa_amd_sdma_engine_id_t)eng, true);
   if (s != HSA_STATUS_SUCCESS) {
     // the kernel must not wait for a copy that was never issued: report it as failed
-    g_hsa.store(sl.comp[slice], -1);
+    g_hsa.store(sl.comp[ci], -1);
     return fail(err, "hsa_amd_memory_async_copy_on_engine", s);
   }
-  sl.issued |= 1u << slice;
+  sl.issued.set(ci);
   return true;
 }
 
@@ -327,7 +341,7 @@ bool drain(int dev, uint32_t timeout_ms, std::string* err, bool* timed_out) {
     }
     if (!wait_landed(sl, timeout_ms, err, timed_out)) return false;
     sl.pending = false;
-    sl.issued = 0;
+    sl.issued.reset();
   }
   return true;
 }

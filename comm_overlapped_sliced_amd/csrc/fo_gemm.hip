@@ -51,31 +51,34 @@ __device__ __forceinline__ void wait_signal(const int64_t* v, uint64_t limit, ui
   }
 }
 
-// Thread 0 waits for every listed signal (null entries are skipped); then the whole workgroup
-// acquires at system scope so that data the copy engine wrote before the signal is seen (no
-// stale cache lines).
-__device__ __forceinline__ void wait_signals_wg(const Plan& p, const int64_t* const* sigs, int n) {
-  if (threadIdx.x == 0) {
+// Thread 0 waits for the completion signal of group `grp` of each listed slice (negative ids are
+// skipped); then the whole workgroup acquires at system scope so that data the copy engine wrote
+// before the signal is seen (no stale cache lines).
+__device__ __forceinline__ void wait_groups_wg(const Plan& p, const int32_t* slices, int n,
+                                               int grp) {
+  if (threadIdx.x == 0 && p.comp_tab != nullptr) {
     for (int i = 0; i < n; ++i)
-      if (sigs[i]) wait_signal(sigs[i], p.spin_limit, p.err);
+      if (slices[i] >= 0)
+        wait_signal(p.comp_tab[slices[i] * kMaxGroups + grp], p.spin_limit, p.err);
   }
   __syncthreads();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
 }
 
-// After a tile of position `pos` is stored: count it; the last tile of the position stores 0 into
-// the position's release signal (polled by the copy engine that carries the next transfer) and
+// After a tile of (position, group) is stored: count it; the last tile of that group stores 0
+// into its release signal (polled by the copy engine that carries the matching transfer) and
 // re-arms the counter.
-__device__ __forceinline__ void release_tile(const Plan& p, int pos, int tiles_per_pos) {
-  if (p.rel[pos] == nullptr) return;
+__device__ __forceinline__ void release_tile(const Plan& p, int pos, int grp) {
+  if (p.rel_tab == nullptr) return;
   __syncthreads();
   if (threadIdx.x == 0) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
-    const uint32_t old = __hip_atomic_fetch_add(p.done + pos, 1u, __ATOMIC_ACQ_REL,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-    if (old + 1 == (uint32_t)tiles_per_pos) {
-      __hip_atomic_store(p.done + pos, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(p.rel[pos], (int64_t)0, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+    uint32_t* cnt = p.done + pos * kMaxGroups + grp;
+    const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if (old + 1 == (uint32_t)(group_rows_of(p.grid, grp) * p.grid.tiles_n)) {
+      __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(p.rel_tab[pos * kMaxGroups + grp], (int64_t)0, __ATOMIC_RELEASE,
+                         __HIP_MEMORY_SCOPE_SYSTEM);
     }
   }
 }
@@ -86,22 +89,6 @@ __device__ __forceinline__ uint16_t to_bf16_rne(float f) {
   if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
   u += 0x7fffu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
-}
-
-// Tile order inside one position. Workgroup b runs on XCD b % 8 (round-robin dispatch). When a
-// position has a multiple of 8 tiles, XCD x is given the x-th contiguous run of tile ids, and
-// ids walk the tile grid in groups of up to 8 tile rows, column by column inside a group: the
-// ~32 tiles an XCD runs at once then form an 8 x 4 block that shares its A row blocks and W
-// column blocks in that XCD's L2.
-__device__ __forceinline__ void tile_coords(int u, int T, int tiles_m, int tiles_n, int& tm,
-                                            int& tn) {
-  const int id = (T % 8) ? u : (u % 8) * (T / 8) + u / 8;
-  const int gm = tiles_m < 8 ? tiles_m : 8;
-  const int gsize = gm * tiles_n;
-  const int g = id / gsize, r = id % gsize;
-  const int rows = tiles_m - g * gm < gm ? tiles_m - g * gm : gm;
-  tm = g * gm + r % rows;
-  tn = r / rows;
 }
 
 // 16-byte streaming load (the partials are read once)
@@ -206,11 +193,9 @@ __device__ __forceinline__ void bf16_tile(const Plan& p, const int tile, uint8_t
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
-  const int T = p.tiles_m * p.tiles_n;
-  const int pos = uni(tile / T);
-  int tm_, tn_;
-  tile_coords(tile - pos * T, T, p.tiles_m, p.tiles_n, tm_, tn_);
-  const int tm = uni(tm_), tn = uni(tn_);
+  int pos_, grp_, tm_, tn_;
+  locate(p.grid, tile, pos_, grp_, tm_, tn_);
+  const int pos = uni(pos_), grp = uni(grp_), tm = uni(tm_), tn = uni(tn_);
 
   const int64_t K = p.K, N = p.N;
   const int64_t row0 = (int64_t)tm * BM;
@@ -220,8 +205,8 @@ __device__ __forceinline__ void bf16_tile(const Plan& p, const int tile, uint8_t
   const uint16_t* A = (const uint16_t*)uni_ptr((const uint16_t*)p.a_pos[pos] + row0 * K);
   const uint16_t* W = (const uint16_t*)uni_ptr((const uint16_t*)p.b + col0);
 
-  // Flash-AG: a received slice is read only after its arrival flag.
-  if (p.gate[pos]) wait_signals_wg(p, p.gate + pos, 1);
+  // Flash-AG: rows of a received slice are read only after their group has landed.
+  if (p.gate_slice[pos] >= 0) wait_groups_wg(p, p.gate_slice + pos, 1, grp);
 
   // ---- loads. Per-lane offsets are fixed for the whole K loop: the K step enters A's loads as
   // the scalar offset and W's through a descriptor re-based on the step's first row (whose
@@ -432,7 +417,7 @@ __device__ __forceinline__ void bf16_tile(const Plan& p, const int tile, uint8_t
   // that stays on the rank, the loads of the received partials, which are all issued before any
   // of them is added (the adds keep the arrival order).
   const bool accum = (pos == p.accum_pos);
-  if (accum) wait_signals_wg(p, p.recv_sig, p.n_recv);
+  if (accum) wait_groups_wg(p, p.recv_slice, p.n_recv, grp);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // LDS stages no longer read
   float* const ep = (float*)lds_ring;  // [ER rows][EW floats] over the whole ring
   constexpr int EW = BN + 8;      // padded row: rows 4 apart land 32 banks apart
@@ -508,7 +493,7 @@ __device__ __forceinline__ void bf16_tile(const Plan& p, const int tile, uint8_t
     }
     __syncthreads();
   }
-  release_tile(p, pos, T);
+  release_tile(p, pos, grp);
 }
 
 // One workgroup per tile, or (grid smaller than the tile count) a persistent grid whose
@@ -516,7 +501,7 @@ __device__ __forceinline__ void bf16_tile(const Plan& p, const int tile, uint8_t
 template <int BM, int BN>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(Plan p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds_ring[kStages * Cfg<BM, BN>::STAGE];
-  const int total = p.npos * p.tiles_m * p.tiles_n;
+  const int total = p.grid.npos * p.grid.tiles_m * p.grid.tiles_n;
   for (int tile = blockIdx.x; tile < total; tile += gridDim.x) bf16_tile<BM, BN>(p, tile, lds_ring);
 }
 
@@ -529,17 +514,15 @@ __device__ __forceinline__ void f32_tile(const Plan& p, const int tile, float (*
   const int tid = threadIdx.x;
   const int tx = tid & 15, ty = tid >> 4;
 
-  const int T = p.tiles_m * p.tiles_n;
-  const int pos = tile / T;
-  const int t = tile - pos * T;
-  const int tm = t % p.tiles_m, tn = t / p.tiles_m;
+  int pos, grp, tm, tn;
+  locate(p.grid, tile, pos, grp, tm, tn);
   const int64_t K = p.K, N = p.N;
   const int64_t row0 = (int64_t)tm * F_BM, col0 = (int64_t)tn * F_BN;
   const int64_t rows_valid = p.m - row0;
   const float* A = (const float*)p.a_pos[pos] + row0 * K;
   const float* B = (const float*)p.b + col0;
 
-  if (p.gate[pos]) wait_signals_wg(p, p.gate + pos, 1);
+  if (p.gate_slice[pos] >= 0) wait_groups_wg(p, p.gate_slice + pos, 1, grp);
 
   float acc[4][4];
 #pragma unroll
@@ -568,7 +551,7 @@ __device__ __forceinline__ void f32_tile(const Plan& p, const int tile, float (*
   }
 
   const bool accum = (pos == p.accum_pos);
-  if (accum) wait_signals_wg(p, p.recv_sig, p.n_recv);
+  if (accum) wait_groups_wg(p, p.recv_slice, p.n_recv, grp);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -585,13 +568,13 @@ __device__ __forceinline__ void f32_tile(const Plan& p, const int tile, float (*
         ((uint16_t*)p.c_pos[pos])[off] = to_bf16_rne(x);
     }
   }
-  release_tile(p, pos, T);
+  release_tile(p, pos, grp);
 }
 
 __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(Plan p) {
   __shared__ float sa[F_BK][F_BM + 4];  // k-major so a thread's 4 rows are one broadcast read
   __shared__ float sb[F_BK][F_BN + 4];
-  const int total = p.npos * p.tiles_m * p.tiles_n;
+  const int total = p.grid.npos * p.grid.tiles_m * p.grid.tiles_n;
   for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
     f32_tile(p, tile, sa, sb);
     __syncthreads();  // the next tile refills sa / sb
@@ -613,16 +596,18 @@ __global__ __launch_bounds__(64) void release_kernel(int64_t* v) {
   }
 }
 
-struct SignalList {
-  const int64_t* v[FO_MAX_P];
-  int32_t n;
+struct SliceList {
+  int32_t s[FO_MAX_P];
+  int32_t n, groups;
 };
 
-// Waits until every listed signal has dropped to zero (the transfers alone, without a GEMM).
-__global__ __launch_bounds__(64) void wait_kernel(SignalList l, uint64_t limit, uint32_t* err) {
+// Waits until every group of every listed slice has landed (the transfers alone, without a GEMM).
+__global__ __launch_bounds__(64) void wait_kernel(const int64_t* const* comp_tab, SliceList l,
+                                                  uint64_t limit, uint32_t* err) {
   if (threadIdx.x == 0)
     for (int i = 0; i < l.n; ++i)
-      if (l.v[i]) wait_signal(l.v[i], limit, err);
+      for (int g = 0; g < l.groups; ++g)
+        wait_signal(comp_tab[l.s[i] * kMaxGroups + g], limit, err);
   __syncthreads();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
 }
@@ -634,13 +619,14 @@ hipError_t launch_release(int64_t* v, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_wait(const int64_t* const* v, int n, uint64_t spin_limit, uint32_t* err,
-                       hipStream_t s) {
-  if (n < 0 || n > FO_MAX_P) return hipErrorInvalidValue;
-  SignalList l{};
-  for (int i = 0; i < n; ++i) l.v[i] = v[i];
+hipError_t launch_wait(const int64_t* const* comp_tab, const int32_t* slices, int n, int groups,
+                       uint64_t spin_limit, uint32_t* err, hipStream_t s) {
+  if (n < 0 || n > FO_MAX_P || groups < 1 || groups > kMaxGroups) return hipErrorInvalidValue;
+  SliceList l{};
+  for (int i = 0; i < n; ++i) l.s[i] = slices[i];
   l.n = n;
-  hipLaunchKernelGGL(wait_kernel, dim3(1), dim3(64), 0, s, l, spin_limit, err);
+  l.groups = groups;
+  hipLaunchKernelGGL(wait_kernel, dim3(1), dim3(64), 0, s, comp_tab, l, spin_limit, err);
   return hipGetLastError();
 }
 
@@ -655,8 +641,29 @@ TileShape tile_shape(int tile) {
   }
 }
 
+// Host-side check of what the kernels index: signal tables behind every gate, awaited partial
+// and release; slice ids and positions inside the tables; row groups that tile the rows.
+static bool plan_ok(const Plan& p) {
+  const TileGrid& g = p.grid;
+  if (g.npos < 1 || g.npos > FO_MAX_P || g.tiles_m < 1 || g.tiles_n < 1) return false;
+  if (g.groups < 1 || g.groups > kMaxGroups || g.group_rows < 1) return false;
+  if ((int64_t)g.groups * g.group_rows < g.tiles_m || (g.groups - 1) * g.group_rows >= g.tiles_m)
+    return false;
+  if (g.lead < 0 || g.trail < 0 || g.lead + g.trail > g.npos) return false;
+  if (p.done == nullptr || p.err == nullptr) return false;
+  for (int i = 0; i < g.npos; ++i)
+    if (p.gate_slice[i] >= FO_MAX_P || (p.gate_slice[i] >= 0 && p.comp_tab == nullptr)) return false;
+  if (p.accum_pos >= g.npos || p.n_recv < 0 || p.n_recv > FO_MAX_P) return false;
+  if (p.accum_pos >= 0)
+    for (int i = 0; i < p.n_recv; ++i)
+      if (p.recv_slice[i] >= FO_MAX_P || (p.recv_slice[i] >= 0 && p.comp_tab == nullptr))
+        return false;
+  return true;
+}
+
 hipError_t launch_gemm(const Plan& p, int in_dt, int tile, hipStream_t s) {
-  const int64_t grid = (int64_t)p.npos * p.tiles_m * p.tiles_n;
+  if (!plan_ok(p)) return hipErrorInvalidValue;
+  const int64_t grid = (int64_t)p.grid.npos * p.grid.tiles_m * p.grid.tiles_n;
   if (in_dt == FO_DT_F32) {
     hipLaunchKernelGGL(gemm_f32_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
     return hipGetLastError();

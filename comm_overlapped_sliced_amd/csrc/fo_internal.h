@@ -8,34 +8,55 @@
 #include <string>
 
 #include "flashovl.h"
+#include "fo_tiles.h"
 
 namespace fo {
 
-// One launch of the sliced GEMM. A "position" is one step of the slice schedule: the kernel's
-// workgroups are laid out position-major, so lower positions are dispatched first.
+// Largest number of row groups a slice is cut into for its transfer and gating.
+constexpr int kMaxGroups = FO_MAX_GROUPS;
+
+// One launch of the sliced GEMM. A "position" is one step of the slice schedule; each position's
+// rows are cut into `groups` row groups of `group_rows` tile rows (the last may be shorter), and
+// a group is the unit of transfer, of gating and of release. Workgroups are laid out in dispatch
+// order: the first `lead` positions whole, then the middle positions group-major (group 0 of
+// every middle position in position order, then group 1, ...), then the last `trail` positions
+// whole. With one group this is plain position order.
 //
-// Arrival and release flags are the 64-bit values of HSA signals. A copy engine decrements the
-// value of a slice's completion signal from 1 to 0 when the slice has landed (a negative value
-// reports a failed copy); the kernel stores 0 into a position's release signal when the position
-// is complete, and a copy engine waiting on that signal then starts the next transfer.
+// Arrival and release flags are the 64-bit values of HSA signals, reached through tables of
+// value addresses indexed [slice or position][group] (kMaxGroups entries per row). A copy engine
+// decrements the value of a group's completion signal from 1 to 0 when the group has landed (a
+// negative value reports a failed copy); the kernel stores 0 into a (position, group) release
+// signal when that group of the position is complete, and a copy engine waiting on it then
+// starts the matching transfer.
 struct Plan {
   const void* a_pos[FO_MAX_P];       // A rows of position p: [m, K], row stride K
   void* c_pos[FO_MAX_P];             // output rows of position p: [m, N], row stride N
   const float* recv[FO_MAX_P];       // partials added in the accumulate epilogue, in arrival order
-  const int64_t* gate[FO_MAX_P];     // completion signal the mainloop of position p waits on
-  const int64_t* recv_sig[FO_MAX_P]; // completion signal of recv[i] (null: resident, no wait)
-  int64_t* rel[FO_MAX_P];            // release signal set when position p is complete (or null)
+  int32_t gate_slice[FO_MAX_P];      // slice whose arrival gates position p's mainloop (-1: none)
+  int32_t recv_slice[FO_MAX_P];      // slice id of recv[i], whose arrival is awaited (-1: resident)
+  const int64_t* const* comp_tab;    // completion-signal values [slice][group]
+  int64_t* const* rel_tab;           // release-signal values [position][group] (null: no release)
   const void* b;                     // W [K, N], row stride N
-  uint32_t* done;                    // per-position completed-tile counters (zero between calls)
+  uint32_t* done;                    // completed-tile counters [position][group] (zero between calls)
   uint32_t* err;                     // 1: a wait ran past spin_limit; 2: a copy reported failure
   uint64_t spin_limit;               // bound of each wait, in wall-clock ticks
   int64_t m, K, N;                   // slice rows, reduction length, output columns
-  int32_t npos;                      // positions in this launch
   int32_t n_recv;                    // partials added at accum_pos
   int32_t accum_pos;                 // position whose epilogue adds recv[] (-1: none)
   int32_t out_f32;                   // 1: fp32 output, 0: bf16 (round to nearest even)
-  int32_t tiles_m, tiles_n;          // tiles per position
+  TileGrid grid;                      // tiles per position, row groups, dispatch layout
 };
+
+// A plan with nothing to wait for: no gates, no awaited partials, no tables, no release.
+inline Plan empty_plan() {
+  Plan p{};
+  for (int i = 0; i < FO_MAX_P; ++i) {
+    p.gate_slice[i] = -1;
+    p.recv_slice[i] = -1;
+  }
+  p.accum_pos = -1;
+  return p;
+}
 
 struct TileShape {
   int bm, bn;
@@ -47,7 +68,9 @@ TileShape tile_shape(int tile);
 int choose_tile(int P, int64_t m, int64_t N, int n_cu);
 
 // Launches the sliced GEMM for `plan` (bf16 MFMA kernel with the given tile, or the fp32
-// kernel when in_dt is FO_DT_F32).
+// kernel when in_dt is FO_DT_F32). A plan whose waits or releases point at no signal table, or
+// whose grid and row groups do not fit together, is refused (hipErrorInvalidValue) before
+// anything is launched.
 hipError_t launch_gemm(const Plan& plan, int in_dt, int tile, hipStream_t stream);
 
 // Stores 0 into the signal value `v` from a one-thread kernel (stream-ordered), after a
@@ -55,10 +78,11 @@ hipError_t launch_gemm(const Plan& plan, int in_dt, int tile, hipStream_t stream
 // before it on `stream`.
 hipError_t launch_release(int64_t* v, hipStream_t stream);
 
-// One-workgroup kernel that waits (bounded by spin_limit ticks) until each of the n signal values
-// has dropped to zero, recording a timeout or a failed copy in *err like the GEMM's waits.
-hipError_t launch_wait(const int64_t* const* v, int n, uint64_t spin_limit, uint32_t* err,
-                       hipStream_t stream);
+// One-workgroup kernel that waits (bounded by spin_limit ticks) until the completion signals of
+// groups 0..groups-1 of each listed slice have dropped to zero (comp_tab as in Plan), recording a
+// timeout or a failed copy in *err like the GEMM's waits.
+hipError_t launch_wait(const int64_t* const* comp_tab, const int32_t* slices, int n, int groups,
+                       uint64_t spin_limit, uint32_t* err, hipStream_t stream);
 
 // Slice schedule: kind 0 = AG, 1 = RS; order = fo_order. Writes P ids.
 int slice_order(int kind, int order, int P, int rank, int32_t* out);
@@ -73,12 +97,13 @@ namespace dma {
 
 constexpr int kSlots = 4;  // calls in flight per device before the host waits for the oldest
 
-// The signals of one call. Values are device-visible addresses of the signals' 64-bit values.
+// The signals of one call: the start signal's value, and the device tables of completion and
+// release signal values ([slice or position][group], kMaxGroups per row) the kernels read.
 struct Call {
   int slot;
-  int64_t* start;              // released by launch_release on the compute stream
-  int64_t* rel[FO_MAX_P];      // per position (RS lockstep)
-  int64_t* comp[FO_MAX_P];     // per slice id: completion of that slice's transfer
+  int64_t* start;
+  const int64_t* const* comp_tab;
+  int64_t* const* rel_tab;
 };
 
 // Per-device setup (called once, under the device lock, with the device current): finds the
@@ -89,14 +114,14 @@ bool init(int dev, void* scratch, std::string* err);
 int n_engines(int dev);
 
 // Starts a call: takes the device's next slot (first waiting, on the host, until the call that
-// used it last is complete: its event done and its copies landed), re-arms the start, release
-// and completion signals to 1, and returns them.
-bool begin(int dev, int P, Call* call, std::string* err);
+// used it last is complete: its event done and its copies landed), re-arms the start signal and
+// the release and completion signals of P slices x `groups` groups to 1, and returns them.
+bool begin(int dev, int P, int groups, Call* call, std::string* err);
 // Copy `bytes` from src to dst on link `link` (engine link mod n_engines), starting once the
-// call's start signal and, when rel_pos >= 0, the release signal of that position are zero.
-// The completion signal of slice `slice` is decremented when the copy has landed.
-bool copy(int dev, const Call& call, int link, int slice, int rel_pos, void* dst, const void* src,
-          size_t bytes, std::string* err);
+// call's start signal and, when rel_pos >= 0, the release signal of (rel_pos, group) are zero.
+// The completion signal of (slice, group) is decremented when the copy has landed.
+bool copy(int dev, const Call& call, int link, int slice, int group, int rel_pos, void* dst,
+          const void* src, size_t bytes, std::string* err);
 // Records, on `stream`, the point after which the call's kernels no longer read its signals
 // (after the call's last kernel).
 bool end(int dev, const Call& call, hipStream_t stream, std::string* err);

@@ -19,10 +19,11 @@ ORDER_FLASH, ORDER_NATURAL = 0, 1
 ARR_DEFAULT, ARR_NONE, ARR_EAGER, ARR_LOCKSTEP = 0, 1, 2, 3
 TILE_AUTO, TILE_256x256, TILE_256x128, TILE_128x256, TILE_128x128, TILE_64x64 = range(6)
 MAX_P = 32
+MAX_GROUPS = 8
 
 EXPORTS = ("fo_opts_init", "fo_ag_gemm", "fo_gemm_rs", "fo_gemm_ref", "fo_transfer_ref",
-           "fo_check", "fo_slice_order", "fo_tile_info", "fo_status_str", "fo_last_error",
-           "fo_version")
+           "fo_check", "fo_slice_order", "fo_tile_info", "fo_tile_order", "fo_status_str",
+           "fo_last_error", "fo_version")
 
 
 class FoError(RuntimeError):
@@ -34,7 +35,7 @@ class FoError(RuntimeError):
 class Opts(ctypes.Structure):
     _fields_ = [("order", ctypes.c_int32), ("arrival", ctypes.c_int32),
                 ("tile", ctypes.c_int32), ("spin_timeout_us", ctypes.c_uint32),
-                ("links", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("links", ctypes.c_int32), ("row_groups", ctypes.c_int32),
                 ("kernel_events", ctypes.c_void_p * 2), ("reserved", ctypes.c_int32 * 2)]
 
 
@@ -65,14 +66,15 @@ def load():
     lib.fo_slice_order.argtypes = [i32, i32, i32, i32, ctypes.POINTER(i32)]
     lib.fo_tile_info.argtypes = [i32, i64, i64, i64, i32, i32, ctypes.POINTER(i32),
                                  ctypes.POINTER(i32), ctypes.POINTER(i64)]
+    lib.fo_tile_order.argtypes = [i32, i32, i64, i64, i64, i32, op, ctypes.POINTER(i32), i64,
+                                  ctypes.POINTER(i64)]
     lib.fo_status_str.argtypes = [i32]
     lib.fo_status_str.restype = ctypes.c_char_p
     lib.fo_last_error.argtypes = []
     lib.fo_last_error.restype = ctypes.c_char_p
     lib.fo_version.argtypes = []
     for f in ("fo_ag_gemm", "fo_gemm_rs", "fo_gemm_ref", "fo_transfer_ref", "fo_check",
-              "fo_slice_order",
-              "fo_tile_info", "fo_version"):
+              "fo_slice_order", "fo_tile_info", "fo_tile_order", "fo_version"):
         getattr(lib, f).restype = ctypes.c_int32
     _lib = lib
     return lib
@@ -91,10 +93,11 @@ def _raise_on(status: int, where: str) -> None:
 
 
 def opts(order=ORDER_FLASH, arrival=ARR_DEFAULT, tile=TILE_AUTO, spin_timeout_us=0, links=0,
-         kernel_events=None) -> Opts:
+         row_groups=0, kernel_events=None) -> Opts:
     o = Opts()
     load().fo_opts_init(ctypes.byref(o))
     o.order, o.arrival, o.tile, o.links = order, arrival, tile, links
+    o.row_groups = row_groups
     if spin_timeout_us:
         o.spin_timeout_us = spin_timeout_us
     if kernel_events is not None:
@@ -224,6 +227,22 @@ def tile_info(P: int, m: int, K: int, N: int, in_dt: int = BF16, tile: int = TIL
                              ctypes.byref(wg))
     _raise_on(st, "fo_tile_info")
     return bm.value, bn.value, wg.value
+
+
+def tile_order(kind: str, P: int, m: int, K: int, N: int, in_dt: int = BF16,
+               o: Opts | None = None):
+    """Dispatch order of one call: a list of (position, row group, tile row, tile column) per
+    workgroup (fo_tile_order)."""
+    lib = load()
+    cnt = ctypes.c_int64()
+    k = 0 if kind == "ag" else 1
+    ob = ctypes.byref(o) if o is not None else None
+    _raise_on(lib.fo_tile_order(k, P, m, K, N, in_dt, ob, None, 0, ctypes.byref(cnt)),
+              "fo_tile_order")
+    buf = (ctypes.c_int32 * (4 * cnt.value))()
+    _raise_on(lib.fo_tile_order(k, P, m, K, N, in_dt, ob, buf, cnt.value, ctypes.byref(cnt)),
+              "fo_tile_order")
+    return [tuple(buf[4 * i:4 * i + 4]) for i in range(cnt.value)]
 
 
 def version() -> int:

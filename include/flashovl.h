@@ -50,7 +50,8 @@ extern "C" {
 #endif
 
 #define FO_VERSION 1
-#define FO_MAX_P 32 /* largest tensor-parallel degree (number of slices) */
+#define FO_MAX_P 32     /* largest tensor-parallel degree (number of slices) */
+#define FO_MAX_GROUPS 8 /* most row groups per slice (fo_opts.row_groups) */
 
 typedef enum fo_status {
   FO_OK = 0,
@@ -101,14 +102,22 @@ typedef struct fo_opts {
                                one after the other. 0 = P-1 (one link per peer, the full xGMI
                                mesh of an 8-GPU node); 1 = a single link, as in a ring whose
                                slices all come from one neighbour */
-  int32_t reserved0;        /* must be zero */
+  int32_t row_groups;       /* granularity of transfer, gating and release: each slice (AG) or
+                               chunk (RS) is cut into this many groups of whole tile rows,
+                               each its own transfer that the tiles of those rows wait for; the
+                               received slices (AG) and the chunks for other ranks (RS) are
+                               then computed group by group across slices (all first groups,
+                               then all second groups, ...), with the local slice (AG) first and
+                               the own chunk (RS) last, each whole. 1 = whole slices, the page's
+                               slice-by-slice order; 0 = one group per tile row, at most
+                               FO_MAX_GROUPS */
   void* kernel_events[2];   /* optional hipEvent_t pair recorded on the compute stream right
                                before and right after the GEMM kernel launch (profiling) */
   int32_t reserved[2];      /* must be zero */
 } fo_opts;
 
 /* Fills *o with the defaults (FLASH order, DEFAULT arrival, AUTO tile, 2 s bound, one link per
-   peer, no events). */
+   peer, one row group per tile row, no events). */
 void fo_opts_init(fo_opts* o);
 
 /*
@@ -167,7 +176,9 @@ fo_status fo_gemm_ref(const void* a, const void* b, void* c, int64_t M, int64_t 
  *   src    host array of P device pointers; src[s] is slice s (slice_bytes bytes). Entry [rank]
  *          is ignored.
  *   dst    device buffer of P*slice_bytes bytes; slice s lands at dst + s*slice_bytes.
- * opts: order, links and spin_timeout_us are used. slice_bytes must be a multiple of 4.
+ * opts: order, links, row_groups (each slice cut into that many equal pieces, issued group by
+ * group like the calls; 0 = whole slices) and spin_timeout_us are used. slice_bytes must be a
+ * multiple of 4.
  */
 fo_status fo_transfer_ref(int32_t kind, const void* const* src, void* dst, int32_t P,
                           int32_t rank, int64_t slice_bytes, void* stream, const fo_opts* opts);
@@ -186,6 +197,13 @@ fo_status fo_slice_order(int32_t kind, int32_t order, int32_t P, int32_t rank, i
    Writes the tile rows/columns and the number of workgroups one call over P slices launches. */
 fo_status fo_tile_info(int32_t P, int64_t m, int64_t K, int64_t N, int32_t in_dt, int32_t tile,
                        int32_t* bm, int32_t* bn, int64_t* workgroups);
+
+/* The dispatch order of one fo_ag_gemm (kind 0) or fo_gemm_rs (kind 1) launch for these sizes and
+   options (order, tile, row_groups are used): workgroup u computes position out[4u], row group
+   out[4u+1], tile row out[4u+2] and tile column out[4u+3] of that position. Writes the first
+   min(capacity, count) workgroups; *count receives the number of workgroups. */
+fo_status fo_tile_order(int32_t kind, int32_t P, int64_t m, int64_t K, int64_t N, int32_t in_dt,
+                        const fo_opts* opts, int32_t* out, int64_t capacity, int64_t* count);
 
 const char* fo_status_str(fo_status s);
 /* Detail of the last failure on the calling thread (empty string if none). */

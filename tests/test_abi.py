@@ -48,7 +48,7 @@ def test_opts_defaults():
     assert (o.order, o.arrival, o.tile, o.links) == (0, 0, 0, 0)
     assert o.spin_timeout_us == 2_000_000
     assert list(o.kernel_events) == [None, None]
-    assert o.reserved0 == 0 and list(o.reserved) == [0, 0]
+    assert o.row_groups == 0 and list(o.reserved) == [0, 0]
     assert ctypes.sizeof(fo.Opts) == 48
 
 
@@ -126,7 +126,7 @@ def test_ag_rejects(lib, kw):
 
 def test_ag_rejects_bad_opts(lib):
     for field, val in [("order", 9), ("arrival", 7), ("tile", 11), ("links", 33), ("links", -1),
-                       ("reserved0", 1)]:
+                       ("row_groups", 9), ("row_groups", -1)]:
         o = fo.opts()
         setattr(o, field, val)
         assert _ag(lib, opts=ctypes.byref(o)) == fo.FO_ERR_INVALID_ARG

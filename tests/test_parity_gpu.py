@@ -199,6 +199,32 @@ def test_bf16_rs_ragged(dev, tile):
         assert rel_frobenius(send[keep], ref_send[keep]) <= TOL_BF16
 
 
+@pytest.mark.parametrize("groups", [1, 2, 3, 0], ids=lambda g: f"groups{g}")
+def test_row_groups(dev, groups):
+    """Slices cut into row groups (each its own transfer, gate and release): ragged slices of five
+    128-row tile rows, every arrival mode and both link layouts, against the oracle."""
+    P, m, K, N = 4, 520, 264, 392
+    x = inputs.normal(7350, (P * m, K), 1.0, "bf16")
+    w = inputs.normal(7351, (K, N), 0.02, "bf16")
+    ref = oracle.gemm(x, w)
+    ag = AG(x, w, P, dev)
+    parts = [inputs.normal(7360 + q, (m, N), 1.0, "f32") for q in range(P)]
+    rs = RS(x, w, parts, P, dev)
+    for r, links in ((1, 0), (2, 1)):
+        ag.x_recv.view(torch.int16).fill_(-1)
+        got = ag.run(r, o=fo.opts(tile=fo.TILE_128x128, row_groups=groups, links=links))
+        assert not np.isnan(got).any()
+        assert rel_frobenius(got, ref) <= TOL_BF16, f"AG rank {r} links {links}"
+        for arrival in (fo.ARR_LOCKSTEP, fo.ARR_EAGER):
+            rs.recv.fill_(float("nan"))
+            out, send = rs.run(r, o=fo.opts(tile=fo.TILE_128x128, row_groups=groups, links=links,
+                                             arrival=arrival))
+            ref_out, ref_send = oracle.rs(x, w, parts, P, r, want_send=True)
+            assert rel_frobenius(out, ref_out) <= TOL_BF16, f"RS rank {r} arrival {arrival}"
+            keep = ~np.isnan(ref_send)
+            assert rel_frobenius(send[keep], ref_send[keep]) <= TOL_BF16
+
+
 # ---- degenerate cases ------------------------------------------------------------------------
 
 def test_single_rank_and_tiny_shapes(dev):
