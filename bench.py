@@ -186,7 +186,8 @@ def main():
         variants = [("mesh_rowgroups", 0, 0), ("mesh_slices", 0, 1), ("onelink_slices", 1, 1)]
 
         def groups_of(kind, case, req):
-            order = fo.tile_order(kind, P, case.m, case.K, case.N, o=fo.opts(row_groups=req))
+            order = fo.tile_order(kind, P, case.m, case.K, case.N, o=fo.opts(row_groups=req),
+                                  out_dt=fo.F32 if kind == "rs" else fo.BF16)
             return max(g for _, g, _, _ in order) + 1
 
         t_ref_ag = timed(lambda: fo.gemm_ref(ag_full, ag_w, ref_y_ag, stream=stream), reps)
@@ -245,7 +246,8 @@ def main():
         dom, dom_ms, dom_flops = "rs", mean_rs, rs_case.flops
     bm, bn, wg = fo.tile_info(P, ag_case.m if dom == "ag" else rs_case.m,
                               ag_case.K if dom == "ag" else rs_case.K,
-                              ag_case.N if dom == "ag" else rs_case.N)
+                              ag_case.N if dom == "ag" else rs_case.N,
+                              out_dt=fo.BF16 if dom == "ag" else fo.F32)
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
     roofline = {
         "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,

@@ -169,10 +169,11 @@ fo_status check_common(int P, int rank, int64_t m, int64_t K, int64_t N, int in_
   return FO_OK;
 }
 
-int resolve_tile(const fo_opts& o, int in_dt, int P, int64_t m, int64_t N, int n_cu) {
+int resolve_tile(const fo_opts& o, int in_dt, int out_dt, int P, int64_t m, int64_t K, int64_t N,
+                 int n_cu) {
   if (in_dt == FO_DT_F32) return 0;
   if (o.tile != FO_TILE_AUTO) return o.tile;
-  return fo::choose_tile(P, m, N, n_cu);
+  return fo::choose_tile(P, m, K, N, out_dt == FO_DT_F32, n_cu);
 }
 
 fo_status tiles_for(int in_dt, int tile, int64_t m, int64_t N, int P, fo::Plan& p,
@@ -284,10 +285,11 @@ fo_status fo_slice_order(int32_t kind, int32_t order, int32_t P, int32_t rank, i
   return FO_OK;
 }
 
-fo_status fo_tile_info(int32_t P, int64_t m, int64_t K, int64_t N, int32_t in_dt, int32_t tile,
-                       int32_t* bm, int32_t* bn, int64_t* workgroups) {
+fo_status fo_tile_info(int32_t P, int64_t m, int64_t K, int64_t N, int32_t in_dt, int32_t out_dt,
+                       int32_t tile, int32_t* bm, int32_t* bn, int64_t* workgroups) {
   fo_status s = check_common(P, 0, m, K, N, in_dt);
   if (s != FO_OK) return s;
+  if (out_dt != FO_DT_BF16 && out_dt != FO_DT_F32) return invalid("out_dt %d is not a fo_dtype", out_dt);
   if (tile < FO_TILE_AUTO || tile > FO_TILE_64x64) return invalid("bad tile %d", tile);
   // the CU count only matters for AUTO; use the device's when one is present
   int n_cu = 256, dev = 0;
@@ -299,7 +301,7 @@ fo_status fo_tile_info(int32_t P, int64_t m, int64_t K, int64_t N, int32_t in_dt
   fo_opts o;
   fo_opts_init(&o);
   o.tile = tile;
-  const int t = resolve_tile(o, in_dt, P, m, N, n_cu);
+  const int t = resolve_tile(o, in_dt, out_dt, P, m, K, N, n_cu);
   fo::Plan p = fo::empty_plan();
   s = tiles_for(in_dt, t, m, N, P, p);
   if (s != FO_OK) return s;
@@ -315,13 +317,15 @@ fo_status fo_tile_info(int32_t P, int64_t m, int64_t K, int64_t N, int32_t in_dt
 }
 
 fo_status fo_tile_order(int32_t kind, int32_t P, int64_t m, int64_t K, int64_t N, int32_t in_dt,
-                        const fo_opts* opts, int32_t* out, int64_t capacity, int64_t* count) {
+                        int32_t out_dt, const fo_opts* opts, int32_t* out, int64_t capacity,
+                        int64_t* count) {
   fo_opts o;
   fo_status s = check_opts(opts, &o);
   if (s != FO_OK) return s;
   if (kind != 0 && kind != 1) return invalid("kind %d is neither 0 (AG) nor 1 (RS)", kind);
   s = check_common(P, 0, m, K, N, in_dt);
   if (s != FO_OK) return s;
+  if (out_dt != FO_DT_BF16 && out_dt != FO_DT_F32) return invalid("out_dt %d is not a fo_dtype", out_dt);
   if (capacity < 0 || (capacity > 0 && !out)) return invalid("bad output buffer");
   int n_cu = 256, dev = 0;
   if (hipGetDevice(&dev) == hipSuccess) {
@@ -333,7 +337,7 @@ fo_status fo_tile_order(int32_t kind, int32_t P, int64_t m, int64_t K, int64_t N
     if (count) *count = 0;
     return FO_OK;
   }
-  const int tile = resolve_tile(o, in_dt, P, m, N, n_cu);
+  const int tile = resolve_tile(o, in_dt, kind == 1 ? FO_DT_F32 : out_dt, P, m, K, N, n_cu);
   fo::Plan p = fo::empty_plan();
   s = tiles_for(in_dt, tile, m, N, P, p);
   if (s != FO_OK) return s;
@@ -391,7 +395,7 @@ fo_status fo_ag_gemm(const void* x_local, const void* const* x_peer, void* x_rec
   s = current_state(&st, &lk);
   if (s != FO_OK) return s;
 
-  const int tile = resolve_tile(o, in_dt, P, m, N, st->n_cu);
+  const int tile = resolve_tile(o, in_dt, out_dt, P, m, K, N, st->n_cu);
   fo::Plan p = fo::empty_plan();
   int bm = 0;
   s = tiles_for(in_dt, tile, m, N, P, p, &bm);
@@ -497,7 +501,7 @@ fo_status fo_gemm_rs(const void* x_shard, const void* w, float* send_buf, float*
   s = current_state(&st, &lk);
   if (s != FO_OK) return s;
 
-  const int tile = resolve_tile(o, in_dt, P, m, N, st->n_cu);
+  const int tile = resolve_tile(o, in_dt, FO_DT_F32, P, m, K, N, st->n_cu);
   fo::Plan p = fo::empty_plan();
   int bm = 0;
   s = tiles_for(in_dt, tile, m, N, P, p, &bm);
@@ -588,7 +592,7 @@ fo_status fo_gemm_ref(const void* a, const void* b, void* c, int64_t M, int64_t 
   fo_opts o;
   fo_opts_init(&o);
   o.tile = tile;
-  const int t = resolve_tile(o, in_dt, 1, M, N, st->n_cu);
+  const int t = resolve_tile(o, in_dt, out_dt, 1, M, K, N, st->n_cu);
   fo::Plan p = fo::empty_plan();
   s = tiles_for(in_dt, t, M, N, 1, p);
   if (s != FO_OK) return s;

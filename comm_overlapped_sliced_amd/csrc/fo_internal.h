@@ -64,8 +64,8 @@ struct TileShape {
 
 // Tile catalogue of the bf16 kernel (indexed by fo_tile, AUTO excluded).
 TileShape tile_shape(int tile);
-// AUTO selection for P slices of m rows; returns a fo_tile value.
-int choose_tile(int P, int64_t m, int64_t N, int n_cu);
+// AUTO selection for P slices of m rows, reduction length K, N columns; returns a fo_tile value.
+int choose_tile(int P, int64_t m, int64_t K, int64_t N, bool out_f32, int n_cu);
 
 // Launches the sliced GEMM for `plan` (bf16 MFMA kernel with the given tile, or the fp32
 // kernel when in_dt is FO_DT_F32). A plan whose waits or releases point at no signal table, or

@@ -31,23 +31,29 @@ int slice_order(int kind, int order, int P, int rank, int32_t* out) {
   return 1;
 }
 
-// AUTO tile choice. 256x256 tiles need the fewest operand bytes per MFMA and win when the grid
-// covers the CUs several times over. When it is at most a few rounds and the last round is only
-// partly filled, 128x256 tiles (half the rounds' granularity) finish sooner. Slices shorter than
-// 256 rows use 128-row tiles, and very small problems fall back to 64x64. Rows of a tile never
-// cross a slice.
-int choose_tile(int P, int64_t m, int64_t N, int n_cu) {
-  auto tiles = [&](int bm, int bn) {
-    return (double)P * (double)((m + bm - 1) / bm) * (double)((N + bn - 1) / bn);
+// AUTO tile choice. Every tile of a launch runs its whole K loop, so a launch takes about
+// ceil(tiles / CUs) rounds of one tile's time, and a 256x256 round costs what two 128x256 rounds
+// cost (128x256 tiles move 50% more operand bytes per flop and run ~3.5% slower per flop). The
+// rules, each checked by timing the sliced calls on MI355X:
+//   - slices of at most 128 rows: 128-row tiles (a 256-row tile would be half empty);
+//   - fp32 output with K <= 4096: 128x256, whose shorter write-back of 128 KB per tile hides behind
+//     other tiles' mainloops (Flash-RS, Llama-70B down projection: 523 vs 614 us);
+//   - a weight above 128 MB: 256x256, the least operand traffic per flop once the operands
+//     outgrow the last-level cache (Llama-405B gate+up: 3.3 vs 3.8 ms);
+//   - otherwise the fewer rounds, counted as above, with ties to 256x256.
+// Rows of a tile never cross a slice.
+int choose_tile(int P, int64_t m, int64_t K, int64_t N, bool out_f32, int n_cu) {
+  auto rounds = [&](int bm, int bn) {
+    const double t = (double)P * (double)((m + bm - 1) / bm) * (double)((N + bn - 1) / bn);
+    return (double)(int64_t)((t + n_cu - 1) / n_cu);
   };
   if (m <= 64 || N <= 64) return FO_TILE_64x64;
   if (m <= 128) return N >= 256 ? FO_TILE_128x256 : FO_TILE_128x128;
   if (N < 256) return FO_TILE_256x128;
-  const double r256 = tiles(256, 256) / n_cu;
-  if (r256 >= 3.0) return FO_TILE_256x256;
-  const double partial = (double)(int64_t)(r256 + 0.999999) - r256;
-  if (partial > 0.1) return FO_TILE_128x256;
-  return FO_TILE_256x256;
+  if (out_f32 && K <= 4096) return FO_TILE_128x256;
+  if ((double)K * (double)N * 2.0 > 128.0 * 1024 * 1024) return FO_TILE_256x256;
+  const double c256 = rounds(256, 256), c128 = rounds(128, 256) * 0.5 / 0.965;
+  return c128 < c256 ? FO_TILE_128x256 : FO_TILE_256x256;
 }
 
 }  // namespace fo

@@ -64,9 +64,9 @@ def load():
     lib.fo_transfer_ref.argtypes = [i32, vp, vp, i32, i32, i64, vp, op]
     lib.fo_check.argtypes = [vp]
     lib.fo_slice_order.argtypes = [i32, i32, i32, i32, ctypes.POINTER(i32)]
-    lib.fo_tile_info.argtypes = [i32, i64, i64, i64, i32, i32, ctypes.POINTER(i32),
+    lib.fo_tile_info.argtypes = [i32, i64, i64, i64, i32, i32, i32, ctypes.POINTER(i32),
                                  ctypes.POINTER(i32), ctypes.POINTER(i64)]
-    lib.fo_tile_order.argtypes = [i32, i32, i64, i64, i64, i32, op, ctypes.POINTER(i32), i64,
+    lib.fo_tile_order.argtypes = [i32, i32, i64, i64, i64, i32, i32, op, ctypes.POINTER(i32), i64,
                                   ctypes.POINTER(i64)]
     lib.fo_status_str.argtypes = [i32]
     lib.fo_status_str.restype = ctypes.c_char_p
@@ -221,27 +221,29 @@ def slice_order(kind: str, P: int, rank: int, order: int = ORDER_FLASH) -> list:
     return list(out)
 
 
-def tile_info(P: int, m: int, K: int, N: int, in_dt: int = BF16, tile: int = TILE_AUTO):
+def tile_info(P: int, m: int, K: int, N: int, in_dt: int = BF16, tile: int = TILE_AUTO,
+              out_dt: int = BF16):
+    """Tile rows, tile columns and workgroups of one call (fo_tile_info); out_dt F32 for RS."""
     bm, bn, wg = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()
-    st = load().fo_tile_info(P, m, K, N, in_dt, tile, ctypes.byref(bm), ctypes.byref(bn),
+    st = load().fo_tile_info(P, m, K, N, in_dt, out_dt, tile, ctypes.byref(bm), ctypes.byref(bn),
                              ctypes.byref(wg))
     _raise_on(st, "fo_tile_info")
     return bm.value, bn.value, wg.value
 
 
 def tile_order(kind: str, P: int, m: int, K: int, N: int, in_dt: int = BF16,
-               o: Opts | None = None):
+               o: Opts | None = None, out_dt: int = BF16):
     """Dispatch order of one call: a list of (position, row group, tile row, tile column) per
     workgroup (fo_tile_order)."""
     lib = load()
     cnt = ctypes.c_int64()
     k = 0 if kind == "ag" else 1
     ob = ctypes.byref(o) if o is not None else None
-    _raise_on(lib.fo_tile_order(k, P, m, K, N, in_dt, ob, None, 0, ctypes.byref(cnt)),
+    _raise_on(lib.fo_tile_order(k, P, m, K, N, in_dt, out_dt, ob, None, 0, ctypes.byref(cnt)),
               "fo_tile_order")
     buf = (ctypes.c_int32 * (4 * cnt.value))()
-    _raise_on(lib.fo_tile_order(k, P, m, K, N, in_dt, ob, buf, cnt.value, ctypes.byref(cnt)),
-              "fo_tile_order")
+    _raise_on(lib.fo_tile_order(k, P, m, K, N, in_dt, out_dt, ob, buf, cnt.value,
+                                ctypes.byref(cnt)), "fo_tile_order")
     return [tuple(buf[4 * i:4 * i + 4]) for i in range(cnt.value)]
 
 

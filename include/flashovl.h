@@ -193,17 +193,20 @@ fo_status fo_check(void* stream);
    computation order to out[0..P-1]. */
 fo_status fo_slice_order(int32_t kind, int32_t order, int32_t P, int32_t rank, int32_t* out);
 
-/* The tile shape the bf16 kernel would use for slices of m rows, K, N (tile: fo_tile request).
-   Writes the tile rows/columns and the number of workgroups one call over P slices launches. */
-fo_status fo_tile_info(int32_t P, int64_t m, int64_t K, int64_t N, int32_t in_dt, int32_t tile,
-                       int32_t* bm, int32_t* bn, int64_t* workgroups);
+/* The tile shape the bf16 kernel would use for slices of m rows, K, N with output out_dt (fp32 for
+   fo_gemm_rs) and the tile request `tile` (a fo_tile). Writes the tile rows/columns and the
+   number of workgroups one call over P slices launches. */
+fo_status fo_tile_info(int32_t P, int64_t m, int64_t K, int64_t N, int32_t in_dt, int32_t out_dt,
+                       int32_t tile, int32_t* bm, int32_t* bn, int64_t* workgroups);
 
-/* The dispatch order of one fo_ag_gemm (kind 0) or fo_gemm_rs (kind 1) launch for these sizes and
-   options (order, tile, row_groups are used): workgroup u computes position out[4u], row group
+/* The dispatch order of one fo_ag_gemm (kind 0) or fo_gemm_rs (kind 1) launch for these sizes,
+   output dtype (fo_gemm_rs always writes fp32) and options (order, tile, row_groups are used):
+   workgroup u computes position out[4u], row group
    out[4u+1], tile row out[4u+2] and tile column out[4u+3] of that position. Writes the first
    min(capacity, count) workgroups; *count receives the number of workgroups. */
 fo_status fo_tile_order(int32_t kind, int32_t P, int64_t m, int64_t K, int64_t N, int32_t in_dt,
-                        const fo_opts* opts, int32_t* out, int64_t capacity, int64_t* count);
+                        int32_t out_dt, const fo_opts* opts, int32_t* out, int64_t capacity,
+                        int64_t* count);
 
 const char* fo_status_str(fo_status s);
 /* Detail of the last failure on the calling thread (empty string if none). */

@@ -18,8 +18,9 @@ TILES = [fo.TILE_AUTO, fo.TILE_256x256, fo.TILE_256x128, fo.TILE_128x256, fo.TIL
          fo.TILE_64x64]
 
 
-def _grid(P, m, N, tile):
-    bm, bn, wg = fo.tile_info(P, m, 64, N, fo.BF16, tile)
+def _grid(kind, P, m, K, N, tile):
+    out_dt = fo.F32 if kind == "rs" else fo.BF16
+    bm, bn, wg = fo.tile_info(P, m, K, N, fo.BF16, tile, out_dt=out_dt)
     return (m + bm - 1) // bm, (N + bn - 1) // bn, wg
 
 
@@ -28,8 +29,9 @@ def _grid(P, m, N, tile):
 def test_every_tile_once(kind, shape):
     P, m, K, N = shape
     for tile, groups in itertools.product(TILES, [0, 1, 2, 3, 8]):
-        tm_n, tn_n, wg = _grid(P, m, N, tile)
-        order = fo.tile_order(kind, P, m, K, N, o=fo.opts(tile=tile, row_groups=groups))
+        tm_n, tn_n, wg = _grid(kind, P, m, K, N, tile)
+        order = fo.tile_order(kind, P, m, K, N, o=fo.opts(tile=tile, row_groups=groups),
+                              out_dt=fo.F32 if kind == "rs" else fo.BF16)
         assert len(order) == wg == P * tm_n * tn_n
         seen = {(p, tm, tn) for p, _, tm, tn in order}
         assert len(seen) == wg, "a tile is computed twice"
@@ -41,10 +43,11 @@ def test_every_tile_once(kind, shape):
 def test_groups_and_layout(kind, shape):
     P, m, K, N = shape
     for tile, req in itertools.product(TILES, [0, 1, 2, 3, 8]):
-        tm_n, tn_n, _ = _grid(P, m, N, tile)
+        tm_n, tn_n, _ = _grid(kind, P, m, K, N, tile)
         G = min(tm_n if req == 0 else req, 8, tm_n)
         gr = -(-tm_n // G)
-        order = fo.tile_order(kind, P, m, K, N, o=fo.opts(tile=tile, row_groups=req))
+        order = fo.tile_order(kind, P, m, K, N, o=fo.opts(tile=tile, row_groups=req),
+                              out_dt=fo.F32 if kind == "rs" else fo.BF16)
         assert all(g == tm // gr for _, g, tm, _ in order), "group is not its tile row's group"
         T = tm_n * tn_n
         lead = 1 if kind == "ag" else 0
@@ -69,10 +72,13 @@ def test_rejects():
     lib = fo.load()
     import ctypes
     cnt = ctypes.c_int64()
-    assert lib.fo_tile_order(2, 4, 64, 64, 64, fo.BF16, None, None, 0, ctypes.byref(cnt)) == \
+    B = fo.BF16
+    assert lib.fo_tile_order(2, 4, 64, 64, 64, B, B, None, None, 0, ctypes.byref(cnt)) == \
         fo.FO_ERR_INVALID_ARG
-    assert lib.fo_tile_order(0, 4, 64, 64, 64, fo.BF16, None, None, 5, ctypes.byref(cnt)) == \
+    assert lib.fo_tile_order(0, 4, 64, 64, 64, B, B, None, None, 5, ctypes.byref(cnt)) == \
+        fo.FO_ERR_INVALID_ARG
+    assert lib.fo_tile_order(0, 4, 64, 64, 64, B, 7, None, None, 0, ctypes.byref(cnt)) == \
         fo.FO_ERR_INVALID_ARG
     o = fo.opts(row_groups=9)
-    assert lib.fo_tile_order(0, 4, 64, 64, 64, fo.BF16, ctypes.byref(o), None, 0,
+    assert lib.fo_tile_order(0, 4, 64, 64, 64, B, B, ctypes.byref(o), None, 0,
                              ctypes.byref(cnt)) == fo.FO_ERR_INVALID_ARG
