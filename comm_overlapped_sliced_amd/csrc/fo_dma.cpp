@@ -17,6 +17,7 @@
 #include <hsa/hsa.h>
 #include <hsa/hsa_ext_amd.h>
 
+#include <algorithm>
 #include <bitset>
 #include <chrono>
 #include <cstdio>
@@ -253,6 +254,12 @@ bool init(int dev, void* scratch, std::string* err) {
     *err = "no SDMA engine accepts device-to-device copies on this device";
     return false;
   }
+  // Engines 2k and 2k+1 share their bandwidth: measured on MI355X, seven concurrent 16 MiB copies
+  // on engines 2..8 run at ~46 GB/s each, on engines 2, 4, ..., 14 at ~58 GB/s each (one engine
+  // alone: ~59 GB/s). Links take one engine of each pair before the second of any pair.
+  std::stable_partition(d.eng, d.eng + d.n_eng, [](uint32_t bit) {
+    return (__builtin_ctz(bit) & 1) == 0;
+  });
   w.issued.reset();
   d.ready = true;
   return true;
