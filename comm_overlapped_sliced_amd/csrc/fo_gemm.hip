@@ -100,7 +100,7 @@ __device__ __forceinline__ float4 ld_nt4(const float* p) {
 
 // ---------------------------------------------------------------- bf16 MFMA kernel ----------
 //
-// A ring of kStages LDS stages; stage s holds the A tile [BM rows][kBK k] (64-byte rows) and the
+// A ring of C::STAGES LDS stages; stage s holds the A tile [BM rows][kBK k] (64-byte rows) and the
 // W tile [kBK rows][BN cols] (2*BN-byte rows). Both are filled straight from HBM by buffer loads
 // that write LDS (16 bytes per lane, no VGPR staging); a load outside the matrix reads zero
 // through the buffer's range check, so ragged edges need no branches. The 16-byte chunks of a
@@ -109,7 +109,7 @@ __device__ __forceinline__ float4 ld_nt4(const float* p) {
 // ds_read_b64_tr_b16 transpose reads, which turn 4 rows x 16 columns of the row-major W tile
 // into 4 K-values per lane.
 
-constexpr int kStages = 4;
+constexpr int kLdsBytes = 160 * 1024;  // LDS of one CU
 constexpr uint32_t kOOB = 0x80000000u;          // offset past every range: the load reads 0
 constexpr int kRsrcWord3 = 0x00020000;          // raw buffer, 32-bit data format
 
@@ -127,7 +127,12 @@ struct Cfg {
   static constexpr int A_LOADS = A_BYTES / 1024 / 4;  // 1 KB loads per wave per stage
   static constexpr int B_LOADS = B_BYTES / 1024 / 4;
   static constexpr int LOADS = A_LOADS + B_LOADS;
+  // Four stages: three K steps in flight while one is consumed. Deeper rings (5 for 256x256, 6
+  // for 128x256, as many as the LDS holds) measured no faster on MI355X, and 256x256 slower.
+  static constexpr int STAGES = 4;
+  static_assert(STAGES * STAGE <= kLdsBytes, "LDS");
   static_assert(A_LOADS >= 1 && B_LOADS >= 1 && FM >= 1 && FN >= 1, "tile");
+  static_assert(STAGES >= 3 && (STAGES - 1) * LOADS < 64, "stages");
 };
 
 // swizzle of the 4 chunks of an A row and of the chunks of a W row
@@ -182,10 +187,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 template <int BM, int BN>
 __device__ __forceinline__ void bf16_tile(const Plan& p, const int tile, uint8_t* const lds_ring) {
   using C = Cfg<BM, BN>;
-  uint8_t* const st0 = lds_ring;
-  uint8_t* const st1 = lds_ring + C::STAGE;
-  uint8_t* const st2 = lds_ring + 2 * C::STAGE;
-  uint8_t* const st3 = lds_ring + 3 * C::STAGE;
+  constexpr int S = C::STAGES;
+  auto st = [&](int i) -> uint8_t* { return lds_ring + i * C::STAGE; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -309,14 +312,16 @@ __device__ __forceinline__ void bf16_tile(const Plan& p, const int tile, uint8_t
   // this wave's loads of the oldest pending stage have landed when at most n later stages'
   // loads are still in flight
   auto wait_stages = [&](int n) {
-    if (n >= 3)
-      wait_vmcnt<3 * C::LOADS>();
-    else if (n == 2)
-      wait_vmcnt<2 * C::LOADS>();
-    else if (n == 1)
-      wait_vmcnt<C::LOADS>();
-    else
-      wait_vmcnt<0>();
+    switch (n) {
+      case 7: wait_vmcnt<(7 < S ? 7 : 0) * C::LOADS>(); break;
+      case 6: wait_vmcnt<(6 < S ? 6 : 0) * C::LOADS>(); break;
+      case 5: wait_vmcnt<(5 < S ? 5 : 0) * C::LOADS>(); break;
+      case 4: wait_vmcnt<(4 < S ? 4 : 0) * C::LOADS>(); break;
+      case 3: wait_vmcnt<(3 < S ? 3 : 0) * C::LOADS>(); break;
+      case 2: wait_vmcnt<2 * C::LOADS>(); break;
+      case 1: wait_vmcnt<C::LOADS>(); break;
+      default: wait_vmcnt<0>(); break;
+    }
   };
   // The workgroup barrier proper: no memory fence, so the prefetches issued before it stay in
   // flight (every wave has already waited for its own loads of the stage it needs).
@@ -327,25 +332,24 @@ __device__ __forceinline__ void bf16_tile(const Plan& p, const int tile, uint8_t
   };
 
   constexpr int NMFMA = C::FM * C::FN, NREAD = C::FM + C::FN;
-  // Software pipeline over K steps of kBK; stage kt % 4 holds step kt. A step runs its MFMAs in
+  // Software pipeline over K steps of kBK; stage kt % S holds step kt. A step runs its MFMAs in
   // two halves (K-substeps 0 and 1). The first half's fragments are already in registers; while
   // its MFMAs issue, the second half's fragments are read. Then, once every wave holds the next
   // stage and nobody reads this one any more (barrier), the second half's MFMAs issue
-  // interleaved with the loads that refill this stage with step kt + 4 and with the reads of the
+  // interleaved with the loads that refill this stage with step kt + S and with the reads of the
   // next step's first-half fragments. The order inside each half is pinned with scheduling
   // barriers so that memory instructions issue under running MFMAs.
   const int KT = uni((int)((K + kBK - 1) / kBK));
   const int KFULL = uni((int)(K / kBK));  // steps that lie entirely inside K
   Frags f0, f1;
   if (KT > 0) {
-    issue_step(0, lds_addr(st0));
-    if (1 < KT) issue_step(1, lds_addr(st1));
-    if (2 < KT) issue_step(2, lds_addr(st2));
-    if (3 < KT) issue_step(3, lds_addr(st3));
-    wait_stages(KT - 1 < 3 ? KT - 1 : 3);
+#pragma unroll
+    for (int i = 0; i < S; ++i)
+      if (i < KT) issue_step(i, lds_addr(st(i)));
+    wait_stages(KT - 1 < S - 1 ? KT - 1 : S - 1);
     barrier();
 #pragma unroll
-    for (int q = 0; q < NREAD; ++q) rd_frag(st0, 0, f0, q);
+    for (int q = 0; q < NREAD; ++q) rd_frag(st(0), 0, f0, q);
   }
   constexpr int NX1 = NMFMA > NREAD ? NMFMA : NREAD;
   constexpr int NX2 = NMFMA > C::LOADS ? (NMFMA > NREAD ? NMFMA : NREAD)
@@ -359,17 +363,17 @@ __device__ __forceinline__ void bf16_tile(const Plan& p, const int tile, uint8_t
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // Steady-state step: stage kt is refilled with step kt + 4, which lies entirely inside K.
+  // Steady-state step: stage kt is refilled with step kt + S, which lies entirely inside K.
   auto step_main = [&](int kt, const uint8_t* cur, const uint8_t* nxt) {
     first_half(cur);
-    wait_stages(2);
+    wait_stages(S - 2);
     barrier();
     const uint32_t cur_lds = lds_addr(cur);
-    const i32x4 rb = w_rsrc(kt + 4);
+    const i32x4 rb = w_rsrc(kt + S);
 #pragma unroll
     for (int x = 0; x < NX2; ++x) {
       if (x < NMFMA) mfma(f1, x);
-      if (x < C::LOADS) issue_one(std::false_type{}, kt + 4, cur_lds, rb, x);
+      if (x < C::LOADS) issue_one(std::false_type{}, kt + S, cur_lds, rb, x);
       if (x < NREAD) rd_frag(nxt, 0, f0, x);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -377,38 +381,35 @@ __device__ __forceinline__ void bf16_tile(const Plan& p, const int tile, uint8_t
   // Any step (start-up, last steps, K tail), with the conditions checked at run time.
   auto step_any = [&](int kt, const uint8_t* cur, const uint8_t* nxt) {
     first_half(cur);
-    const int later = KT - 2 - kt;  // steps issued beyond kt + 1 (at most 2 at this point)
-    wait_stages(later < 0 ? 0 : (later > 2 ? 2 : later));
+    const int later = KT - 2 - kt;  // steps issued beyond kt + 1 (at most S - 2 at this point)
+    wait_stages(later < 0 ? 0 : (later > S - 2 ? S - 2 : later));
     barrier();
-    const bool refill = kt + 4 < KT, tail = kt + 4 >= KFULL, more = kt + 1 < KT;
+    const bool refill = kt + S < KT, tail = kt + S >= KFULL, more = kt + 1 < KT;
     const uint32_t cur_lds = lds_addr(cur);
     i32x4 rb{};
-    if (refill) rb = w_rsrc(kt + 4);
+    if (refill) rb = w_rsrc(kt + S);
 #pragma unroll
     for (int x = 0; x < NX2; ++x) {
       if (x < NMFMA) mfma(f1, x);
       if (x < C::LOADS && refill) {
         if (tail)
-          issue_one(std::true_type{}, kt + 4, cur_lds, rb, x);
+          issue_one(std::true_type{}, kt + S, cur_lds, rb, x);
         else
-          issue_one(std::false_type{}, kt + 4, cur_lds, rb, x);
+          issue_one(std::false_type{}, kt + S, cur_lds, rb, x);
       }
       if (x < NREAD && more) rd_frag(nxt, 0, f0, x);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
   int kt = 0;
-  for (; kt + 8 <= KFULL; kt += 4) {
-    step_main(kt, st0, st1);
-    step_main(kt + 1, st1, st2);
-    step_main(kt + 2, st2, st3);
-    step_main(kt + 3, st3, st0);
+  for (; kt + 2 * S <= KFULL; kt += S) {
+#pragma unroll
+    for (int i = 0; i < S; ++i) step_main(kt + i, st(i), st((i + 1) % S));
   }
-  for (; kt < KT; kt += 4) {
-    step_any(kt, st0, st1);
-    if (kt + 1 < KT) step_any(kt + 1, st1, st2);
-    if (kt + 2 < KT) step_any(kt + 2, st2, st3);
-    if (kt + 3 < KT) step_any(kt + 3, st3, st0);
+  for (; kt < KT; kt += S) {
+#pragma unroll
+    for (int i = 0; i < S; ++i)
+      if (kt + i < KT) step_any(kt + i, st(i), st((i + 1) % S));
   }
 
   // ---- epilogue ---------------------------------------------------------------------------
@@ -421,10 +422,10 @@ __device__ __forceinline__ void bf16_tile(const Plan& p, const int tile, uint8_t
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // LDS stages no longer read
   float* const ep = (float*)lds_ring;  // [ER rows][EW floats] over the whole ring
   constexpr int EW = BN + 8;      // padded row: rows 4 apart land 32 banks apart
-  constexpr int ER = (BM * EW * 4 <= kStages * C::STAGE)         ? BM
-                     : (BM / 2 * EW * 4 <= kStages * C::STAGE)   ? BM / 2
+  constexpr int ER = (BM * EW * 4 <= S * C::STAGE)         ? BM
+                     : (BM / 2 * EW * 4 <= S * C::STAGE)   ? BM / 2
                                                                 : BM / 4;
-  static_assert(ER * EW * 4 <= kStages * C::STAGE && ER % 32 == 0, "epilogue block");
+  static_assert(ER * EW * 4 <= S * C::STAGE && ER % 32 == 0, "epilogue block");
   constexpr int CPR = BN / 4;                   // 4-float chunks per row
   constexpr int CPT = ER * CPR / kThreads;      // chunks per thread per block
   static_assert(CPT >= 1 && (ER * CPR) % kThreads == 0, "epilogue chunks");
@@ -500,7 +501,7 @@ __device__ __forceinline__ void bf16_tile(const Plan& p, const int tile, uint8_t
 // workgroups walk the tiles with a stride of the grid size, in the same order.
 template <int BM, int BN>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(Plan p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_ring[kStages * Cfg<BM, BN>::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_ring[Cfg<BM, BN>::STAGES * Cfg<BM, BN>::STAGE];
   const int total = p.grid.npos * p.grid.tiles_m * p.grid.tiles_n;
   for (int tile = blockIdx.x; tile < total; tile += gridDim.x) bf16_tile<BM, BN>(p, tile, lds_ring);
 }
