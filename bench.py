@@ -132,15 +132,21 @@ def main():
     def ev():
         return torch.cuda.Event(enable_timing=True)
 
-    def ag_call(evs=None, arrival=fo.ARR_DEFAULT, links=args.links, groups=args.row_groups):
-        o = fo.opts(links=links, row_groups=groups, arrival=arrival, kernel_events=evs)
+    def ag_call(evs=None, arrival=fo.ARR_DEFAULT, links=args.links, groups=args.row_groups,
+                order=fo.ORDER_FLASH, rank=r):
+        o = fo.opts(order=order, links=links, row_groups=groups, arrival=arrival,
+                    kernel_events=evs)
         peers = None if arrival == fo.ARR_NONE else ag_slices
-        fo.ag_gemm(ag_slices[r], peers, ag_recv, ag_w, ag_y, P, r, compute_stream=stream, o=o)
+        fo.ag_gemm(ag_slices[rank], peers, ag_recv, ag_w, ag_y, P, rank, compute_stream=stream,
+                   o=o)
 
-    def rs_call(evs=None, arrival=fo.ARR_DEFAULT, links=args.links, groups=args.row_groups):
-        o = fo.opts(links=links, row_groups=groups, arrival=arrival, kernel_events=evs)
+    def rs_call(evs=None, arrival=fo.ARR_DEFAULT, links=args.links, groups=args.row_groups,
+                order=fo.ORDER_FLASH, rank=r):
+        o = fo.opts(order=order, links=links, row_groups=groups, arrival=arrival,
+                    kernel_events=evs)
         peers = None if arrival == fo.ARR_NONE else rs_peer
-        fo.gemm_rs(rs_x, rs_w, rs_send, rs_out, peers, rs_recv, P, r, compute_stream=stream, o=o)
+        fo.gemm_rs(rs_x, rs_w, rs_send, rs_out, peers, rs_recv, P, rank, compute_stream=stream,
+                   o=o)
 
     def step(evs=None):
         ag_call(evs[0] if evs else None)
@@ -215,6 +221,31 @@ def main():
                 f"slice {ts_ag*1e3:.0f} xfer {tx_ag*1e3:.0f} -> {exposure[name]['ag']['exposed_frac']:.3f}; "
                 f"RS ref {t_ref_rs*1e3:.0f} slice0 {t0_rs*1e3:.0f} slice {ts_rs*1e3:.0f} "
                 f"xfer {tx_rs*1e3:.0f} -> {exposure[name]['rs']['exposed_frac']:.3f}")
+        # the page's comparison at the rank that data slicing serves worst (P-1: its own RS chunk
+        # and its local AG slice come last in index order): vanilla (all transfers, then the
+        # GEMM, nothing overlapped), data slicing (index order, whole slices) and Flash (the
+        # defaults). "removed" = the share of the transfer time that does not show in the
+        # latency, the page's communication-overhead reduction against vanilla.
+        rb = P - 1
+        tw = fo.opts(row_groups=1)
+        tx_ag = timed(lambda: fo.transfer_ref("ag", ag_slices, ag_recv, P, rb,
+                                              ag_case.m * ag_case.K * 2, stream, tw), reps)
+        tx_rs = timed(lambda: fo.transfer_ref("rs", rs_peer, rs_recv, P, rb,
+                                              rs_case.m * rs_case.N * 4, stream, tw), reps)
+        base = {}
+        for kind, t_ref, t_x, call in (("ag", t_ref_ag, tx_ag, ag_call), ("rs", t_ref_rs, tx_rs, rs_call)):
+            t_ds = timed(lambda: call(order=fo.ORDER_NATURAL, groups=1, rank=rb), reps)
+            t_fl = timed(lambda: call(rank=rb), reps)
+            van = t_ref + t_x
+            base[kind] = {"rank": rb, "t_ref_us": t_ref * 1e3, "t_xfer_us": t_x * 1e3,
+                          "vanilla_us": van * 1e3, "data_slicing_us": t_ds * 1e3,
+                          "flash_us": t_fl * 1e3,
+                          "removed_data_slicing": (van - t_ds) / t_x,
+                          "removed_flash": (van - t_fl) / t_x}
+            log(f"baselines {kind} rank {rb}: vanilla {van*1e3:.0f} us, data slicing "
+                f"{t_ds*1e3:.0f} us ({base[kind]['removed_data_slicing']:.2f} removed), flash "
+                f"{t_fl*1e3:.0f} us ({base[kind]['removed_flash']:.2f} removed)")
+        exposure["baselines"] = base
         fo.check(stream)
         step()
         fo.check(stream)

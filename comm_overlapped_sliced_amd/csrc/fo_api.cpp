@@ -202,13 +202,13 @@ void set_groups(int req, fo::Plan& p) {
 }
 
 // Dispatch layout of a call of `kind` (0 AG, 1 RS): Flash-AG puts the local slice first, whole,
-// and computes the received slices group by group (NATURAL: every slice group by group in index
-// order); Flash-RS computes the chunks for the other ranks group by group and its own chunk last,
-// whole.
+// and computes the received slices group by group; Flash-RS computes the chunks for the other
+// ranks group by group and its own chunk last, whole. NATURAL: every slice group by group in
+// index order.
 void set_layout(int kind, const fo_opts& o, fo::Plan& p) {
   set_groups(o.row_groups, p);
   p.grid.lead = (kind == 0 && o.order == FO_ORDER_FLASH) ? 1 : 0;
-  p.grid.trail = kind == 1 ? 1 : 0;
+  p.grid.trail = (kind == 1 && o.order == FO_ORDER_FLASH) ? 1 : 0;
 }
 
 // Element rows [*r0, *r1) of row group g of a slice of m rows with tile height bm.
@@ -462,10 +462,6 @@ fo_status fo_gemm_rs(const void* x_shard, const void* w, float* send_buf, float*
   if (s != FO_OK) return s;
   s = check_common(P, rank, m, K, N, in_dt);
   if (s != FO_OK) return s;
-  if (o.order != FO_ORDER_FLASH) {
-    set_error("fo_gemm_rs implements the Flash-RS order only");
-    return FO_ERR_UNSUPPORTED;
-  }
   const int arrival = o.arrival == FO_ARR_DEFAULT ? FO_ARR_LOCKSTEP : o.arrival;
   const bool arrivals = peer_partial != nullptr && arrival != FO_ARR_NONE && P > 1;
   const size_t es = dt_size(in_dt);
@@ -508,17 +504,22 @@ fo_status fo_gemm_rs(const void* x_shard, const void* w, float* send_buf, float*
   if (s != FO_OK) return s;
   set_layout(1, o, p);
   const bool lockstep = arrivals && arrival == FO_ARR_LOCKSTEP;
+  // NATURAL (data slicing): chunks in index order, the own chunk written plainly where it falls,
+  // and the partials added after the GEMM by a separate kernel
+  const bool natural = o.order == FO_ORDER_NATURAL;
   fo::dma::Call call{};
   if (arrivals) FO_DMA(fo::dma::begin(st->dev, P, p.grid.groups, &call, &e_));
   int32_t order[FO_MAX_P];
-  fo::slice_order(1, FO_ORDER_FLASH, P, rank, order);
+  fo::slice_order(1, o.order, P, rank, order);
+  int own_pos = 0;
   for (int pos = 0; pos < P; ++pos) {
     const int d = order[pos];
     p.a_pos[pos] = (const uint8_t*)x_shard + (size_t)d * m * K * es;
     p.c_pos[pos] = d == rank ? (void*)out : (void*)((uint8_t*)send_buf + (size_t)d * chunk_b);
     p.gate_slice[pos] = -1;
-    if (d == rank) p.accum_pos = pos;
+    if (d == rank) own_pos = pos;
   }
+  if (!natural) p.accum_pos = own_pos;
   p.comp_tab = call.comp_tab;
   p.rel_tab = lockstep ? call.rel_tab : nullptr;
   // partials arrive from rank-1, rank-2, ... (mod P) and are added in that order
@@ -543,6 +544,25 @@ fo_status fo_gemm_rs(const void* x_shard, const void* w, float* send_buf, float*
   if (arrivals) FO_HIP(fo::launch_release(call.start, cs));
   s = launch_with_events(p, in_dt, tile, cs, o);
   if (s != FO_OK) return s;
+  if (natural && P > 1) {
+    fo::ReduceArgs ra{};
+    ra.out = out;
+    ra.n_recv = P - 1;
+    bool al = aligned(out, 16) && ((size_t)m * N) % 4 == 0;
+    for (int i = 0; i < P - 1; ++i) {
+      ra.recv[i] = p.recv[i];
+      ra.recv_slice[i] = p.recv_slice[i];
+      al = al && aligned(p.recv[i], 16);
+    }
+    ra.comp_tab = call.comp_tab;
+    ra.groups = p.grid.groups;
+    ra.vec4 = al ? 1 : 0;
+    ra.count = m * N;
+    ra.spin_limit = p.spin_limit;
+    ra.err = st->err;
+    ra.max_blocks = 2 * st->n_cu;
+    FO_HIP(fo::launch_reduce(ra, cs));
+  }
   if (arrivals) FO_DMA(fo::dma::end(st->dev, call, cs, &e_));
   FO_HIP(hipEventRecord(st->ev_last, cs));
   st->have_last = true;
@@ -550,6 +570,8 @@ fo_status fo_gemm_rs(const void* x_shard, const void* w, float* send_buf, float*
     // transfer t brings the partial of peer rank-1-t. In lockstep that peer sends its group g at
     // its own unit (t, g), which (peers progressing together) ends when this rank ends its unit
     // (t, g): the copy waits for that release.
+    // In the NATURAL order every rank computes chunk d at step d, so all partials for this rank
+    // are sent when its own position is complete.
     int seq[FO_MAX_P];
     const int n = arrival_sequence(1, FO_ORDER_FLASH, P, rank, seq);
     const int L = links_for(o, P);
@@ -560,7 +582,8 @@ fo_status fo_gemm_rs(const void* x_shard, const void* w, float* send_buf, float*
       for (int t = 0; t < n; ++t) {
         const int q = seq[t];
         const size_t off = (size_t)q * chunk_b + (size_t)r0 * row_b;
-        FO_DMA(fo::dma::copy(st->dev, call, t % L, q, g, lockstep ? t : -1,
+        const int rel_pos = !lockstep ? -1 : (natural ? own_pos : t);
+        FO_DMA(fo::dma::copy(st->dev, call, t % L, q, g, rel_pos,
                              (uint8_t*)recv_buf + off,
                              (const uint8_t*)peer_partial[q] + (size_t)r0 * row_b,
                              (size_t)(r1 - r0) * row_b, &e_));

@@ -15,6 +15,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "fo_internal.h"
@@ -613,6 +614,72 @@ __global__ __launch_bounds__(64) void wait_kernel(const int64_t* const* comp_tab
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
 }
 
+typedef __attribute__((ext_vector_type(4))) float v4f;
+
+// Loads that are coherent at system scope (sc0 sc1): they return what the copy engines wrote to
+// memory whatever the L1 and L2 of this CU hold, so the reader needs no cache invalidation. Their
+// completion is awaited with an explicit s_waitcnt (wait_loads) before the values are used.
+__device__ __forceinline__ v4f ld_sys4(const float* p) {
+  v4f v;
+  asm volatile("global_load_dwordx4 %0, %1, off sc0 sc1" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+__device__ __forceinline__ float ld_sys1(const float* p) {
+  float v;
+  asm volatile("global_load_dword %0, %1, off sc0 sc1" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// out += the received partials, in arrival order (the tail of Flash-RS in the data-slicing
+// order). HBM-bound: one pass over out and each partial, 16-byte accesses when aligned. The grid
+// is persistent (about two blocks per CU) so that few blocks poll the arrival signals; the
+// partials are read with system-coherent loads, so no block needs a cache invalidation (a
+// system-scope acquire in every block costs more than the pass itself).
+__global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
+  if (threadIdx.x == 0 && a.comp_tab != nullptr)
+    for (int i = 0; i < a.n_recv; ++i)
+      if (a.recv_slice[i] >= 0)
+        for (int g = 0; g < a.groups; ++g)
+          wait_signal(a.comp_tab[a.recv_slice[i] * kMaxGroups + g], a.spin_limit, a.err);
+  __syncthreads();
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t first = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  constexpr int B = 8;  // partials whose loads are in flight together
+  if (a.vec4) {
+    v4f* o = (v4f*)a.out;
+    for (int64_t i = first; i < a.count / 4; i += stride) {
+      v4f x = o[i];
+      for (int q0 = 0; q0 < a.n_recv; q0 += B) {
+        v4f t[B];
+#pragma unroll
+        for (int j = 0; j < B; ++j)
+          if (q0 + j < a.n_recv) t[j] = ld_sys4(a.recv[q0 + j] + 4 * i);
+        wait_loads();
+#pragma unroll
+        for (int j = 0; j < B; ++j)
+          if (q0 + j < a.n_recv) x += t[j];
+      }
+      o[i] = x;
+    }
+  } else {
+    for (int64_t i = first; i < a.count; i += stride) {
+      float x = a.out[i];
+      for (int q0 = 0; q0 < a.n_recv; q0 += B) {
+        float t[B];
+#pragma unroll
+        for (int j = 0; j < B; ++j)
+          if (q0 + j < a.n_recv) t[j] = ld_sys1(a.recv[q0 + j] + i);
+        wait_loads();
+#pragma unroll
+        for (int j = 0; j < B; ++j)
+          if (q0 + j < a.n_recv) x += t[j];
+      }
+      a.out[i] = x;
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_release(int64_t* v, hipStream_t s) {
@@ -628,6 +695,19 @@ hipError_t launch_wait(const int64_t* const* comp_tab, const int32_t* slices, in
   l.n = n;
   l.groups = groups;
   hipLaunchKernelGGL(wait_kernel, dim3(1), dim3(64), 0, s, comp_tab, l, spin_limit, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s) {
+  if (a.n_recv < 0 || a.n_recv > FO_MAX_P || a.groups < 1 || a.groups > kMaxGroups || a.count < 0)
+    return hipErrorInvalidValue;
+  for (int i = 0; i < a.n_recv; ++i)
+    if (a.recv_slice[i] >= FO_MAX_P || (a.recv_slice[i] >= 0 && a.comp_tab == nullptr))
+      return hipErrorInvalidValue;
+  const int64_t items = a.vec4 ? a.count / 4 : a.count;
+  const int64_t blocks =
+      std::max<int64_t>(1, std::min<int64_t>((items + 255) / 256, std::max(1, a.max_blocks)));
+  hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -84,6 +84,24 @@ hipError_t launch_release(int64_t* v, hipStream_t stream);
 hipError_t launch_wait(const int64_t* const* comp_tab, const int32_t* slices, int n, int groups,
                        uint64_t spin_limit, uint32_t* err, hipStream_t stream);
 
+// The received partials added onto `out` after the GEMM (Flash-RS in the data-slicing order,
+// where the own chunk is not the last one computed): out[i] += recv[0][i] + recv[1][i] + ... in
+// that order, for i < count, once every row group of every awaited slice has landed.
+struct ReduceArgs {
+  float* out;
+  const float* recv[FO_MAX_P];   // in arrival order
+  int32_t recv_slice[FO_MAX_P];  // slice id whose arrival is awaited (-1: resident)
+  int32_t n_recv;
+  const int64_t* const* comp_tab;  // completion-signal values [slice][group] (null: no waits)
+  int32_t groups;
+  int32_t vec4;                    // every pointer 16-byte aligned and count % 4 == 0
+  int64_t count;
+  uint64_t spin_limit;
+  uint32_t* err;
+  int32_t max_blocks;              // persistent grid: each block waits and acquires once
+};
+hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);
+
 // Slice schedule: kind 0 = AG, 1 = RS; order = fo_order. Writes P ids.
 int slice_order(int kind, int order, int P, int rank, int32_t* out);
 

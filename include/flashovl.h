@@ -65,8 +65,11 @@ typedef enum fo_status {
 typedef enum fo_dtype { FO_DT_BF16 = 0, FO_DT_F32 = 1 } fo_dtype;
 
 /* Slice order. FLASH: the page's schedule (AG: local slice first, then ring arrivals; RS: chunks
-   for the other ranks first, own chunk last). NATURAL: slices in index order 0..P-1, the
-   data-slicing baseline of the page's problem statement. */
+   for the other ranks first, own chunk last, partials added in its write-back). NATURAL: slices
+   in index order 0..P-1, the data-slicing baseline of the page's problem statement; in fo_gemm_rs
+   the own chunk is then written where it falls and the partials are added after the GEMM by a
+   separate pass (the tail that data slicing cannot hide), with the same adds in the same order,
+   so both orders give bitwise the same result. */
 typedef enum fo_order { FO_ORDER_FLASH = 0, FO_ORDER_NATURAL = 1 } fo_order;
 
 /* How emulated peer data arrives. NONE: the data is already resident in the receive buffer and
@@ -150,7 +153,10 @@ fo_status fo_ag_gemm(const void* x_local, const void* const* x_peer, void* x_rec
  *                sends for this rank's chunk. Entry [rank] ignored. NULL: no transfers, the
  *                partials are already in recv_buf.
  *   recv_buf     device [P*m, N] fp32; peer q's partial arrives at recv_buf + q*m*N.
- * Chunks are computed in the Flash-RS order (rank+1, ..., rank+P-1, rank mod P).
+ * Chunks are computed in the Flash-RS order (rank+1, ..., rank+P-1, rank mod P), or in index order
+ * with opts->order NATURAL. LOCKSTEP arrivals: peer rank-1-t sends its partial when this rank ends
+ * its step t (FLASH), or when this rank ends the step of its own chunk (NATURAL, where every rank
+ * computes chunk d at step d).
  */
 fo_status fo_gemm_rs(const void* x_shard, const void* w, float* send_buf, float* out,
                      const float* const* peer_partial, float* recv_buf, int32_t P, int32_t rank,

@@ -174,9 +174,10 @@ def test_rs_rejects(lib, kw):
     assert _rs(lib, **kw) == fo.FO_ERR_INVALID_ARG
 
 
-def test_rs_natural_order_unsupported(lib):
+def test_rs_bad_order_rejected(lib):
     o = fo.opts(order=fo.ORDER_NATURAL)
-    assert _rs(lib, opts=ctypes.byref(o)) == fo.FO_ERR_UNSUPPORTED
+    o.order = 5
+    assert _rs(lib, opts=ctypes.byref(o)) == fo.FO_ERR_INVALID_ARG
 
 
 def test_transfer_ref_rejects(lib):

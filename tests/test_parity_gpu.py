@@ -138,6 +138,45 @@ def test_tiny_fp32_rs_bit_exact(dev, links, arrival):
                 assert np.array_equal(send[d * m:(d + 1) * m], ref_send[d * m:(d + 1) * m])
 
 
+@pytest.mark.parametrize("arrival", [("lockstep", fo.ARR_LOCKSTEP), ("eager", fo.ARR_EAGER),
+                                     ("resident", None)], ids=lambda a: a[0])
+def test_tiny_fp32_natural_order_bit_exact(dev, arrival):
+    """The data-slicing order (NATURAL): slices in index order; for RS the own chunk is written
+    where it falls and the partials are added after the GEMM. Exact on integers, every rank."""
+    c = configs.TINY_AG
+    prob = AG(c.x(), c.w(), c.P, dev, out_dt="f32")
+    cr = configs.TINY_RS
+    parts = [cr.partial(q) for q in range(cr.P)]
+    rs = RS(cr.x(), cr.w(), parts, cr.P, dev)
+    for r in range(c.P):
+        if arrival[1] != fo.ARR_LOCKSTEP:
+            got = prob.run(r, o=fo.opts(order=fo.ORDER_NATURAL,
+                                        arrival=arrival[1] or fo.ARR_DEFAULT),
+                           resident=arrival[1] is None)
+            assert np.array_equal(got, oracle.ag(prob.slices, c.w(), c.P, r)), f"AG rank {r}"
+        out, send = rs.run(r, o=fo.opts(order=fo.ORDER_NATURAL,
+                                        arrival=arrival[1] or fo.ARR_DEFAULT),
+                           resident=arrival[1] is None)
+        ref_out, ref_send = oracle.rs(cr.x(), cr.w(), parts, cr.P, r, want_send=True)
+        assert np.array_equal(out, ref_out), f"RS rank {r}"
+        keep = ~np.isnan(ref_send)
+        assert np.array_equal(send[keep], ref_send[keep])
+
+
+def test_natural_rs_matches_flash_bitwise(dev):
+    """Both orders add the same partials in the same order onto the same fp32 accumulator."""
+    P, m, K, N = 4, 520, 264, 392
+    x = inputs.normal(7380, (P * m, K), 1.0, "bf16")
+    w = inputs.normal(7381, (K, N), 0.02, "bf16")
+    parts = [inputs.normal(7390 + q, (m, N), 1.0, "f32") for q in range(P)]
+    rs = RS(x, w, parts, P, dev)
+    for r in (0, 3):
+        flash, _ = rs.run(r, o=fo.opts(tile=fo.TILE_128x128))
+        nat, _ = rs.run(r, o=fo.opts(tile=fo.TILE_128x128, order=fo.ORDER_NATURAL, row_groups=1))
+        assert np.array_equal(flash, nat), f"rank {r}"
+        assert rel_frobenius(nat, oracle.rs(x, w, parts, P, r)) <= TOL_BF16
+
+
 def test_fp32_non_integer_tolerance(dev):
     """Non-integer fp32 operands pin the fp32 path itself (integers are exact in bf16 too)."""
     P, M, K, N = 4, 256, 256, 512

@@ -61,11 +61,14 @@ def test_groups_and_layout(kind, shape):
             assert [p for p, *_ in order] == sorted(p for p, *_ in order)
 
 
-def test_natural_order_has_no_lead():
-    order = fo.tile_order("ag", 4, 512, 256, 512, o=fo.opts(order=fo.ORDER_NATURAL, row_groups=2,
-                                                            tile=fo.TILE_128x256))
+@pytest.mark.parametrize("kind", ["ag", "rs"])
+def test_natural_order_is_group_major_over_every_slice(kind):
+    order = fo.tile_order(kind, 4, 512, 256, 512, o=fo.opts(order=fo.ORDER_NATURAL, row_groups=2,
+                                                            tile=fo.TILE_128x256),
+                          out_dt=fo.F32 if kind == "rs" else fo.BF16)
     keys = [(g, p) for p, g, _, _ in order]
     assert keys == sorted(keys)
+    assert {p for p, *_ in order[:len(order) // 2]} == {0, 1, 2, 3}  # no slice is held back
 
 
 def test_rejects():
