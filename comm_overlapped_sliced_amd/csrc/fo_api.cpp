@@ -75,6 +75,8 @@ struct DevState {
   int n_cu = 0;
   int wall_khz = 100000;     // wall-clock counter rate read by the kernels' bounded waits
   uint32_t* err = nullptr;   // wait record: 1 timeout, 2 failed copy (uncached memory)
+  uint32_t* go = nullptr;    // the tail reduce's start word (same uncached block)
+  uint32_t go_value = 0;
   uint32_t* done = nullptr;  // completed-tile counters [position][group]
   void* scratch = nullptr;   // source and destination of the DMA engines' first copies
   hipEvent_t ev_last = nullptr;
@@ -93,6 +95,7 @@ fo_status ensure_ready(int dev, DevState& st) {
   void* p = nullptr;
   FO_HIP(hipExtMallocWithFlags(&p, 4096, hipDeviceMallocUncached));
   st.err = (uint32_t*)p;
+  st.go = (uint32_t*)((uint8_t*)p + 256);
   FO_HIP(hipMemset(p, 0, 4096));
   const size_t counters = (size_t)FO_MAX_P * fo::kMaxGroups * sizeof(uint32_t);
   FO_HIP(hipMalloc(&p, counters));
@@ -561,6 +564,9 @@ fo_status fo_gemm_rs(const void* x_shard, const void* w, float* send_buf, float*
     ra.spin_limit = p.spin_limit;
     ra.err = st->err;
     ra.max_blocks = 2 * st->n_cu;
+    ra.go = st->go;
+    if (++st->go_value == 0) ++st->go_value;
+    ra.go_value = st->go_value;
     FO_HIP(fo::launch_reduce(ra, cs));
   }
   if (arrivals) FO_DMA(fo::dma::end(st->dev, call, cs, &e_));

@@ -631,17 +631,38 @@ __device__ __forceinline__ float ld_sys1(const float* p) {
 }
 __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Bounded wait until a device word holds `v` (or a wait of the call has failed).
+__device__ __forceinline__ void wait_word(const uint32_t* w, uint32_t v, uint64_t limit,
+                                          uint32_t* err) {
+  const uint64_t t0 = wall_clock64();
+  while (__hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != v) {
+    if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != 0u) return;
+    if (wall_clock64() - t0 > limit) {
+      __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
 // out += the received partials, in arrival order (the tail of Flash-RS in the data-slicing
 // order). HBM-bound: one pass over out and each partial, 16-byte accesses when aligned. The grid
-// is persistent (about two blocks per CU) so that few blocks poll the arrival signals; the
-// partials are read with system-coherent loads, so no block needs a cache invalidation (a
-// system-scope acquire in every block costs more than the pass itself).
+// is persistent (about two blocks per CU, all resident at once). Only block 0 polls the arrival
+// signals (host memory: hundreds of pollers would slow the copy engines); it then sets a device
+// word the other blocks wait on. The partials are read with system-coherent loads, so no block
+// needs a cache invalidation (a system-scope acquire in every block costs more than the pass).
 __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
-  if (threadIdx.x == 0 && a.comp_tab != nullptr)
-    for (int i = 0; i < a.n_recv; ++i)
-      if (a.recv_slice[i] >= 0)
-        for (int g = 0; g < a.groups; ++g)
-          wait_signal(a.comp_tab[a.recv_slice[i] * kMaxGroups + g], a.spin_limit, a.err);
+  if (threadIdx.x == 0 && a.comp_tab != nullptr) {
+    if (blockIdx.x == 0) {
+      for (int i = 0; i < a.n_recv; ++i)
+        if (a.recv_slice[i] >= 0)
+          for (int g = 0; g < a.groups; ++g)
+            wait_signal(a.comp_tab[a.recv_slice[i] * kMaxGroups + g], a.spin_limit, a.err);
+      __hip_atomic_store(a.go, a.go_value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    } else {
+      wait_word(a.go, a.go_value, a.spin_limit, a.err);
+    }
+  }
   __syncthreads();
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int64_t first = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -699,7 +720,8 @@ hipError_t launch_wait(const int64_t* const* comp_tab, const int32_t* slices, in
 }
 
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s) {
-  if (a.n_recv < 0 || a.n_recv > FO_MAX_P || a.groups < 1 || a.groups > kMaxGroups || a.count < 0)
+  if (a.n_recv < 0 || a.n_recv > FO_MAX_P || a.groups < 1 || a.groups > kMaxGroups || a.count < 0 ||
+      a.go == nullptr)
     return hipErrorInvalidValue;
   for (int i = 0; i < a.n_recv; ++i)
     if (a.recv_slice[i] >= FO_MAX_P || (a.recv_slice[i] >= 0 && a.comp_tab == nullptr))

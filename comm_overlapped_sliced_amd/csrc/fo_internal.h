@@ -98,7 +98,9 @@ struct ReduceArgs {
   int64_t count;
   uint64_t spin_limit;
   uint32_t* err;
-  int32_t max_blocks;              // persistent grid: each block waits and acquires once
+  int32_t max_blocks;              // persistent grid size
+  uint32_t* go;                    // device word (uncached) block 0 sets to go_value once every
+  uint32_t go_value;               // partial has landed; the other blocks wait on it
 };
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);
 
