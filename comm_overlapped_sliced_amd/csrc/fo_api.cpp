@@ -169,6 +169,10 @@ fo_status check_common(int P, int rank, int64_t m, int64_t K, int64_t N, int in_
   if (in_dt == FO_DT_BF16 && (K % 8 || N % 8))
     return invalid("bf16 operands need K and N to be multiples of 8 (K %lld, N %lld)",
                    (long long)K, (long long)N);
+  // the bf16 kernel addresses a tile's rows of A and of the output with 31-bit byte offsets
+  if (in_dt == FO_DT_BF16 && (K > ((int64_t)1 << 21) || N > ((int64_t)1 << 20)))
+    return invalid("bf16 operands need K <= 2^21 and N <= 2^20 (K %lld, N %lld)",
+                   (long long)K, (long long)N);
   return FO_OK;
 }
 

@@ -68,9 +68,11 @@ __device__ __forceinline__ void wait_groups_wg(const Plan& p, const int32_t* sli
 
 // After a tile of (position, group) is stored: count it; the last tile of that group stores 0
 // into its release signal (polled by the copy engine that carries the matching transfer) and
-// re-arms the counter.
+// re-arms the counter. Every wave first waits for its own stores of the tile (the workgroup
+// barrier does not), so that the release below covers the whole tile.
 __device__ __forceinline__ void release_tile(const Plan& p, int pos, int grp) {
   if (p.rel_tab == nullptr) return;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
@@ -84,19 +86,12 @@ __device__ __forceinline__ void release_tile(const Plan& p, int pos, int grp) {
   }
 }
 
-// fp32 -> bf16, round to nearest, ties to even (quiet NaN kept).
-__device__ __forceinline__ uint16_t to_bf16_rne(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
-// 16-byte streaming load (the partials are read once)
-__device__ __forceinline__ float4 ld_nt4(const float* p) {
-  typedef __attribute__((ext_vector_type(4))) float v4;
-  const v4 v = __builtin_nontemporal_load((const v4*)p);
-  return make_float4(v.x, v.y, v.z, v.w);
+// fp32 -> bf16, round to nearest, ties to even (quiet NaN kept); branch-free (a select).
+__device__ __forceinline__ uint32_t to_bf16_rne(float f) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, f);
+  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t quiet = (u >> 16) | 0x40u;
+  return (u & 0x7fffffffu) > 0x7f800000u ? quiet : rounded;
 }
 
 // ---------------------------------------------------------------- bf16 MFMA kernel ----------
@@ -128,12 +123,24 @@ struct Cfg {
   static constexpr int A_LOADS = A_BYTES / 1024 / 4;  // 1 KB loads per wave per stage
   static constexpr int B_LOADS = B_BYTES / 1024 / 4;
   static constexpr int LOADS = A_LOADS + B_LOADS;
+  // A step's loads go out in two groups, half a step apart (see the pipeline below).
+  static constexpr int L0 = LOADS / 2, L1 = LOADS - L0;
   // Four stages: three K steps in flight while one is consumed. Deeper rings (5 for 256x256, 6
   // for 128x256, as many as the LDS holds) measured no faster on MI355X, and 256x256 slower.
   static constexpr int STAGES = 4;
-  static_assert(STAGES * STAGE <= kLdsBytes, "LDS");
-  static_assert(A_LOADS >= 1 && B_LOADS >= 1 && FM >= 1 && FN >= 1, "tile");
+  static constexpr int RING = STAGES * STAGE;
+  // Epilogue staging: fp32 rows padded by 8 floats (rows 4 apart land 32 banks apart), in
+  // blocks of ER rows; the LDS allocation grows past the ring (up to the CU's LDS) so that the
+  // block holds the whole tile, or half of it.
+  static constexpr int EW = BN + 8;
+  static constexpr int ER = (BM * EW * 4 <= (RING > kLdsBytes ? RING : kLdsBytes)) ? BM
+                            : (BM / 2 * EW * 4 <= kLdsBytes)                        ? BM / 2
+                                                                                    : BM / 4;
+  static constexpr int LDS = RING > ER * EW * 4 ? RING : ER * EW * 4;
+  static_assert(LDS <= kLdsBytes, "LDS");
+  static_assert(A_LOADS >= 1 && B_LOADS >= 1 && FM >= 1 && FN >= 1 && L0 >= 1, "tile");
   static_assert(STAGES >= 3 && (STAGES - 1) * LOADS < 64, "stages");
+  static_assert(ER % 32 == 0 && BM % ER == 0, "epilogue block");
 };
 
 // swizzle of the 4 chunks of an A row and of the chunks of a W row
@@ -150,6 +157,7 @@ __device__ __forceinline__ const void* uni_ptr(const void* p) {
 }
 
 typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(2))) int i32x2;
 
 // Raw buffer descriptor (base, stride 0, num_records bytes, 32-bit data format); every field is
 // wave-uniform so it lives in SGPRs.
@@ -162,20 +170,26 @@ __device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
   r.w = kRsrcWord3;
   return r;
 }
+// The same descriptor in the type the buffer load/store builtins take.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_res(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(uni_ptr(base)), (short)0,
+                                           (int)uni((int)bytes), kRsrcWord3);
+}
 
-// 16 bytes per lane from the buffer at byte offset voff into LDS at lds_base + 16 * lane (an
-// offset past num_records reads zeros). Issued as inline assembly so that the compiler neither
-// orders later LDS reads behind it nor drains it at barriers: completion is tracked by hand with
-// wait_vmcnt, which counts these loads.
-__device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t lds_base, uint32_t voff,
+// 16 bytes per lane from the buffer at byte offset voff into LDS at base + imm + 16 * lane (an
+// offset past num_records reads zeros); imm folds to a constant once the loops are unrolled, so
+// a wave keeps one LDS base per operand instead of one per load. Issued as inline assembly so
+// that the compiler neither orders later LDS reads behind it nor drains it at barriers:
+// completion is tracked by hand with wait_vmcnt, which counts these loads.
+__device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t base, int imm, uint32_t voff,
                                            uint32_t soff) {
   asm volatile(
-      "s_mov_b32 m0, %0\n\t"
+      "s_add_u32 m0, %0, %1\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, %3 offen lds"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds"
       :
-      : "s"(lds_base), "v"(voff), "s"(rsrc), "s"(soff)
-      : "m0");
+      : "s"(base), "i"(imm), "v"(voff), "s"(rsrc), "s"(soff)
+      : "m0", "scc");
 }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding)
@@ -185,11 +199,24 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// The workgroup barrier proper: this wave's LDS accesses are done, no memory fence (vector
+// loads and stores in flight stay in flight); the "memory" clobber keeps the compiler from
+// moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// position of the q-th of n memory instructions among nx issue slots (evenly spread)
+__host__ __device__ constexpr int spread_slot(int q, int n, int nx) { return (2 * q + 1) * nx / (2 * n); }
+
 template <int BM, int BN>
 __device__ __forceinline__ void bf16_tile(const Plan& p, const int tile, uint8_t* const lds_ring) {
   using C = Cfg<BM, BN>;
   constexpr int S = C::STAGES;
   auto st = [&](int i) -> uint8_t* { return lds_ring + i * C::STAGE; };
+  auto lds_addr = [](const uint8_t* q) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)q;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -216,6 +243,9 @@ __device__ __forceinline__ void bf16_tile(const Plan& p, const int tile, uint8_t
   // the scalar offset and W's through a descriptor re-based on the step's first row (whose
   // num_records also cuts off rows past K). Lanes outside the tile carry kOOB and read zeros.
   const i32x4 rsrc_a = buffer_rsrc(A, (uint32_t)(a_rows * K * 2));
+  const uint32_t lds0 = lds_addr(lds_ring);
+  const uint32_t a_base = (uint32_t)uni((int)(lds0 + wave * C::A_LOADS * 1024));
+  const uint32_t b_base = (uint32_t)uni((int)(lds0 + C::A_BYTES + wave * C::B_LOADS * 1024));
   uint32_t a_voff[C::A_LOADS];
   int a_kel[C::A_LOADS];
 #pragma unroll
@@ -233,39 +263,39 @@ __device__ __forceinline__ void bf16_tile(const Plan& p, const int tile, uint8_t
     b_voff[j] = col0 + n < N ? (uint32_t)(((int64_t)kr * N + n) * 2) : kOOB;
   }
 
-  // load number l (A loads first, then W loads) of K step kt into the stage at LDS address lds;
-  // rb is W's descriptor for that step (from w_rsrc). TAIL: the step runs past K, so A columns
-  // beyond K are redirected to kOOB (W rows beyond K fall outside rb's range by themselves).
+  // load number l (A loads first, then W loads) of K step kt into stage si (0..S-1); rb is W's
+  // descriptor for that step (from w_rsrc). TAIL: the step runs past K, so A columns beyond K
+  // are redirected to kOOB (W rows beyond K fall outside rb's range by themselves).
   auto w_rsrc = [&](int kt) {
     const int64_t k0 = (int64_t)kt * kBK;
     const int64_t rows = K - k0 < kBK ? K - k0 : kBK;
     return buffer_rsrc(W + k0 * N, (uint32_t)(rows * N * 2));
   };
-  auto issue_one = [&](auto tail, int kt, uint32_t lds, const i32x4& rb, int l) {
+  auto issue_one = [&](auto tail, int kt, int si, const i32x4& rb, int l) {
     const int64_t k0 = (int64_t)kt * kBK;
     if (l < C::A_LOADS) {
       uint32_t v = a_voff[l];
       if constexpr (decltype(tail)::value) {
         if (k0 + a_kel[l] >= K) v = kOOB;
       }
-      load_lds16(rsrc_a, lds + (wave * C::A_LOADS + l) * 1024, v, (uint32_t)(k0 * 2));
+      load_lds16(rsrc_a, a_base, si * C::STAGE + l * 1024, v, (uint32_t)(k0 * 2));
     } else {
       const int j = l - C::A_LOADS;
-      load_lds16(rb, lds + C::A_BYTES + (wave * C::B_LOADS + j) * 1024, b_voff[j], 0u);
+      load_lds16(rb, b_base, si * C::STAGE + j * 1024, b_voff[j], 0u);
     }
   };
-  auto issue_step = [&](int kt, uint32_t lds) {
+  // loads [l0, l1) of step kt into stage si
+  auto issue_range = [&](int kt, int si, int l0, int l1) {
     const i32x4 rb = w_rsrc(kt);
     if ((int64_t)(kt + 1) * kBK > K) {
 #pragma unroll
-      for (int l = 0; l < C::LOADS; ++l) issue_one(std::true_type{}, kt, lds, rb, l);
+      for (int l = 0; l < C::LOADS; ++l)
+        if (l >= l0 && l < l1) issue_one(std::true_type{}, kt, si, rb, l);
     } else {
 #pragma unroll
-      for (int l = 0; l < C::LOADS; ++l) issue_one(std::false_type{}, kt, lds, rb, l);
+      for (int l = 0; l < C::LOADS; ++l)
+        if (l >= l0 && l < l1) issue_one(std::false_type{}, kt, si, rb, l);
     }
-  };
-  auto lds_addr = [](const uint8_t* stage) {
-    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)stage;
   };
 
   f32x16 acc[C::FM][C::FN];
@@ -324,154 +354,208 @@ __device__ __forceinline__ void bf16_tile(const Plan& p, const int tile, uint8_t
       default: wait_vmcnt<0>(); break;
     }
   };
-  // The workgroup barrier proper: no memory fence, so the prefetches issued before it stay in
-  // flight (every wave has already waited for its own loads of the stage it needs).
-  auto barrier = [&]() {
-    // lgkmcnt(0): this wave's LDS reads are done; the "memory" clobber keeps the compiler from
-    // moving LDS accesses across the barrier
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  };
 
   constexpr int NMFMA = C::FM * C::FN, NREAD = C::FM + C::FN;
   // Software pipeline over K steps of kBK; stage kt % S holds step kt. A step runs its MFMAs in
   // two halves (K-substeps 0 and 1). The first half's fragments are already in registers; while
   // its MFMAs issue, the second half's fragments are read. Then, once every wave holds the next
   // stage and nobody reads this one any more (barrier), the second half's MFMAs issue
-  // interleaved with the loads that refill this stage with step kt + S and with the reads of the
-  // next step's first-half fragments. The order inside each half is pinned with scheduling
-  // barriers so that memory instructions issue under running MFMAs.
+  // interleaved with the reads of the next step's first-half fragments.
+  // The stage freed at a barrier is refilled with the step S ahead in two groups of loads: the
+  // first group during the second half that follows the barrier, the second during the next
+  // step's first half. Spreading them over the whole step keeps the address unit busy evenly
+  // instead of in one burst after each barrier (a burst stalls the issuing waves). The count of
+  // loads issued after any given step is unchanged, so the waits are the same as with one group.
+  // The order inside each half is pinned with scheduling barriers so that memory instructions
+  // issue under running MFMAs.
   const int KT = uni((int)((K + kBK - 1) / kBK));
   const int KFULL = uni((int)(K / kBK));  // steps that lie entirely inside K
   Frags f0, f1;
   if (KT > 0) {
 #pragma unroll
-    for (int i = 0; i < S; ++i)
-      if (i < KT) issue_step(i, lds_addr(st(i)));
-    wait_stages(KT - 1 < S - 1 ? KT - 1 : S - 1);
-    barrier();
+    for (int i = 0; i < S - 1; ++i)
+      if (i < KT) issue_range(i, i, 0, C::LOADS);
+    if (S - 1 < KT) issue_range(S - 1, S - 1, 0, C::L0);
+    // step 0 landed: at most the later steps' loads still in flight (rounded down to whole steps)
+    wait_stages(KT - 1 < S - 2 ? KT - 1 : S - 2);
+    lds_barrier();
 #pragma unroll
     for (int q = 0; q < NREAD; ++q) rd_frag(st(0), 0, f0, q);
   }
   constexpr int NX1 = NMFMA > NREAD ? NMFMA : NREAD;
-  constexpr int NX2 = NMFMA > C::LOADS ? (NMFMA > NREAD ? NMFMA : NREAD)
-                                       : (C::LOADS > NREAD ? C::LOADS : NREAD);
-  // first half of step kt: MFMAs of f0 with the reads of f1 under them
-  auto first_half = [&](const uint8_t* cur) {
+  constexpr int NX1L = NMFMA > C::L1 ? NMFMA : C::L1;
+  constexpr int NX2L = NMFMA > C::L0 ? NMFMA : C::L0;
+  constexpr int NXA = NX1 > NX1L ? NX1 : NX1L;
+  constexpr int NXB = NX1 > NX2L ? NX1 : NX2L;
+  // load l of step kt into stage si, with the K-tail check when `tail` (branches around single
+  // load instructions only, so that the MFMA sequence is not duplicated)
+  auto issue_if = [&](bool issue, bool tail, int kt, int si, const i32x4& rb, int l) {
+    if (issue) {
+      if (tail)
+        issue_one(std::true_type{}, kt, si, rb, l);
+      else
+        issue_one(std::false_type{}, kt, si, rb, l);
+    }
+  };
+  // first half of step kt (stage si): MFMAs of f0 with the reads of f1 and, when `issue`, the
+  // second load group of step `late` into the stage freed at the previous barrier
+  auto first_half = [&](int si, int late, bool issue, bool tail) {
+    const i32x4 rb = issue ? w_rsrc(late) : i32x4{};
+    const int ls = (si + S - 1) % S;
 #pragma unroll
-    for (int x = 0; x < NX1; ++x) {
+    for (int x = 0; x < NXA; ++x) {
       if (x < NMFMA) mfma(f0, x);
-      if (x < NREAD) rd_frag(cur, 1, f1, x);
+      if (x < NREAD) rd_frag(st(si), 1, f1, x);
+#pragma unroll
+      for (int q = 0; q < C::L1; ++q)
+        if (x == spread_slot(q, C::L1, NX1L)) issue_if(issue, tail, late, ls, rb, C::L0 + q);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // Steady-state step: stage kt is refilled with step kt + S, which lies entirely inside K.
-  auto step_main = [&](int kt, const uint8_t* cur, const uint8_t* nxt) {
-    first_half(cur);
-    wait_stages(S - 2);
-    barrier();
-    const uint32_t cur_lds = lds_addr(cur);
-    const i32x4 rb = w_rsrc(kt + S);
+  // second half of step kt: MFMAs of f1, the first load group of step kt + S into stage si when
+  // `issue`, and the reads of the next step's f0 when `more`
+  auto second_half = [&](int kt, int si, bool issue, bool tail, bool more) {
+    const i32x4 rb = issue ? w_rsrc(kt + S) : i32x4{};
 #pragma unroll
-    for (int x = 0; x < NX2; ++x) {
+    for (int x = 0; x < NXB; ++x) {
       if (x < NMFMA) mfma(f1, x);
-      if (x < C::LOADS) issue_one(std::false_type{}, kt + S, cur_lds, rb, x);
-      if (x < NREAD) rd_frag(nxt, 0, f0, x);
+#pragma unroll
+      for (int q = 0; q < C::L0; ++q)
+        if (x == spread_slot(q, C::L0, NX2L)) issue_if(issue, tail, kt + S, si, rb, q);
+      if (x < NREAD && more) rd_frag(st((si + 1) % S), 0, f0, x);
       __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  // Steady-state step: every step it loads lies entirely inside K.
+  auto step_main = [&](int kt, int si) {
+    first_half(si, kt + S - 1, true, false);
+    wait_stages(S - 2);
+    lds_barrier();
+    second_half(kt, si, true, false, true);
   };
   // Any step (start-up, last steps, K tail), with the conditions checked at run time.
-  auto step_any = [&](int kt, const uint8_t* cur, const uint8_t* nxt) {
-    first_half(cur);
+  auto step_any = [&](int kt, int si) {
+    const int late = kt + S - 1;
+    first_half(si, late, late < KT, late >= KFULL);
     const int later = KT - 2 - kt;  // steps issued beyond kt + 1 (at most S - 2 at this point)
     wait_stages(later < 0 ? 0 : (later > S - 2 ? S - 2 : later));
-    barrier();
-    const bool refill = kt + S < KT, tail = kt + S >= KFULL, more = kt + 1 < KT;
-    const uint32_t cur_lds = lds_addr(cur);
-    i32x4 rb{};
-    if (refill) rb = w_rsrc(kt + S);
-#pragma unroll
-    for (int x = 0; x < NX2; ++x) {
-      if (x < NMFMA) mfma(f1, x);
-      if (x < C::LOADS && refill) {
-        if (tail)
-          issue_one(std::true_type{}, kt + S, cur_lds, rb, x);
-        else
-          issue_one(std::false_type{}, kt + S, cur_lds, rb, x);
-      }
-      if (x < NREAD && more) rd_frag(nxt, 0, f0, x);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    lds_barrier();
+    second_half(kt, si, kt + S < KT, kt + S >= KFULL, kt + 1 < KT);
   };
   int kt = 0;
   for (; kt + 2 * S <= KFULL; kt += S) {
 #pragma unroll
-    for (int i = 0; i < S; ++i) step_main(kt + i, st(i), st((i + 1) % S));
+    for (int i = 0; i < S; ++i) step_main(kt + i, i);
   }
   for (; kt < KT; kt += S) {
 #pragma unroll
     for (int i = 0; i < S; ++i)
-      if (kt + i < KT) step_any(kt + i, st(i), st((i + 1) % S));
+      if (kt + i < KT) step_any(kt + i, i);
   }
 
   // ---- epilogue ---------------------------------------------------------------------------
   // The accumulators go through LDS (free now) in blocks of ER rows so that every global access
   // is a row-contiguous 16-byte (fp32) or 8-byte (bf16) vector: output stores, and for the chunk
   // that stays on the rank, the loads of the received partials, which are all issued before any
-  // of them is added (the adds keep the arrival order).
+  // of them is added (the adds keep the arrival order). Stores go through a buffer descriptor
+  // that covers the tile's valid rows, so rows past the slice are dropped by the range check;
+  // columns past N get an offset outside every range. Nothing waits for the stores here: the
+  // next tile's loads overlap them (release_tile waits for them where a copy engine reads them).
   const bool accum = (pos == p.accum_pos);
   if (accum) wait_groups_wg(p, p.recv_slice, p.n_recv, grp);
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // LDS stages no longer read
-  float* const ep = (float*)lds_ring;  // [ER rows][EW floats] over the whole ring
-  constexpr int EW = BN + 8;      // padded row: rows 4 apart land 32 banks apart
-  constexpr int ER = (BM * EW * 4 <= S * C::STAGE)         ? BM
-                     : (BM / 2 * EW * 4 <= S * C::STAGE)   ? BM / 2
-                                                                : BM / 4;
-  static_assert(ER * EW * 4 <= S * C::STAGE && ER % 32 == 0, "epilogue block");
+  lds_barrier();  // LDS stages no longer read
+  float* const ep = (float*)lds_ring;  // [ER rows][EW floats]
+  constexpr int ER = C::ER, EW = C::EW;
   constexpr int CPR = BN / 4;                   // 4-float chunks per row
   constexpr int CPT = ER * CPR / kThreads;      // chunks per thread per block
   static_assert(CPT >= 1 && (ER * CPR) % kThreads == 0, "epilogue chunks");
   constexpr int BATCH = CPT < 4 ? CPT : 4;      // chunks whose partial loads are in flight together
+  const int esz = p.out_f32 ? 4 : 2;
+  const uint32_t nn = (uint32_t)N;
+  const __amdgpu_buffer_rsrc_t out_res =
+      buffer_res((const uint8_t*)p.c_pos[pos] + row0 * N * esz, (uint32_t)a_rows * nn * esz);
+  // Chunk b of this thread in a block is chunk b * kThreads + tid: row b * (kThreads / CPR) +
+  // tid / CPR, the same 4 columns for every b. Its element offset is e0 + b * e_step (e0 for the
+  // block's first row); a thread whose columns lie past N stores nowhere (kOOB).
+  static_assert(kThreads % CPR == 0, "epilogue rows");
+  constexpr int RPB = kThreads / CPR;  // rows covered by one chunk of every thread
+  const uint32_t gcol = (uint32_t)col0 + (tid % CPR) * 4;
+  const bool col_ok = gcol < nn;
+  const uint32_t e_step = (uint32_t)RPB * nn;
+  // Per-lane LDS offsets of the staging rows, re-derived in each block behind an empty asm:
+  // otherwise the compiler precomputes one address per chunk at kernel start, spills them, and
+  // the reloads in the store loop wait for every store in flight.
+  int ep_rd = 0, ep_wr = 0;
+  auto chunk_lds = [&](int b) -> float4 { return *(const float4*)(ep + ep_rd + b * RPB * EW); };
 #pragma unroll
   for (int blk = 0; blk < BM / ER; ++blk) {
+    ep_rd = (tid / CPR) * EW + (tid % CPR) * 4;
+    ep_wr = 4 * lh * EW + wn * C::WTN + lr;
+    asm volatile("" : "+v"(ep_rd), "+v"(ep_wr));
 #pragma unroll
     for (int i = 0; i < C::FM; ++i) {
       const int fr = wm * C::WTM + i * 32;  // first tile row of fragment row i
       if (fr < blk * ER || fr >= (blk + 1) * ER) continue;
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j)
+      for (int j = 0; j < C::FN; ++j) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int r = fr - blk * ER + 8 * (v >> 2) + 4 * lh + (v & 3);
-          ep[r * EW + wn * C::WTN + j * 32 + lr] = acc[i][j][v];
+          const int r = fr - blk * ER + 8 * (v >> 2) + (v & 3);
+          ep[ep_wr + r * EW + j * 32] = acc[i][j][v];
         }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int b0 = 0; b0 < CPT; b0 += BATCH) {
-      float4 x[BATCH];
-      int64_t off[BATCH];
-      bool ok[BATCH];
-#pragma unroll
-      for (int b = 0; b < BATCH; ++b) {
-        const int c = (b0 + b) * kThreads + tid;  // consecutive threads: consecutive chunks
-        const int r = c / CPR, cc = c % CPR;
-        const int64_t grow = row0 + blk * ER + r, gcol = col0 + cc * 4;
-        ok[b] = grow < p.m && gcol < N;
-        off[b] = grow * N + gcol;
-        x[b] = *(const float4*)(ep + r * EW + cc * 4);
+        // one fragment at a time: the accumulators stay in place until written (no spills)
+        __builtin_amdgcn_sched_barrier(0);
       }
-      if (accum) {
+    }
+    lds_barrier();
+    const uint32_t e0 = (uint32_t)(blk * ER + tid / CPR) * nn + gcol;
+    auto chunk_off = [&](int b, int scale) -> uint32_t {
+      return col_ok ? (e0 + b * e_step) * scale : kOOB;
+    };
+    if (!accum) {
+      if (p.out_f32) {
+#pragma unroll
+        for (int b = 0; b < CPT; ++b) {
+          const float4 x = chunk_lds(b);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, x), out_res,
+                                                 chunk_off(b, 4), 0, 0);
+          if (b % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+#pragma unroll
+        for (int b = 0; b < CPT; ++b) {
+          const float4 x = chunk_lds(b);
+          const uint32_t lo = to_bf16_rne(x.x) | (to_bf16_rne(x.y) << 16);
+          const uint32_t hi = to_bf16_rne(x.z) | (to_bf16_rne(x.w) << 16);
+          __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)lo, (int)hi}, out_res, chunk_off(b, 2),
+                                                0, 0);
+          if (b % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    } else {
+      // the own chunk of Flash-RS (fp32 output): partial q at the same element offset in
+      // recv[q] + row0 * N
+#pragma unroll
+      for (int b0 = 0; b0 < CPT; b0 += BATCH) {
+        float4 x[BATCH];
+#pragma unroll
+        for (int b = 0; b < BATCH; ++b) x[b] = chunk_lds(b0 + b);
         for (int q0 = 0; q0 < p.n_recv; q0 += 4) {
           float4 t[4][BATCH];
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
+          for (int q = 0; q < 4; ++q) {
+            if (q0 + q < p.n_recv) {
+              const __amdgpu_buffer_rsrc_t rr =
+                  buffer_res(p.recv[q0 + q] + row0 * N, (uint32_t)a_rows * nn * 4);
 #pragma unroll
-            for (int b = 0; b < BATCH; ++b)
-              t[q][b] = (q0 + q < p.n_recv && ok[b])
-                            ? ld_nt4(p.recv[q0 + q] + off[b])
-                            : make_float4(0.f, 0.f, 0.f, 0.f);
+              for (int b = 0; b < BATCH; ++b)  // streaming: the partials are read once
+                t[q][b] = __builtin_bit_cast(
+                    float4, __builtin_amdgcn_raw_buffer_load_b128(rr, chunk_off(b0 + b, 4), 0, 2));
+            }
+          }
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
+          for (int q = 0; q < 4; ++q) {
+            if (q0 + q >= p.n_recv) break;
 #pragma unroll
             for (int b = 0; b < BATCH; ++b) {
               x[b].x += t[q][b].x;
@@ -479,21 +563,15 @@ __device__ __forceinline__ void bf16_tile(const Plan& p, const int tile, uint8_t
               x[b].z += t[q][b].z;
               x[b].w += t[q][b].w;
             }
+          }
         }
-      }
 #pragma unroll
-      for (int b = 0; b < BATCH; ++b) {
-        if (!ok[b]) continue;
-        if (p.out_f32) {
-          *(float4*)((float*)p.c_pos[pos] + off[b]) = x[b];
-        } else {
-          const uint32_t lo = (uint32_t)to_bf16_rne(x[b].x) | ((uint32_t)to_bf16_rne(x[b].y) << 16);
-          const uint32_t hi = (uint32_t)to_bf16_rne(x[b].z) | ((uint32_t)to_bf16_rne(x[b].w) << 16);
-          *(uint2*)((uint16_t*)p.c_pos[pos] + off[b]) = make_uint2(lo, hi);
-        }
+        for (int b = 0; b < BATCH; ++b)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, x[b]), out_res,
+                                                 chunk_off(b0 + b, 4), 0, 0);
       }
     }
-    __syncthreads();
+    lds_barrier();  // the next block, or the next tile's loads, overwrite the staging rows
   }
   release_tile(p, pos, grp);
 }
@@ -502,7 +580,7 @@ __device__ __forceinline__ void bf16_tile(const Plan& p, const int tile, uint8_t
 // workgroups walk the tiles with a stride of the grid size, in the same order.
 template <int BM, int BN>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(Plan p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_ring[Cfg<BM, BN>::STAGES * Cfg<BM, BN>::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_ring[Cfg<BM, BN>::LDS];
   const int total = p.grid.npos * p.grid.tiles_m * p.grid.tiles_n;
   for (int tile = blockIdx.x; tile < total; tile += gridDim.x) bf16_tile<BM, BN>(p, tile, lds_ring);
 }
@@ -757,6 +835,7 @@ static bool plan_ok(const Plan& p) {
   for (int i = 0; i < g.npos; ++i)
     if (p.gate_slice[i] >= FO_MAX_P || (p.gate_slice[i] >= 0 && p.comp_tab == nullptr)) return false;
   if (p.accum_pos >= g.npos || p.n_recv < 0 || p.n_recv > FO_MAX_P) return false;
+  if (p.accum_pos >= 0 && !p.out_f32) return false;  // partials are added in fp32 output only
   if (p.accum_pos >= 0)
     for (int i = 0; i < p.n_recv; ++i)
       if (p.recv_slice[i] >= FO_MAX_P || (p.recv_slice[i] >= 0 && p.comp_tab == nullptr))

@@ -120,6 +120,7 @@ def _ag(lib, **kw):
 @pytest.mark.parametrize("kw", [
     dict(P=0), dict(P=33), dict(rank=4), dict(rank=-1), dict(m=-1), dict(K=-8),
     dict(K=260), dict(N=500), dict(in_dt=5), dict(out_dt=2), dict(x_local=None), dict(w=None),
+    dict(K=(1 << 21) + 8), dict(N=(1 << 20) + 8),  # past the kernel's 31-bit tile offsets
     dict(y=None), dict(x_recv=None), dict(x_local=A + 2), dict(w=C + 8), dict(y=D + 1),
     dict(y=A),                                   # output overlaps the local slice
     dict(y=B + 4096),                            # output overlaps the receive buffer
@@ -195,5 +196,6 @@ def test_ref_rejects(lib):
     assert lib.fo_gemm_ref(A, B, C, 64, 256, 500, fo.BF16, fo.BF16, 0, None) == fo.FO_ERR_INVALID_ARG
     assert lib.fo_gemm_ref(A, B, A, 64, 256, 512, fo.BF16, fo.BF16, 0, None) == fo.FO_ERR_INVALID_ARG
     assert lib.fo_gemm_ref(A, B, C, 64, 256, 512, fo.BF16, fo.BF16, 9, None) == fo.FO_ERR_INVALID_ARG
+    assert lib.fo_gemm_ref(A, B, C, 64, 256, (1 << 20) + 8, fo.BF16, fo.BF16, 0, None) == fo.FO_ERR_INVALID_ARG
     assert lib.fo_gemm_ref(None, B, C, 64, 256, 512, fo.BF16, fo.BF16, 0, None) == fo.FO_ERR_INVALID_ARG
     assert lib.fo_gemm_ref(A, B, C, 0, 256, 512, fo.BF16, fo.BF16, 0, None) == fo.FO_OK
