@@ -399,12 +399,15 @@ __device__ __forceinline__ void bf16_tile(const Plan& p, const int tile, uint8_t
   };
   // first half of step kt (stage si): MFMAs of f0 with the reads of f1 and, when `issue`, the
   // second load group of step `late` into the stage freed at the previous barrier
+  // (The descriptor of a load group is computed under the first MFMA of its half, not ahead of
+  // it, so that its scalar arithmetic does not hold back the MFMA that follows a barrier.)
   auto first_half = [&](int si, int late, bool issue, bool tail) {
-    const i32x4 rb = issue ? w_rsrc(late) : i32x4{};
+    i32x4 rb{};
     const int ls = (si + S - 1) % S;
 #pragma unroll
     for (int x = 0; x < NXA; ++x) {
       if (x < NMFMA) mfma(f0, x);
+      if (x == 0 && issue) rb = w_rsrc(late);
       if (x < NREAD) rd_frag(st(si), 1, f1, x);
 #pragma unroll
       for (int q = 0; q < C::L1; ++q)
@@ -415,10 +418,11 @@ __device__ __forceinline__ void bf16_tile(const Plan& p, const int tile, uint8_t
   // second half of step kt: MFMAs of f1, the first load group of step kt + S into stage si when
   // `issue`, and the reads of the next step's f0 when `more`
   auto second_half = [&](int kt, int si, bool issue, bool tail, bool more) {
-    const i32x4 rb = issue ? w_rsrc(kt + S) : i32x4{};
+    i32x4 rb{};
 #pragma unroll
     for (int x = 0; x < NXB; ++x) {
       if (x < NMFMA) mfma(f1, x);
+      if (x == 0 && issue) rb = w_rsrc(kt + S);
 #pragma unroll
       for (int q = 0; q < C::L0; ++q)
         if (x == spread_slot(q, C::L0, NX2L)) issue_if(issue, tail, kt + S, si, rb, q);

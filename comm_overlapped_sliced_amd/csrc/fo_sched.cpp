@@ -31,29 +31,24 @@ int slice_order(int kind, int order, int P, int rank, int32_t* out) {
   return 1;
 }
 
-// AUTO tile choice. Every tile of a launch runs its whole K loop, so a launch takes about
-// ceil(tiles / CUs) rounds of one tile's time, and a 256x256 round costs what two 128x256 rounds
-// cost (128x256 tiles move 50% more operand bytes per flop and run ~3.5% slower per flop). The
-// rules, each checked by timing the sliced calls on MI355X:
-//   - slices of at most 128 rows: 128-row tiles (a 256-row tile would be half empty);
-//   - fp32 output with K <= 4096: 128x256, whose shorter write-back of 128 KB per tile hides behind
-//     other tiles' mainloops (Flash-RS, Llama-70B down projection: 523 vs 614 us);
-//   - a weight above 128 MB: 256x256, the least operand traffic per flop once the operands
-//     outgrow the last-level cache (Llama-405B gate+up: 3.3 vs 3.8 ms);
-//   - otherwise the fewer rounds, counted as above, with ties to 256x256.
+// AUTO tile choice. 256x256 tiles move the fewest operand bytes per flop and keep the LDS
+// below its bandwidth (128x256 tiles spend ~1.5x the LDS traffic per MFMA); the other shapes
+// serve where a 256x256 tile would be half empty or where finer work pays. The rules, each
+// checked by timing the sliced calls with arrivals on MI355X:
+//   - slices of at most 128 rows: 128-row tiles (Llama-70B gate+up at 1K tokens: 176 vs 237 us);
+//   - fewer than 256 columns: 256x128;
+//   - a sliced call with fp32 output and K <= 4096 (Flash-RS at Llama-70B down-projection
+//     shapes): 128x256. Such a call waits on its transfers more than on its GEMM, and the
+//     smaller tiles finish the first outgoing row groups sooner (450 vs 493 us);
+//   - otherwise 256x256 (Llama-70B gate+up, 2K-16K tokens, and both Llama-405B calls).
 // Rows of a tile never cross a slice.
 int choose_tile(int P, int64_t m, int64_t K, int64_t N, bool out_f32, int n_cu) {
-  auto rounds = [&](int bm, int bn) {
-    const double t = (double)P * (double)((m + bm - 1) / bm) * (double)((N + bn - 1) / bn);
-    return (double)(int64_t)((t + n_cu - 1) / n_cu);
-  };
+  (void)n_cu;
   if (m <= 64 || N <= 64) return FO_TILE_64x64;
   if (m <= 128) return N >= 256 ? FO_TILE_128x256 : FO_TILE_128x128;
   if (N < 256) return FO_TILE_256x128;
-  if (out_f32 && K <= 4096) return FO_TILE_128x256;
-  if ((double)K * (double)N * 2.0 > 128.0 * 1024 * 1024) return FO_TILE_256x256;
-  const double c256 = rounds(256, 256), c128 = rounds(128, 256) * 0.5 / 0.965;
-  return c128 < c256 ? FO_TILE_128x256 : FO_TILE_256x256;
+  if (P > 1 && out_f32 && K <= 4096) return FO_TILE_128x256;
+  return FO_TILE_256x256;
 }
 
 }  // namespace fo

@@ -77,21 +77,21 @@ def test_slice_order_rejects(lib):
 
 
 def test_tile_choice_for_the_workloads():
-    # Tiles never cross a slice. A launch takes ~ceil(tiles / 256) rounds, and one 256x256 round
-    # costs about two 128x256 rounds.
-    # 70B gate+up: 2 rounds of 256x256 against 4 of 128x256.
-    assert fo.tile_info(8, 512, 8192, 7168)[:2] == (256, 256)
-    # 70B down (fp32 out, K = 3584): the short K favours the shorter 128x256 write-back
+    # Tiles never cross a slice; 256x256 unless a rule below applies.
+    assert fo.tile_info(8, 512, 8192, 7168)[:2] == (256, 256)    # 70B gate+up
+    # 70B down in Flash-RS (fp32 out, K = 3584): transfer-bound, finer tiles release sooner
     assert fo.tile_info(8, 512, 3584, 8192, out_dt=fo.F32)[:2] == (128, 256)
     assert fo.tile_info(8, 512, 3584, 8192)[:2] == (256, 256)    # the same with bf16 out
-    # 405B: weights of 436 MB / 218 MB, beyond the last-level cache: 256x256
+    assert fo.tile_info(1, 4096, 3584, 8192, out_dt=fo.F32)[:2] == (256, 256)  # monolithic
+    # 405B
     assert fo.tile_info(8, 1024, 16384, 13312)[:2] == (256, 256)
     assert fo.tile_info(8, 1024, 6656, 16384, out_dt=fo.F32)[:2] == (256, 256)
-    # 70B sweep, M = 8192: 3.5 rounds of 256x256 (4) against 7 of 128x256 (~3.6)
-    assert fo.tile_info(8, 1024, 8192, 7168)[:2] == (128, 256)
-    assert fo.tile_info(8, 2048, 8192, 7168)[:2] == (256, 256)  # M = 16384: exactly 7 rounds
+    # 70B gate+up sweep, M = 2048 .. 16384
+    for m in (256, 512, 1024, 2048):
+        assert fo.tile_info(8, m, 8192, 7168)[:2] == (256, 256)
     bm, bn, wg = fo.tile_info(8, 128, 8192, 7168)       # M = 1024: slices of 128 rows
     assert (bm, bn) == (128, 256) and wg == 8 * 28
+    assert fo.tile_info(8, 512, 8192, 200)[:2] == (256, 128)
     assert fo.tile_info(4, 64, 256, 512, fo.F32)[:2] == (64, 64)
     assert fo.tile_info(8, 512, 8192, 7168, fo.BF16, fo.TILE_128x128) == (128, 128, 8 * 4 * 56)
 
