@@ -72,7 +72,7 @@ def parse():
                     help="emulated links per call (0: one DMA engine per peer; 1: one link)")
     ap.add_argument("--row-groups", type=int, default=0,
                     help="row groups per slice (0: one per tile row; 1: whole slices)")
-    ap.add_argument("--exposure-reps", type=int, default=15)
+    ap.add_argument("--exposure-reps", type=int, default=10)
     ap.add_argument("--no-exposure", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample (0 disables)")
@@ -153,15 +153,20 @@ def main():
         rs_call(evs[1] if evs else None)
 
     def timed(fn, reps):
-        """Median duration (ms) of fn() on the compute stream."""
+        """Steady-state duration (ms) of one fn() on the compute stream: `reps` calls enqueued
+        back to back, as a training step enqueues them, so that the host's set-up of a call
+        (signals, the enqueueing of its copies) runs ahead of the GPU instead of delaying the
+        first copy; median over three such batches."""
+        fn()
         out = []
-        for _ in range(reps):
+        for _ in range(3):
             a, b = ev(), ev()
             a.record(stream)
-            fn()
+            for _ in range(reps):
+                fn()
             b.record(stream)
             b.synchronize()
-            out.append(a.elapsed_time(b))
+            out.append(a.elapsed_time(b) / reps)
         return statistics.median(out)
 
     for _ in range(args.warmup):
