@@ -78,6 +78,9 @@ struct DevState {
   uint32_t* go = nullptr;    // the tail reduce's start word (same uncached block)
   uint32_t go_value = 0;
   uint32_t* done = nullptr;  // completed-tile counters [position][group]
+  uint32_t* arr_lead = nullptr;   // arrival-poller election and landed words [slice][group]
+  uint32_t* arr_ready = nullptr;  // (uncached)
+  uint32_t gen = 0;          // number of the last call (the kernels' election round)
   void* scratch = nullptr;   // source and destination of the DMA engines' first copies
   hipEvent_t ev_last = nullptr;
   bool have_last = false;
@@ -97,6 +100,11 @@ fo_status ensure_ready(int dev, DevState& st) {
   st.err = (uint32_t*)p;
   st.go = (uint32_t*)((uint8_t*)p + 256);
   FO_HIP(hipMemset(p, 0, 4096));
+  const size_t words = (size_t)FO_MAX_P * fo::kMaxGroups * sizeof(uint32_t);
+  FO_HIP(hipExtMallocWithFlags(&p, 2 * words, hipDeviceMallocUncached));
+  st.arr_lead = (uint32_t*)p;
+  st.arr_ready = (uint32_t*)((uint8_t*)p + words);
+  FO_HIP(hipMemset(p, 0, 2 * words));
   const size_t counters = (size_t)FO_MAX_P * fo::kMaxGroups * sizeof(uint32_t);
   FO_HIP(hipMalloc(&p, counters));
   st.done = (uint32_t*)p;
@@ -421,6 +429,9 @@ fo_status fo_ag_gemm(const void* x_local, const void* const* x_peer, void* x_rec
   p.comp_tab = call.comp_tab;
   p.b = w;
   p.done = st->done;
+  p.lead = st->arr_lead;
+  p.ready = st->arr_ready;
+  p.gen = ++st->gen;
   p.err = st->err;
   p.spin_limit = spin_ticks(*st, o.spin_timeout_us);
   p.m = m;
@@ -538,6 +549,9 @@ fo_status fo_gemm_rs(const void* x_shard, const void* w, float* send_buf, float*
   p.n_recv = P - 1;
   p.b = w;
   p.done = st->done;
+  p.lead = st->arr_lead;
+  p.ready = st->arr_ready;
+  p.gen = ++st->gen;
   p.err = st->err;
   p.spin_limit = spin_ticks(*st, o.spin_timeout_us);
   p.m = m;
@@ -633,6 +647,9 @@ fo_status fo_gemm_ref(const void* a, const void* b, void* c, int64_t M, int64_t 
   p.c_pos[0] = c;
   p.b = b;
   p.done = st->done;
+  p.lead = st->arr_lead;
+  p.ready = st->arr_ready;
+  p.gen = ++st->gen;
   p.err = st->err;
   p.spin_limit = spin_ticks(*st, kDefaultTimeoutUs);
   p.m = M;

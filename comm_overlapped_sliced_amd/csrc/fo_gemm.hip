@@ -52,15 +52,47 @@ __device__ __forceinline__ void wait_signal(const int64_t* v, uint64_t limit, ui
   }
 }
 
-// Thread 0 waits for the completion signal of group `grp` of each listed slice (negative ids are
-// skipped); then the whole workgroup acquires at system scope so that data the copy engine wrote
-// before the signal is seen (no stale cache lines).
+// Bounded wait until a device word has reached `gen` (or a wait of the call has failed). The
+// word is uncached device memory, so every read sees the latest store from any XCD.
+__device__ __forceinline__ void wait_gen(const uint32_t* w, uint32_t gen, uint64_t limit,
+                                         uint32_t* err) {
+  const uint64_t t0 = wall_clock64();
+  while (__hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < gen) {
+    if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != 0u) return;
+    if (wall_clock64() - t0 > limit) {
+      __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(8);
+  }
+}
+
+// Wait for group `grp` of `slice` to have landed. The signal values live in host memory, and
+// hundreds of workgroups polling them slow the copy engines down, so only one workgroup per
+// (slice, group) and call polls the signal: the first to get there, elected by raising
+// lead[slice][group] to the call's number `gen` (numbers only grow, so nothing is re-armed
+// between calls). It then raises ready[slice][group] to gen, which the other workgroups poll in
+// device memory. A failed or timed-out wait still raises it (the call's error record is set).
+__device__ __forceinline__ void wait_group(const Plan& p, int slice, int grp) {
+  const int k = slice * kMaxGroups + grp;
+  const uint32_t prev =
+      __hip_atomic_fetch_max(p.lead + k, p.gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (prev < p.gen) {
+    wait_signal(p.comp_tab[k], p.spin_limit, p.err);
+    __hip_atomic_store(p.ready + k, p.gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    wait_gen(p.ready + k, p.gen, p.spin_limit, p.err);
+  }
+}
+
+// Thread 0 waits for group `grp` of each listed slice (negative ids are skipped); then the whole
+// workgroup acquires at system scope so that data the copy engine wrote before the signal is
+// seen (no stale cache lines).
 __device__ __forceinline__ void wait_groups_wg(const Plan& p, const int32_t* slices, int n,
                                                int grp) {
   if (threadIdx.x == 0 && p.comp_tab != nullptr) {
     for (int i = 0; i < n; ++i)
-      if (slices[i] >= 0)
-        wait_signal(p.comp_tab[slices[i] * kMaxGroups + grp], p.spin_limit, p.err);
+      if (slices[i] >= 0) wait_group(p, slices[i], grp);
   }
   __syncthreads();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
@@ -836,6 +868,7 @@ static bool plan_ok(const Plan& p) {
     return false;
   if (g.lead < 0 || g.trail < 0 || g.lead + g.trail > g.npos) return false;
   if (p.done == nullptr || p.err == nullptr) return false;
+  if (p.comp_tab != nullptr && (p.lead == nullptr || p.ready == nullptr || p.gen == 0)) return false;
   for (int i = 0; i < g.npos; ++i)
     if (p.gate_slice[i] >= FO_MAX_P || (p.gate_slice[i] >= 0 && p.comp_tab == nullptr)) return false;
   if (p.accum_pos >= g.npos || p.n_recv < 0 || p.n_recv > FO_MAX_P) return false;

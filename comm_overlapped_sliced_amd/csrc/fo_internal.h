@@ -39,6 +39,9 @@ struct Plan {
   const void* b;                     // W [K, N], row stride N
   uint32_t* done;                    // completed-tile counters [position][group] (zero between calls)
   uint32_t* err;                     // 1: a wait ran past spin_limit; 2: a copy reported failure
+  uint32_t* lead;                    // [slice][group]: the last call whose poller is elected
+  uint32_t* ready;                   // [slice][group]: the last call whose group has landed
+  uint32_t gen;                      // this call's number (> 0, grows by one per call)
   uint64_t spin_limit;               // bound of each wait, in wall-clock ticks
   int64_t m, K, N;                   // slice rows, reduction length, output columns
   int32_t n_recv;                    // partials added at accum_pos
