@@ -82,7 +82,9 @@ struct DevState {
   uint32_t* arr_ready = nullptr;  // (uncached)
   uint32_t gen = 0;          // number of the last call (the kernels' election round)
   void* scratch = nullptr;   // source and destination of the DMA engines' first copies
-  hipEvent_t ev_last = nullptr;
+  hipEvent_t ev_last = nullptr;     // recorded after a call that has no copy slot
+  hipEvent_t last_ev = nullptr;     // the event recorded after the device's last call
+  hipStream_t last_stream = nullptr;
   bool have_last = false;
 };
 
@@ -253,6 +255,28 @@ int arrival_sequence(int kind, int order, int P, int rank, int* seq) {
     for (int i = 1; i < P; ++i) seq[n++] = ((rank - i) % P + P) % P;
   }
   return n;
+}
+
+// Every call on a device is ordered after the previous one (they share the device's signals,
+// counters and words): a call on another stream first waits for the previous call's event; on
+// the same stream the order is already given.
+fo_status order_after_last(DevState* st, hipStream_t cs) {
+  if (st->have_last && cs != st->last_stream) FO_HIP(hipStreamWaitEvent(cs, st->last_ev, 0));
+  return FO_OK;
+}
+
+// Marks the end of a call on `cs`: the copy slot's event when the call has one (already
+// recorded), else the device's own event.
+fo_status mark_last(DevState* st, hipStream_t cs, hipEvent_t slot_ev) {
+  if (slot_ev) {
+    st->last_ev = slot_ev;
+  } else {
+    FO_HIP(hipEventRecord(st->ev_last, cs));
+    st->last_ev = st->ev_last;
+  }
+  st->last_stream = cs;
+  st->have_last = true;
+  return FO_OK;
 }
 
 fo_status launch_with_events(const fo::Plan& p, int in_dt, int tile, hipStream_t cs,
@@ -443,13 +467,15 @@ fo_status fo_ag_gemm(const void* x_local, const void* const* x_peer, void* x_rec
   p.out_f32 = out_dt == FO_DT_F32;
 
   hipStream_t cs = (hipStream_t)compute_stream;
-  if (st->have_last) FO_HIP(hipStreamWaitEvent(cs, st->ev_last, 0));
-  if (arrivals) FO_HIP(fo::launch_release(call.start, cs));
+  if (arrivals) p.start = call.start;
+  s = order_after_last(st, cs);
+  if (s != FO_OK) return s;
   s = launch_with_events(p, in_dt, tile, cs, o);
   if (s != FO_OK) return s;
-  if (arrivals) FO_DMA(fo::dma::end(st->dev, call, cs, &e_));
-  FO_HIP(hipEventRecord(st->ev_last, cs));
-  st->have_last = true;
+  hipEvent_t slot_ev = nullptr;
+  if (arrivals) FO_DMA(fo::dma::end(st->dev, call, cs, &e_, &slot_ev));
+  s = mark_last(st, cs, slot_ev);
+  if (s != FO_OK) return s;
   if (arrivals) {
     // group-major, in arrival order inside a group: the order the kernel consumes them in
     int seq[FO_MAX_P];
@@ -561,8 +587,9 @@ fo_status fo_gemm_rs(const void* x_shard, const void* w, float* send_buf, float*
   p.out_f32 = 1;
 
   hipStream_t cs = (hipStream_t)compute_stream;
-  if (st->have_last) FO_HIP(hipStreamWaitEvent(cs, st->ev_last, 0));
-  if (arrivals) FO_HIP(fo::launch_release(call.start, cs));
+  if (arrivals) p.start = call.start;
+  s = order_after_last(st, cs);
+  if (s != FO_OK) return s;
   s = launch_with_events(p, in_dt, tile, cs, o);
   if (s != FO_OK) return s;
   if (natural && P > 1) {
@@ -587,9 +614,10 @@ fo_status fo_gemm_rs(const void* x_shard, const void* w, float* send_buf, float*
     ra.go_value = st->go_value;
     FO_HIP(fo::launch_reduce(ra, cs));
   }
-  if (arrivals) FO_DMA(fo::dma::end(st->dev, call, cs, &e_));
-  FO_HIP(hipEventRecord(st->ev_last, cs));
-  st->have_last = true;
+  hipEvent_t slot_ev = nullptr;
+  if (arrivals) FO_DMA(fo::dma::end(st->dev, call, cs, &e_, &slot_ev));
+  s = mark_last(st, cs, slot_ev);
+  if (s != FO_OK) return s;
   if (arrivals) {
     // transfer t brings the partial of peer rank-1-t. In lockstep that peer sends its group g at
     // its own unit (t, g), which (peers progressing together) ends when this rank ends its unit
@@ -691,12 +719,14 @@ fo_status fo_transfer_ref(int32_t kind, const void* const* src, void* dst, int32
   int seq[FO_MAX_P];
   const int n = arrival_sequence(kind, o.order, P, rank, seq);
   hipStream_t ks = (hipStream_t)stream;
-  if (st->have_last) FO_HIP(hipStreamWaitEvent(ks, st->ev_last, 0));
+  s = order_after_last(st, ks);
+  if (s != FO_OK) return s;
   FO_HIP(fo::launch_release(call.start, ks));
   FO_HIP(fo::launch_wait(call.comp_tab, seq, n, G, spin_ticks(*st, o.spin_timeout_us), st->err, ks));
-  FO_DMA(fo::dma::end(st->dev, call, ks, &e_));
-  FO_HIP(hipEventRecord(st->ev_last, ks));
-  st->have_last = true;
+  hipEvent_t slot_ev = nullptr;
+  FO_DMA(fo::dma::end(st->dev, call, ks, &e_, &slot_ev));
+  s = mark_last(st, ks, slot_ev);
+  if (s != FO_OK) return s;
   const int L = links_for(o, P);
   const size_t piece = ((size_t)slice_bytes / G + 255) / 256 * 256;
   for (int g = 0; g < G; ++g) {

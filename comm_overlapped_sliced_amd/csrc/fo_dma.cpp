@@ -327,11 +327,12 @@ bool copy(int dev, const Call& call, int link, int slice, int group, int rel_pos
   return true;
 }
 
-bool end(int dev, const Call& call, hipStream_t stream, std::string* err) {
+bool end(int dev, const Call& call, hipStream_t stream, std::string* err, hipEvent_t* ev) {
   if (hipEventRecord(g_dev[dev].slot[call.slot].ev, stream) != hipSuccess) {
     *err = "hipEventRecord failed";
     return false;
   }
+  if (ev) *ev = g_dev[dev].slot[call.slot].ev;
   return true;
 }
 

@@ -612,11 +612,22 @@ __device__ __forceinline__ void bf16_tile(const Plan& p, const int tile, uint8_t
   release_tile(p, pos, grp);
 }
 
+// The call's copies wait for its start signal. Workgroup 0, the first one dispatched, stores 0
+// into it when the kernel starts (everything enqueued before the kernel is then complete), after
+// a system-scope release so that the copy engines see that work's writes.
+__device__ __forceinline__ void release_start(const Plan& p) {
+  if (p.start != nullptr && blockIdx.x == 0 && threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
+    __hip_atomic_store(p.start, (int64_t)0, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+}
+
 // One workgroup per tile, or (grid smaller than the tile count) a persistent grid whose
 // workgroups walk the tiles with a stride of the grid size, in the same order.
 template <int BM, int BN>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(Plan p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds_ring[Cfg<BM, BN>::LDS];
+  release_start(p);
   const int total = p.grid.npos * p.grid.tiles_m * p.grid.tiles_n;
   for (int tile = blockIdx.x; tile < total; tile += gridDim.x) bf16_tile<BM, BN>(p, tile, lds_ring);
 }
@@ -688,6 +699,7 @@ __device__ __forceinline__ void f32_tile(const Plan& p, const int tile, float (*
 }
 
 __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(Plan p) {
+  release_start(p);
   __shared__ float sa[F_BK][F_BM + 4];  // k-major so a thread's 4 rows are one broadcast read
   __shared__ float sb[F_BK][F_BN + 4];
   const int total = p.grid.npos * p.grid.tiles_m * p.grid.tiles_n;

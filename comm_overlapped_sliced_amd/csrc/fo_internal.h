@@ -42,6 +42,8 @@ struct Plan {
   uint32_t* lead;                    // [slice][group]: the last call whose poller is elected
   uint32_t* ready;                   // [slice][group]: the last call whose group has landed
   uint32_t gen;                      // this call's number (> 0, grows by one per call)
+  int64_t* start;                    // the call's start signal value, stored 0 at kernel start
+                                     // (null: no copies wait for this kernel)
   uint64_t spin_limit;               // bound of each wait, in wall-clock ticks
   int64_t m, K, N;                   // slice rows, reduction length, output columns
   int32_t n_recv;                    // partials added at accum_pos
@@ -58,6 +60,7 @@ inline Plan empty_plan() {
     p.recv_slice[i] = -1;
   }
   p.accum_pos = -1;
+  p.start = nullptr;
   return p;
 }
 
@@ -146,8 +149,8 @@ bool begin(int dev, int P, int groups, Call* call, std::string* err);
 bool copy(int dev, const Call& call, int link, int slice, int group, int rel_pos, void* dst,
           const void* src, size_t bytes, std::string* err);
 // Records, on `stream`, the point after which the call's kernels no longer read its signals
-// (after the call's last kernel).
-bool end(int dev, const Call& call, hipStream_t stream, std::string* err);
+// (after the call's last kernel); *ev receives the recorded event.
+bool end(int dev, const Call& call, hipStream_t stream, std::string* err, hipEvent_t* ev = nullptr);
 // Waits (host, bounded) until every copy issued on the device has landed. On failure
 // *timed_out tells a copy still in flight at the bound from one the engine reported as failed.
 bool drain(int dev, uint32_t timeout_ms, std::string* err, bool* timed_out);
