@@ -118,6 +118,16 @@ __device__ __forceinline__ void release_tile(const Plan& p, int pos, int grp) {
   }
 }
 
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
+// Two fp32 -> bf16 (a in the low half), round to nearest even: one v_cvt_pk_bf16_f32 (CDNA4),
+// in the kernel's default float mode (round to nearest even, denormals kept). Five integer
+// operations per value instead made the bf16 write-back of a 256x256 tile VALU-bound.
+__device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+
 // fp32 -> bf16, round to nearest, ties to even (quiet NaN kept); branch-free (a select).
 __device__ __forceinline__ uint32_t to_bf16_rne(float f) {
   const uint32_t u = __builtin_bit_cast(uint32_t, f);
@@ -561,8 +571,7 @@ __device__ __forceinline__ void bf16_tile(const Plan& p, const int tile, uint8_t
 #pragma unroll
         for (int b = 0; b < CPT; ++b) {
           const float4 x = chunk_lds(b);
-          const uint32_t lo = to_bf16_rne(x.x) | (to_bf16_rne(x.y) << 16);
-          const uint32_t hi = to_bf16_rne(x.z) | (to_bf16_rne(x.w) << 16);
+          const uint32_t lo = cvt_bf16x2(x.x, x.y), hi = cvt_bf16x2(x.z, x.w);
           __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)lo, (int)hi}, out_res, chunk_off(b, 2),
                                                 0, 0);
           if (b % 4 == 3) __builtin_amdgcn_sched_barrier(0);

@@ -211,15 +211,24 @@ def test_bf16_ragged_all_tiles(dev, tile, shape):
     ref = oracle.gemm(x, w)
     y_ref = torch.empty_like(prob.y)
     fo.gemm_ref(to_dev(x, dev), prob.w_d, y_ref, tile=tile[1], stream=_stream())
+    outs = {}
     for r in sorted({0, P - 1}):
-        got = prob.run(r, o=fo.opts(tile=tile[1]))
+        got = outs[r] = prob.run(r, o=fo.opts(tile=tile[1]))
         assert rel_frobenius(got, ref) <= TOL_BF16, f"rank {r}"
         # exactness of slicing: the sliced product equals the unsliced one bit for bit
         assert np.array_equal(got, from_dev(y_ref)), f"rank {r}"
-    # fp32 output of the same product
+    # fp32 output of the same product; the bf16 output is that fp32 sum rounded to nearest even
     prob32 = AG(x, w, P, dev, out_dt="f32")
     got32 = prob32.run(0, o=fo.opts(tile=tile[1]))
     assert rel_frobenius(got32, ref) <= 1e-5
+    assert np.array_equal(_round_bf16(got32), outs[0])
+
+
+def _round_bf16(x: np.ndarray) -> np.ndarray:
+    """fp32 values rounded to the nearest bf16, ties to even (finite inputs), as fp64."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32).astype(np.float64)
 
 
 @pytest.mark.parametrize("tile", TILES, ids=lambda t: t[0])
