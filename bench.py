@@ -141,12 +141,12 @@ def main():
                    o=o)
 
     def rs_call(evs=None, arrival=fo.ARR_DEFAULT, links=args.links, groups=args.row_groups,
-                order=fo.ORDER_FLASH, rank=r):
+                order=fo.ORDER_FLASH, rank=r, x=None):
         o = fo.opts(order=order, links=links, row_groups=groups, arrival=arrival,
                     kernel_events=evs)
         peers = None if arrival == fo.ARR_NONE else rs_peer
-        fo.gemm_rs(rs_x, rs_w, rs_send, rs_out, peers, rs_recv, P, rank, compute_stream=stream,
-                   o=o)
+        fo.gemm_rs(rs_x if x is None else x, rs_w, rs_send, rs_out, peers, rs_recv, P, rank,
+                   compute_stream=stream, o=o)
 
     def step(evs=None):
         ag_call(evs[0] if evs else None)
@@ -251,6 +251,38 @@ def main():
                 f"{t_ds*1e3:.0f} us ({base[kind]['removed_data_slicing']:.2f} removed), flash "
                 f"{t_fl*1e3:.0f} us ({base[kind]['removed_flash']:.2f} removed)")
         exposure["baselines"] = base
+
+        # the MLP block of the page's latency experiment: AG (gate+up) -> SwiGLU -> RS (down),
+        # the RS reading the activation H that SwiGLU makes of the AG output. Vanilla = each
+        # projection's transfers, then its GEMM, nothing overlapped.
+        mlp_h = torch.empty((rs_case.M, rs_case.K), dtype=torch.bfloat16, device=dev)
+        t_act = timed(lambda: fo.swiglu(ag_y, mlp_h, stream), reps)
+
+        def block(rank, natural):
+            g = 1 if natural else args.row_groups
+            o = fo.ORDER_NATURAL if natural else fo.ORDER_FLASH
+            ag_call(order=o, groups=g, rank=rank)
+            fo.swiglu(ag_y, mlp_h, stream)
+            rs_call(order=o, groups=g, rank=rank, x=mlp_h)
+
+        mlp = {"swiglu_us": t_act * 1e3,
+               "swiglu_gbps": (ag_case.M * ag_case.N * 2 + rs_case.M * rs_case.K * 2) / t_act / 1e6}
+        for rb in (0, P - 1):
+            tx_a = timed(lambda: fo.transfer_ref("ag", ag_slices, ag_recv, P, rb,
+                                                 ag_case.m * ag_case.K * 2, stream, tw), reps)
+            tx_r = timed(lambda: fo.transfer_ref("rs", rs_peer, rs_recv, P, rb,
+                                                 rs_case.m * rs_case.N * 4, stream, tw), reps)
+            van = t_ref_ag + tx_a + t_act + t_ref_rs + tx_r
+            t_fl = timed(lambda: block(rb, False), reps)
+            t_ds = timed(lambda: block(rb, True), reps)
+            mlp[f"rank{rb}"] = {"vanilla_us": van * 1e3, "data_slicing_us": t_ds * 1e3,
+                                "flash_us": t_fl * 1e3,
+                                "latency_reduction_data_slicing": (van - t_ds) / van,
+                                "latency_reduction_flash": (van - t_fl) / van}
+            log(f"MLP block rank {rb}: vanilla {van*1e3:.0f} us, data slicing {t_ds*1e3:.0f} us "
+                f"({(van - t_ds) / van:.3f} less), flash {t_fl*1e3:.0f} us ({(van - t_fl) / van:.3f} less)")
+        log(f"SwiGLU {t_act*1e3:.1f} us, {mlp['swiglu_gbps']:.0f} GB/s")
+        exposure["mlp_block"] = mlp
         fo.check(stream)
         step()
         fo.check(stream)

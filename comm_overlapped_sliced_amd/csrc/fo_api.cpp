@@ -692,6 +692,20 @@ fo_status fo_gemm_ref(const void* a, const void* b, void* c, int64_t M, int64_t 
   return FO_OK;
 }
 
+fo_status fo_swiglu(const void* y, void* h, int64_t rows, int64_t inter, void* stream) {
+  if (rows < 0 || inter < 0) return invalid("negative size (rows %lld, inter %lld)", (long long)rows,
+                                            (long long)inter);
+  if (inter % 8) return invalid("inter %lld is not a multiple of 8", (long long)inter);
+  if (rows > ((int64_t)1 << 40) || inter > ((int64_t)1 << 30)) return invalid("sizes too large");
+  if (rows == 0 || inter == 0) return FO_OK;
+  if (!y || !h) return invalid("NULL buffer");
+  if (!aligned(y, 16) || !aligned(h, 16)) return invalid("misaligned buffer (16-byte alignment)");
+  if (overlap(rng(y, (size_t)rows * 2 * inter * 2), rng(h, (size_t)rows * inter * 2)))
+    return invalid("h overlaps y");
+  FO_HIP(fo::launch_swiglu(y, h, rows, inter, (hipStream_t)stream));
+  return FO_OK;
+}
+
 fo_status fo_transfer_ref(int32_t kind, const void* const* src, void* dst, int32_t P,
                           int32_t rank, int64_t slice_bytes, void* stream, const fo_opts* opts) {
   fo_opts o;

@@ -110,6 +110,10 @@ struct ReduceArgs {
 };
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);
 
+// h[rows, inter] = silu(y[:, :inter]) * y[:, inter:] in bf16 (fp32 arithmetic, one rounding to
+// nearest even); y is [rows, 2*inter] bf16. inter % 8 == 0, both 16-byte aligned.
+hipError_t launch_swiglu(const void* y, void* h, int64_t rows, int64_t inter, hipStream_t stream);
+
 // Slice schedule: kind 0 = AG, 1 = RS; order = fo_order. Writes P ids.
 int slice_order(int kind, int order, int P, int rank, int32_t* out);
 

@@ -21,9 +21,9 @@ TILE_AUTO, TILE_256x256, TILE_256x128, TILE_128x256, TILE_128x128, TILE_64x64 = 
 MAX_P = 32
 MAX_GROUPS = 8
 
-EXPORTS = ("fo_opts_init", "fo_ag_gemm", "fo_gemm_rs", "fo_gemm_ref", "fo_transfer_ref",
-           "fo_check", "fo_slice_order", "fo_tile_info", "fo_tile_order", "fo_status_str",
-           "fo_last_error", "fo_version")
+EXPORTS = ("fo_opts_init", "fo_ag_gemm", "fo_gemm_rs", "fo_gemm_ref", "fo_swiglu",
+           "fo_transfer_ref", "fo_check", "fo_slice_order", "fo_tile_info", "fo_tile_order",
+           "fo_status_str", "fo_last_error", "fo_version")
 
 
 class FoError(RuntimeError):
@@ -61,6 +61,7 @@ def load():
     lib.fo_ag_gemm.argtypes = [vp, vp, vp, vp, vp, i32, i32, i64, i64, i64, i32, i32, vp, op]
     lib.fo_gemm_rs.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i64, i64, i64, i32, vp, op]
     lib.fo_gemm_ref.argtypes = [vp, vp, vp, i64, i64, i64, i32, i32, i32, vp]
+    lib.fo_swiglu.argtypes = [vp, vp, i64, i64, vp]
     lib.fo_transfer_ref.argtypes = [i32, vp, vp, i32, i32, i64, vp, op]
     lib.fo_check.argtypes = [vp]
     lib.fo_slice_order.argtypes = [i32, i32, i32, i32, ctypes.POINTER(i32)]
@@ -73,7 +74,7 @@ def load():
     lib.fo_last_error.argtypes = []
     lib.fo_last_error.restype = ctypes.c_char_p
     lib.fo_version.argtypes = []
-    for f in ("fo_ag_gemm", "fo_gemm_rs", "fo_gemm_ref", "fo_transfer_ref", "fo_check",
+    for f in ("fo_ag_gemm", "fo_gemm_rs", "fo_gemm_ref", "fo_swiglu", "fo_transfer_ref", "fo_check",
               "fo_slice_order", "fo_tile_info", "fo_tile_order", "fo_version"):
         getattr(lib, f).restype = ctypes.c_int32
     _lib = lib
@@ -190,6 +191,17 @@ def gemm_ref(a, b, c, tile: int = TILE_AUTO, stream=None, raw: bool = False):
     if raw:
         return st
     _raise_on(st, "fo_gemm_ref")
+    return st
+
+
+def swiglu(y, h, stream=None, raw: bool = False):
+    """h = silu(y[:, :inter]) * y[:, inter:] (fo_swiglu); y [rows, 2*inter] bf16, h [rows, inter]
+    bf16."""
+    rows, inter = h.shape
+    st = load().fo_swiglu(_ptr(y), _ptr(h), rows, inter, _stream(stream))
+    if raw:
+        return st
+    _raise_on(st, "fo_swiglu")
     return st
 
 

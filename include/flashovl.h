@@ -173,6 +173,21 @@ fo_status fo_gemm_ref(const void* a, const void* b, void* c, int64_t M, int64_t 
                       int32_t in_dt, int32_t out_dt, int32_t tile, void* stream);
 
 /*
+ * The activation of the MLP block between fo_ag_gemm (gate+up projection) and fo_gemm_rs (down
+ * projection): h[r, j] = silu(y[r, j]) * y[r, inter + j] with silu(g) = g / (1 + e^-g), for
+ * r < rows, j < inter. The FlashOverlap page measures its MLP-layer latency (technical summary
+ * section 4) on the block these three make; for the Llama-3.1 shapes of the workloads the
+ * activation is SwiGLU.
+ *   y  device [rows, 2*inter] bf16: the gate+up output, gate in columns [0, inter) and up in
+ *      [inter, 2*inter) (a plain concatenation of the two projections).
+ *   h  device [rows, inter] bf16, not overlapping y.
+ * fp32 arithmetic and one round-to-nearest-even to bf16. inter must be a multiple of 8 and both
+ * pointers 16-byte aligned (else FO_ERR_INVALID_ARG, nothing enqueued). Enqueued on `stream`
+ * (hipStream_t), ordered only by that stream.
+ */
+fo_status fo_swiglu(const void* y, void* h, int64_t rows, int64_t inter, void* stream);
+
+/*
  * The emulated transfers of one fo_ag_gemm (kind 0) or fo_gemm_rs (kind 1) call on their own,
  * without the GEMM: the same copies, links and arrival order (RS releases are not awaited). On
  * `stream` it enqueues the release of the copies and a one-workgroup kernel that waits until all

@@ -32,7 +32,7 @@ def build(force: bool = True, src: str = _SRC, out: str = _LIB) -> str:
     if force or not os.path.exists(out):
         tmp = out + ".tmp"
         cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-Wall", "-shared", "-fPIC",
-               src, "-o", tmp]
+               src, "-o", tmp, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, out)
     return out
@@ -94,9 +94,12 @@ class Oracle:
         lib.oracle_rs_send_sampled.argtypes = [vp, i32, vp, i32, i32, i64, i64, i64, vp, vp, i64,
                                                vp]
         lib.oracle_num_threads.argtypes = []
+        lib.oracle_swiglu.argtypes = [vp, i64, i64, vp]
+        lib.oracle_round_bf16.argtypes = [vp, i64, vp]
         for f in (lib.oracle_ag_order, lib.oracle_rs_order, lib.oracle_gemm, lib.oracle_ag,
                   lib.oracle_rs, lib.oracle_ag_sampled, lib.oracle_rs_sampled,
-                  lib.oracle_rs_send_sampled, lib.oracle_num_threads):
+                  lib.oracle_rs_send_sampled, lib.oracle_num_threads, lib.oracle_swiglu,
+                  lib.oracle_round_bf16):
             f.restype = ctypes.c_int
         self.lib = lib
         self.path = path
@@ -215,6 +218,33 @@ class Oracle:
         _check(rc, "rs_send_sampled")
         return out
 
+    # ---- the MLP block ------------------------------------------------------------------
+
+    def swiglu(self, y: np.ndarray) -> np.ndarray:
+        """h = silu(y[:, :inter]) * y[:, inter:] in fp64; y bf16 bits [rows, 2*inter]."""
+        y = _c(y)
+        if y.dtype != np.uint16 or y.ndim != 2 or y.shape[1] % 2:
+            raise ValueError("y is bf16 bits [rows, 2*inter]")
+        rows, inter = y.shape[0], y.shape[1] // 2
+        h = np.empty((rows, inter), dtype=np.float64)
+        _check(self.lib.oracle_swiglu(_ptr(y), rows, inter, _ptr(h)), "swiglu")
+        return h
+
+    def round_bf16(self, x: np.ndarray) -> np.ndarray:
+        """x (fp64) rounded to the nearest bf16, ties to even, as bf16 bits (same shape)."""
+        x = np.ascontiguousarray(x, dtype=np.float64)
+        out = np.empty(x.shape, dtype=np.uint16)
+        _check(self.lib.oracle_round_bf16(_ptr(x), x.size, _ptr(out)), "round_bf16")
+        return out
+
+    def mlp_block(self, x_slices, w_gu: np.ndarray, w_down: np.ndarray, partials, P: int,
+                  r: int) -> np.ndarray:
+        """Rank r's output of the MLP block: Y = Flash-AG(x_slices, w_gu) rounded to bf16,
+        H = swiglu(Y) rounded to bf16, then Flash-RS(H, w_down, partials) (fp64 [m, N])."""
+        y = self.round_bf16(self.ag(x_slices, w_gu, P, r))
+        h = self.round_bf16(self.swiglu(y))
+        return self.rs(h, w_down, partials, P, r)
+
 
 _default = None
 
@@ -230,6 +260,6 @@ def default() -> Oracle:
 def __getattr__(name):
     # module-level shortcuts: oracle.gemm(...), oracle.ag(...), ...
     if name in ("num_threads", "ag_order", "rs_order", "gemm", "ag", "rs", "ag_sampled",
-                "rs_sampled", "rs_send_sampled"):
+                "rs_sampled", "rs_send_sampled", "swiglu", "round_bf16", "mlp_block"):
         return getattr(default(), name)
     raise AttributeError(name)

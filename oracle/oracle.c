@@ -28,6 +28,7 @@
  * Inputs are decoded exactly to fp64 (bf16 and fp32 both embed exactly in fp64).
  * Build: gcc -O2 -fopenmp -ffp-contract=off -shared -fPIC oracle.c -o liboracle.so
  */
+#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -249,6 +250,48 @@ int oracle_rs_send_sampled(const void* x_shard, int x_dt, const void* W, int w_d
 #pragma omp parallel for schedule(dynamic, 16)
   for (int64_t t = 0; t < n; ++t)
     out[t] = dot_entry(x_shard, x_dt, W, w_dt, (int64_t)d * m + rows[t], cols[t], K, N);
+  return 0;
+}
+
+/* ---- The MLP block (NEXT: the workload of the page's MLP-layer latency) ------------------
+ *
+ * Section 4 of the technical summary reports the end-to-end latency of an MLP layer: the
+ * column-parallel projection (Flash-AG), the activation, and the row-parallel projection
+ * (Flash-RS). The workloads' shapes are Llama-3.1's, whose MLP activation is SwiGLU (a reading:
+ * the page does not name it): h = silu(gate) * up with silu(g) = g / (1 + e^-g), gate and up
+ * being the two halves [0, inter) and [inter, 2*inter) of the gate+up projection's columns.
+ * Between the kernels the activations are bf16: each intermediate is rounded to the nearest bf16
+ * value, ties to even. */
+
+/* h[r][j] = silu(y[r][j]) * y[r][inter + j] in fp64; y is bf16 [rows, 2*inter]. */
+int oracle_swiglu(const uint16_t* y, int64_t rows, int64_t inter, double* h) {
+  if (!y || !h || rows < 0 || inter < 0) return 1;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t j = 0; j < inter; ++j) {
+      const double g = decode_bf16(y[r * 2 * inter + j]);
+      const double u = decode_bf16(y[r * 2 * inter + inter + j]);
+      h[r * inter + j] = g / (1.0 + exp(-g)) * u;
+    }
+  return 0;
+}
+
+/* x rounded to 8 significant bits (the bf16 precision), to nearest, ties to even, written as
+   bf16 bit patterns. For finite x within bf16's normal range (or zero): x = f * 2^e with
+   0.5 <= |f| < 1, f * 2^8 is rounded to an integer (nearbyint rounds ties to even in the default
+   rounding mode) and scaled back; the result has at most 8 significant bits, so it is exact as a
+   float, whose upper 16 bits are the bf16 pattern. */
+int oracle_round_bf16(const double* x, int64_t n, uint16_t* out) {
+  if (!x || !out || n < 0) return 1;
+  for (int64_t i = 0; i < n; ++i) {
+    int e = 0;
+    const double f = frexp(x[i], &e);
+    const double v = ldexp(nearbyint(ldexp(f, 8)), e - 8);
+    const float fv = (float)v;
+    uint32_t bits;
+    memcpy(&bits, &fv, sizeof bits);
+    out[i] = (uint16_t)(bits >> 16);
+  }
   return 0;
 }
 

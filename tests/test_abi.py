@@ -199,3 +199,12 @@ def test_ref_rejects(lib):
     assert lib.fo_gemm_ref(A, B, C, 64, 256, (1 << 20) + 8, fo.BF16, fo.BF16, 0, None) == fo.FO_ERR_INVALID_ARG
     assert lib.fo_gemm_ref(None, B, C, 64, 256, 512, fo.BF16, fo.BF16, 0, None) == fo.FO_ERR_INVALID_ARG
     assert lib.fo_gemm_ref(A, B, C, 0, 256, 512, fo.BF16, fo.BF16, 0, None) == fo.FO_OK
+
+
+def test_swiglu_rejects(lib):
+    assert lib.fo_swiglu(A, C, 64, 100, None) == fo.FO_ERR_INVALID_ARG   # inter % 8
+    assert lib.fo_swiglu(A + 2, C, 64, 128, None) == fo.FO_ERR_INVALID_ARG  # misaligned
+    assert lib.fo_swiglu(None, C, 64, 128, None) == fo.FO_ERR_INVALID_ARG
+    assert lib.fo_swiglu(A, A + 4096, 64, 128, None) == fo.FO_ERR_INVALID_ARG  # h inside y
+    assert lib.fo_swiglu(A, C, -1, 128, None) == fo.FO_ERR_INVALID_ARG
+    assert lib.fo_swiglu(A, C, 0, 128, None) == fo.FO_OK  # nothing to do
