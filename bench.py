@@ -133,12 +133,12 @@ def main():
         return torch.cuda.Event(enable_timing=True)
 
     def ag_call(evs=None, arrival=fo.ARR_DEFAULT, links=args.links, groups=args.row_groups,
-                order=fo.ORDER_FLASH, rank=r):
+                order=fo.ORDER_FLASH, rank=r, epilogue=fo.EPI_NONE, y=None):
         o = fo.opts(order=order, links=links, row_groups=groups, arrival=arrival,
-                    kernel_events=evs)
+                    kernel_events=evs, epilogue=epilogue)
         peers = None if arrival == fo.ARR_NONE else ag_slices
-        fo.ag_gemm(ag_slices[rank], peers, ag_recv, ag_w, ag_y, P, rank, compute_stream=stream,
-                   o=o)
+        fo.ag_gemm(ag_slices[rank], peers, ag_recv, ag_w, ag_y if y is None else y, P, rank,
+                   compute_stream=stream, o=o)
 
     def rs_call(evs=None, arrival=fo.ARR_DEFAULT, links=args.links, groups=args.row_groups,
                 order=fo.ORDER_FLASH, rank=r, x=None):
@@ -258,15 +258,21 @@ def main():
         mlp_h = torch.empty((rs_case.M, rs_case.K), dtype=torch.bfloat16, device=dev)
         t_act = timed(lambda: fo.swiglu(ag_y, mlp_h, stream), reps)
 
-        def block(rank, natural):
+        def block(rank, natural, fused=False):
             g = 1 if natural else args.row_groups
             o = fo.ORDER_NATURAL if natural else fo.ORDER_FLASH
-            ag_call(order=o, groups=g, rank=rank)
-            fo.swiglu(ag_y, mlp_h, stream)
+            if fused:  # the activation in the gate+up projection's write-back
+                ag_call(order=o, groups=g, rank=rank, epilogue=fo.EPI_SWIGLU, y=mlp_h)
+            else:
+                ag_call(order=o, groups=g, rank=rank)
+                fo.swiglu(ag_y, mlp_h, stream)
             rs_call(order=o, groups=g, rank=rank, x=mlp_h)
 
+        t_ag_fused = timed(lambda: ag_call(epilogue=fo.EPI_SWIGLU, y=mlp_h), reps)
+        t_ag = timed(lambda: ag_call(), reps)
         mlp = {"swiglu_us": t_act * 1e3,
-               "swiglu_gbps": (ag_case.M * ag_case.N * 2 + rs_case.M * rs_case.K * 2) / t_act / 1e6}
+               "swiglu_gbps": (ag_case.M * ag_case.N * 2 + rs_case.M * rs_case.K * 2) / t_act / 1e6,
+               "ag_us": t_ag * 1e3, "ag_swiglu_fused_us": t_ag_fused * 1e3}
         for rb in (0, P - 1):
             tx_a = timed(lambda: fo.transfer_ref("ag", ag_slices, ag_recv, P, rb,
                                                  ag_case.m * ag_case.K * 2, stream, tw), reps)
@@ -274,14 +280,18 @@ def main():
                                                  rs_case.m * rs_case.N * 4, stream, tw), reps)
             van = t_ref_ag + tx_a + t_act + t_ref_rs + tx_r
             t_fl = timed(lambda: block(rb, False), reps)
+            t_ff = timed(lambda: block(rb, False, True), reps)
             t_ds = timed(lambda: block(rb, True), reps)
             mlp[f"rank{rb}"] = {"vanilla_us": van * 1e3, "data_slicing_us": t_ds * 1e3,
-                                "flash_us": t_fl * 1e3,
+                                "flash_us": t_fl * 1e3, "flash_fused_us": t_ff * 1e3,
                                 "latency_reduction_data_slicing": (van - t_ds) / van,
-                                "latency_reduction_flash": (van - t_fl) / van}
+                                "latency_reduction_flash": (van - t_fl) / van,
+                                "latency_reduction_flash_fused": (van - t_ff) / van}
             log(f"MLP block rank {rb}: vanilla {van*1e3:.0f} us, data slicing {t_ds*1e3:.0f} us "
-                f"({(van - t_ds) / van:.3f} less), flash {t_fl*1e3:.0f} us ({(van - t_fl) / van:.3f} less)")
-        log(f"SwiGLU {t_act*1e3:.1f} us, {mlp['swiglu_gbps']:.0f} GB/s")
+                f"({(van - t_ds) / van:.3f} less), flash {t_fl*1e3:.0f} us ({(van - t_fl) / van:.3f} "
+                f"less), flash with the fused activation {t_ff*1e3:.0f} us ({(van - t_ff) / van:.3f} less)")
+        log(f"SwiGLU {t_act*1e3:.1f} us, {mlp['swiglu_gbps']:.0f} GB/s; AG {t_ag*1e3:.0f} us, "
+            f"AG with the SwiGLU epilogue {t_ag_fused*1e3:.0f} us")
         exposure["mlp_block"] = mlp
         fo.check(stream)
         step()

@@ -161,7 +161,9 @@ fo_status check_opts(const fo_opts* o, fo_opts* out) {
     return invalid("opts.links %d outside [0, %d]", o->links, FO_MAX_P);
   if (o->row_groups < 0 || o->row_groups > fo::kMaxGroups)
     return invalid("opts.row_groups %d outside [0, %d]", o->row_groups, fo::kMaxGroups);
-  if (o->reserved[0] || o->reserved[1]) return invalid("opts.reserved must be zero");
+  if (o->epilogue != FO_EPI_NONE && o->epilogue != FO_EPI_SWIGLU)
+    return invalid("opts.epilogue %d is not a fo_epilogue", o->epilogue);
+  if (o->reserved) return invalid("opts.reserved must be zero");
   *out = *o;
   if (out->spin_timeout_us == 0) out->spin_timeout_us = kDefaultTimeoutUs;
   return FO_OK;
@@ -405,6 +407,11 @@ fo_status fo_ag_gemm(const void* x_local, const void* const* x_peer, void* x_rec
   if (s != FO_OK) return s;
   if (out_dt != FO_DT_BF16 && out_dt != FO_DT_F32) return invalid("out_dt %d is not a fo_dtype", out_dt);
   if (o.arrival == FO_ARR_LOCKSTEP) return invalid("LOCKSTEP arrivals apply to fo_gemm_rs only");
+  const bool act = o.epilogue == FO_EPI_SWIGLU;
+  if (act && (in_dt != FO_DT_BF16 || out_dt != FO_DT_BF16 || N % 16))
+    return invalid("the SwiGLU epilogue needs bf16 operands and output and N %% 16 == 0 (N %lld)",
+                   (long long)N);
+  const int64_t n_out = act ? N / 2 : N;  // columns of y
   const bool arrivals = x_peer != nullptr && o.arrival != FO_ARR_NONE && P > 1;
   const size_t es = dt_size(in_dt), os = dt_size(out_dt);
   const size_t align = in_dt == FO_DT_BF16 ? 16 : 4;
@@ -413,7 +420,7 @@ fo_status fo_ag_gemm(const void* x_local, const void* const* x_peer, void* x_rec
       !aligned(y, os))
     return invalid("misaligned buffer (inputs need %zu-byte alignment)", align);
   const size_t slice_b = (size_t)m * K * es;
-  const Range r_y = rng(y, (size_t)P * m * N * os);
+  const Range r_y = rng(y, (size_t)P * m * n_out * os);
   const Range r_recv = rng(x_recv, x_recv ? (size_t)P * slice_b : 0);
   if (overlap(r_y, rng(x_local, slice_b)) || overlap(r_y, rng(w, (size_t)K * N * es)) ||
       overlap(r_y, r_recv))
@@ -447,7 +454,7 @@ fo_status fo_ag_gemm(const void* x_local, const void* const* x_peer, void* x_rec
   for (int pos = 0; pos < P; ++pos) {
     const int sl = order[pos];
     p.a_pos[pos] = sl == rank ? x_local : (const uint8_t*)x_recv + (size_t)sl * slice_b;
-    p.c_pos[pos] = (uint8_t*)y + (size_t)sl * m * N * os;
+    p.c_pos[pos] = (uint8_t*)y + (size_t)sl * m * n_out * os;
     p.gate_slice[pos] = (arrivals && sl != rank) ? sl : -1;
   }
   p.comp_tab = call.comp_tab;
@@ -465,6 +472,7 @@ fo_status fo_ag_gemm(const void* x_local, const void* const* x_peer, void* x_rec
   p.n_recv = 0;
   p.accum_pos = -1;
   p.out_f32 = out_dt == FO_DT_F32;
+  p.act = act ? 1 : 0;
 
   hipStream_t cs = (hipStream_t)compute_stream;
   if (arrivals) p.start = call.start;
@@ -506,6 +514,7 @@ fo_status fo_gemm_rs(const void* x_shard, const void* w, float* send_buf, float*
   if (s != FO_OK) return s;
   s = check_common(P, rank, m, K, N, in_dt);
   if (s != FO_OK) return s;
+  if (o.epilogue != FO_EPI_NONE) return invalid("opts.epilogue applies to fo_ag_gemm only");
   const int arrival = o.arrival == FO_ARR_DEFAULT ? FO_ARR_LOCKSTEP : o.arrival;
   const bool arrivals = peer_partial != nullptr && arrival != FO_ARR_NONE && P > 1;
   const size_t es = dt_size(in_dt);
@@ -711,6 +720,7 @@ fo_status fo_transfer_ref(int32_t kind, const void* const* src, void* dst, int32
   fo_opts o;
   fo_status s = check_opts(opts, &o);
   if (s != FO_OK) return s;
+  if (o.epilogue != FO_EPI_NONE) return invalid("opts.epilogue applies to fo_ag_gemm only");
   if (kind != 0 && kind != 1) return invalid("kind %d is neither 0 (AG) nor 1 (RS)", kind);
   if (P < 1 || P > FO_MAX_P || rank < 0 || rank >= P) return invalid("bad P %d / rank %d", P, rank);
   if (slice_bytes < 0 || slice_bytes % 4) return invalid("slice_bytes must be a multiple of 4");

@@ -251,7 +251,7 @@ __device__ __forceinline__ void lds_barrier() {
 // position of the q-th of n memory instructions among nx issue slots (evenly spread)
 __host__ __device__ constexpr int spread_slot(int q, int n, int nx) { return (2 * q + 1) * nx / (2 * n); }
 
-template <int BM, int BN>
+template <int BM, int BN, bool ACT>
 __device__ __forceinline__ void bf16_tile(const Plan& p, const int tile, uint8_t* const lds_ring) {
   using C = Cfg<BM, BN>;
   constexpr int S = C::STAGES;
@@ -271,12 +271,17 @@ __device__ __forceinline__ void bf16_tile(const Plan& p, const int tile, uint8_t
   const int pos = uni(pos_), grp = uni(grp_), tm = uni(tm_), tn = uni(tn_);
 
   const int64_t K = p.K, N = p.N;
+  // With the SwiGLU epilogue (act) the tile's first BN/2 columns are gate columns and its last
+  // BN/2 the up columns of the same hidden units (W columns inter + ...); it writes BN/2
+  // columns of h = silu(gate) * up. col0 is the tile's first output column.
+  constexpr bool act = ACT;
+  const int64_t inter = N / 2;
   const int64_t row0 = (int64_t)tm * BM;
-  const int64_t col0 = (int64_t)tn * BN;
+  const int64_t col0 = (int64_t)tn * (act ? BN / 2 : BN);
   const int64_t rows_valid = p.m - row0;  // >= 1
   const int a_rows = uni((int)(rows_valid < BM ? rows_valid : BM));
   const uint16_t* A = (const uint16_t*)uni_ptr((const uint16_t*)p.a_pos[pos] + row0 * K);
-  const uint16_t* W = (const uint16_t*)uni_ptr((const uint16_t*)p.b + col0);
+  const uint16_t* W = (const uint16_t*)uni_ptr(p.b);
 
   // Flash-AG: rows of a received slice are read only after their group has landed.
   if (p.gate_slice[pos] >= 0) wait_groups_wg(p, p.gate_slice + pos, 1, grp);
@@ -302,7 +307,18 @@ __device__ __forceinline__ void bf16_tile(const Plan& p, const int tile, uint8_t
     const int P = (wave * C::B_LOADS + j) * 1024 + lane * 16;
     const int kr = P / C::B_ROW;
     const int n = ((((P % C::B_ROW) >> 4) ^ swz_b(kr))) * 8;
-    b_voff[j] = col0 + n < N ? (uint32_t)(((int64_t)kr * N + n) * 2) : kOOB;
+    int64_t wc;  // W column of tile column n
+    bool ok;
+    if constexpr (act) {
+      const int half = n >= BN / 2 ? 1 : 0;
+      const int64_t c = col0 + n - half * (BN / 2);
+      ok = c < inter;
+      wc = c + half * inter;
+    } else {
+      wc = col0 + n;
+      ok = wc < N;
+    }
+    b_voff[j] = ok ? (uint32_t)(((int64_t)kr * N + wc) * 2) : kOOB;
   }
 
   // load number l (A loads first, then W loads) of K step kt into stage si (0..S-1); rb is W's
@@ -518,8 +534,9 @@ __device__ __forceinline__ void bf16_tile(const Plan& p, const int tile, uint8_t
   constexpr int BATCH = CPT < 4 ? CPT : 4;      // chunks whose partial loads are in flight together
   const int esz = p.out_f32 ? 4 : 2;
   const uint32_t nn = (uint32_t)N;
+  const int64_t n_out = act ? inter : N;  // output row stride
   const __amdgpu_buffer_rsrc_t out_res =
-      buffer_res((const uint8_t*)p.c_pos[pos] + row0 * N * esz, (uint32_t)a_rows * nn * esz);
+      buffer_res((const uint8_t*)p.c_pos[pos] + row0 * n_out * esz, (uint32_t)(a_rows * n_out * esz));
   // Chunk b of this thread in a block is chunk b * kThreads + tid: row b * (kThreads / CPR) +
   // tid / CPR, the same 4 columns for every b. Its element offset is e0 + b * e_step (e0 for the
   // block's first row); a thread whose columns lie past N stores nowhere (kOOB).
@@ -554,6 +571,32 @@ __device__ __forceinline__ void bf16_tile(const Plan& p, const int tile, uint8_t
       }
     }
     lds_barrier();
+    if constexpr (act) {
+      // h = silu(gate) * up: gate in staging columns [0, BN/2), up in [BN/2, BN); BN/2 output
+      // columns of h (row stride inter), 4 per chunk
+      constexpr int CPRA = BN / 8, RPBA = kThreads / CPRA, CPTA = ER * CPRA / kThreads;
+      static_assert(kThreads % CPRA == 0 && CPTA >= 1 && (ER * CPRA) % kThreads == 0, "act chunks");
+      const uint32_t gca = (uint32_t)col0 + (tid % CPRA) * 4;
+      const bool oka = gca < (uint32_t)inter;
+      // the block's byte offset, behind an empty asm like the LDS offsets (else the compiler
+      // precomputes every chunk's offset at kernel start and spills them)
+      uint32_t va = ((uint32_t)(blk * ER + tid / CPRA) * (uint32_t)inter + gca) * 2;
+      int ep_a = (tid / CPRA) * EW + (tid % CPRA) * 4;
+      asm volatile("" : "+v"(ep_a), "+v"(va));
+      const uint32_t va_step = (uint32_t)RPBA * (uint32_t)inter * 2;
+#pragma unroll
+      for (int b = 0; b < CPTA; ++b) {
+        const float4 g = *(const float4*)(ep + ep_a + b * RPBA * EW);
+        const float4 u = *(const float4*)(ep + ep_a + b * RPBA * EW + BN / 2);
+        const uint32_t lo = cvt_bf16x2(silu_mul(g.x, u.x), silu_mul(g.y, u.y));
+        const uint32_t hi = cvt_bf16x2(silu_mul(g.z, u.z), silu_mul(g.w, u.w));
+        const uint32_t off = oka ? va + (uint32_t)b * va_step : kOOB;
+        __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)lo, (int)hi}, out_res, off, 0, 0);
+        if (b % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+      }
+      lds_barrier();
+      continue;
+    }
     const uint32_t e0 = (uint32_t)(blk * ER + tid / CPR) * nn + gcol;
     auto chunk_off = [&](int b, int scale) -> uint32_t {
       return col_ok ? (e0 + b * e_step) * scale : kOOB;
@@ -633,12 +676,13 @@ __device__ __forceinline__ void release_start(const Plan& p) {
 
 // One workgroup per tile, or (grid smaller than the tile count) a persistent grid whose
 // workgroups walk the tiles with a stride of the grid size, in the same order.
-template <int BM, int BN>
+template <int BM, int BN, bool ACT>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(Plan p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds_ring[Cfg<BM, BN>::LDS];
   release_start(p);
   const int total = p.grid.npos * p.grid.tiles_m * p.grid.tiles_n;
-  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) bf16_tile<BM, BN>(p, tile, lds_ring);
+  for (int tile = blockIdx.x; tile < total; tile += gridDim.x)
+    bf16_tile<BM, BN, ACT>(p, tile, lds_ring);
 }
 
 // ---------------------------------------------------------------- fp32 kernel ----------------
@@ -720,7 +764,12 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(Plan p) {
 
 template <int BM, int BN>
 hipError_t launch_bf16(const Plan& p, int64_t grid, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN>), dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+  if (p.act)
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, true>), dim3((unsigned)grid), dim3(kThreads), 0,
+                       s, p);
+  else
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, false>), dim3((unsigned)grid), dim3(kThreads), 0,
+                       s, p);
   return hipGetLastError();
 }
 
@@ -894,6 +943,8 @@ static bool plan_ok(const Plan& p) {
     if (p.gate_slice[i] >= FO_MAX_P || (p.gate_slice[i] >= 0 && p.comp_tab == nullptr)) return false;
   if (p.accum_pos >= g.npos || p.n_recv < 0 || p.n_recv > FO_MAX_P) return false;
   if (p.accum_pos >= 0 && !p.out_f32) return false;  // partials are added in fp32 output only
+  // the SwiGLU epilogue: bf16 output, no added partials, gate and up halves of 8-column chunks
+  if (p.act && (p.out_f32 || p.accum_pos >= 0 || p.N % 16 != 0)) return false;
   if (p.accum_pos >= 0)
     for (int i = 0; i < p.n_recv; ++i)
       if (p.recv_slice[i] >= FO_MAX_P || (p.recv_slice[i] >= 0 && p.comp_tab == nullptr))
@@ -905,6 +956,7 @@ hipError_t launch_gemm(const Plan& p, int in_dt, int tile, hipStream_t s) {
   if (!plan_ok(p)) return hipErrorInvalidValue;
   const int64_t grid = (int64_t)p.grid.npos * p.grid.tiles_m * p.grid.tiles_n;
   if (in_dt == FO_DT_F32) {
+    if (p.act) return hipErrorInvalidValue;  // the fp32 kernel has no SwiGLU epilogue
     hipLaunchKernelGGL(gemm_f32_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
     return hipGetLastError();
   }

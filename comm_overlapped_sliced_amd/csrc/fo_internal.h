@@ -42,6 +42,7 @@ struct Plan {
   uint32_t* lead;                    // [slice][group]: the last call whose poller is elected
   uint32_t* ready;                   // [slice][group]: the last call whose group has landed
   uint32_t gen;                      // this call's number (> 0, grows by one per call)
+  int32_t act;                       // 1: SwiGLU epilogue (Flash-AG of the MLP block's gate+up)
   int64_t* start;                    // the call's start signal value, stored 0 at kernel start
                                      // (null: no copies wait for this kernel)
   uint64_t spin_limit;               // bound of each wait, in wall-clock ticks
@@ -61,6 +62,7 @@ inline Plan empty_plan() {
   }
   p.accum_pos = -1;
   p.start = nullptr;
+  p.act = 0;
   return p;
 }
 
@@ -109,6 +111,10 @@ struct ReduceArgs {
   uint32_t go_value;               // partial has landed; the other blocks wait on it
 };
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);
+
+// silu(g) * u = g / (1 + e^-g) * u in fp32: the SwiGLU of the MLP block (fo_swiglu and the
+// GEMM's SwiGLU epilogue compute it the same way)
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
 // h[rows, inter] = silu(y[:, :inter]) * y[:, inter:] in bf16 (fp32 arithmetic, one rounding to
 // nearest even); y is [rows, 2*inter] bf16. inter % 8 == 0, both 16-byte aligned.

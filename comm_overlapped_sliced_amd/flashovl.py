@@ -18,6 +18,7 @@ BF16, F32 = 0, 1
 ORDER_FLASH, ORDER_NATURAL = 0, 1
 ARR_DEFAULT, ARR_NONE, ARR_EAGER, ARR_LOCKSTEP = 0, 1, 2, 3
 TILE_AUTO, TILE_256x256, TILE_256x128, TILE_128x256, TILE_128x128, TILE_64x64 = range(6)
+EPI_NONE, EPI_SWIGLU = 0, 1
 MAX_P = 32
 MAX_GROUPS = 8
 
@@ -36,7 +37,8 @@ class Opts(ctypes.Structure):
     _fields_ = [("order", ctypes.c_int32), ("arrival", ctypes.c_int32),
                 ("tile", ctypes.c_int32), ("spin_timeout_us", ctypes.c_uint32),
                 ("links", ctypes.c_int32), ("row_groups", ctypes.c_int32),
-                ("kernel_events", ctypes.c_void_p * 2), ("reserved", ctypes.c_int32 * 2)]
+                ("kernel_events", ctypes.c_void_p * 2), ("epilogue", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 _lib = None
@@ -94,11 +96,11 @@ def _raise_on(status: int, where: str) -> None:
 
 
 def opts(order=ORDER_FLASH, arrival=ARR_DEFAULT, tile=TILE_AUTO, spin_timeout_us=0, links=0,
-         row_groups=0, kernel_events=None) -> Opts:
+         row_groups=0, kernel_events=None, epilogue=EPI_NONE) -> Opts:
     o = Opts()
     load().fo_opts_init(ctypes.byref(o))
     o.order, o.arrival, o.tile, o.links = order, arrival, tile, links
-    o.row_groups = row_groups
+    o.row_groups, o.epilogue = row_groups, epilogue
     if spin_timeout_us:
         o.spin_timeout_us = spin_timeout_us
     if kernel_events is not None:
@@ -149,7 +151,8 @@ def _ptr_array(ptrs):
 def ag_gemm(x_local, x_peer, x_recv, w, y, P: int, rank: int, compute_stream=None,
             o: Opts | None = None, raw: bool = False):
     """Flash-AG (fo_ag_gemm). x_local [m, K], x_peer list of P tensors (or None), x_recv
-    [P*m, K], w [K, N], y [P*m, N]. Returns the status when raw=True, else raises on error."""
+    [P*m, K], w [K, N], y [P*m, N] ([P*m, N/2] with the SwiGLU epilogue). Returns the status
+    when raw=True, else raises on error."""
     m, K = x_local.shape
     N = w.shape[1]
     peers = None if x_peer is None else _ptr_array(x_peer)

@@ -95,6 +95,13 @@ typedef enum fo_tile {
   FO_TILE_64x64 = 5
 } fo_tile;
 
+/* Epilogue of fo_ag_gemm. NONE: y = X . W. SWIGLU: the gate+up projection of the MLP block with
+   its activation fused into the write-back: W is [K, N] with the gate projection in columns
+   [0, N/2) and the up projection in [N/2, N); y receives h = silu(X . W_gate) * (X . W_up),
+   [P*m, N/2] bf16, from the fp32 accumulators (one rounding; fo_swiglu on a bf16 y rounds
+   twice). Needs bf16 operands and output and N a multiple of 16. */
+typedef enum fo_epilogue { FO_EPI_NONE = 0, FO_EPI_SWIGLU = 1 } fo_epilogue;
+
 typedef struct fo_opts {
   int32_t order;            /* fo_order */
   int32_t arrival;          /* fo_arrival */
@@ -116,7 +123,8 @@ typedef struct fo_opts {
                                FO_MAX_GROUPS */
   void* kernel_events[2];   /* optional hipEvent_t pair recorded on the compute stream right
                                before and right after the GEMM kernel launch (profiling) */
-  int32_t reserved[2];      /* must be zero */
+  int32_t epilogue;         /* fo_epilogue (fo_ag_gemm only; else FO_ERR_INVALID_ARG) */
+  int32_t reserved;         /* must be zero */
 } fo_opts;
 
 /* Fills *o with the defaults (FLASH order, DEFAULT arrival, AUTO tile, 2 s bound, one link per
@@ -131,7 +139,8 @@ void fo_opts_init(fo_opts* o);
  *   x_recv   device [P*m, K] in_dt receive buffer; slice s arrives at x_recv + s*m*K. The rows of
  *            slice `rank` are neither read nor written.
  *   w        device [K, N] in_dt, this rank's column shard of the weight.
- *   y        device [P*m, N] out_dt; rows s*m .. s*m+m-1 hold X_s . W.
+ *   y        device [P*m, N] out_dt; rows s*m .. s*m+m-1 hold X_s . W (with opts.epilogue
+ *            FO_EPI_SWIGLU: [P*m, N/2] bf16 holding silu(X_s . W_gate) * (X_s . W_up)).
  * Slices are computed in the Flash-AG order (rank, rank-1, ..., rank-P+1 mod P); slice s != rank
  * is read only after its transfer has landed. in_dt and out_dt: BF16 or F32; out_dt BF16
  * rounds the fp32 accumulator to nearest-even. No output may overlap an input.

@@ -95,11 +95,12 @@ class Oracle:
                                                vp]
         lib.oracle_num_threads.argtypes = []
         lib.oracle_swiglu.argtypes = [vp, i64, i64, vp]
+        lib.oracle_swiglu_f64.argtypes = [vp, i64, i64, vp]
         lib.oracle_round_bf16.argtypes = [vp, i64, vp]
         for f in (lib.oracle_ag_order, lib.oracle_rs_order, lib.oracle_gemm, lib.oracle_ag,
                   lib.oracle_rs, lib.oracle_ag_sampled, lib.oracle_rs_sampled,
                   lib.oracle_rs_send_sampled, lib.oracle_num_threads, lib.oracle_swiglu,
-                  lib.oracle_round_bf16):
+                  lib.oracle_swiglu_f64, lib.oracle_round_bf16):
             f.restype = ctypes.c_int
         self.lib = lib
         self.path = path
@@ -221,13 +222,15 @@ class Oracle:
     # ---- the MLP block ------------------------------------------------------------------
 
     def swiglu(self, y: np.ndarray) -> np.ndarray:
-        """h = silu(y[:, :inter]) * y[:, inter:] in fp64; y bf16 bits [rows, 2*inter]."""
+        """h = silu(y[:, :inter]) * y[:, inter:] in fp64; y bf16 bits (uint16) or fp64
+        [rows, 2*inter]."""
         y = _c(y)
-        if y.dtype != np.uint16 or y.ndim != 2 or y.shape[1] % 2:
-            raise ValueError("y is bf16 bits [rows, 2*inter]")
+        if y.dtype not in (np.uint16, np.float64) or y.ndim != 2 or y.shape[1] % 2:
+            raise ValueError("y is bf16 bits or fp64 [rows, 2*inter]")
         rows, inter = y.shape[0], y.shape[1] // 2
         h = np.empty((rows, inter), dtype=np.float64)
-        _check(self.lib.oracle_swiglu(_ptr(y), rows, inter, _ptr(h)), "swiglu")
+        fn = self.lib.oracle_swiglu if y.dtype == np.uint16 else self.lib.oracle_swiglu_f64
+        _check(fn(_ptr(y), rows, inter, _ptr(h)), "swiglu")
         return h
 
     def round_bf16(self, x: np.ndarray) -> np.ndarray:
@@ -238,10 +241,13 @@ class Oracle:
         return out
 
     def mlp_block(self, x_slices, w_gu: np.ndarray, w_down: np.ndarray, partials, P: int,
-                  r: int) -> np.ndarray:
+                  r: int, fused: bool = False) -> np.ndarray:
         """Rank r's output of the MLP block: Y = Flash-AG(x_slices, w_gu) rounded to bf16,
-        H = swiglu(Y) rounded to bf16, then Flash-RS(H, w_down, partials) (fp64 [m, N])."""
-        y = self.round_bf16(self.ag(x_slices, w_gu, P, r))
+        H = swiglu(Y) rounded to bf16, then Flash-RS(H, w_down, partials) (fp64 [m, N]).
+        fused: the activation reads Y before any rounding (H is still rounded to bf16)."""
+        y = self.ag(x_slices, w_gu, P, r)
+        if not fused:
+            y = self.round_bf16(y)
         h = self.round_bf16(self.swiglu(y))
         return self.rs(h, w_down, partials, P, r)
 

@@ -276,6 +276,20 @@ int oracle_swiglu(const uint16_t* y, int64_t rows, int64_t inter, double* h) {
   return 0;
 }
 
+/* The same activation on an fp64 y [rows, 2*inter] (gate half, then up half): the fused form,
+   where the activation reads the projection's sums before any rounding. */
+int oracle_swiglu_f64(const double* y, int64_t rows, int64_t inter, double* h) {
+  if (!y || !h || rows < 0 || inter < 0) return 1;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t j = 0; j < inter; ++j) {
+      const double g = y[r * 2 * inter + j];
+      const double u = y[r * 2 * inter + inter + j];
+      h[r * inter + j] = g / (1.0 + exp(-g)) * u;
+    }
+  return 0;
+}
+
 /* x rounded to 8 significant bits (the bf16 precision), to nearest, ties to even, written as
    bf16 bit patterns. For finite x within bf16's normal range (or zero): x = f * 2^e with
    0.5 <= |f| < 1, f * 2^8 is rounded to an integer (nearbyint rounds ties to even in the default

@@ -48,7 +48,7 @@ def test_opts_defaults():
     assert (o.order, o.arrival, o.tile, o.links) == (0, 0, 0, 0)
     assert o.spin_timeout_us == 2_000_000
     assert list(o.kernel_events) == [None, None]
-    assert o.row_groups == 0 and list(o.reserved) == [0, 0]
+    assert o.row_groups == 0 and o.epilogue == fo.EPI_NONE and o.reserved == 0
     assert ctypes.sizeof(fo.Opts) == 48
 
 
@@ -134,15 +134,30 @@ def test_ag_rejects(lib, kw):
 
 def test_ag_rejects_bad_opts(lib):
     for field, val in [("order", 9), ("arrival", 7), ("tile", 11), ("links", 33), ("links", -1),
-                       ("row_groups", 9), ("row_groups", -1)]:
+                       ("row_groups", 9), ("row_groups", -1), ("epilogue", 2),
+                       ("epilogue", -1), ("reserved", 1)]:
         o = fo.opts()
         setattr(o, field, val)
         assert _ag(lib, opts=ctypes.byref(o)) == fo.FO_ERR_INVALID_ARG
-    o = fo.opts()
-    o.reserved[1] = 1
-    assert _ag(lib, opts=ctypes.byref(o)) == fo.FO_ERR_INVALID_ARG
     o = fo.opts(arrival=fo.ARR_LOCKSTEP)
     assert _ag(lib, opts=ctypes.byref(o)) == fo.FO_ERR_INVALID_ARG
+
+
+def test_ag_swiglu_epilogue_rejects(lib):
+    # the fused SwiGLU write-back needs bf16 in and out and N a multiple of 16
+    o = ctypes.byref(fo.opts(epilogue=fo.EPI_SWIGLU))
+    assert _ag(lib, opts=o, out_dt=fo.F32) == fo.FO_ERR_INVALID_ARG
+    assert _ag(lib, opts=o, in_dt=fo.F32, out_dt=fo.F32) == fo.FO_ERR_INVALID_ARG
+    assert _ag(lib, opts=o, N=520) == fo.FO_ERR_INVALID_ARG
+    assert "SwiGLU" in lib.fo_last_error().decode()
+    # y is [P*m, N/2] bf16: one that reaches into x_recv is rejected; m = 0 is a no-op
+    half = 4 * 64 * 256 * 2
+    assert _ag(lib, opts=o, y=B - half + 16) == fo.FO_ERR_INVALID_ARG
+    assert _ag(lib, opts=o, m=0) == fo.FO_OK
+    assert _rs(lib, opts=o) == fo.FO_ERR_INVALID_ARG
+    src = (ctypes.c_void_p * 4)(0x50000000, 0x60000000, 0x70000000, 0x78000000)
+    assert lib.fo_transfer_ref(0, ctypes.cast(src, ctypes.c_void_p), B, 4, 0, 4096, None,
+                               o) == fo.FO_ERR_INVALID_ARG
 
 
 def test_ag_empty_is_a_no_op(lib):

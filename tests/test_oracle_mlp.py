@@ -58,10 +58,17 @@ def _bits(vals):
     return (np.asarray(vals, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
 
 
-def test_swiglu_closed_forms():
+def _enc(vals, form):
+    """A y row as bf16 bits or as fp64 (the two input forms of the activation)."""
+    v = np.asarray(vals, dtype=np.float32)
+    return _bits(v) if form == "bf16" else v.astype(np.float64)
+
+
+@pytest.mark.parametrize("form", ["bf16", "f64"])
+def test_swiglu_closed_forms(form):
     g = np.array([0.0, 1.0, -1.0, 2.5, -2.5, 30.0, -30.0, 0.125], dtype=np.float32)
     ones = np.ones_like(g)
-    y = np.stack([_bits(np.concatenate([g, ones]))])          # gate = g, up = 1
+    y = np.stack([_enc(np.concatenate([g, ones]), form)])     # gate = g, up = 1
     h = oracle.swiglu(y)[0]
     assert h[0] == 0.0                                          # silu(0) = 0
     assert h[1] == pytest.approx(1.0 / (1.0 + np.exp(-1.0)), rel=1e-15)
@@ -70,7 +77,7 @@ def test_swiglu_closed_forms():
     assert h[5] == pytest.approx(30.0, rel=1e-12) and abs(h[6]) < 1e-11
     # the up half multiplies: gate = 1, up = v gives silu(1) * v
     v = np.array([3.0, -0.5, 0.0, 8.0], dtype=np.float32)
-    y2 = np.stack([_bits(np.concatenate([np.ones(4, np.float32), v]))])
+    y2 = np.stack([_enc(np.concatenate([np.ones(4, np.float32), v]), form)])
     assert np.allclose(oracle.swiglu(y2)[0], v / (1.0 + np.exp(-1.0)), rtol=1e-15, atol=0)
 
 
@@ -105,3 +112,30 @@ def test_mlp_block_is_the_three_steps():
         full = dec(hb) @ dec(w_d)
         expect = full[r * m:(r + 1) * m] + sum(parts[q].astype(np.float64) for q in range(P) if q != r)
         assert np.allclose(oracle.mlp_block(xs, w_gu, w_d, parts, P, r), expect, rtol=1e-12, atol=1e-12)
+
+
+def test_swiglu_f64_reads_unrounded_values():
+    # 1 + 2^-10 has no bf16 form: the fp64 input keeps it (silu(g) * 1 with g = 1 + 2^-10)
+    g = 1 + 2.0**-10
+    h = oracle.swiglu(np.array([[g, 1.0]]))[0, 0]
+    assert h == pytest.approx(g / (1 + np.exp(-g)), rel=1e-15)
+    assert h != pytest.approx(1 / (1 + np.exp(-1.0)), rel=1e-6)
+
+
+def test_mlp_block_fused_skips_the_y_rounding():
+    """fused=True: SwiGLU reads the unrounded fp64 projection, only H is rounded to bf16."""
+    rng = np.random.default_rng(19)
+    P, m, K, inter, N = 2, 3, 8, 4, 5
+    xs = [_bits(rng.normal(0, 1, (m, K))) for _ in range(P)]
+    w_gu = _bits(rng.normal(0, 0.3, (K, 2 * inter)))
+    w_d = _bits(rng.normal(0, 0.3, (inter, N)))
+    parts = [rng.normal(0, 1, (m, N)).astype(np.float32) for _ in range(P)]
+    dec = lambda b: (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    for r in range(P):
+        y = np.concatenate([dec(x) for x in xs]) @ dec(w_gu)
+        g, u = y[:, :inter], y[:, inter:]
+        hb = _nearest_bf16_brute((g / (1 + np.exp(-g)) * u).ravel()).reshape(g.shape)
+        full = dec(hb) @ dec(w_d)
+        expect = full[r * m:(r + 1) * m] + sum(parts[q].astype(np.float64) for q in range(P) if q != r)
+        got = oracle.mlp_block(xs, w_gu, w_d, parts, P, r, fused=True)
+        assert np.allclose(got, expect, rtol=1e-12, atol=1e-12)
