@@ -112,9 +112,16 @@ struct ReduceArgs {
 };
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);
 
-// silu(g) * u = g / (1 + e^-g) * u in fp32: the SwiGLU of the MLP block (fo_swiglu and the
-// GEMM's SwiGLU epilogue compute it the same way)
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+// silu(g) * u = g * u / (1 + e^-g) in fp32: the SwiGLU of the MLP block (fo_swiglu and the
+// GEMM's SwiGLU epilogue compute it the same way). e^-g = 2^(-g log2 e) by the hardware exp2 and
+// the quotient by the hardware reciprocal (each about 1 ulp of fp32, far below the bf16 rounding
+// that follows) instead of an IEEE division, whose fix-up sequence costs the epilogue several
+// times more VALU work. Large |g|: 2^(+big) = inf gives a reciprocal of 0 and h = 0; 2^(-big) =
+// 0 gives h = g * u.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  const float e = __builtin_amdgcn_exp2f(g * -1.44269504088896341f);
+  return g * u * __builtin_amdgcn_rcpf(1.0f + e);
+}
 
 // h[rows, inter] = silu(y[:, :inter]) * y[:, inter:] in bf16 (fp32 arithmetic, one rounding to
 // nearest even); y is [rows, 2*inter] bf16. inter % 8 == 0, both 16-byte aligned.
