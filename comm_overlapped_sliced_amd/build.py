@@ -9,7 +9,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libflashovl.so")
-SOURCES = ["fo_api.cpp", "fo_dma.cpp", "fo_sched.cpp", "fo_gemm.hip", "fo_mlp.hip"]
+SOURCES = ["fo_api.cpp", "fo_dma.cpp", "fo_sched.cpp", "fo_gemm.hip", "fo_mlp.hip", "fo_attn.hip"]
 ARCH = "gfx950"
 
 

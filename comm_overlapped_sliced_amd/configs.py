@@ -75,3 +75,42 @@ def scaled(case: Case, **kw) -> Case:
     d = {f: getattr(case, f) for f in case.__dataclass_fields__}
     d.update(kw)
     return Case(**d)
+
+
+@dataclass(frozen=True)
+class AttnCase:
+    """One rank's share of attention under Ulysses (sequence) parallelism: after the All-to-All
+    the rank holds hq query heads and hkv key/value heads of the whole sequence of S = P*m
+    tokens, as P slices of m tokens (one per peer)."""
+    config: int
+    P: int
+    S: int
+    hq: int
+    hkv: int
+    head_dim: int = 128
+    causal: bool = True
+    name: str = ""
+
+    @property
+    def m(self) -> int:
+        return self.S // self.P
+
+    @property
+    def row(self) -> int:
+        """Values per token row: [hq query heads | hkv key heads | hkv value heads] x head_dim."""
+        return (self.hq + 2 * self.hkv) * self.head_dim
+
+    @property
+    def flops(self) -> int:
+        """Score and value products over the (query, key) pairs attended (causal: j <= i)."""
+        pairs = self.S * (self.S + 1) // 2 if self.causal else self.S * self.S
+        return 4 * pairs * self.head_dim * self.hq
+
+    def qkv(self) -> np.ndarray:
+        """The gathered QKV rows [S, row] bf16: N(0, 1) queries, keys and values."""
+        return inputs.draw(self.config, inputs.X_ID, (self.S, self.row), _N01, "bf16")
+
+
+# Llama-3.1-70B attention (64 query heads, 8 key/value heads, head_dim 128) under Ulysses
+# parallelism over 8 ranks: 8 query heads and 1 key/value head per rank, causal, 8K tokens
+L70B_ATTN = AttnCase(6, 8, 8192, 8, 1, name="Llama-3.1-70B attention, Ulysses 8 rank share, seq 8192")

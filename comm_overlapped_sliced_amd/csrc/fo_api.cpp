@@ -13,6 +13,7 @@
 #include <hip/hip_ext.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -42,6 +43,16 @@ fo_status invalid(const char* fmt, ...) {
   va_end(ap);
   g_last_error = buf;
   return FO_ERR_INVALID_ARG;
+}
+
+fo_status unsupported(const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return FO_ERR_UNSUPPORTED;
 }
 
 #define FO_HIP(call)                                                              \
@@ -712,6 +723,140 @@ fo_status fo_swiglu(const void* y, void* h, int64_t rows, int64_t inter, void* s
   if (overlap(rng(y, (size_t)rows * 2 * inter * 2), rng(h, (size_t)rows * inter * 2)))
     return invalid("h overlaps y");
   FO_HIP(fo::launch_swiglu(y, h, rows, inter, (hipStream_t)stream));
+  return FO_OK;
+}
+
+// Shapes of the attention calls: head_dim 128 only, whole query heads per key head (GQA), and
+// 32-bit byte offsets inside one slice of rows.
+static fo_status check_attn(int32_t P, int32_t rank, int64_t m, int32_t hq, int32_t hkv,
+                            int32_t head_dim, int32_t causal) {
+  if (P < 1 || P > FO_MAX_P || rank < 0 || rank >= P) return invalid("bad P %d / rank %d", P, rank);
+  if (m < 0) return invalid("negative m %lld", (long long)m);
+  if (hq < 1 || hkv < 1 || hq % hkv) return invalid("hq %d must be a positive multiple of hkv %d", hq, hkv);
+  if (causal != 0 && causal != 1) return invalid("causal must be 0 or 1");
+  if (head_dim != 128) return unsupported("head_dim %d (the attention kernel is built for 128)", head_dim);
+  const int64_t W = (int64_t)(hq + 2 * hkv) * 256;
+  if ((m + 128) * W >= ((int64_t)1 << 31)) return invalid("a slice of rows is too large");
+  return FO_OK;
+}
+
+static fo_status launch_attn_events(const fo::AttnPlan& p, hipStream_t cs, const fo_opts& o) {
+  if (o.kernel_events[0]) FO_HIP(hipEventRecord((hipEvent_t)o.kernel_events[0], cs));
+  FO_HIP(fo::launch_attn(p, cs));
+  if (o.kernel_events[1]) FO_HIP(hipEventRecord((hipEvent_t)o.kernel_events[1], cs));
+  return FO_OK;
+}
+
+fo_status fo_attn(const void* qkv_local, const void* const* qkv_peer, void* qkv_recv, void* out,
+                  int32_t P, int32_t rank, int64_t m, int32_t hq, int32_t hkv, int32_t head_dim,
+                  int32_t causal, void* compute_stream, const fo_opts* opts) {
+  fo_opts o;
+  fo_status s = check_opts(opts, &o);
+  if (s != FO_OK) return s;
+  s = check_attn(P, rank, m, hq, hkv, head_dim, causal);
+  if (s != FO_OK) return s;
+  if (o.arrival == FO_ARR_LOCKSTEP) return invalid("LOCKSTEP arrivals apply to fo_gemm_rs only");
+  if (o.tile != FO_TILE_AUTO) return invalid("opts.tile applies to the GEMM calls only");
+  if (o.row_groups > 1) return invalid("fo_attn transfers whole slices (opts.row_groups 0 or 1)");
+  if (o.epilogue != FO_EPI_NONE) return invalid("opts.epilogue applies to fo_ag_gemm only");
+  const bool arrivals = qkv_peer != nullptr && o.arrival != FO_ARR_NONE && P > 1;
+  const size_t W = (size_t)(hq + 2 * hkv) * 256, slice_b = (size_t)m * W;
+  if (!qkv_local || !out || (P > 1 && !qkv_recv)) return invalid("NULL buffer");
+  if (!aligned(qkv_local, 16) || !aligned(out, 16) || (qkv_recv && !aligned(qkv_recv, 16)))
+    return invalid("misaligned buffer (16-byte alignment)");
+  const Range r_out = rng(out, (size_t)P * m * hq * 256);
+  const Range r_recv = rng(qkv_recv, qkv_recv ? (size_t)P * slice_b : 0);
+  if (overlap(r_out, rng(qkv_local, slice_b)) || overlap(r_out, r_recv))
+    return invalid("out overlaps an input");
+  if (arrivals) {
+    for (int q = 0; q < P; ++q) {
+      if (q == rank) continue;
+      if (!qkv_peer[q]) return invalid("qkv_peer[%d] is NULL", q);
+      if (!aligned(qkv_peer[q], 16)) return invalid("qkv_peer[%d] misaligned", q);
+      const Range rp = rng(qkv_peer[q], slice_b);
+      if (overlap(rp, r_recv) || overlap(rp, r_out)) return invalid("qkv_peer[%d] overlaps qkv_recv or out", q);
+    }
+  }
+  if (m == 0) return FO_OK;
+
+  DevState* st = nullptr;
+  std::unique_lock<std::mutex> lk;
+  s = current_state(&st, &lk);
+  if (s != FO_OK) return s;
+  fo::AttnPlan p{};
+  fo::dma::Call call{};
+  if (arrivals) FO_DMA(fo::dma::begin(st->dev, P, 1, &call, &e_));
+  int32_t order[FO_MAX_P];
+  fo::slice_order(0, o.order, P, rank, order);
+  for (int i = 0; i < P; ++i) {
+    p.order[i] = order[i];
+    p.slice[i] = i == rank ? qkv_local : (const uint8_t*)qkv_recv + (size_t)i * slice_b;
+    p.gated[i] = (arrivals && i != rank) ? 1 : 0;
+  }
+  p.out = out;
+  p.comp_tab = call.comp_tab;
+  p.lead = st->arr_lead;
+  p.ready = st->arr_ready;
+  p.gen = ++st->gen;
+  p.err = st->err;
+  p.spin_limit = spin_ticks(*st, o.spin_timeout_us);
+  p.m = m;
+  p.P = P;
+  p.hq = hq;
+  p.hkv = hkv;
+  p.causal = causal;
+  p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
+
+  hipStream_t cs = (hipStream_t)compute_stream;
+  if (arrivals) p.start = call.start;
+  s = order_after_last(st, cs);
+  if (s != FO_OK) return s;
+  s = launch_attn_events(p, cs, o);
+  if (s != FO_OK) return s;
+  hipEvent_t slot_ev = nullptr;
+  if (arrivals) FO_DMA(fo::dma::end(st->dev, call, cs, &e_, &slot_ev));
+  s = mark_last(st, cs, slot_ev);
+  if (s != FO_OK) return s;
+  if (arrivals) {
+    int seq[FO_MAX_P];
+    const int n = arrival_sequence(0, o.order, P, rank, seq);
+    const int L = links_for(o, P);
+    for (int t = 0; t < n; ++t) {
+      const int sl = seq[t];
+      FO_DMA(fo::dma::copy(st->dev, call, t % L, sl, 0, -1, (uint8_t*)qkv_recv + (size_t)sl * slice_b,
+                           qkv_peer[sl], slice_b, &e_));
+    }
+  }
+  return FO_OK;
+}
+
+fo_status fo_attn_ref(const void* qkv, void* out, int64_t S, int32_t hq, int32_t hkv,
+                      int32_t head_dim, int32_t causal, void* stream) {
+  fo_status s = check_attn(1, 0, S, hq, hkv, head_dim, causal);
+  if (s != FO_OK) return s;
+  if (!qkv || !out) return invalid("NULL buffer");
+  if (!aligned(qkv, 16) || !aligned(out, 16)) return invalid("misaligned buffer (16-byte alignment)");
+  if (overlap(rng(out, (size_t)S * hq * 256), rng(qkv, (size_t)S * (hq + 2 * hkv) * 256)))
+    return invalid("out overlaps qkv");
+  if (S == 0) return FO_OK;
+  DevState* st = nullptr;
+  std::unique_lock<std::mutex> lk;
+  s = current_state(&st, &lk);
+  if (s != FO_OK) return s;
+  fo::AttnPlan p{};
+  p.order[0] = 0;
+  p.slice[0] = qkv;
+  p.gated[0] = 0;
+  p.out = out;
+  p.err = st->err;
+  p.spin_limit = spin_ticks(*st, kDefaultTimeoutUs);
+  p.m = S;
+  p.P = 1;
+  p.hq = hq;
+  p.hkv = hkv;
+  p.causal = causal;
+  p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
+  FO_HIP(fo::launch_attn(p, (hipStream_t)stream));
   return FO_OK;
 }
 

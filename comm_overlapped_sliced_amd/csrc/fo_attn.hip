@@ -1,0 +1,340 @@
+// Query-split attention behind a Flash All-to-All: one rank's share of Ulysses (sequence)
+// parallelism on MI355X (gfx950).
+//
+// The FlashOverlap page (gist.science paper 2604.24013), technical summary §2 "Methodology",
+// extends the sliced overlap in two ways: attention computed by query slices, for overlap at a
+// finer grain, and the All-to-All of Ulysses parallelism decomposed like the All-Gather. After
+// the All-to-All a rank holds, for its own heads, the query, key and value rows of every peer's
+// sequence chunk (slice s = sequence positions s*m .. s*m+m-1). Here the slices arrive one by
+// one (emulated copies, as for Flash-AG) and the attention runs by query slices: a workgroup
+// takes 128 queries of one head of slice s as soon as slice s has landed, and walks the key
+// slices in arrival order, waiting for each one (with causal masking only the slices j <= s). The
+// online softmax makes the order of the key slices irrelevant up to rounding.
+//
+// Kernel design (CDNA4):
+// - One workgroup per (slice, 128-query tile, head): 4 waves of 32 queries; key tiles of 64.
+// - Scores are computed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16, K from LDS as the A
+//   operand, Q in registers as the B operand), so that each lane owns one query: the softmax
+//   row state (running max and sum) is per lane, and a row reduction needs one cross-lane swap.
+// - The output is accumulated transposed too, O^T += V^T P^T: the probabilities go from the
+//   score accumulators straight into the B operand (bf16) without moving between lanes, because
+//   the keys of a 16-key MFMA step are numbered in the order the accumulator holds them; V^T's A
+//   operand is read with the same numbering by transpose reads (ds_read_b64_tr_b16).
+// - K and V tiles are filled straight from HBM into a 2-stage LDS ring by LDS-writing buffer
+//   loads (16 bytes per lane); rows past a slice read zeros through the buffer range check and
+//   are masked. K rows are XOR-swizzled by key (the A-operand reads of 32 keys at one offset
+//   spread over the banks), V rows by key mod 4 (the transpose reads).
+// - Two workgroups per CU (64 KB of LDS each): one workgroup's softmax overlaps the other's
+//   MFMAs.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fo_internal.h"
+#include "fo_wait.h"
+
+namespace fo {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
+constexpr int kThreads = 256;
+constexpr int kAQ = 128;                   // queries per workgroup (4 waves x 32)
+constexpr int kAK = 64;                    // keys per tile
+constexpr int kAD = 128;                   // head dim
+constexpr int kRowB = kAD * 2;             // one head's row of K or V: 256 bytes
+constexpr int kTileB = kAK * kRowB;        // one K or V tile in LDS: 16 KB
+constexpr int kStage = 2 * kTileB;         // K tile, then V tile
+constexpr int kStages = 2;
+constexpr int kPieces = kTileB / 1024;     // 1 KB loads per tile (16), 4 per wave
+constexpr int kLoads = 2 * kPieces / 4;    // loads per wave per key tile (K and V): 8
+constexpr int kOutStride = kRowB + 16;     // output staging row (bytes): 16-byte aligned, padded
+constexpr float kNegBig = -1.0e30f;        // "minus infinity" that keeps exp2 finite
+constexpr int kRsrcWord3 = 0x00020000;     // raw buffer, 32-bit data format
+static_assert(4 * 32 * kOutStride <= kStages * kStage, "output staging fits in the ring");
+
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ const void* uni_ptr(const void* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = (uint32_t)uni((int)(uint32_t)v), hi = (uint32_t)uni((int)(uint32_t)(v >> 32));
+  return (const void*)(((uint64_t)hi << 32) | lo);
+}
+// raw buffer descriptor (wave-uniform: SGPRs), as the int vector the LDS-load asm takes
+__device__ __forceinline__ i32x4 rsrc_i(const void* base, uint32_t bytes) {
+  const uint64_t v = (uint64_t)uni_ptr(base);
+  i32x4 r;
+  r.x = uni((int)(uint32_t)v);
+  r.y = uni((int)(uint32_t)(v >> 32));
+  r.z = uni((int)bytes);
+  r.w = kRsrcWord3;
+  return r;
+}
+// the same descriptor in the type of the buffer load/store builtins
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_b(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(uni_ptr(base)), (short)0,
+                                           (int)uni((int)bytes), kRsrcWord3);
+}
+
+// 16 bytes per lane from the buffer at byte offset voff into LDS at m0v + 16 * lane (an offset
+// past num_records reads zeros). Issued as inline assembly so that the compiler neither waits
+// for it at barriers nor orders LDS reads behind it; completion is counted with wait_vmcnt.
+__device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t m0v, uint32_t voff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(m0v), "v"(voff), "s"(rsrc)
+      : "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// workgroup barrier after this wave's LDS accesses, without a memory fence
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+
+// Thread 0 waits until slice j has landed; then the workgroup acquires at system scope so that
+// the copy engine's data is seen.
+__device__ __forceinline__ void wait_slice(const AttnPlan& p, int j) {
+  if (threadIdx.x == 0 && p.comp_tab != nullptr)
+    wait_group(p.comp_tab, p.lead, p.ready, p.gen, p.spin_limit, p.err, j, 0);
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
+}
+
+__device__ __forceinline__ void attn_tile(const AttnPlan& p, const int u, uint8_t* const lds) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uni(tid >> 6);
+  const int lh = lane >> 5, l32 = lane & 31, g16 = lane >> 4, i16 = lane & 15;
+  const int m = (int)p.m;
+  const int hq = p.hq;
+  const int qtiles = (m + kAQ - 1) / kAQ;
+  const int per_pos = qtiles * hq;
+  const int pos = uni(u / per_pos);
+  const int rr = u - pos * per_pos;
+  // inside a slice, the query tiles with the most keys (the last ones, under causal masking)
+  // are dispatched first
+  const int qt = uni(qtiles - 1 - rr / hq);
+  const int h = uni(rr % hq);
+  const int s = uni(p.order[pos]);
+  const int kvh = h / (hq / p.hkv);
+  const int W = (hq + 2 * p.hkv) * kRowB;  // bytes of one token's Q, K and V rows
+  const int q0 = qt * kAQ;
+  const int qrows = m - q0 < kAQ ? m - q0 : kAQ;
+  const int64_t qpos = (int64_t)s * m + q0 + 32 * wave + l32;  // this lane's query position
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
+
+  if (p.gated[s]) wait_slice(p, s);
+
+  // Q of this lane's query as the B operand of S^T = K Q^T: K step kd holds the head-dim values
+  // 16 kd + 8 lh .. 16 kd + 8 lh + 7 (rows past the slice read zeros and are never stored)
+  bf16x8 qf[kAD / 16];
+  {
+    const __amdgpu_buffer_rsrc_t qres = rsrc_b(p.slice[s], (uint32_t)m * (uint32_t)W);
+    const uint32_t qoff = (uint32_t)(q0 + 32 * wave + l32) * (uint32_t)W + h * kRowB + lh * 16;
+#pragma unroll
+    for (int kd = 0; kd < kAD / 16; ++kd)
+      qf[kd] = __builtin_bit_cast(bf16x8,
+                                  __builtin_amdgcn_raw_buffer_load_b128(qres, qoff + kd * 32, 0, 0));
+  }
+  wait_vmcnt<0>();
+
+  f32x16 oacc[kAD / 32];
+#pragma unroll
+  for (int i = 0; i < kAD / 32; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) oacc[i][v] = 0.f;
+  float mrow = kNegBig, lrow = 0.f;
+
+  // per-lane LDS offsets of the loads: a 1 KB piece covers 4 key rows, lane -> (row, chunk)
+  const int prow = lane >> 4, pch = lane & 15;
+
+  for (int jp = 0; jp < p.P; ++jp) {
+    const int j = uni(p.order[jp]);
+    if (p.causal && j > s) continue;
+    if (j != s && p.gated[j]) wait_slice(p, j);
+    // keys of slice j to visit: all of them, or (the diagonal slice, causal) up to the tile's
+    // last query
+    const int nk = (p.causal && j == s) ? (q0 + qrows) : m;
+    const int nt = (nk + kAK - 1) / kAK;
+    const int64_t kpos0 = (int64_t)j * m;
+    const i32x4 kvres = rsrc_i(p.slice[j], (uint32_t)m * (uint32_t)W);
+    const uint32_t kcol = (uint32_t)(hq + kvh) * kRowB, vcol = (uint32_t)(hq + p.hkv + kvh) * kRowB;
+    // key tile t into stage st: K rows with chunk c at position c ^ (key & 15), V rows with
+    // chunk c at c ^ 2 (key & 3)
+    auto issue = [&](int t, int st) {
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) {
+        const bool isv = i >= kLoads / 2;
+        const int piece = wave * (kLoads / 2) + (i % (kLoads / 2));
+        const int row = 4 * piece + prow;
+        const int gch = isv ? (pch ^ (2 * (row & 3))) : (pch ^ (row & 15));
+        const uint32_t voff =
+            (uint32_t)(t * kAK + row) * (uint32_t)W + (isv ? vcol : kcol) + gch * 16;
+        load_lds16(kvres, (uint32_t)uni((int)(lds0 + st * kStage + (isv ? kTileB : 0) + piece * 1024)),
+                   voff);
+      }
+    };
+    issue(0, 0);
+    for (int t = 0; t < nt; ++t) {
+      const int st = t & 1;
+      wait_vmcnt<0>();  // tile t has landed (this wave's loads)
+      lds_barrier();    // every wave's loads of tile t landed; tile t-1's stage is free
+      if (t + 1 < nt) issue(t + 1, st ^ 1);
+      const uint8_t* kt = lds + st * kStage;
+      const uint8_t* vt = kt + kTileB;
+
+      // S^T = K Q^T for 64 keys (two fragments of 32) x this wave's 32 queries
+      f32x16 sacc[2];
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sacc[f][v] = 0.f;
+        const int key = 32 * f + l32;
+#pragma unroll
+        for (int kd = 0; kd < kAD / 16; ++kd) {
+          const int ch = (2 * kd + lh) ^ (key & 15);
+          const bf16x8 a = __builtin_bit_cast(bf16x8, *(const uint4*)(kt + key * kRowB + ch * 16));
+          sacc[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kd], sacc[f], 0, 0, 0);
+        }
+      }
+
+      // online softmax in base 2; value v of fragment f is key 32 f + 8 (v / 4) + 4 lh + v % 4
+      const int kb = t * kAK;
+      float mx = kNegBig;
+      float sv[2][16];
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int kj = kb + 32 * f + 8 * (v >> 2) + 4 * lh + (v & 3);
+          const bool ok = kj < m && (!p.causal || kpos0 + kj <= qpos);
+          sv[f][v] = ok ? sacc[f][v] * p.scale_log2 : kNegBig;
+          mx = fmaxf(mx, sv[f][v]);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(mrow, mx);
+      const float alpha = __builtin_amdgcn_exp2f(mrow - mnew);
+      float psum = 0.f;
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float e = sv[f][v] > kNegBig ? __builtin_amdgcn_exp2f(sv[f][v] - mnew) : 0.f;
+          sv[f][v] = e;
+          psum += e;
+        }
+      lrow = lrow * alpha + psum;
+      mrow = mnew;
+#pragma unroll
+      for (int i = 0; i < kAD / 32; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oacc[i][v] *= alpha;
+      // P^T as B operands: 16-key step kk takes values 8 (kk % 2) .. 8 (kk % 2) + 7 of fragment
+      // kk / 2, i.e. keys 16 kk + 8 (e / 4) + 4 lh + e % 4 for e = 0..7
+      bf16x8 pb[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int f = kk >> 1, b = 8 * (kk & 1);
+        uint4 w;
+        w.x = cvt_bf16x2(sv[f][b + 0], sv[f][b + 1]);
+        w.y = cvt_bf16x2(sv[f][b + 2], sv[f][b + 3]);
+        w.z = cvt_bf16x2(sv[f][b + 4], sv[f][b + 5]);
+        w.w = cvt_bf16x2(sv[f][b + 6], sv[f][b + 7]);
+        pb[kk] = __builtin_bit_cast(bf16x8, w);
+      }
+      // O^T += V^T P^T: A operand row d = 32 i + l32 with the keys of step kk in the same order,
+      // from two transpose reads (keys 16 kk + 4 lh + 0..3, then 8 further)
+#pragma unroll
+      for (int i = 0; i < kAD / 32; ++i) {
+        const int d = 32 * i + 16 * (g16 & 1) + 4 * (i16 & 3);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const int kr = 16 * kk + 4 * (g16 >> 1) + (i16 >> 2);
+          const int off = kr * kRowB + (((d >> 3) ^ (2 * (kr & 3))) * 16) + ((d >> 2) & 1) * 8;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + off));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + off + 8 * kRowB));
+          const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+          const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(l2.x, l2.y, h2.x, h2.y));
+          oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kk], oacc[i], 0, 0, 0);
+        }
+      }
+    }
+    lds_barrier();  // every wave is done with the stages before the next slice refills them
+  }
+
+  // ---- epilogue: O = O^T / l, staged per wave as [query][d] bf16, stored row-contiguous -----
+  const float ltot = lrow + __shfl_xor(lrow, 32);
+  const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+  uint8_t* const ost = lds + wave * 32 * kOutStride;
+#pragma unroll
+  for (int i = 0; i < kAD / 32; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; v += 2) {
+      const int d = 32 * i + 8 * (v >> 2) + 4 * lh + (v & 3);
+      *(uint32_t*)(ost + l32 * kOutStride + d * 2) = cvt_bf16x2(oacc[i][v] * inv, oacc[i][v + 1] * inv);
+    }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's staging writes are done
+  const int ow = hq * kRowB;
+  const __amdgpu_buffer_rsrc_t ores =
+      rsrc_b((const uint8_t*)p.out + (int64_t)s * m * ow, (uint32_t)m * (uint32_t)ow);
+#pragma unroll
+  for (int k = 0; k < 32 * kRowB / 16 / 64; ++k) {
+    const int c = lane + 64 * k;
+    const int row = c >> 4, ch = c & 15;
+    const uint4 x = *(const uint4*)(ost + row * kOutStride + ch * 16);
+    const uint32_t off = (uint32_t)(q0 + 32 * wave + row) * (uint32_t)ow + h * kRowB + ch * 16;
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, x), ores, off, 0, 0);
+  }
+  lds_barrier();  // the next tile's loads overwrite the staging rows
+}
+
+__global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnPlan p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * kStage];
+  release_start(p.start);
+  const int qtiles = (int)((p.m + kAQ - 1) / kAQ);
+  const int total = p.P * qtiles * p.hq;
+  for (int u = blockIdx.x; u < total; u += gridDim.x) attn_tile(p, u, lds);
+}
+
+}  // namespace
+
+bool attn_plan_ok(const AttnPlan& p) {
+  if (p.P < 1 || p.P > FO_MAX_P || p.m < 1 || p.hq < 1 || p.hkv < 1 || p.hq % p.hkv != 0)
+    return false;
+  if (p.err == nullptr) return false;
+  const int64_t W = (int64_t)(p.hq + 2 * p.hkv) * kRowB;
+  if ((p.m + kAQ) * W >= ((int64_t)1 << 31) || (p.m + kAQ) * p.hq * kRowB >= ((int64_t)1 << 31))
+    return false;
+  for (int i = 0; i < p.P; ++i) {
+    if (p.order[i] < 0 || p.order[i] >= p.P || p.slice[i] == nullptr) return false;
+    if (p.gated[i] && (p.comp_tab == nullptr || p.lead == nullptr || p.ready == nullptr || p.gen == 0))
+      return false;
+  }
+  return true;
+}
+
+hipError_t launch_attn(const AttnPlan& p, hipStream_t s) {
+  if (!attn_plan_ok(p)) return hipErrorInvalidValue;
+  const int64_t total = (int64_t)p.P * ((p.m + kAQ - 1) / kAQ) * p.hq;
+  hipLaunchKernelGGL(attn_kernel, dim3((unsigned)total), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace fo

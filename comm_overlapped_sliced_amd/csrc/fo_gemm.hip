@@ -19,6 +19,7 @@
 #include <type_traits>
 
 #include "fo_internal.h"
+#include "fo_wait.h"
 
 namespace fo {
 namespace {
@@ -31,58 +32,9 @@ constexpr int kBK = 32;  // K step
 
 // ---------------------------------------------------------------- waits and flags -----------
 
-// Bounded wait until a signal value has dropped to zero (the copy engine decrements it from 1
-// when its transfer has landed; a negative value reports a failed copy, recorded as err = 2).
-// Once any wait of the call has run past the bound (err set), later waits give up at once, so a
-// missing arrival costs one bound, not one per workgroup.
-__device__ __forceinline__ void wait_signal(const int64_t* v, uint64_t limit, uint32_t* err) {
-  const uint64_t t0 = wall_clock64();
-  for (;;) {
-    const int64_t x = __hip_atomic_load(v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    if (x <= 0) {
-      if (x < 0) __hip_atomic_store(err, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-      return;
-    }
-    if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != 0u) return;
-    if (wall_clock64() - t0 > limit) {
-      __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-      return;
-    }
-    __builtin_amdgcn_s_sleep(2);
-  }
-}
-
-// Bounded wait until a device word has reached `gen` (or a wait of the call has failed). The
-// word is uncached device memory, so every read sees the latest store from any XCD.
-__device__ __forceinline__ void wait_gen(const uint32_t* w, uint32_t gen, uint64_t limit,
-                                         uint32_t* err) {
-  const uint64_t t0 = wall_clock64();
-  while (__hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < gen) {
-    if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != 0u) return;
-    if (wall_clock64() - t0 > limit) {
-      __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-      return;
-    }
-    __builtin_amdgcn_s_sleep(8);
-  }
-}
-
-// Wait for group `grp` of `slice` to have landed. The signal values live in host memory, and
-// hundreds of workgroups polling them slow the copy engines down, so only one workgroup per
-// (slice, group) and call polls the signal: the first to get there, elected by raising
-// lead[slice][group] to the call's number `gen` (numbers only grow, so nothing is re-armed
-// between calls). It then raises ready[slice][group] to gen, which the other workgroups poll in
-// device memory. A failed or timed-out wait still raises it (the call's error record is set).
+// Wait for group `grp` of `slice` to have landed (the elected poller of fo_wait.h).
 __device__ __forceinline__ void wait_group(const Plan& p, int slice, int grp) {
-  const int k = slice * kMaxGroups + grp;
-  const uint32_t prev =
-      __hip_atomic_fetch_max(p.lead + k, p.gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (prev < p.gen) {
-    wait_signal(p.comp_tab[k], p.spin_limit, p.err);
-    __hip_atomic_store(p.ready + k, p.gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  } else {
-    wait_gen(p.ready + k, p.gen, p.spin_limit, p.err);
-  }
+  fo::wait_group(p.comp_tab, p.lead, p.ready, p.gen, p.spin_limit, p.err, slice, grp);
 }
 
 // Thread 0 waits for group `grp` of each listed slice (negative ids are skipped); then the whole
@@ -664,15 +616,8 @@ __device__ __forceinline__ void bf16_tile(const Plan& p, const int tile, uint8_t
   release_tile(p, pos, grp);
 }
 
-// The call's copies wait for its start signal. Workgroup 0, the first one dispatched, stores 0
-// into it when the kernel starts (everything enqueued before the kernel is then complete), after
-// a system-scope release so that the copy engines see that work's writes.
-__device__ __forceinline__ void release_start(const Plan& p) {
-  if (p.start != nullptr && blockIdx.x == 0 && threadIdx.x == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
-    __hip_atomic_store(p.start, (int64_t)0, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
-  }
-}
+// The call's copies wait for its start signal (fo_wait.h).
+__device__ __forceinline__ void release_start(const Plan& p) { fo::release_start(p.start); }
 
 // One workgroup per tile, or (grid smaller than the tile count) a persistent grid whose
 // workgroups walk the tiles with a stride of the grid size, in the same order.

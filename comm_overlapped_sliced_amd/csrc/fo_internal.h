@@ -127,6 +127,30 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 // nearest even); y is [rows, 2*inter] bf16. inter % 8 == 0, both 16-byte aligned.
 hipError_t launch_swiglu(const void* y, void* h, int64_t rows, int64_t inter, hipStream_t stream);
 
+// Query-split attention of one rank after a Flash All-to-All (fo_attn): slice s holds the query,
+// key and value rows of sequence positions s*m .. s*m+m-1 for this rank's heads, one row per
+// token laid out as [hq query heads | hkv key heads | hkv value heads] x 128 bf16. Workgroups
+// take (slice, 128-query tile, head) in `order` (position -> slice id) and walk the key slices
+// in the same order, waiting for a slice whose `gated` entry is set (whole slices: row group 0).
+struct AttnPlan {
+  const void* slice[FO_MAX_P];       // by slice id: its rows [m, (hq + 2 hkv) * 128]
+  void* out;                         // [P*m, hq * 128] bf16, query position-major
+  int32_t order[FO_MAX_P];           // arrival order: position -> slice id
+  int32_t gated[FO_MAX_P];           // by slice id: 1 = wait for its arrival
+  const int64_t* const* comp_tab;    // completion-signal values [slice][group]
+  uint32_t* lead;                    // elected-poller words, as in Plan
+  uint32_t* ready;
+  uint32_t gen;
+  uint32_t* err;
+  uint64_t spin_limit;
+  int64_t* start;                    // the call's start signal (null: no copies)
+  int64_t m;                         // tokens per slice
+  int32_t P, hq, hkv, causal;
+  float scale_log2;                  // log2(e) / sqrt(128)
+};
+bool attn_plan_ok(const AttnPlan& p);
+hipError_t launch_attn(const AttnPlan& p, hipStream_t stream);
+
 // Slice schedule: kind 0 = AG, 1 = RS; order = fo_order. Writes P ids.
 int slice_order(int kind, int order, int P, int rank, int32_t* out);
 

@@ -22,7 +22,8 @@ EPI_NONE, EPI_SWIGLU = 0, 1
 MAX_P = 32
 MAX_GROUPS = 8
 
-EXPORTS = ("fo_opts_init", "fo_ag_gemm", "fo_gemm_rs", "fo_gemm_ref", "fo_swiglu",
+EXPORTS = ("fo_opts_init", "fo_ag_gemm", "fo_gemm_rs", "fo_gemm_ref", "fo_swiglu", "fo_attn",
+           "fo_attn_ref",
            "fo_transfer_ref", "fo_check", "fo_slice_order", "fo_tile_info", "fo_tile_order",
            "fo_status_str", "fo_last_error", "fo_version")
 
@@ -64,6 +65,8 @@ def load():
     lib.fo_gemm_rs.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i64, i64, i64, i32, vp, op]
     lib.fo_gemm_ref.argtypes = [vp, vp, vp, i64, i64, i64, i32, i32, i32, vp]
     lib.fo_swiglu.argtypes = [vp, vp, i64, i64, vp]
+    lib.fo_attn.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32, i32, i32, vp, op]
+    lib.fo_attn_ref.argtypes = [vp, vp, i64, i32, i32, i32, i32, vp]
     lib.fo_transfer_ref.argtypes = [i32, vp, vp, i32, i32, i64, vp, op]
     lib.fo_check.argtypes = [vp]
     lib.fo_slice_order.argtypes = [i32, i32, i32, i32, ctypes.POINTER(i32)]
@@ -76,7 +79,8 @@ def load():
     lib.fo_last_error.argtypes = []
     lib.fo_last_error.restype = ctypes.c_char_p
     lib.fo_version.argtypes = []
-    for f in ("fo_ag_gemm", "fo_gemm_rs", "fo_gemm_ref", "fo_swiglu", "fo_transfer_ref", "fo_check",
+    for f in ("fo_ag_gemm", "fo_gemm_rs", "fo_gemm_ref", "fo_swiglu", "fo_attn", "fo_attn_ref",
+              "fo_transfer_ref", "fo_check",
               "fo_slice_order", "fo_tile_info", "fo_tile_order", "fo_version"):
         getattr(lib, f).restype = ctypes.c_int32
     _lib = lib
@@ -275,3 +279,31 @@ def runtimes_mapped(name: str = "libamdhip64") -> set:
             if name in line:
                 paths.add(os.path.realpath(line.split()[-1]))
     return paths
+
+
+def attn(qkv_local, qkv_peer, qkv_recv, out, P: int, rank: int, hq: int, hkv: int,
+         causal: bool = True, compute_stream=None, o: Opts | None = None, raw: bool = False):
+    """Query-split attention after a Flash All-to-All (fo_attn). qkv_local [m, (hq+2hkv)*128]
+    bf16, qkv_peer list of P tensors (or None), qkv_recv [P*m, same], out [P*m, hq*128] bf16."""
+    m, row = qkv_local.shape
+    d = row // (hq + 2 * hkv)
+    peers = None if qkv_peer is None else _ptr_array(qkv_peer)
+    st = load().fo_attn(_ptr(qkv_local), ctypes.cast(peers, ctypes.c_void_p) if peers else None,
+                        _ptr(qkv_recv), _ptr(out), P, rank, m, hq, hkv, d, int(causal),
+                        _stream(compute_stream), ctypes.byref(o) if o is not None else None)
+    if raw:
+        return st
+    _raise_on(st, "fo_attn")
+    return st
+
+
+def attn_ref(qkv, out, hq: int, hkv: int, causal: bool = True, stream=None, raw: bool = False):
+    """The same attention on one resident sequence (fo_attn_ref): qkv [S, (hq+2hkv)*128] bf16,
+    out [S, hq*128] bf16."""
+    S, row = qkv.shape
+    d = row // (hq + 2 * hkv)
+    st = load().fo_attn_ref(_ptr(qkv), _ptr(out), S, hq, hkv, d, int(causal), _stream(stream))
+    if raw:
+        return st
+    _raise_on(st, "fo_attn_ref")
+    return st

@@ -197,6 +197,47 @@ fo_status fo_gemm_ref(const void* a, const void* b, void* c, int64_t M, int64_t 
 fo_status fo_swiglu(const void* y, void* h, int64_t rows, int64_t inter, void* stream);
 
 /*
+ * Query-split attention after a Flash All-to-All: one rank's share of Ulysses (sequence)
+ * parallelism. The FlashOverlap page (gist.science paper 2604.24013, technical summary section
+ * 2 "Methodology") applies its sliced overlap to attention by query slices and to the
+ * All-to-All of Ulysses parallelism. After the All-to-All, rank `rank` holds, for its own hq
+ * query heads and hkv key/value heads, the rows of every peer's sequence chunk: slice s is the
+ * m tokens at sequence positions s*m .. s*m+m-1. Slice `rank` is local; slice s != rank is
+ * copied from qkv_peer[s] into qkv_recv (emulated arrival, one copy per slice, in the Flash-AG
+ * arrival order). The attention runs by query slices: the work for the queries of slice s
+ * starts once slice s has landed and reads key slices in arrival order as each one lands (with
+ * causal masking only slices j <= s). Per head h (key head h / (hq / hkv)) and query position i:
+ *     out[i, h] = sum_j softmax_j(q_i . k_j / sqrt(head_dim)) v_j, over key positions j (j <= i
+ *     when causal).
+ *   qkv_local  device [m, (hq + 2*hkv) * head_dim] bf16: one row per token, [hq query heads |
+ *              hkv key heads | hkv value heads], each head_dim values.
+ *   qkv_peer   host array of P device pointers (entry [rank] ignored), each [m, row] like
+ *              qkv_local; NULL = the slices are already in qkv_recv (no arrivals).
+ *   qkv_recv   device [P*m, row] bf16; slice s at rows s*m (the rows of slice `rank` unused).
+ *   out        device [P*m, hq * head_dim] bf16: row i is query position i, heads side by side.
+ * Computed in fp32 (bf16 MFMA products, fp32 sums, fp32 softmax in base 2); the probabilities
+ * enter the value product as bf16; one round to nearest even of the output.
+ * head_dim must be 128 (else FO_ERR_UNSUPPORTED); hq a multiple of hkv; causal 0 or 1; every
+ * pointer 16-byte aligned; out must not overlap an input (else FO_ERR_INVALID_ARG, nothing
+ * enqueued). opts: order (FLASH: local slice first, then rank-1, rank-2, ...; NATURAL: index
+ * order), arrival (NONE, EAGER or DEFAULT = EAGER), links, spin_timeout_us and kernel_events
+ * are used; tile must be AUTO, row_groups 0 or 1, epilogue NONE. Enqueued on compute_stream
+ * like fo_ag_gemm, with the same ordering, timeout and error reporting through fo_check.
+ */
+fo_status fo_attn(const void* qkv_local, const void* const* qkv_peer, void* qkv_recv, void* out,
+                  int32_t P, int32_t rank, int64_t m, int32_t hq, int32_t hkv, int32_t head_dim,
+                  int32_t causal, void* compute_stream, const fo_opts* opts);
+
+/*
+ * The same attention with every slice resident (one sequence of S tokens, no transfers): the
+ * pure-attention latency of the exposed-transfer fraction and the unsliced result of the
+ * exactness check. qkv [S, (hq + 2*hkv) * head_dim] bf16, out [S, hq * head_dim] bf16; the
+ * checks of fo_attn apply. Enqueued on `stream`.
+ */
+fo_status fo_attn_ref(const void* qkv, void* out, int64_t S, int32_t hq, int32_t hkv,
+                      int32_t head_dim, int32_t causal, void* stream);
+
+/*
  * The emulated transfers of one fo_ag_gemm (kind 0) or fo_gemm_rs (kind 1) call on their own,
  * without the GEMM: the same copies, links and arrival order (RS releases are not awaited). On
  * `stream` it enqueues the release of the copies and a one-workgroup kernel that waits until all

@@ -96,11 +96,12 @@ class Oracle:
         lib.oracle_num_threads.argtypes = []
         lib.oracle_swiglu.argtypes = [vp, i64, i64, vp]
         lib.oracle_swiglu_f64.argtypes = [vp, i64, i64, vp]
+        lib.oracle_attn.argtypes = [vp, i64, i32, i32, i32, i32, vp, i64, vp]
         lib.oracle_round_bf16.argtypes = [vp, i64, vp]
         for f in (lib.oracle_ag_order, lib.oracle_rs_order, lib.oracle_gemm, lib.oracle_ag,
                   lib.oracle_rs, lib.oracle_ag_sampled, lib.oracle_rs_sampled,
                   lib.oracle_rs_send_sampled, lib.oracle_num_threads, lib.oracle_swiglu,
-                  lib.oracle_swiglu_f64, lib.oracle_round_bf16):
+                  lib.oracle_swiglu_f64, lib.oracle_round_bf16, lib.oracle_attn):
             f.restype = ctypes.c_int
         self.lib = lib
         self.path = path
@@ -233,6 +234,22 @@ class Oracle:
         _check(fn(_ptr(y), rows, inter, _ptr(h)), "swiglu")
         return h
 
+    def attn(self, qkv: np.ndarray, hq: int, hkv: int, causal: bool = True, rows=None,
+             d: int = 128) -> np.ndarray:
+        """Scaled dot-product attention in fp64 of one sequence: qkv bf16 bits [S, (hq+2hkv)*d]
+        (token row = [query heads | key heads | value heads]); returns [len(rows) or S, hq*d] for
+        the query positions `rows` (default all)."""
+        qkv = _c(qkv)
+        if qkv.dtype != np.uint16 or qkv.ndim != 2 or qkv.shape[1] != (hq + 2 * hkv) * d:
+            raise ValueError("qkv is bf16 bits [S, (hq + 2 hkv) * d]")
+        S = qkv.shape[0]
+        r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+        n = S if r is None else len(r)
+        out = np.empty((n, hq * d), dtype=np.float64)
+        _check(self.lib.oracle_attn(_ptr(qkv), S, hq, hkv, d, int(causal),
+                                    None if r is None else _ptr(r), n, _ptr(out)), "attn")
+        return out
+
     def round_bf16(self, x: np.ndarray) -> np.ndarray:
         """x (fp64) rounded to the nearest bf16, ties to even, as bf16 bits (same shape)."""
         x = np.ascontiguousarray(x, dtype=np.float64)
@@ -266,6 +283,6 @@ def default() -> Oracle:
 def __getattr__(name):
     # module-level shortcuts: oracle.gemm(...), oracle.ag(...), ...
     if name in ("num_threads", "ag_order", "rs_order", "gemm", "ag", "rs", "ag_sampled",
-                "rs_sampled", "rs_send_sampled", "swiglu", "round_bf16", "mlp_block"):
+                "rs_sampled", "rs_send_sampled", "swiglu", "round_bf16", "mlp_block", "attn"):
         return getattr(default(), name)
     raise AttributeError(name)

@@ -324,3 +324,57 @@ int oracle_num_threads(void) {
   }
   return n;
 }
+
+/* Attention of one rank after the All-to-All of Ulysses (sequence) parallelism. The page
+   (technical summary section 2, "Query Split Attention" and "Flash All-to-All") splits the
+   attention by query slices to overlap it with the arriving slices; the softmax is taken over
+   all key positions a query sees, so the result is plain scaled dot-product attention whatever
+   the split and order. This is that definition in fp64, per query position i and head h:
+     s_j = (q_i,h . k_j,g) / sqrt(d) for key positions j (j <= i when causal), g = h / (hq / hkv);
+     out[i, h] = sum_j exp(s_j - max s) v_j,g / sum_j exp(s_j - max s).
+   qkv: bf16 [S, (hq + 2 hkv) * d], a token's row = [hq query heads | hkv key heads | hkv value
+   heads]. rows: the nrows query positions to compute (NULL: all S, in order). out: fp64
+   [nrows, hq * d]. */
+int oracle_attn(const uint16_t* qkv, int64_t S, int hq, int hkv, int d, int causal,
+                const int64_t* rows, int64_t nrows, double* out) {
+  if (!qkv || !out || S < 0 || hq < 1 || hkv < 1 || hq % hkv || d < 1) return 1;
+  if (!rows) nrows = S;
+  if (nrows < 0) return 1;
+  const int64_t W = (int64_t)(hq + 2 * hkv) * d;
+  const double scale = 1.0 / sqrt((double)d);
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+  for (int64_t t = 0; t < nrows; ++t) {
+    const int64_t i = rows ? rows[t] : t;
+    if (i < 0 || i >= S) { bad = 1; continue; }
+    const int64_t nk = causal ? i + 1 : S;
+    double* sc = (double*)malloc(sizeof(double) * (size_t)nk);
+    if (!sc) { bad = 1; continue; }
+    for (int h = 0; h < hq; ++h) {
+      const int g = h / (hq / hkv);
+      const uint16_t* q = qkv + i * W + (int64_t)h * d;
+      double mx = -INFINITY;
+      for (int64_t j = 0; j < nk; ++j) {
+        const uint16_t* k = qkv + j * W + (int64_t)(hq + g) * d;
+        double dot = 0.0;
+        for (int e = 0; e < d; ++e) dot += decode_bf16(q[e]) * decode_bf16(k[e]);
+        sc[j] = dot * scale;
+        if (sc[j] > mx) mx = sc[j];
+      }
+      double den = 0.0;
+      for (int64_t j = 0; j < nk; ++j) {
+        sc[j] = exp(sc[j] - mx);
+        den += sc[j];
+      }
+      double* o = out + t * (int64_t)hq * d + (int64_t)h * d;
+      for (int e = 0; e < d; ++e) o[e] = 0.0;
+      for (int64_t j = 0; j < nk; ++j) {
+        const uint16_t* v = qkv + j * W + (int64_t)(hq + hkv + g) * d;
+        for (int e = 0; e < d; ++e) o[e] += sc[j] * decode_bf16(v[e]);
+      }
+      for (int e = 0; e < d; ++e) o[e] /= den;
+    }
+    free(sc);
+  }
+  return bad ? 1 : 0;
+}

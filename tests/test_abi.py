@@ -223,3 +223,49 @@ def test_swiglu_rejects(lib):
     assert lib.fo_swiglu(A, A + 4096, 64, 128, None) == fo.FO_ERR_INVALID_ARG  # h inside y
     assert lib.fo_swiglu(A, C, -1, 128, None) == fo.FO_ERR_INVALID_ARG
     assert lib.fo_swiglu(A, C, 0, 128, None) == fo.FO_OK  # nothing to do
+
+
+def _attn(lib, **kw):
+    args = dict(local=A, peers=None, recv=B, out=C, P=4, rank=0, m=64, hq=8, hkv=2, d=128,
+                causal=1, opts=None)
+    args.update(kw)
+    peers = args["peers"]
+    if peers is not None:
+        arr = (ctypes.c_void_p * len(peers))(*peers)
+        peers = ctypes.cast(arr, ctypes.c_void_p)
+    return lib.fo_attn(args["local"], peers, args["recv"], args["out"], args["P"], args["rank"],
+                       args["m"], args["hq"], args["hkv"], args["d"], args["causal"], None,
+                       args["opts"])
+
+
+@pytest.mark.parametrize("kw", [dict(hq=6, hkv=4), dict(hq=0), dict(hkv=0), dict(causal=2),
+                                dict(m=-1), dict(P=0), dict(rank=4), dict(local=0),
+                                dict(out=0), dict(recv=0), dict(out=A + 8), dict(local=A + 4),
+                                dict(out=B + 64),  # out overlaps qkv_recv
+                                dict(m=1 << 22)],
+                         ids=lambda k: ",".join(f"{a}={b}" for a, b in k.items()))
+def test_attn_rejects(lib, kw):
+    assert _attn(lib, **kw) == fo.FO_ERR_INVALID_ARG
+    assert lib.fo_last_error().decode() != ""
+
+
+def test_attn_head_dim_is_unsupported(lib):
+    assert _attn(lib, d=64) == fo.FO_ERR_UNSUPPORTED
+    assert lib.fo_attn_ref(A, C, 64, 8, 2, 96, 1, None) == fo.FO_ERR_UNSUPPORTED
+
+
+def test_attn_rejects_bad_opts(lib):
+    for kw in (dict(arrival=fo.ARR_LOCKSTEP), dict(tile=fo.TILE_256x256), dict(row_groups=2),
+               dict(epilogue=fo.EPI_SWIGLU), dict(order=7)):
+        o = fo.opts()
+        for k, v in kw.items():
+            setattr(o, k, v)
+        assert _attn(lib, opts=ctypes.byref(o)) == fo.FO_ERR_INVALID_ARG, kw
+    peers = [0x50000000, 0, 0x60000000, 0x70000000]   # a NULL peer with arrivals on
+    assert _attn(lib, peers=peers) == fo.FO_ERR_INVALID_ARG
+
+
+def test_attn_empty_is_a_no_op(lib):
+    assert _attn(lib, m=0) == fo.FO_OK
+    assert lib.fo_attn_ref(A, C, 0, 8, 2, 128, 1, None) == fo.FO_OK
+    assert lib.fo_attn_ref(A, A + 16, 4, 8, 2, 128, 1, None) == fo.FO_ERR_INVALID_ARG

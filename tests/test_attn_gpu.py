@@ -1,0 +1,130 @@
+"""GPU parity of the query-split attention behind a Flash All-to-All (fo_attn) and of its
+resident form (fo_attn_ref), against the CPU oracle on the same seeded inputs, through the C ABI.
+
+Tolerance: the kernel rounds the probabilities to bf16 before the value product (relative error
+at most 2^-9 on each term p_j v_j, while the normalizing sum uses the unrounded p_j) and the
+output to bf16 once (at most 2^-9 of the value). So each element is within
+2^-9 (sum_j p_j |v_j| / sum_j p_j + |out|), up to fp32 sums; the oracle gives the first term as
+the attention of the same scores over |V|. The check allows twice that, and a relative Frobenius
+error of 3e-3 (two roundings; the output rounding alone is about 1.5e-3 on these inputs)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from comm_overlapped_sliced_amd import configs, flashovl as fo, inputs
+from tests.gpu_helpers import from_dev, rel_frobenius, to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+TOL_ATTN = 3e-3
+D = 128
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+    fo.load()
+    return torch.device("cuda:0")
+
+
+def _abs_values(qkv, hq, hkv):
+    """qkv with every value entry replaced by its magnitude (sign bit cleared)."""
+    a = qkv.copy()
+    a[:, (hq + hkv) * D:] &= np.uint16(0x7FFF)
+    return a
+
+
+def _check(got, qkv, hq, hkv, causal, what, rows=None):
+    ref = oracle.attn(qkv, hq, hkv, causal, rows=rows)
+    err = rel_frobenius(got, ref)
+    print(f"{what}: relF {err:.2e}", flush=True)
+    assert err <= TOL_ATTN, f"{what}: relF {err:.3e}"
+    mag = oracle.attn(_abs_values(qkv, hq, hkv), hq, hkv, causal, rows=rows)
+    bad = np.abs(got - ref) > 2.0 ** -8 * (mag + np.abs(ref)) + 1e-6
+    assert not bad.any(), f"{what}: {bad.sum()} elements off, e.g. {np.argwhere(bad)[:3]}"
+
+
+@pytest.mark.parametrize("S,hq,hkv,causal", [(200, 4, 2, True), (200, 4, 2, False),
+                                             (1, 2, 1, True), (64, 8, 1, True),
+                                             (300, 2, 2, False), (129, 8, 8, True)])
+def test_attn_ref_against_oracle(dev, S, hq, hkv, causal):
+    qkv = inputs.normal(8000 + S + hq, (S, (hq + 2 * hkv) * D), 1.0, "bf16")
+    out = torch.full((S, hq * D), float("nan"), dtype=torch.bfloat16, device=dev)
+    fo.attn_ref(to_dev(qkv, dev), out, hq, hkv, causal, stream=torch.cuda.current_stream())
+    fo.check(torch.cuda.current_stream())
+    _check(from_dev(out), qkv, hq, hkv, causal, f"S{S} hq{hq} hkv{hkv} causal{causal}")
+
+
+def _sliced(dev, qkv, P, rank, hq, hkv, causal, o=None, arrivals=True):
+    S, row = qkv.shape
+    m = S // P
+    slices = [to_dev(qkv[s * m:(s + 1) * m], dev) for s in range(P)]
+    recv = torch.empty((S, row), dtype=torch.bfloat16, device=dev)
+    if not arrivals:  # the slices already in place
+        for s in range(P):
+            recv[s * m:(s + 1) * m] = slices[s]
+    out = torch.full((S, hq * D), float("nan"), dtype=torch.bfloat16, device=dev)
+    st = torch.cuda.current_stream()
+    o = o or fo.opts()
+    if not arrivals:
+        o.arrival = fo.ARR_NONE
+    fo.attn(slices[rank], slices if arrivals else None, recv, out, P, rank, hq, hkv, causal,
+            compute_stream=st, o=o)
+    fo.check(st)
+    assert not torch.isnan(out).any().item()
+    return out
+
+
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+@pytest.mark.parametrize("order", [fo.ORDER_FLASH, fo.ORDER_NATURAL], ids=["flash", "natural"])
+def test_attn_sliced_against_oracle(dev, causal, order):
+    # P = 4 slices of 72 tokens: ragged query tiles (72 of 128) and key tiles (72 = 64 + 8)
+    P, m, hq, hkv = 4, 72, 4, 1
+    qkv = inputs.normal(8100 + causal, (P * m, (hq + 2 * hkv) * D), 1.0, "bf16")
+    for rank in (0, P - 1):
+        out = _sliced(dev, qkv, P, rank, hq, hkv, causal, fo.opts(order=order))
+        _check(from_dev(out), qkv, hq, hkv, causal, f"rank {rank} order {order} causal {causal}")
+
+
+def test_attn_arrivals_match_resident_slices(dev):
+    """Gating changes when a key slice is read, not what is computed: the call with arrivals
+    equals the same call on slices already in place, bit for bit."""
+    P, m, hq, hkv = 4, 200, 2, 1
+    qkv = inputs.normal(8200, (P * m, (hq + 2 * hkv) * D), 1.0, "bf16")
+    for rank in (1, 3):
+        a = _sliced(dev, qkv, P, rank, hq, hkv, True)
+        b = _sliced(dev, qkv, P, rank, hq, hkv, True, arrivals=False)
+        assert torch.equal(a, b), f"rank {rank}"
+
+
+def test_attn_sliced_equals_resident_in_natural_order(dev):
+    """With the slices walked in index order the sliced call visits the keys in the order of the
+    resident call, so the two agree bit for bit."""
+    P, m, hq, hkv = 4, 128, 2, 2
+    qkv = inputs.normal(8300, (P * m, (hq + 2 * hkv) * D), 1.0, "bf16")
+    sl = _sliced(dev, qkv, P, 2, hq, hkv, True, fo.opts(order=fo.ORDER_NATURAL))
+    ref = torch.empty_like(sl)
+    fo.attn_ref(to_dev(qkv, dev), ref, hq, hkv, True, stream=torch.cuda.current_stream())
+    fo.check(torch.cuda.current_stream())
+    assert torch.equal(sl, ref)
+
+
+@pytest.mark.parametrize("rank", [0, 7])
+def test_attn_l70b_sampled_rows(dev, rank):
+    """The Llama-3.1-70B Ulysses share (8 slices of 1024 tokens, 8 query heads, 1 key/value head,
+    causal) with arrivals: every head of the first, a middle and the last query of each slice
+    plus random queries, against the oracle's rows."""
+    c = configs.L70B_ATTN
+    qkv = c.qkv()
+    out = _sliced(dev, qkv, c.P, rank, c.hq, c.hkv, c.causal)
+    rng = np.random.default_rng(8400 + rank)
+    rows = np.unique(np.concatenate([[s * c.m, s * c.m + c.m // 2 + 3, s * c.m + c.m - 1]
+                                     for s in range(c.P)] + [rng.integers(0, c.S, 24)]))
+    got = from_dev(out[torch.from_numpy(rows).to(dev)])
+    _check(got, qkv, c.hq, c.hkv, c.causal, f"L70B rank {rank}", rows=rows)
