@@ -82,6 +82,49 @@ def parse():
     return ap.parse_args()
 
 
+def attention_section(fo, dev, stream, timed, reps, log):
+    """Query-split attention behind a Flash All-to-All on the Llama-3.1-70B Ulysses share: the
+    resident attention (T_ref), the sliced call with every slice resident (T_slice0) and with
+    emulated arrivals (T_slice, FLASH order; the data-slicing order NATURAL beside it), and the
+    transfers alone (T_xfer), at ranks 0 and P-1."""
+    import numpy as np
+    import torch
+    from comm_overlapped_sliced_amd import configs
+    c = configs.L70B_ATTN
+    qkv_np = c.qkv()
+    qkv = torch.from_numpy(qkv_np.view(np.int16)).to(dev).view(torch.bfloat16)
+    del qkv_np
+    slices = [qkv[s * c.m:(s + 1) * c.m].contiguous() for s in range(c.P)]
+    recv = torch.empty_like(qkv)
+    out = torch.empty((c.S, c.hq * c.head_dim), dtype=torch.bfloat16, device=dev)
+    t_ref = timed(lambda: fo.attn_ref(qkv, out, c.hq, c.hkv, c.causal, stream=stream), reps)
+    res = {"workload": c.name, "S": c.S, "P": c.P, "hq": c.hq, "hkv": c.hkv,
+           "head_dim": c.head_dim, "causal": c.causal, "gflop": c.flops / 1e9,
+           "t_ref_us": t_ref * 1e3, "tflops_ref": c.flops / t_ref / 1e9}
+    slice_b = c.m * c.row * 2
+    for rb in (0, c.P - 1):
+        for s in range(c.P):
+            recv[s * c.m:(s + 1) * c.m] = slices[s]
+        t0 = timed(lambda: fo.attn(slices[rb], None, recv, out, c.P, rb, c.hq, c.hkv, c.causal,
+                                   compute_stream=stream, o=fo.opts(arrival=fo.ARR_NONE)), reps)
+        t1 = timed(lambda: fo.attn(slices[rb], slices, recv, out, c.P, rb, c.hq, c.hkv, c.causal,
+                                   compute_stream=stream), reps)
+        tn = timed(lambda: fo.attn(slices[rb], slices, recv, out, c.P, rb, c.hq, c.hkv, c.causal,
+                                   compute_stream=stream, o=fo.opts(order=fo.ORDER_NATURAL)), reps)
+        tx = timed(lambda: fo.transfer_ref("ag", slices, recv, c.P, rb, slice_b, stream,
+                                           fo.opts(row_groups=1)), reps)
+        van = t_ref + tx
+        res[f"rank{rb}"] = {"t_slice0_us": t0 * 1e3, "t_slice_us": t1 * 1e3,
+                            "data_slicing_us": tn * 1e3, "t_xfer_us": tx * 1e3,
+                            "vanilla_us": van * 1e3, "exposed_frac": (t1 - t_ref) / tx,
+                            "latency_reduction_flash": (van - t1) / van,
+                            "latency_reduction_data_slicing": (van - tn) / van}
+        log(f"attention rank {rb}: ref {t_ref*1e3:.0f} us ({res['tflops_ref']:.0f} TFLOP/s), slice0 "
+            f"{t0*1e3:.0f}, flash {t1*1e3:.0f}, data slicing {tn*1e3:.0f}, xfer {tx*1e3:.0f}, vanilla "
+            f"{van*1e3:.0f} -> exposed {(t1 - t_ref) / tx:.2f}, {(van - t1) / van:.3f} less than vanilla")
+    return res
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -293,6 +336,8 @@ def main():
         log(f"SwiGLU {t_act*1e3:.1f} us, {mlp['swiglu_gbps']:.0f} GB/s; AG {t_ag*1e3:.0f} us, "
             f"AG with the SwiGLU epilogue {t_ag_fused*1e3:.0f} us")
         exposure["mlp_block"] = mlp
+        fo.check(stream)
+        exposure["attention"] = attention_section(fo, dev, stream, timed, reps, log)
         fo.check(stream)
         step()
         fo.check(stream)

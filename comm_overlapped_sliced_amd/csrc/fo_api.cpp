@@ -757,7 +757,6 @@ fo_status fo_attn(const void* qkv_local, const void* const* qkv_peer, void* qkv_
   if (s != FO_OK) return s;
   if (o.arrival == FO_ARR_LOCKSTEP) return invalid("LOCKSTEP arrivals apply to fo_gemm_rs only");
   if (o.tile != FO_TILE_AUTO) return invalid("opts.tile applies to the GEMM calls only");
-  if (o.row_groups > 1) return invalid("fo_attn transfers whole slices (opts.row_groups 0 or 1)");
   if (o.epilogue != FO_EPI_NONE) return invalid("opts.epilogue applies to fo_ag_gemm only");
   const bool arrivals = qkv_peer != nullptr && o.arrival != FO_ARR_NONE && P > 1;
   const size_t W = (size_t)(hq + 2 * hkv) * 256, slice_b = (size_t)m * W;
@@ -784,8 +783,15 @@ fo_status fo_attn(const void* qkv_local, const void* const* qkv_peer, void* qkv_
   s = current_state(&st, &lk);
   if (s != FO_OK) return s;
   fo::AttnPlan p{};
+  // row groups: opts.row_groups (0: whole slices), each a multiple of the 128-row query tile.
+  // Whole slices by default: every further copy costs the engine ~9 us of its own, more than a
+  // group's earlier start saves here.
+  const int req = o.row_groups ? o.row_groups : 1;
+  const int64_t gr = ((m + req - 1) / req + 127) / 128 * 128;
+  p.group_rows = gr;
+  p.groups = (int32_t)((m + gr - 1) / gr);
   fo::dma::Call call{};
-  if (arrivals) FO_DMA(fo::dma::begin(st->dev, P, 1, &call, &e_));
+  if (arrivals) FO_DMA(fo::dma::begin(st->dev, P, p.groups, &call, &e_));
   int32_t order[FO_MAX_P];
   fo::slice_order(0, o.order, P, rank, order);
   for (int i = 0; i < P; ++i) {
@@ -821,10 +827,14 @@ fo_status fo_attn(const void* qkv_local, const void* const* qkv_peer, void* qkv_
     int seq[FO_MAX_P];
     const int n = arrival_sequence(0, o.order, P, rank, seq);
     const int L = links_for(o, P);
-    for (int t = 0; t < n; ++t) {
-      const int sl = seq[t];
-      FO_DMA(fo::dma::copy(st->dev, call, t % L, sl, 0, -1, (uint8_t*)qkv_recv + (size_t)sl * slice_b,
-                           qkv_peer[sl], slice_b, &e_));
+    for (int g = 0; g < p.groups; ++g) {
+      const int64_t r0 = g * gr, r1 = std::min<int64_t>(m, r0 + gr);
+      for (int t = 0; t < n; ++t) {
+        const int sl = seq[t];
+        FO_DMA(fo::dma::copy(st->dev, call, t % L, sl, g, -1,
+                             (uint8_t*)qkv_recv + (size_t)sl * slice_b + (size_t)r0 * W,
+                             (const uint8_t*)qkv_peer[sl] + (size_t)r0 * W, (size_t)(r1 - r0) * W, &e_));
+      }
     }
   }
   return FO_OK;
@@ -844,6 +854,8 @@ fo_status fo_attn_ref(const void* qkv, void* out, int64_t S, int32_t hq, int32_t
   s = current_state(&st, &lk);
   if (s != FO_OK) return s;
   fo::AttnPlan p{};
+  p.group_rows = (S + 127) / 128 * 128;
+  p.groups = 1;
   p.order[0] = 0;
   p.slice[0] = qkv;
   p.gated[0] = 0;

@@ -5,11 +5,12 @@
 // extends the sliced overlap in two ways: attention computed by query slices, for overlap at a
 // finer grain, and the All-to-All of Ulysses parallelism decomposed like the All-Gather. After
 // the All-to-All a rank holds, for its own heads, the query, key and value rows of every peer's
-// sequence chunk (slice s = sequence positions s*m .. s*m+m-1). Here the slices arrive one by
-// one (emulated copies, as for Flash-AG) and the attention runs by query slices: a workgroup
-// takes 128 queries of one head of slice s as soon as slice s has landed, and walks the key
-// slices in arrival order, waiting for each one (with causal masking only the slices j <= s). The
-// online softmax makes the order of the key slices irrelevant up to rounding.
+// sequence chunk (slice s = sequence positions s*m .. s*m+m-1). Here the slices arrive in row
+// groups (emulated copies, group by group as for Flash-AG; whole slices by default) and the
+// attention runs by query slices: a workgroup takes 128 queries of one head of slice s as soon as
+// their row group has landed, and walks the key slices in arrival order, waiting before each for
+// the row groups that hold the keys it reads (with causal masking only the slices j <= s). The
+// online softmax makes the order of the keys irrelevant up to rounding.
 //
 // Kernel design (CDNA4):
 // - One workgroup per (slice, 128-query tile, head): 4 waves of 32 queries; key tiles of 64.
@@ -108,11 +109,12 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
-// Thread 0 waits until slice j has landed; then the workgroup acquires at system scope so that
-// the copy engine's data is seen.
-__device__ __forceinline__ void wait_slice(const AttnPlan& p, int j) {
+// Thread 0 waits until row groups g0..g1 of slice j have landed; then the workgroup acquires at
+// system scope so that the copy engine's data is seen.
+__device__ __forceinline__ void wait_groups(const AttnPlan& p, int j, int g0, int g1) {
   if (threadIdx.x == 0 && p.comp_tab != nullptr)
-    wait_group(p.comp_tab, p.lead, p.ready, p.gen, p.spin_limit, p.err, j, 0);
+    for (int g = g0; g <= g1; ++g)
+      wait_group(p.comp_tab, p.lead, p.ready, p.gen, p.spin_limit, p.err, j, g);
   __syncthreads();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
 }
@@ -140,7 +142,9 @@ __device__ __forceinline__ void attn_tile(const AttnPlan& p, const int u, uint8_
   const int64_t qpos = (int64_t)s * m + q0 + 32 * wave + l32;  // this lane's query position
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
 
-  if (p.gated[s]) wait_slice(p, s);
+  const int gr = (int)p.group_rows;
+  // the query rows' group (group_rows is a multiple of the 128-row query tile)
+  if (p.gated[s]) wait_groups(p, s, 0, q0 / gr);
 
   // Q of this lane's query as the B operand of S^T = K Q^T: K step kd holds the head-dim values
   // 16 kd + 8 lh .. 16 kd + 8 lh + 7 (rows past the slice read zeros and are never stored)
@@ -168,11 +172,13 @@ __device__ __forceinline__ void attn_tile(const AttnPlan& p, const int u, uint8_
   for (int jp = 0; jp < p.P; ++jp) {
     const int j = uni(p.order[jp]);
     if (p.causal && j > s) continue;
-    if (j != s && p.gated[j]) wait_slice(p, j);
     // keys of slice j to visit: all of them, or (the diagonal slice, causal) up to the tile's
     // last query
     const int nk = (p.causal && j == s) ? (q0 + qrows) : m;
     const int nt = (nk + kAK - 1) / kAK;
+    // the row groups holding those keys, all before the walk (a wait inside the tile loop slows
+    // its code down more than an earlier start of a slice's first groups gains)
+    if (p.gated[j]) wait_groups(p, j, 0, (nk - 1) / gr);
     const int64_t kpos0 = (int64_t)j * m;
     const i32x4 kvres = rsrc_i(p.slice[j], (uint32_t)m * (uint32_t)W);
     const uint32_t kcol = (uint32_t)(hq + kvh) * kRowB, vcol = (uint32_t)(hq + p.hkv + kvh) * kRowB;
@@ -319,6 +325,9 @@ bool attn_plan_ok(const AttnPlan& p) {
   if (p.P < 1 || p.P > FO_MAX_P || p.m < 1 || p.hq < 1 || p.hkv < 1 || p.hq % p.hkv != 0)
     return false;
   if (p.err == nullptr) return false;
+  if (p.groups < 1 || p.groups > kMaxGroups || p.group_rows < 1 || p.group_rows % kAQ != 0 ||
+      p.group_rows * p.groups < p.m)
+    return false;
   const int64_t W = (int64_t)(p.hq + 2 * p.hkv) * kRowB;
   if ((p.m + kAQ) * W >= ((int64_t)1 << 31) || (p.m + kAQ) * p.hq * kRowB >= ((int64_t)1 << 31))
     return false;

@@ -131,7 +131,9 @@ hipError_t launch_swiglu(const void* y, void* h, int64_t rows, int64_t inter, hi
 // key and value rows of sequence positions s*m .. s*m+m-1 for this rank's heads, one row per
 // token laid out as [hq query heads | hkv key heads | hkv value heads] x 128 bf16. Workgroups
 // take (slice, 128-query tile, head) in `order` (position -> slice id) and walk the key slices
-// in the same order, waiting for a slice whose `gated` entry is set (whole slices: row group 0).
+// in the same order. A slice whose `gated` entry is set arrives in `groups` row groups of
+// `group_rows` rows (a multiple of 128; the last may be shorter): a query tile waits for the
+// group holding its rows and a key tile for the group holding its keys.
 struct AttnPlan {
   const void* slice[FO_MAX_P];       // by slice id: its rows [m, (hq + 2 hkv) * 128]
   void* out;                         // [P*m, hq * 128] bf16, query position-major
@@ -145,6 +147,8 @@ struct AttnPlan {
   uint64_t spin_limit;
   int64_t* start;                    // the call's start signal (null: no copies)
   int64_t m;                         // tokens per slice
+  int64_t group_rows;                // rows per arrival group (multiple of 128)
+  int32_t groups;                    // arrival groups per slice (1..kMaxGroups)
   int32_t P, hq, hkv, causal;
   float scale_log2;                  // log2(e) / sqrt(128)
 };

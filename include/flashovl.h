@@ -220,8 +220,11 @@ fo_status fo_swiglu(const void* y, void* h, int64_t rows, int64_t inter, void* s
  * head_dim must be 128 (else FO_ERR_UNSUPPORTED); hq a multiple of hkv; causal 0 or 1; every
  * pointer 16-byte aligned; out must not overlap an input (else FO_ERR_INVALID_ARG, nothing
  * enqueued). opts: order (FLASH: local slice first, then rank-1, rank-2, ...; NATURAL: index
- * order), arrival (NONE, EAGER or DEFAULT = EAGER), links, spin_timeout_us and kernel_events
- * are used; tile must be AUTO, row_groups 0 or 1, epilogue NONE. Enqueued on compute_stream
+ * order), arrival (NONE, EAGER or DEFAULT = EAGER), links, row_groups (each slice sent in that
+ * many row groups, group by group, of a whole number of 128-row query tiles; 0 = whole
+ * slices), spin_timeout_us and kernel_events are used: a query tile waits for the group holding
+ * its rows, and the walk over a key slice for the groups holding the keys it reads. tile must be AUTO,
+ * epilogue NONE. Enqueued on compute_stream
  * like fo_ag_gemm, with the same ordering, timeout and error reporting through fo_check.
  */
 fo_status fo_attn(const void* qkv_local, const void* const* qkv_peer, void* qkv_recv, void* out,

@@ -255,7 +255,7 @@ def test_attn_head_dim_is_unsupported(lib):
 
 
 def test_attn_rejects_bad_opts(lib):
-    for kw in (dict(arrival=fo.ARR_LOCKSTEP), dict(tile=fo.TILE_256x256), dict(row_groups=2),
+    for kw in (dict(arrival=fo.ARR_LOCKSTEP), dict(tile=fo.TILE_256x256), dict(row_groups=9),
                dict(epilogue=fo.EPI_SWIGLU), dict(order=7)):
         o = fo.opts()
         for k, v in kw.items():

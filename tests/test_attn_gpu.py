@@ -92,6 +92,22 @@ def test_attn_sliced_against_oracle(dev, causal, order):
         _check(from_dev(out), qkv, hq, hkv, causal, f"rank {rank} order {order} causal {causal}")
 
 
+@pytest.mark.parametrize("groups", [1, 2, 3, 8])
+def test_attn_row_group_arrivals(dev, groups):
+    """Slices sent in row groups (each a whole number of 128-row query tiles; m = 200 leaves a
+    short last group): every query and key tile waits for its own group."""
+    P, m, hq, hkv = 3, 200 if groups < 8 else 1024, 2, 1
+    qkv = inputs.normal(8150 + groups, (P * m, (hq + 2 * hkv) * D), 1.0, "bf16")
+    for rank in (0, P - 1):
+        out = _sliced(dev, qkv, P, rank, hq, hkv, True, fo.opts(row_groups=groups))
+        if m <= 256:
+            _check(from_dev(out), qkv, hq, hkv, True, f"groups {groups} rank {rank}")
+        else:
+            rows = np.arange(0, P * m, 37)
+            _check(from_dev(out[torch.from_numpy(rows).to(dev)]), qkv, hq, hkv, True,
+                   f"groups {groups} rank {rank}", rows=rows)
+
+
 def test_attn_arrivals_match_resident_slices(dev):
     """Gating changes when a key slice is read, not what is computed: the call with arrivals
     equals the same call on slices already in place, bit for bit."""
