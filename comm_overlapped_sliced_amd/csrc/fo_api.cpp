@@ -740,6 +740,13 @@ static fo_status check_attn(int32_t P, int32_t rank, int64_t m, int32_t hq, int3
   return FO_OK;
 }
 
+// Causal attention whose workgroups all fit at once (two per CU) and fill the second slot of
+// every CU: pair long and short query tiles (AttnPlan::pair_half).
+static int32_t attn_pair_half(int32_t P, int64_t m, int32_t hq, int32_t causal, int n_cu) {
+  const int64_t total = (int64_t)P * ((m + 127) / 128) * hq;
+  return (causal && total % 2 == 0 && total > n_cu && total <= 2 * (int64_t)n_cu) ? (int32_t)(total / 2) : 0;
+}
+
 static fo_status launch_attn_events(const fo::AttnPlan& p, hipStream_t cs, const fo_opts& o) {
   if (o.kernel_events[0]) FO_HIP(hipEventRecord((hipEvent_t)o.kernel_events[0], cs));
   FO_HIP(fo::launch_attn(p, cs));
@@ -812,6 +819,7 @@ fo_status fo_attn(const void* qkv_local, const void* const* qkv_peer, void* qkv_
   p.hkv = hkv;
   p.causal = causal;
   p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
+  p.pair_half = attn_pair_half(P, m, hq, causal, st->n_cu);
 
   hipStream_t cs = (hipStream_t)compute_stream;
   if (arrivals) p.start = call.start;
@@ -868,6 +876,7 @@ fo_status fo_attn_ref(const void* qkv, void* out, int64_t S, int32_t hq, int32_t
   p.hkv = hkv;
   p.causal = causal;
   p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
+  p.pair_half = attn_pair_half(1, S, hq, causal, st->n_cu);
   FO_HIP(fo::launch_attn(p, (hipStream_t)stream));
   return FO_OK;
 }

@@ -127,14 +127,26 @@ __device__ __forceinline__ void attn_tile(const AttnPlan& p, const int u, uint8_
   const int m = (int)p.m;
   const int hq = p.hq;
   const int qtiles = (m + kAQ - 1) / kAQ;
-  const int per_pos = qtiles * hq;
-  const int pos = uni(u / per_pos);
-  const int rr = u - pos * per_pos;
-  // inside a slice, the query tiles with the most keys (the last ones, under causal masking)
-  // are dispatched first
-  const int qt = uni(qtiles - 1 - rr / hq);
-  const int h = uni(rr % hq);
-  const int s = uni(p.order[pos]);
+  int s, qt, h;
+  if (p.pair_half > 0) {
+    // items by global query tile, most keys first; the second half of the grid in reverse, so
+    // that workgroup b and workgroup b + pair_half (which share a CU) sum to about the same work
+    const int total = p.P * qtiles * hq;
+    const int v = u < p.pair_half ? u : total - 1 - (u - p.pair_half);
+    const int g = p.P * qtiles - 1 - v / hq;
+    s = uni(g / qtiles);
+    qt = uni(g % qtiles);
+    h = uni(v % hq);
+  } else {
+    const int per_pos = qtiles * hq;
+    const int pos = uni(u / per_pos);
+    const int rr = u - pos * per_pos;
+    // inside a slice, the query tiles with the most keys (the last ones, under causal masking)
+    // are dispatched first
+    qt = uni(qtiles - 1 - rr / hq);
+    h = uni(rr % hq);
+    s = uni(p.order[pos]);
+  }
   const int kvh = h / (hq / p.hkv);
   const int W = (hq + 2 * p.hkv) * kRowB;  // bytes of one token's Q, K and V rows
   const int q0 = qt * kAQ;

@@ -150,6 +150,10 @@ struct AttnPlan {
   int64_t group_rows;                // rows per arrival group (multiple of 128)
   int32_t groups;                    // arrival groups per slice (1..kMaxGroups)
   int32_t P, hq, hkv, causal;
+  // > 0: the workgroups are dispatched as two halves of pair_half, the first taking the query
+  // tiles with the most keys first and the second the fewest first, so that the pair of
+  // workgroups that shares a CU has a balanced amount of work (causal, one workgroup per slot)
+  int32_t pair_half;
   float scale_log2;                  // log2(e) / sqrt(128)
 };
 bool attn_plan_ok(const AttnPlan& p);
