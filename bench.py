@@ -72,6 +72,9 @@ def parse():
                     help="emulated links per call (0: one DMA engine per peer; 1: one link)")
     ap.add_argument("--row-groups", type=int, default=0,
                     help="row groups per slice (0: one per tile row; 1: whole slices)")
+    ap.add_argument("--ag-k-chunks", type=int, default=4,
+                    help="Flash-AG slices stored and sent in this many K blocks (opts.k_chunks; "
+                         "0: row-major slices)")
     ap.add_argument("--exposure-reps", type=int, default=10)
     ap.add_argument("--no-exposure", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -158,6 +161,15 @@ def main():
                  for s in range(P)]
     ag_full = dev_of(xa)
     del xa
+    # Flash-AG slices in the K-block layout of opts.k_chunks (block j = columns j*K/c .. of every
+    # row), the form the sending rank keeps them in; the row-major slices stay for the baselines
+    kc = args.ag_k_chunks
+
+    def k_blocks(t, c):
+        m_, k_ = t.shape
+        return t.reshape(m_, c, k_ // c).permute(1, 0, 2).contiguous().reshape(m_, k_)
+
+    ag_chunked = [k_blocks(t, kc) for t in ag_slices] if kc > 1 else ag_slices
     ag_w = dev_of(ag_case.w())
     ag_recv = torch.empty((ag_case.M, ag_case.K), dtype=torch.bfloat16, device=dev)
     ag_y = torch.empty((ag_case.M, ag_case.N), dtype=torch.bfloat16, device=dev)
@@ -176,11 +188,12 @@ def main():
         return torch.cuda.Event(enable_timing=True)
 
     def ag_call(evs=None, arrival=fo.ARR_DEFAULT, links=args.links, groups=args.row_groups,
-                order=fo.ORDER_FLASH, rank=r, epilogue=fo.EPI_NONE, y=None):
+                order=fo.ORDER_FLASH, rank=r, epilogue=fo.EPI_NONE, y=None, chunks=kc):
         o = fo.opts(order=order, links=links, row_groups=groups, arrival=arrival,
-                    kernel_events=evs, epilogue=epilogue)
-        peers = None if arrival == fo.ARR_NONE else ag_slices
-        fo.ag_gemm(ag_slices[rank], peers, ag_recv, ag_w, ag_y if y is None else y, P, rank,
+                    kernel_events=evs, epilogue=epilogue, k_chunks=chunks)
+        sl = ag_chunked if chunks > 1 else ag_slices
+        peers = None if arrival == fo.ARR_NONE else sl
+        fo.ag_gemm(sl[rank], peers, ag_recv, ag_w, ag_y if y is None else y, P, rank,
                    compute_stream=stream, o=o)
 
     def rs_call(evs=None, arrival=fo.ARR_DEFAULT, links=args.links, groups=args.row_groups,
@@ -237,26 +250,40 @@ def main():
         # one DMA engine per peer (the xGMI mesh) with row-group arrivals (the default), the same
         # with whole slices (the page's granularity), and every transfer over one link (the
         # ring of the page's Flash-AG, where all slices come from one neighbour)
-        variants = [("mesh_rowgroups", 0, 0), ("mesh_slices", 0, 1), ("onelink_slices", 1, 1)]
+        # (name, links, row groups, Flash-AG K blocks). With --ag-k-chunks > 1 the K-block
+        # variant is the timed step's configuration; it changes Flash-AG only, so its RS entry
+        # repeats the row-major one.
+        variants = [("mesh_rowgroups", 0, 0, 0), ("mesh_slices", 0, 1, 0),
+                    ("onelink_slices", 1, 1, 0)]
+        if kc > 1:
+            variants.insert(1, ("mesh_rowgroups_kblocks", 0, 0, kc))
 
-        def groups_of(kind, case, req):
-            order = fo.tile_order(kind, P, case.m, case.K, case.N, o=fo.opts(row_groups=req),
+        def groups_of(kind, case, req, chunks=0):
+            order = fo.tile_order(kind, P, case.m, case.K, case.N,
+                                  o=fo.opts(row_groups=req, k_chunks=chunks),
                                   out_dt=fo.F32 if kind == "rs" else fo.BF16)
             return max(g for _, g, _, _ in order) + 1
 
         t_ref_ag = timed(lambda: fo.gemm_ref(ag_full, ag_w, ref_y_ag, stream=stream), reps)
         t_ref_rs = timed(lambda: fo.gemm_ref(rs_x, rs_w, ref_y_rs, stream=stream), reps)
-        t0_ag = timed(lambda: ag_call(arrival=fo.ARR_NONE), reps)
         t0_rs = timed(lambda: rs_call(arrival=fo.ARR_NONE), reps)
-        for name, links, req in variants:
-            to_ag = fo.opts(links=links, row_groups=groups_of("ag", ag_case, req))
+        for name, links, req, chunks in variants:
+            t0_ag = timed(lambda: ag_call(arrival=fo.ARR_NONE, chunks=chunks), reps)
+            # the same copies alone: each row group of each slice in `chunks` equal K blocks
+            to_ag = fo.opts(links=links,
+                            row_groups=groups_of("ag", ag_case, req, chunks) * max(1, chunks))
             to_rs = fo.opts(links=links, row_groups=groups_of("rs", rs_case, req))
             tx_ag = timed(lambda: fo.transfer_ref("ag", ag_slices, ag_recv, P, r,
                                                   ag_case.m * ag_case.K * 2, stream, to_ag), reps)
-            tx_rs = timed(lambda: fo.transfer_ref("rs", rs_peer, rs_recv, P, r,
-                                                  rs_case.m * rs_case.N * 4, stream, to_rs), reps)
-            ts_ag = timed(lambda: ag_call(links=links, groups=req), reps)
-            ts_rs = timed(lambda: rs_call(links=links, groups=req), reps)
+            ts_ag = timed(lambda: ag_call(links=links, groups=req, chunks=chunks), reps)
+            if chunks > 1 and "mesh_rowgroups" in exposure:
+                tx_rs, ts_rs = tx_rs_prev, ts_rs_prev
+            else:
+                tx_rs = timed(lambda: fo.transfer_ref("rs", rs_peer, rs_recv, P, r,
+                                                      rs_case.m * rs_case.N * 4, stream, to_rs),
+                              reps)
+                ts_rs = timed(lambda: rs_call(links=links, groups=req), reps)
+            tx_rs_prev, ts_rs_prev = tx_rs, ts_rs
             exposure[name] = {
                 "ag": {"t_ref_us": t_ref_ag * 1e3, "t_slice0_us": t0_ag * 1e3,
                        "t_slice_us": ts_ag * 1e3, "t_xfer_us": tx_ag * 1e3,
@@ -271,8 +298,8 @@ def main():
                 f"xfer {tx_rs*1e3:.0f} -> {exposure[name]['rs']['exposed_frac']:.3f}")
         # the page's comparison at the rank that data slicing serves worst (P-1: its own RS chunk
         # and its local AG slice come last in index order): vanilla (all transfers, then the
-        # GEMM, nothing overlapped), data slicing (index order, whole slices) and Flash (the
-        # defaults). "removed" = the share of the transfer time that does not show in the
+        # GEMM, nothing overlapped), data slicing (index order, whole row-major slices) and Flash
+        # (the defaults). "removed" = the share of the transfer time that does not show in the
         # latency, the page's communication-overhead reduction against vanilla.
         rb = P - 1
         tw = fo.opts(row_groups=1)
@@ -281,8 +308,10 @@ def main():
         tx_rs = timed(lambda: fo.transfer_ref("rs", rs_peer, rs_recv, P, rb,
                                               rs_case.m * rs_case.N * 4, stream, tw), reps)
         base = {}
+        natural = {"ag": lambda: ag_call(order=fo.ORDER_NATURAL, groups=1, rank=rb, chunks=0),
+                   "rs": lambda: rs_call(order=fo.ORDER_NATURAL, groups=1, rank=rb)}
         for kind, t_ref, t_x, call in (("ag", t_ref_ag, tx_ag, ag_call), ("rs", t_ref_rs, tx_rs, rs_call)):
-            t_ds = timed(lambda: call(order=fo.ORDER_NATURAL, groups=1, rank=rb), reps)
+            t_ds = timed(natural[kind], reps)
             t_fl = timed(lambda: call(rank=rb), reps)
             van = t_ref + t_x
             base[kind] = {"rank": rb, "t_ref_us": t_ref * 1e3, "t_xfer_us": t_x * 1e3,
@@ -304,10 +333,11 @@ def main():
         def block(rank, natural, fused=False):
             g = 1 if natural else args.row_groups
             o = fo.ORDER_NATURAL if natural else fo.ORDER_FLASH
+            c = 0 if natural else kc  # data slicing keeps row-major slices
             if fused:  # the activation in the gate+up projection's write-back
-                ag_call(order=o, groups=g, rank=rank, epilogue=fo.EPI_SWIGLU, y=mlp_h)
+                ag_call(order=o, groups=g, rank=rank, epilogue=fo.EPI_SWIGLU, y=mlp_h, chunks=c)
             else:
-                ag_call(order=o, groups=g, rank=rank)
+                ag_call(order=o, groups=g, rank=rank, chunks=c)
                 fo.swiglu(ag_y, mlp_h, stream)
             rs_call(order=o, groups=g, rank=rank, x=mlp_h)
 
@@ -379,6 +409,14 @@ def main():
         "kernel": f"gemm_bf16_kernel<{bm},{bn}> ({'fo_ag_gemm' if dom == 'ag' else 'fo_gemm_rs'})",
         "kernel_us": round(dom_ms * 1e3, 1), "workgroups": wg,
         "ag_kernel_us": round(mean_ag * 1e3, 1), "rs_kernel_us": round(mean_rs * 1e3, 1),
+        # both launches of the step against the same peak; each launch's time includes its
+        # in-kernel waits for the emulated transfers (the RS one waits for 117 MB of partials)
+        "per_kernel": {
+            kind: {"kernel_us": round(t * 1e3, 1),
+                   "achieved": round(f / (t * 1e-3) / 1e12, 1),
+                   "frac": round(f / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                   "traffic": traffic_for(kind)}
+            for kind, t, f in (("ag", mean_ag, ag_case.flops), ("rs", mean_rs, rs_case.flops))},
     }
     log(f"timed: {args.steps} steps {total_ms:.2f} ms (host {host_s*1e3:.2f} ms), "
         f"{ms_per_step*1e3:.1f} us/step, {value:.1f} TFLOP/s; AG kernel {mean_ag*1e3:.1f} us, "
@@ -397,6 +435,7 @@ def main():
                    "transfers": "SDMA engines, %s" % ("one per peer" if args.links == 0
                                                       else "%d link(s)" % args.links),
                    "row_groups": "one per tile row" if args.row_groups == 0 else args.row_groups,
+                   "ag_k_blocks": kc if kc > 1 else "row-major slices",
                    "ag_arrival": "eager", "rs_arrival": "lockstep"},
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "exposed_transfer": exposure,

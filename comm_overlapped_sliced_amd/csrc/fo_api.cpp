@@ -174,7 +174,8 @@ fo_status check_opts(const fo_opts* o, fo_opts* out) {
     return invalid("opts.row_groups %d outside [0, %d]", o->row_groups, fo::kMaxGroups);
   if (o->epilogue != FO_EPI_NONE && o->epilogue != FO_EPI_SWIGLU)
     return invalid("opts.epilogue %d is not a fo_epilogue", o->epilogue);
-  if (o->reserved) return invalid("opts.reserved must be zero");
+  if (o->k_chunks < 0 || o->k_chunks > fo::kMaxGroups)
+    return invalid("opts.k_chunks %d outside [0, %d]", o->k_chunks, fo::kMaxGroups);
   *out = *o;
   if (out->spin_timeout_us == 0) out->spin_timeout_us = kDefaultTimeoutUs;
   return FO_OK;
@@ -237,6 +238,9 @@ void set_groups(int req, fo::Plan& p) {
 // index order.
 void set_layout(int kind, const fo_opts& o, fo::Plan& p) {
   set_groups(o.row_groups, p);
+  // Flash-AG with K-chunk-major slices: groups x chunks arrival units per slice
+  const int c = kind == 0 ? std::max(1, o.k_chunks) : 1;
+  if (c > 1 && p.grid.groups * c > fo::kMaxGroups) set_groups(fo::kMaxGroups / c, p);
   p.grid.lead = (kind == 0 && o.order == FO_ORDER_FLASH) ? 1 : 0;
   p.grid.trail = (kind == 1 && o.order == FO_ORDER_FLASH) ? 1 : 0;
 }
@@ -423,6 +427,12 @@ fo_status fo_ag_gemm(const void* x_local, const void* const* x_peer, void* x_rec
     return invalid("the SwiGLU epilogue needs bf16 operands and output and N %% 16 == 0 (N %lld)",
                    (long long)N);
   const int64_t n_out = act ? N / 2 : N;  // columns of y
+  const int chunks = std::max(1, o.k_chunks);
+  if (chunks > 1 && (in_dt != FO_DT_BF16 || K % (256 * chunks) ||
+                     (double)m * K * 2 > (double)(1 << 30)))
+    return unsupported("opts.k_chunks %d needs bf16 operands, K a multiple of 256 * k_chunks and "
+                       "m * K * 2 <= 2^30 bytes (K %lld, m %lld)", chunks, (long long)K,
+                       (long long)m);
   const bool arrivals = x_peer != nullptr && o.arrival != FO_ARR_NONE && P > 1;
   const size_t es = dt_size(in_dt), os = dt_size(out_dt);
   const size_t align = in_dt == FO_DT_BF16 ? 16 : 4;
@@ -458,8 +468,12 @@ fo_status fo_ag_gemm(const void* x_local, const void* const* x_peer, void* x_rec
   s = tiles_for(in_dt, tile, m, N, P, p, &bm);
   if (s != FO_OK) return s;
   set_layout(0, o, p);
+  p.chunks = chunks;
+  // ceil(2^32 / steps per chunk): umulhi(step, magic) = step / steps per chunk (steps < 2^16)
+  p.chunk_magic = chunks > 1 ? (uint32_t)((((uint64_t)1 << 32) + K / chunks / 32 - 1) /
+                                          (uint64_t)(K / chunks / 32)) : 0u;
   fo::dma::Call call{};
-  if (arrivals) FO_DMA(fo::dma::begin(st->dev, P, p.grid.groups, &call, &e_));
+  if (arrivals) FO_DMA(fo::dma::begin(st->dev, P, p.grid.groups * chunks, &call, &e_));
   int32_t order[FO_MAX_P];
   fo::slice_order(0, o.order, P, rank, order);
   for (int pos = 0; pos < P; ++pos) {
@@ -500,16 +514,21 @@ fo_status fo_ag_gemm(const void* x_local, const void* const* x_peer, void* x_rec
     int seq[FO_MAX_P];
     const int n = arrival_sequence(0, o.order, P, rank, seq);
     const int L = links_for(o, P);
-    const size_t row_b = (size_t)K * es;
+    // a K-chunk-major slice sends each row group block by block (unit g * chunks + j): rows
+    // r0 .. r1 of block j are contiguous, at (j * m + r0) rows of K / chunks values
+    const size_t row_b = (size_t)(K / chunks) * es;
     for (int g = 0; g < p.grid.groups; ++g) {
       int64_t r0, r1;
       group_span(p, bm, m, g, &r0, &r1);
       for (int t = 0; t < n; ++t) {
         const int sl = seq[t];
-        const size_t off = (size_t)sl * slice_b + (size_t)r0 * row_b;
-        FO_DMA(fo::dma::copy(st->dev, call, t % L, sl, g, -1, (uint8_t*)x_recv + off,
-                             (const uint8_t*)x_peer[sl] + (size_t)r0 * row_b,
-                             (size_t)(r1 - r0) * row_b, &e_));
+        for (int j = 0; j < chunks; ++j) {
+          const size_t in_slice = ((size_t)j * m + (size_t)r0) * row_b;
+          FO_DMA(fo::dma::copy(st->dev, call, t % L, sl, g * chunks + j, -1,
+                               (uint8_t*)x_recv + (size_t)sl * slice_b + in_slice,
+                               (const uint8_t*)x_peer[sl] + in_slice, (size_t)(r1 - r0) * row_b,
+                               &e_));
+        }
       }
     }
   }
@@ -526,6 +545,7 @@ fo_status fo_gemm_rs(const void* x_shard, const void* w, float* send_buf, float*
   s = check_common(P, rank, m, K, N, in_dt);
   if (s != FO_OK) return s;
   if (o.epilogue != FO_EPI_NONE) return invalid("opts.epilogue applies to fo_ag_gemm only");
+  if (o.k_chunks > 1) return invalid("opts.k_chunks applies to fo_ag_gemm only");
   const int arrival = o.arrival == FO_ARR_DEFAULT ? FO_ARR_LOCKSTEP : o.arrival;
   const bool arrivals = peer_partial != nullptr && arrival != FO_ARR_NONE && P > 1;
   const size_t es = dt_size(in_dt);
@@ -765,6 +785,7 @@ fo_status fo_attn(const void* qkv_local, const void* const* qkv_peer, void* qkv_
   if (o.arrival == FO_ARR_LOCKSTEP) return invalid("LOCKSTEP arrivals apply to fo_gemm_rs only");
   if (o.tile != FO_TILE_AUTO) return invalid("opts.tile applies to the GEMM calls only");
   if (o.epilogue != FO_EPI_NONE) return invalid("opts.epilogue applies to fo_ag_gemm only");
+  if (o.k_chunks > 1) return invalid("opts.k_chunks applies to fo_ag_gemm only");
   const bool arrivals = qkv_peer != nullptr && o.arrival != FO_ARR_NONE && P > 1;
   const size_t W = (size_t)(hq + 2 * hkv) * 256, slice_b = (size_t)m * W;
   if (!qkv_local || !out || (P > 1 && !qkv_recv)) return invalid("NULL buffer");
@@ -887,6 +908,7 @@ fo_status fo_transfer_ref(int32_t kind, const void* const* src, void* dst, int32
   fo_status s = check_opts(opts, &o);
   if (s != FO_OK) return s;
   if (o.epilogue != FO_EPI_NONE) return invalid("opts.epilogue applies to fo_ag_gemm only");
+  if (o.k_chunks > 1) return invalid("opts.k_chunks applies to fo_ag_gemm only");
   if (kind != 0 && kind != 1) return invalid("kind %d is neither 0 (AG) nor 1 (RS)", kind);
   if (P < 1 || P > FO_MAX_P || rank < 0 || rank >= P) return invalid("bad P %d / rank %d", P, rank);
   if (slice_bytes < 0 || slice_bytes % 4) return invalid("slice_bytes must be a multiple of 4");

@@ -232,16 +232,25 @@ __device__ __forceinline__ void bf16_tile(const Plan& p, const int tile, uint8_t
   const int64_t col0 = (int64_t)tn * (act ? BN / 2 : BN);
   const int64_t rows_valid = p.m - row0;  // >= 1
   const int a_rows = uni((int)(rows_valid < BM ? rows_valid : BM));
-  const uint16_t* A = (const uint16_t*)uni_ptr((const uint16_t*)p.a_pos[pos] + row0 * K);
+  // A slice is row-major [m, K] (chunks = 1) or K-chunk-major: `chunks` blocks [m, Kc] one
+  // after another. A points at the tile's first row in block 0; element (row, k) of the tile is
+  // at A + row * Kc + (k - j * Kc) + j * m * Kc for block j = k / Kc.
+  const int chunks = uni(p.chunks);
+  const int64_t Kc = chunks > 1 ? K / chunks : K;
+  const int64_t chunk_extra = (p.m - 1) * Kc;  // block j starts j * chunk_extra past k = j * Kc
+  const uint32_t chunk_magic = (uint32_t)uni((int)p.chunk_magic);
+  const uint16_t* A = (const uint16_t*)uni_ptr((const uint16_t*)p.a_pos[pos] + row0 * Kc);
   const uint16_t* W = (const uint16_t*)uni_ptr(p.b);
 
-  // Flash-AG: rows of a received slice are read only after their group has landed.
-  if (p.gate_slice[pos] >= 0) wait_groups_wg(p, p.gate_slice + pos, 1, grp);
+  // Flash-AG: rows of a received slice are read only after their group (its first K block when
+  // the slice travels in K blocks) has landed.
+  const int gslice = uni(p.gate_slice[pos]);
+  if (gslice >= 0) wait_groups_wg(p, p.gate_slice + pos, 1, grp * chunks);
 
   // ---- loads. Per-lane offsets are fixed for the whole K loop: the K step enters A's loads as
   // the scalar offset and W's through a descriptor re-based on the step's first row (whose
   // num_records also cuts off rows past K). Lanes outside the tile carry kOOB and read zeros.
-  const i32x4 rsrc_a = buffer_rsrc(A, (uint32_t)(a_rows * K * 2));
+  const i32x4 rsrc_a = buffer_rsrc(A, (uint32_t)(((chunks - 1) * p.m * Kc + a_rows * Kc) * 2));
   const uint32_t lds0 = lds_addr(lds_ring);
   const uint32_t a_base = (uint32_t)uni((int)(lds0 + wave * C::A_LOADS * 1024));
   const uint32_t b_base = (uint32_t)uni((int)(lds0 + C::A_BYTES + wave * C::B_LOADS * 1024));
@@ -251,7 +260,7 @@ __device__ __forceinline__ void bf16_tile(const Plan& p, const int tile, uint8_t
   for (int j = 0; j < C::A_LOADS; ++j) {
     const int row = (wave * C::A_LOADS + j) * 16 + (lane >> 2);
     a_kel[j] = ((lane & 3) ^ swz_a(row)) * 8;
-    a_voff[j] = row < a_rows ? (uint32_t)(((int64_t)row * K + a_kel[j]) * 2) : kOOB;
+    a_voff[j] = row < a_rows ? (uint32_t)(((int64_t)row * Kc + a_kel[j]) * 2) : kOOB;
   }
   uint32_t b_voff[C::B_LOADS];
 #pragma unroll
@@ -288,7 +297,11 @@ __device__ __forceinline__ void bf16_tile(const Plan& p, const int tile, uint8_t
       if constexpr (decltype(tail)::value) {
         if (k0 + a_kel[l] >= K) v = kOOB;
       }
-      load_lds16(rsrc_a, a_base, si * C::STAGE + l * 1024, v, (uint32_t)(k0 * 2));
+      // K block of this step (0 when row-major: chunk_magic = 0)
+      const uint32_t blk =
+          (uint32_t)__builtin_amdgcn_readfirstlane((int)__umulhi((uint32_t)kt, chunk_magic));
+      load_lds16(rsrc_a, a_base, si * C::STAGE + l * 1024, v,
+                 (uint32_t)((k0 + (int64_t)blk * chunk_extra) * 2));
     } else {
       const int j = l - C::A_LOADS;
       load_lds16(rb, b_base, si * C::STAGE + j * 1024, b_voff[j], 0u);
@@ -440,10 +453,28 @@ __device__ __forceinline__ void bf16_tile(const Plan& p, const int tile, uint8_t
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  // A received slice that travels in K blocks: the first loads of block j (step j * spc) are
+  // issued after the barrier of step j * spc - S, so before that barrier thread 0 waits for
+  // block j of the tile's row group to have landed (and acquires, like the wait at the start);
+  // the barrier holds the other waves until then. gate_kt = -1: nothing left to wait for.
+  const int spc = (int)(Kc / kBK);
+  int gate_kt = (gslice >= 0 && chunks > 1) ? spc - S : -1;
+  int gate_j = 1;
+  auto chunk_gate = [&](int kt) {
+    if (kt == gate_kt) {
+      if (tid == 0) {
+        wait_group(p, gslice, grp * chunks + gate_j);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
+      }
+      ++gate_j;
+      gate_kt = gate_j < chunks ? gate_kt + spc : -1;
+    }
+  };
   // Steady-state step: every step it loads lies entirely inside K.
   auto step_main = [&](int kt, int si) {
     first_half(si, kt + S - 1, true, false);
     wait_stages(S - 2);
+    chunk_gate(kt);
     lds_barrier();
     second_half(kt, si, true, false, true);
   };
@@ -453,6 +484,7 @@ __device__ __forceinline__ void bf16_tile(const Plan& p, const int tile, uint8_t
     first_half(si, late, late < KT, late >= KFULL);
     const int later = KT - 2 - kt;  // steps issued beyond kt + 1 (at most S - 2 at this point)
     wait_stages(later < 0 ? 0 : (later > S - 2 ? S - 2 : later));
+    chunk_gate(kt);
     lds_barrier();
     second_half(kt, si, kt + S < KT, kt + S >= KFULL, kt + 1 < KT);
   };

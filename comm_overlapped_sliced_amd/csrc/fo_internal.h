@@ -51,6 +51,11 @@ struct Plan {
   int32_t accum_pos;                 // position whose epilogue adds recv[] (-1: none)
   int32_t out_f32;                   // 1: fp32 output, 0: bf16 (round to nearest even)
   TileGrid grid;                      // tiles per position, row groups, dispatch layout
+  // K chunks of every A slice (1: row-major [m, K]; c > 1: c blocks [m, K/c] one after another).
+  // A gated tile waits for arrival unit grp * chunks + j before it reads block j. chunk_magic =
+  // ceil(2^32 / (K / c / 32)) gives a K step's block as umulhi(step, chunk_magic); 0 when c = 1.
+  int32_t chunks;
+  uint32_t chunk_magic;
 };
 
 // A plan with nothing to wait for: no gates, no awaited partials, no tables, no release.
@@ -63,6 +68,8 @@ inline Plan empty_plan() {
   p.accum_pos = -1;
   p.start = nullptr;
   p.act = 0;
+  p.chunks = 1;
+  p.chunk_magic = 0;
   return p;
 }
 

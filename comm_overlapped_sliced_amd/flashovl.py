@@ -39,7 +39,7 @@ class Opts(ctypes.Structure):
                 ("tile", ctypes.c_int32), ("spin_timeout_us", ctypes.c_uint32),
                 ("links", ctypes.c_int32), ("row_groups", ctypes.c_int32),
                 ("kernel_events", ctypes.c_void_p * 2), ("epilogue", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("k_chunks", ctypes.c_int32)]
 
 
 _lib = None
@@ -100,11 +100,11 @@ def _raise_on(status: int, where: str) -> None:
 
 
 def opts(order=ORDER_FLASH, arrival=ARR_DEFAULT, tile=TILE_AUTO, spin_timeout_us=0, links=0,
-         row_groups=0, kernel_events=None, epilogue=EPI_NONE) -> Opts:
+         row_groups=0, kernel_events=None, epilogue=EPI_NONE, k_chunks=0) -> Opts:
     o = Opts()
     load().fo_opts_init(ctypes.byref(o))
     o.order, o.arrival, o.tile, o.links = order, arrival, tile, links
-    o.row_groups, o.epilogue = row_groups, epilogue
+    o.row_groups, o.epilogue, o.k_chunks = row_groups, epilogue, k_chunks
     if spin_timeout_us:
         o.spin_timeout_us = spin_timeout_us
     if kernel_events is not None:

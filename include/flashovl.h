@@ -124,7 +124,16 @@ typedef struct fo_opts {
   void* kernel_events[2];   /* optional hipEvent_t pair recorded on the compute stream right
                                before and right after the GEMM kernel launch (profiling) */
   int32_t epilogue;         /* fo_epilogue (fo_ag_gemm only; else FO_ERR_INVALID_ARG) */
-  int32_t reserved;         /* must be zero */
+  int32_t k_chunks;         /* fo_ag_gemm only (else it must be 0 or 1): 0 or 1 = every X slice
+                               row-major [m, K]. c in 2..FO_MAX_GROUPS = every X slice (x_local,
+                               each x_peer[s], and slice s of x_recv) stored K-chunk-major: c
+                               blocks one after another, block j holding columns j*K/c ..
+                               (j+1)*K/c - 1 of the slice's m rows, row-major [m, K/c]. Each row
+                               group of a received slice then travels as c transfers, block by
+                               block, and its tiles start once block 0 has landed, waiting for
+                               block j only before they read its columns. Needs bf16 operands,
+                               K a multiple of 256*c and m*K*2 <= 2^30 bytes (else
+                               FO_ERR_UNSUPPORTED); row groups are capped at FO_MAX_GROUPS / c */
 } fo_opts;
 
 /* Fills *o with the defaults (FLASH order, DEFAULT arrival, AUTO tile, 2 s bound, one link per
@@ -144,6 +153,9 @@ void fo_opts_init(fo_opts* o);
  * Slices are computed in the Flash-AG order (rank, rank-1, ..., rank-P+1 mod P); slice s != rank
  * is read only after its transfer has landed. in_dt and out_dt: BF16 or F32; out_dt BF16
  * rounds the fp32 accumulator to nearest-even. No output may overlap an input.
+ * With opts.k_chunks = c > 1 every X slice (x_local, x_peer[s], slice s of x_recv, each m*K
+ * values at the same places) is in the K-chunk-major layout described at fo_opts; y is
+ * unchanged and equal, bit for bit, to the row-major call's.
  */
 fo_status fo_ag_gemm(const void* x_local, const void* const* x_peer, void* x_recv, const void* w,
                      void* y, int32_t P, int32_t rank, int64_t m, int64_t K, int64_t N,

@@ -48,7 +48,7 @@ def test_opts_defaults():
     assert (o.order, o.arrival, o.tile, o.links) == (0, 0, 0, 0)
     assert o.spin_timeout_us == 2_000_000
     assert list(o.kernel_events) == [None, None]
-    assert o.row_groups == 0 and o.epilogue == fo.EPI_NONE and o.reserved == 0
+    assert o.row_groups == 0 and o.epilogue == fo.EPI_NONE and o.k_chunks == 0
     assert ctypes.sizeof(fo.Opts) == 48
 
 
@@ -135,12 +135,33 @@ def test_ag_rejects(lib, kw):
 def test_ag_rejects_bad_opts(lib):
     for field, val in [("order", 9), ("arrival", 7), ("tile", 11), ("links", 33), ("links", -1),
                        ("row_groups", 9), ("row_groups", -1), ("epilogue", 2),
-                       ("epilogue", -1), ("reserved", 1)]:
+                       ("epilogue", -1), ("k_chunks", 9), ("k_chunks", -1)]:
         o = fo.opts()
         setattr(o, field, val)
         assert _ag(lib, opts=ctypes.byref(o)) == fo.FO_ERR_INVALID_ARG
     o = fo.opts(arrival=fo.ARR_LOCKSTEP)
     assert _ag(lib, opts=ctypes.byref(o)) == fo.FO_ERR_INVALID_ARG
+
+
+def test_ag_k_chunks_unsupported_shapes(lib):
+    # K-chunk-major slices: bf16 only, K a multiple of 256 per chunk, slices of at most 2^30 bytes
+    o = ctypes.byref(fo.opts(k_chunks=2))
+    assert _ag(lib, opts=o, K=256) == fo.FO_ERR_UNSUPPORTED          # 128 columns per chunk
+    assert _ag(lib, opts=o, K=768) == fo.FO_ERR_UNSUPPORTED          # 384 columns per chunk
+    assert _ag(lib, opts=o, K=512, in_dt=fo.F32, out_dt=fo.F32) == fo.FO_ERR_UNSUPPORTED
+    assert _ag(lib, opts=o, m=65536, K=16384) == fo.FO_ERR_UNSUPPORTED  # 2^31-byte slices
+    assert "k_chunks" in lib.fo_last_error().decode()
+
+
+def test_k_chunks_only_for_ag(lib):
+    o = ctypes.byref(fo.opts(k_chunks=2))
+    assert _rs(lib, opts=o, K=512) == fo.FO_ERR_INVALID_ARG
+    assert _attn(lib, opts=o) == fo.FO_ERR_INVALID_ARG
+    # 0 and 1 both mean row-major, accepted everywhere
+    for c in (0, 1):
+        o = ctypes.byref(fo.opts(k_chunks=c))
+        assert _rs(lib, opts=o, m=0) == fo.FO_OK
+        assert _attn(lib, opts=o, m=0) == fo.FO_OK
 
 
 def test_ag_swiglu_epilogue_rejects(lib):

@@ -1,0 +1,144 @@
+"""GPU tests of Flash-AG with K-chunk-major slices (opts.k_chunks): every X slice stored as c
+column blocks [m, K/c] one after another, each row group of a received slice sent block by block,
+and a tile waiting for block j only before it reads block j's columns.
+
+The accumulation order over K is the same as with row-major slices (K steps in order), so the
+output must equal the row-major call's bit for bit; it is also checked against the oracle. Late
+blocks are forced by the sizes (large slices over one emulated link against a narrow GEMM), so
+that the waits inside the K loop are exercised, with NaN-poisoned receive buffers."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from comm_overlapped_sliced_amd import configs, flashovl as fo, inputs
+from tests.gpu_helpers import TOL_BF16, from_dev, rel_frobenius, sample_indices, to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+    fo.load()
+    return torch.device("cuda:0")
+
+
+def _stream():
+    return torch.cuda.current_stream()
+
+
+def chunk_major(t, c: int):
+    """[m, K] -> the same values as c blocks [m, K/c] one after another (block j = columns
+    j*K/c .. (j+1)*K/c - 1)."""
+    m, K = t.shape
+    return t.reshape(m, c, K // c).permute(1, 0, 2).contiguous().reshape(m, K)
+
+
+class AGC:
+    """Device buffers of one Flash-AG problem, row-major and K-chunk-major."""
+
+    def __init__(self, x: np.ndarray, w: np.ndarray, P: int, c: int, dev):
+        self.P, self.c = P, c
+        self.M, self.K = x.shape
+        self.m = self.M // P
+        self.N = w.shape[1]
+        xd = to_dev(x, dev)
+        self.rows = [xd[s * self.m:(s + 1) * self.m].contiguous() for s in range(P)]
+        self.chunked = [chunk_major(r, c) for r in self.rows]
+        self.w_d = to_dev(w, dev)
+        self.x_recv = torch.empty((self.M, self.K), dtype=torch.bfloat16, device=dev)
+        self.y = torch.empty((self.M, self.N), dtype=torch.bfloat16, device=dev)
+
+    def run(self, r, chunks=True, resident=False, **kw):
+        peers = self.chunked if chunks else self.rows
+        o = fo.opts(k_chunks=self.c if chunks else 0, **kw)
+        if resident:
+            for s in range(self.P):
+                if s != r:
+                    self.x_recv[s * self.m:(s + 1) * self.m].copy_(peers[s])
+        self.y.view(torch.int16).fill_(-1)
+        fo.ag_gemm(peers[r], None if resident else peers, self.x_recv, self.w_d, self.y, self.P,
+                   r, compute_stream=_stream(), o=o)
+        fo.check(_stream())
+        return from_dev(self.y)
+
+
+@pytest.mark.parametrize("shape,c", [((8, 512, 2048, 1024), 2), ((8, 512, 2048, 1024), 4),
+                                     ((8, 512, 2048, 1024), 8), ((4, 200, 1024, 392), 2),
+                                     ((4, 200, 1024, 392), 4), ((3, 300, 512, 136), 2)],
+                         ids=lambda v: str(v))
+@pytest.mark.parametrize("tile", [fo.TILE_AUTO, fo.TILE_128x256, fo.TILE_128x128, fo.TILE_64x64])
+def test_kchunks_equal_row_major(dev, shape, c, tile):
+    P, m, K, N = shape
+    x = inputs.normal(8100 + c, (P * m, K), 1.0, "bf16")
+    w = inputs.normal(8101, (K, N), 0.02, "bf16")
+    prob = AGC(x, w, P, c, dev)
+    ref = oracle.gemm(x, w)
+    for r, groups, links in ((0, 0, 0), (P - 1, 1, 0), (1 % P, 0, 1)):
+        base = prob.run(r, chunks=False, tile=tile, row_groups=groups, links=links)
+        got = prob.run(r, tile=tile, row_groups=groups, links=links)
+        assert np.array_equal(got, base), f"rank {r}: chunk-major != row-major"
+        assert rel_frobenius(got, ref) <= TOL_BF16
+        res = prob.run(r, resident=True, tile=tile, row_groups=groups)
+        assert np.array_equal(res, base), f"rank {r}: resident chunk-major != row-major"
+
+
+@pytest.mark.parametrize("c", [2, 4, 8])
+def test_kchunks_late_blocks_poisoned(dev, c):
+    """Seven 8 MiB slices over one link against a GEMM with N = 128: every tile of a received
+    slice waits for its blocks inside the K loop; the receive buffer is NaN before each call."""
+    P, m, K, N = 8, 1024, 4096, 128
+    x = inputs.normal(8200 + c, (P * m, K), 1.0, "bf16")
+    w = inputs.normal(8201, (K, N), 0.02, "bf16")
+    prob = AGC(x, w, P, c, dev)
+    ref = oracle.gemm(x, w)
+    for r in (2, 5):
+        for links in (1, 0):
+            prob.x_recv.view(torch.int16).fill_(-1)
+            got = prob.run(r, links=links)
+            assert not np.isnan(got).any()
+            assert rel_frobenius(got, ref) <= TOL_BF16, f"rank {r} links {links}"
+
+
+def test_kchunks_missed_block_times_out(dev):
+    """A 1 us bound on the in-kernel waits against blocks that take a millisecond to arrive: the
+    call reports FO_ERR_TIMEOUT, every kernel finishes, and the next call is correct again."""
+    P, m, K, N = 8, 1024, 4096, 128
+    x = inputs.normal(8300, (P * m, K), 1.0, "bf16")
+    w = inputs.normal(8301, (K, N), 0.02, "bf16")
+    prob = AGC(x, w, P, 4, dev)
+    st = fo.ag_gemm(prob.chunked[1], prob.chunked, prob.x_recv, prob.w_d, prob.y, P, 1,
+                    compute_stream=_stream(), o=fo.opts(spin_timeout_us=1, links=1, k_chunks=4),
+                    raw=True)
+    assert st == fo.FO_OK
+    with pytest.raises(fo.FoError) as ei:
+        fo.check(_stream())
+    assert ei.value.status == fo.FO_ERR_TIMEOUT
+    fo.check(_stream())
+    got = prob.run(1)
+    assert rel_frobenius(got, oracle.gemm(x, w)) <= TOL_BF16
+
+
+@pytest.mark.parametrize("case,c", [(configs.L70B_AG, 4), (configs.L70B_AG, 2),
+                                    (configs.L405B_AG, 2)],
+                         ids=lambda v: v.name.split(",")[0] if hasattr(v, "name") else str(v))
+def test_kchunks_full_size(dev, case, c):
+    x, w = case.x(), case.w()
+    prob = AGC(x, w, case.P, c, dev)
+    y_ref = torch.empty_like(prob.y)
+    fo.gemm_ref(to_dev(x, dev), prob.w_d, y_ref, stream=_stream())
+    torch.cuda.synchronize()
+    mono = from_dev(y_ref)
+    rows, cols = sample_indices(case.M, case.N, 1500, seed=case.M + c, block_rows=case.m)
+    slices = [x[s * case.m:(s + 1) * case.m] for s in range(case.P)]
+    ref = oracle.ag_sampled(slices, w, rows, cols)
+    for r in (0, 5):
+        got = prob.run(r)
+        assert rel_frobenius(got[rows, cols], ref) <= TOL_BF16, f"rank {r}"
+        assert np.array_equal(got, mono), f"rank {r}: chunk-major sliced != unsliced"

@@ -71,6 +71,19 @@ def test_natural_order_is_group_major_over_every_slice(kind):
     assert {p for p, *_ in order[:len(order) // 2]} == {0, 1, 2, 3}  # no slice is held back
 
 
+@pytest.mark.parametrize("chunks,groups", [(2, 0), (4, 0), (4, 8), (8, 0), (8, 2), (3, 0)])
+def test_k_chunks_cap_the_row_groups(chunks, groups):
+    """K-chunk-major Flash-AG: each row group of a received slice travels as `chunks` transfers,
+    so the row groups per slice are capped at FO_MAX_GROUPS / chunks (8 arrival units)."""
+    P, m, K, N = 8, 1024, 16384, 13312
+    order = fo.tile_order("ag", P, m, K, N, o=fo.opts(tile=fo.TILE_128x256, row_groups=groups,
+                                                      k_chunks=chunks))
+    G = len({g for _, g, _, _ in order})
+    want = min(8 if groups == 0 else groups, 8 // chunks)
+    assert G == want and G * chunks <= 8
+    assert len({(p, tm, tn) for p, _, tm, tn in order}) == P * 8 * 52
+
+
 def test_rejects():
     lib = fo.load()
     import ctypes
