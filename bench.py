@@ -422,7 +422,7 @@ def main():
         f"{ms_per_step*1e3:.1f} us/step, {value:.1f} TFLOP/s; AG kernel {mean_ag*1e3:.1f} us, "
         f"RS kernel {mean_rs*1e3:.1f} us")
 
-    cpu = cpu_baseline(ag_case, args.cpu_seconds) if args.cpu_seconds > 0 else None
+    cpu = cpu_baseline(ag_case, rs_case, args.cpu_seconds) if args.cpu_seconds > 0 else None
 
     line = {
         "metric": "sliced AG/RS-GEMM TFLOP/s, % bf16 MFMA peak, exposed-transfer % (1 GPU)",
@@ -461,30 +461,34 @@ def traffic_for(dom: str):
     return ent.get("bytes_per_launch")
 
 
-def cpu_baseline(case, target_s: float):
-    """The oracle (plain fp64 C, OpenMP) on a bounded sample of the Flash-AG product: the first
-    R rows of X times the full W, R chosen so the run takes about target_s seconds."""
+def cpu_baseline(ag_case, rs_case, target_s: float):
+    """The oracle (plain fp64 C, OpenMP) on a bounded sample of the step's two products: rows of
+    the Flash-AG product (X times the full W), then rows of the Flash-RS product, in batches of
+    doubling size (32 rows per thread first) until about target_s seconds have been spent. Every
+    batch is a full oracle call on rows not computed before; the rate is all flops over all time."""
     import oracle
 
-    x = case.x()
-    w = case.w()
     orc = oracle.default()
-    probes = []
-    for n in (16, 64):  # separate the per-call decode of W from the per-row cost
-        t0 = time.perf_counter()
-        orc.gemm(x[:n], w)
-        probes.append(time.perf_counter() - t0)
-    per_row = max((probes[1] - probes[0]) / 48, 1e-6)
-    fixed = max(probes[0] - 16 * per_row, 0.0)
-    rows = int(max(64, min(case.M, (target_s - fixed) / per_row)))
-    t0 = time.perf_counter()
-    orc.gemm(x[:rows], w)
-    secs = time.perf_counter() - t0
-    fl = 2.0 * rows * case.K * case.N
-    return {"value": round(fl / secs / 1e12, 6), "unit": "TFLOP/s", "cores": orc.num_threads(),
-            "kind": "oracle",
-            "sample": f"first {rows} of {case.M} rows of the Flash-AG product "
-                      f"(K={case.K}, N={case.N}), fp64, {secs:.1f} s"}
+    threads = orc.num_threads()
+    parts, fl, secs = [], 0.0, 0.0
+    for case in (ag_case, rs_case):
+        if secs >= target_s:
+            break
+        x = case.x()
+        w = case.w()
+        done, batch = 0, 32 * threads
+        while done < case.M and secs < target_s:
+            n = min(batch, case.M - done)
+            t0 = time.perf_counter()
+            orc.gemm(x[done:done + n], w)
+            secs += time.perf_counter() - t0
+            fl += 2.0 * n * case.K * case.N
+            done += n
+            batch *= 2
+        parts.append(f"first {done} of {case.M} rows of the {case.call.upper()} product "
+                     f"(K={case.K}, N={case.N})")
+    return {"value": round(fl / secs / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle", "sample": "; ".join(parts) + f"; fp64, {secs:.1f} s"}
 
 
 if __name__ == "__main__":
