@@ -110,6 +110,7 @@ struct Slot {
   hipEvent_t ev = nullptr;  // recorded after the call's last kernel that reads the signals
   bool pending = false;     // used by a call that may not be complete yet
   std::bitset<kSignals> issued;  // completion signals a copy will decrement
+  uint32_t started = 0;          // engines that already hold a copy of the call waiting on start
 };
 
 struct Dev {
@@ -294,6 +295,7 @@ bool begin(int dev, int P, int groups, Call* call, std::string* err) {
       g_hsa.store(sl.comp[i * kMaxGroups + g], 1);
     }
   sl.issued.reset();
+  sl.started = 0;
   sl.pending = true;
   d.next = (k + 1) % kSlots;
   call->slot = k;
@@ -312,12 +314,22 @@ bool copy(int dev, const Call& call, int link, int slice, int group, int rel_pos
     g_hsa.store(sl.comp[ci], 0);
     return true;
   }
-  hsa_signal_t deps[2] = {sl.start, {}};
-  uint32_t n = 1;
-  if (rel_pos >= 0) deps[n++] = sl.rel[rel_pos * kMaxGroups + group];
-  const uint32_t eng = d.eng[(link % d.n_eng + d.n_eng) % d.n_eng];
-  const hsa_status_t s = g_hsa.copy(dst, d.agent, src, d.agent, bytes, n, deps, sl.comp[ci],
-                                    (hsa_amd_sdma_engine_id_t)eng, true);
+  // An engine runs its copies one after the other in issue order, so only the call's first copy
+  // on an engine waits for the start signal; a copy gated on a release signal needs no start
+  // signal at all (the kernel stores the release after it has started).
+  const int ei = (link % d.n_eng + d.n_eng) % d.n_eng;
+  const uint32_t eng = d.eng[ei];
+  hsa_signal_t deps[1];
+  uint32_t n = 0;
+  if (rel_pos >= 0) {
+    deps[n++] = sl.rel[rel_pos * kMaxGroups + group];
+  } else if (!(sl.started & (1u << ei))) {
+    deps[n++] = sl.start;
+    sl.started |= 1u << ei;
+  }
+  // (the runtime rejects a dependency array with a count of zero: pass none then)
+  const hsa_status_t s = g_hsa.copy(dst, d.agent, src, d.agent, bytes, n, n ? deps : nullptr,
+                                    sl.comp[ci], (hsa_amd_sdma_engine_id_t)eng, true);
   if (s != HSA_STATUS_SUCCESS) {
     // the kernel must not wait for a copy that was never issued: report it as failed
     g_hsa.store(sl.comp[ci], -1);
