@@ -87,6 +87,7 @@ struct DevState {
   int wall_khz = 100000;     // wall-clock counter rate read by the kernels' bounded waits
   uint32_t* err = nullptr;   // wait record: 1 timeout, 2 failed copy (uncached memory)
   uint32_t* go = nullptr;    // the tail reduce's start word (same uncached block)
+  uint32_t* own_done = nullptr;  // Flash-RS tail: own-chunk row groups stored [group] (same block)
   uint32_t go_value = 0;
   uint32_t* done = nullptr;  // completed-tile counters [position][group]
   uint32_t* arr_lead = nullptr;   // arrival-poller election and landed words [slice][group]
@@ -112,6 +113,7 @@ fo_status ensure_ready(int dev, DevState& st) {
   FO_HIP(hipExtMallocWithFlags(&p, 4096, hipDeviceMallocUncached));
   st.err = (uint32_t*)p;
   st.go = (uint32_t*)((uint8_t*)p + 256);
+  st.own_done = (uint32_t*)((uint8_t*)p + 512);
   FO_HIP(hipMemset(p, 0, 4096));
   const size_t words = (size_t)FO_MAX_P * fo::kMaxGroups * sizeof(uint32_t);
   FO_HIP(hipExtMallocWithFlags(&p, 2 * words, hipDeviceMallocUncached));
@@ -625,6 +627,22 @@ fo_status fo_gemm_rs(const void* x_shard, const void* w, float* send_buf, float*
   p.N = N;
   p.grid.npos = P;
   p.out_f32 = 1;
+  // Flash-RS tail: the own chunk's tiles store their sums and workgroups appended to the grid add
+  // the partials (same order, same bits), spread over the CUs the other chunks have freed. Needs
+  // 16-byte aligned out and partials (else the own tiles add them in their epilogue).
+  if (!natural && P > 1 && in_dt == FO_DT_BF16 && aligned(out, 16) &&
+      (double)m * N * 4 < (double)(1u << 31)) {
+    bool al = true;
+    for (int i = 0; i < P - 1; ++i) al = al && aligned(p.recv[i], 16);
+    if (al) {
+      const int64_t rows_g = (int64_t)p.grid.group_rows * bm;
+      const int64_t pieces = rows_g * N / 4;  // 16-byte pieces of a full group
+      p.tail_per_group = (int32_t)std::max<int64_t>(1, std::min<int64_t>(128, pieces / 2048));
+      p.tail_units = p.grid.groups * p.tail_per_group;
+      p.tail_bm = bm;
+      p.own_done = st->own_done;
+    }
+  }
 
   hipStream_t cs = (hipStream_t)compute_stream;
   if (arrivals) p.start = call.start;

@@ -54,8 +54,11 @@ __device__ __forceinline__ void wait_groups_wg(const Plan& p, const int32_t* sli
 // into its release signal (polled by the copy engine that carries the matching transfer) and
 // re-arms the counter. Every wave first waits for its own stores of the tile (the workgroup
 // barrier does not), so that the release below covers the whole tile.
+// With the Flash-RS tail, the last tile of a row group of the own chunk also raises
+// own_done[group] to the call's number, which the tail workgroups of that group wait for.
 __device__ __forceinline__ void release_tile(const Plan& p, int pos, int grp) {
-  if (p.rel_tab == nullptr) return;
+  const bool own = p.tail_units > 0 && pos == p.accum_pos;
+  if (p.rel_tab == nullptr && !own) return;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -64,8 +67,11 @@ __device__ __forceinline__ void release_tile(const Plan& p, int pos, int grp) {
     const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     if (old + 1 == (uint32_t)(group_rows_of(p.grid, grp) * p.grid.tiles_n)) {
       __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(p.rel_tab[pos * kMaxGroups + grp], (int64_t)0, __ATOMIC_RELEASE,
-                         __HIP_MEMORY_SCOPE_SYSTEM);
+      if (p.rel_tab != nullptr)
+        __hip_atomic_store(p.rel_tab[pos * kMaxGroups + grp], (int64_t)0, __ATOMIC_RELEASE,
+                           __HIP_MEMORY_SCOPE_SYSTEM);
+      if (own)
+        __hip_atomic_store(p.own_done + grp, p.gen, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -507,7 +513,8 @@ __device__ __forceinline__ void bf16_tile(const Plan& p, const int tile, uint8_t
   // that covers the tile's valid rows, so rows past the slice are dropped by the range check;
   // columns past N get an offset outside every range. Nothing waits for the stores here: the
   // next tile's loads overlap them (release_tile waits for them where a copy engine reads them).
-  const bool accum = (pos == p.accum_pos);
+  // the own chunk adds its partials here, unless the tail workgroups do (tail_units > 0)
+  const bool accum = (pos == p.accum_pos) && p.tail_units == 0;
   if (accum) wait_groups_wg(p, p.recv_slice, p.n_recv, grp);
   lds_barrier();  // LDS stages no longer read
   float* const ep = (float*)lds_ring;  // [ER rows][EW floats]
@@ -651,13 +658,85 @@ __device__ __forceinline__ void bf16_tile(const Plan& p, const int tile, uint8_t
 // The call's copies wait for its start signal (fo_wait.h).
 __device__ __forceinline__ void release_start(const Plan& p) { fo::release_start(p.start); }
 
+// Flash-RS tail unit u: piece u % tail_per_group of row group g = u / tail_per_group of the own
+// chunk. Once the group's tiles have stored their fp32 sums (own_done) and the group's partials
+// have landed, out += recv[0], then recv[1], ... for each element, the fused epilogue's order,
+// so the result is the same bit for bit. The last group's partials land together at the end of
+// the call; spread over these workgroups their adds take a few microseconds instead of running
+// through the group's own tiles alone. 16-byte pieces throughout (the host checks alignment).
+__device__ __forceinline__ void rs_tail_unit(const Plan& p, int u) {
+  const int g = u / p.tail_per_group, k = u % p.tail_per_group;
+  const int64_t r0 = (int64_t)g * p.grid.group_rows * p.tail_bm;
+  const int64_t r1 = (int64_t)(g + 1) * p.grid.group_rows * p.tail_bm < p.m
+                         ? (int64_t)(g + 1) * p.grid.group_rows * p.tail_bm : p.m;
+  if (r0 >= r1) return;
+  if (threadIdx.x == 0) {
+    wait_gen(p.own_done + g, p.gen, p.spin_limit, p.err);
+    if (p.comp_tab != nullptr)
+      for (int i = 0; i < p.n_recv; ++i)
+        if (p.recv_slice[i] >= 0) wait_group(p, p.recv_slice[i], g);
+  }
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
+  const int64_t N = p.N;
+  const int64_t e4 = (r1 - r0) * N / 4;  // 16-byte pieces of the group
+  const int64_t lo = e4 * k / p.tail_per_group, hi = e4 * (k + 1) / p.tail_per_group;
+  const uint32_t bytes = (uint32_t)((r1 - r0) * N * 4);
+  const __amdgpu_buffer_rsrc_t out_r = buffer_res((float*)p.c_pos[p.accum_pos] + r0 * N, bytes);
+  // two pieces per thread per pass; pieces past hi get an offset outside the range (kOOB): their
+  // loads read zeros and their stores are dropped
+  constexpr int TB = 2;
+  for (int64_t j0 = lo + threadIdx.x; j0 < hi; j0 += TB * kThreads) {
+    uint32_t off[TB];
+    float4 x[TB];
+#pragma unroll
+    for (int b = 0; b < TB; ++b) {
+      const int64_t j = j0 + b * kThreads;
+      off[b] = j < hi ? (uint32_t)(j * 16) : kOOB;
+      x[b] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(out_r, off[b], 0, 0));
+    }
+    for (int q0 = 0; q0 < p.n_recv; q0 += 4) {  // four partials' loads in flight, then their adds
+      float4 t[4][TB];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (q0 + q < p.n_recv) {
+          const __amdgpu_buffer_rsrc_t rr = buffer_res(p.recv[q0 + q] + r0 * N, bytes);
+#pragma unroll
+          for (int b = 0; b < TB; ++b)  // streaming: the partials are read once
+            t[q][b] = __builtin_bit_cast(float4,
+                                         __builtin_amdgcn_raw_buffer_load_b128(rr, off[b], 0, 2));
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (q0 + q >= p.n_recv) break;
+#pragma unroll
+        for (int b = 0; b < TB; ++b) {
+          x[b].x += t[q][b].x;
+          x[b].y += t[q][b].y;
+          x[b].z += t[q][b].z;
+          x[b].w += t[q][b].w;
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < TB; ++b)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, x[b]), out_r, off[b], 0, 0);
+  }
+}
+
 // One workgroup per tile, or (grid smaller than the tile count) a persistent grid whose
-// workgroups walk the tiles with a stride of the grid size, in the same order.
+// workgroups walk the tiles with a stride of the grid size, in the same order. With the Flash-RS
+// tail, tail_units more workgroups follow the tiles.
 template <int BM, int BN, bool ACT>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(Plan p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds_ring[Cfg<BM, BN>::LDS];
   release_start(p);
   const int total = p.grid.npos * p.grid.tiles_m * p.grid.tiles_n;
+  if ((int)blockIdx.x >= total) {
+    rs_tail_unit(p, (int)blockIdx.x - total);
+    return;
+  }
   for (int tile = blockIdx.x; tile < total; tile += gridDim.x)
     bf16_tile<BM, BN, ACT>(p, tile, lds_ring);
 }
@@ -707,7 +786,8 @@ __device__ __forceinline__ void f32_tile(const Plan& p, const int tile, float (*
     __syncthreads();
   }
 
-  const bool accum = (pos == p.accum_pos);
+  // the own chunk adds its partials here, unless the tail workgroups do (tail_units > 0)
+  const bool accum = (pos == p.accum_pos) && p.tail_units == 0;
   if (accum) wait_groups_wg(p, p.recv_slice, p.n_recv, grp);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -926,17 +1006,26 @@ static bool plan_ok(const Plan& p) {
     for (int i = 0; i < p.n_recv; ++i)
       if (p.recv_slice[i] >= FO_MAX_P || (p.recv_slice[i] >= 0 && p.comp_tab == nullptr))
         return false;
+  if (p.tail_units < 0) return false;
+  if (p.tail_units > 0 &&
+      (p.accum_pos < 0 || p.own_done == nullptr || p.tail_per_group < 1 || p.tail_bm < 1 ||
+       p.tail_units != g.groups * p.tail_per_group || p.act || p.N % 4 != 0 ||
+       g.groups * g.group_rows * (int64_t)p.tail_bm < p.m ||
+       (p.m * p.N * 4) >= ((int64_t)1 << 31)))
+    return false;
   return true;
 }
 
 hipError_t launch_gemm(const Plan& p, int in_dt, int tile, hipStream_t s) {
   if (!plan_ok(p)) return hipErrorInvalidValue;
-  const int64_t grid = (int64_t)p.grid.npos * p.grid.tiles_m * p.grid.tiles_n;
+  int64_t grid = (int64_t)p.grid.npos * p.grid.tiles_m * p.grid.tiles_n;
   if (in_dt == FO_DT_F32) {
-    if (p.act) return hipErrorInvalidValue;  // the fp32 kernel has no SwiGLU epilogue
+    // the fp32 kernel has no SwiGLU epilogue and adds its partials itself
+    if (p.act || p.tail_units) return hipErrorInvalidValue;
     hipLaunchKernelGGL(gemm_f32_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
     return hipGetLastError();
   }
+  grid += p.tail_units;
   switch (tile) {
     case FO_TILE_256x256: return launch_bf16<256, 256>(p, grid, s);
     case FO_TILE_256x128: return launch_bf16<256, 128>(p, grid, s);

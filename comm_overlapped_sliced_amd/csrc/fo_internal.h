@@ -56,6 +56,12 @@ struct Plan {
   // ceil(2^32 / (K / c / 32)) gives a K step's block as umulhi(step, chunk_magic); 0 when c = 1.
   int32_t chunks;
   uint32_t chunk_magic;
+  // Flash-RS tail (tail_units > 0): the accum_pos tiles store their plain fp32 sums, and
+  // tail_units workgroups appended to the grid (tail_per_group per row group of tail_bm-row
+  // tiles) add the partials onto them once the group's tiles are stored (own_done[group] = gen)
+  // and its partials have landed, in the same order as the fused epilogue.
+  int32_t tail_units, tail_per_group, tail_bm;
+  uint32_t* own_done;
 };
 
 // A plan with nothing to wait for: no gates, no awaited partials, no tables, no release.
@@ -70,6 +76,10 @@ inline Plan empty_plan() {
   p.act = 0;
   p.chunks = 1;
   p.chunk_magic = 0;
+  p.tail_units = 0;
+  p.tail_per_group = 0;
+  p.tail_bm = 0;
+  p.own_done = nullptr;
   return p;
 }
 

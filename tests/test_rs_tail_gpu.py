@@ -1,0 +1,98 @@
+"""GPU tests of the Flash-RS tail: with 16-byte aligned buffers the own chunk's tiles store their
+fp32 sums and workgroups appended to the grid add the received partials onto them; otherwise the
+own tiles add them in their epilogue. Both add the same partials in the same order onto the same
+fp32 accumulator, so the results must be equal bit for bit: the fused epilogue is forced by an
+output buffer that is 4-byte but not 16-byte aligned."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from comm_overlapped_sliced_amd import configs, flashovl as fo, inputs
+from tests.gpu_helpers import TOL_BF16, from_dev, rel_frobenius, to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+    fo.load()
+    return torch.device("cuda:0")
+
+
+def _stream():
+    return torch.cuda.current_stream()
+
+
+class RSPair:
+    """One Flash-RS problem with two outputs: aligned (tail workgroups) and offset by one float
+    (the own tiles' fused epilogue)."""
+
+    def __init__(self, x, w, parts, P, dev):
+        self.P = P
+        self.m = x.shape[0] // P
+        self.N = w.shape[1]
+        self.x_d, self.w_d = to_dev(x, dev), to_dev(w, dev)
+        self.peer = [to_dev(p, dev) for p in parts]
+        self.send = torch.empty((P * self.m, self.N), dtype=torch.float32, device=dev)
+        self.recv = torch.empty((P * self.m, self.N), dtype=torch.float32, device=dev)
+        self.out_a = torch.empty((self.m, self.N), dtype=torch.float32, device=dev)
+        self.buf = torch.empty(self.m * self.N + 4, dtype=torch.float32, device=dev)
+        self.out_u = self.buf[1:1 + self.m * self.N].view(self.m, self.N)  # 4 bytes past 16
+
+    def run(self, r, out, o=None, resident=False):
+        out.fill_(float("nan"))
+        if resident:
+            for q in range(self.P):
+                if q != r:
+                    self.recv[q * self.m:(q + 1) * self.m].copy_(self.peer[q])
+        fo.gemm_rs(self.x_d, self.w_d, self.send, out, None if resident else self.peer,
+                   self.recv, self.P, r, compute_stream=_stream(), o=o)
+        fo.check(_stream())
+        return from_dev(out)
+
+
+@pytest.mark.parametrize("shape", [(4, 200, 520, 392), (8, 512, 512, 1024), (3, 300, 256, 136),
+                                   (2, 64, 128, 64)], ids=lambda s: "P%d_m%d_K%d_N%d" % s)
+@pytest.mark.parametrize("tile", [fo.TILE_AUTO, fo.TILE_128x256, fo.TILE_64x64, fo.TILE_256x256])
+def test_tail_equals_fused_epilogue(dev, shape, tile):
+    P, m, K, N = shape
+    x = inputs.normal(8400 + m, (P * m, K), 1.0, "bf16")
+    w = inputs.normal(8401, (K, N), 0.02, "bf16")
+    parts = [inputs.normal(8410 + q, (m, N), 1.0, "f32") for q in range(P)]
+    prob = RSPair(x, w, parts, P, dev)
+    assert prob.out_u.data_ptr() % 16 == 4
+    for r in sorted({0, P - 1, 1 % P}):
+        ref = oracle.rs(x, w, parts, P, r)
+        for arrival, groups, resident in ((fo.ARR_LOCKSTEP, 0, False), (fo.ARR_EAGER, 1, False),
+                                          (fo.ARR_NONE, 0, True), (fo.ARR_LOCKSTEP, 2, False)):
+            o = fo.opts(tile=tile, arrival=arrival, row_groups=groups)
+            a = prob.run(r, prob.out_a, o, resident)
+            u = prob.run(r, prob.out_u, o, resident)
+            assert not np.isnan(a).any()
+            assert np.array_equal(a, u), f"rank {r} arrival {arrival} groups {groups}"
+            assert rel_frobenius(a, ref) <= TOL_BF16
+
+
+def test_tail_l70b_down(dev):
+    """The 70B down projection at ranks 0 and 7: tail equals the fused epilogue bit for bit, and
+    both equal the oracle on sampled rows."""
+    c = configs.L70B_RS
+    x, w = c.x(), c.w()
+    parts = [c.partial(q) for q in range(c.P)]
+    prob = RSPair(x, w, parts, c.P, dev)
+    rows = np.array([0, 1, 127, 128, 255, 256, 383, 384, 510, 511])
+    for r in (0, 7):
+        a = prob.run(r, prob.out_a)
+        u = prob.run(r, prob.out_u)
+        assert np.array_equal(a, u), f"rank {r}"
+        xr = x[r * c.m:(r + 1) * c.m][rows]
+        ref = oracle.gemm(xr, w) + sum(parts[q][rows].astype(np.float64)
+                                       for q in range(c.P) if q != r)
+        assert rel_frobenius(a[rows], ref) <= TOL_BF16, f"rank {r}"
