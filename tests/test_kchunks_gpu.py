@@ -142,3 +142,30 @@ def test_kchunks_full_size(dev, case, c):
         got = prob.run(r)
         assert rel_frobenius(got[rows, cols], ref) <= TOL_BF16, f"rank {r}"
         assert np.array_equal(got, mono), f"rank {r}: chunk-major sliced != unsliced"
+
+
+@pytest.mark.parametrize("c", [2, 4])
+def test_kchunks_with_swiglu_epilogue_and_natural_order(dev, c):
+    """K blocks combine with the fused SwiGLU write-back and with the data-slicing (index) order:
+    each output equals the row-major call's with the same options, bit for bit."""
+    P, m, K, N = 8, 256, 2048, 1024
+    x = inputs.normal(8500 + c, (P * m, K), 1.0, "bf16")
+    w = inputs.normal(8501, (K, N), 0.02, "bf16")
+    prob = AGC(x, w, P, c, dev)
+    h = torch.empty((P * m, N // 2), dtype=torch.bfloat16, device=dev)
+
+    def swiglu_call(r, chunks):
+        peers = prob.chunked if chunks else prob.rows
+        h.view(torch.int16).fill_(-1)
+        fo.ag_gemm(peers[r], peers, prob.x_recv, prob.w_d, h, P, r, compute_stream=_stream(),
+                   o=fo.opts(epilogue=fo.EPI_SWIGLU, k_chunks=c if chunks else 0))
+        fo.check(_stream())
+        return from_dev(h)
+
+    for r in (0, P - 1):
+        a, b = swiglu_call(r, True), swiglu_call(r, False)
+        assert not np.isnan(a).any()
+        assert np.array_equal(a, b), f"SwiGLU rank {r}"
+        nat = prob.run(r, order=fo.ORDER_NATURAL)
+        base = prob.run(r, chunks=False, order=fo.ORDER_NATURAL)
+        assert np.array_equal(nat, base), f"natural order rank {r}"
