@@ -170,6 +170,10 @@ fo_status fo_ag_gemm(const void* x_local, const void* const* x_peer, void* x_rec
  *                the partial this rank would send to rank d. Chunk `rank` is not written.
  *   out          device [m, N] fp32: X_shard[rank rows] . W + sum of the incoming partials, added
  *                onto the fp32 accumulator in arrival order q = rank-1, rank-2, ... (mod P).
+ *                With bf16 operands and 16-byte aligned out and recv_buf chunks the adds run in
+ *                workgroups of the same launch after a row group's tiles have stored their sums
+ *                (spread over the CUs the other chunks freed), else in the tiles' write-back;
+ *                the order of the adds, and so every bit of out, is the same.
  *   peer_partial host array of P device pointers; peer_partial[q] ([m, N] fp32) is what peer q
  *                sends for this rank's chunk. Entry [rank] ignored. NULL: no transfers, the
  *                partials are already in recv_buf.
@@ -281,7 +285,8 @@ fo_status fo_slice_order(int32_t kind, int32_t order, int32_t P, int32_t rank, i
 
 /* The tile shape the bf16 kernel would use for slices of m rows, K, N with output out_dt (fp32 for
    fo_gemm_rs) and the tile request `tile` (a fo_tile). Writes the tile rows/columns and the
-   number of workgroups one call over P slices launches. */
+   number of tile workgroups one call over P slices launches (a fo_gemm_rs launch may append
+   workgroups that add the partials after them). */
 fo_status fo_tile_info(int32_t P, int64_t m, int64_t K, int64_t N, int32_t in_dt, int32_t out_dt,
                        int32_t tile, int32_t* bm, int32_t* bn, int64_t* workgroups);
 
