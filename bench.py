@@ -128,6 +128,83 @@ def attention_section(fo, dev, stream, timed, reps, log):
     return res
 
 
+def sweep_section(fo, dev, stream, timed, reps, log, kc):
+    """The other workloads of the measurement, each in the three forms of the metric: the 70B
+    gate+up AG-GEMM at 1K to 16K tokens and the 405B AG and RS shares at 8K tokens, rank 0, one
+    DMA engine per peer, row groups (AG slices in kc K blocks where K allows). Per call: T_ref
+    (monolithic GEMM), T_slice0 (slices resident), T_slice (arrivals), T_xfer (the same copies
+    alone); TFLOP/s and the share of the bf16 peak from T_slice; exposed = (T_slice - T_ref) /
+    T_xfer."""
+    import numpy as np
+    import torch
+    from comm_overlapped_sliced_amd import configs
+
+    def dev_of(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    def k_blocks(t, c):
+        m_, k_ = t.shape
+        return t.reshape(m_, c, k_ // c).permute(1, 0, 2).contiguous().reshape(m_, k_)
+
+    def groups_of(kind, case, chunks):
+        order = fo.tile_order(kind, case.P, case.m, case.K, case.N, o=fo.opts(k_chunks=chunks),
+                              out_dt=fo.F32 if kind == "rs" else fo.BF16)
+        return max(g for _, g, _, _ in order) + 1
+
+    res = []
+    for case in configs.SWEEP_AG + (configs.L405B_AG, configs.L405B_RS):
+        P, m = case.P, case.m
+        x = dev_of(case.x())
+        w = dev_of(case.w())
+        if case.call == "ag":
+            c = kc if kc > 1 and case.K % (256 * kc) == 0 else 0
+            rows = [x[s_ * m:(s_ + 1) * m].contiguous() for s_ in range(P)]
+            sl = [k_blocks(t, c) for t in rows] if c else rows
+            recv = torch.empty_like(x)
+            y = torch.empty((case.M, case.N), dtype=torch.bfloat16, device=dev)
+            for s_ in range(P):
+                recv[s_ * m:(s_ + 1) * m] = sl[s_]
+            t_ref = timed(lambda: fo.gemm_ref(x, w, y, stream=stream), reps)
+            t0 = timed(lambda: fo.ag_gemm(sl[0], None, recv, w, y, P, 0, compute_stream=stream,
+                                          o=fo.opts(arrival=fo.ARR_NONE, k_chunks=c)), reps)
+            t1 = timed(lambda: fo.ag_gemm(sl[0], sl, recv, w, y, P, 0, compute_stream=stream,
+                                          o=fo.opts(k_chunks=c)), reps)
+            pieces = groups_of("ag", case, c) * max(1, c)
+            tx = timed(lambda: fo.transfer_ref("ag", sl, recv, P, 0, m * case.K * 2, stream,
+                                               fo.opts(row_groups=min(8, pieces))), reps)
+            del rows, sl, recv, y
+        else:
+            c = 0
+            peers = [dev_of(case.partial(q)) for q in range(P)]
+            send = torch.empty((case.M, case.N), dtype=torch.float32, device=dev)
+            out = torch.empty((m, case.N), dtype=torch.float32, device=dev)
+            recv = torch.empty((case.M, case.N), dtype=torch.float32, device=dev)
+            t_ref = timed(lambda: fo.gemm_ref(x, w, send, stream=stream), reps)
+            t0 = timed(lambda: fo.gemm_rs(x, w, send, out, None, recv, P, 0,
+                                          compute_stream=stream,
+                                          o=fo.opts(arrival=fo.ARR_NONE)), reps)
+            t1 = timed(lambda: fo.gemm_rs(x, w, send, out, peers, recv, P, 0,
+                                          compute_stream=stream), reps)
+            tx = timed(lambda: fo.transfer_ref("rs", peers, recv, P, 0, m * case.N * 4, stream,
+                                               fo.opts(row_groups=groups_of("rs", case, 0))),
+                       reps)
+            del peers, send, out, recv
+        del x, w
+        torch.cuda.empty_cache()
+        tf = case.flops / t1 / 1e9
+        ent = {"workload": case.name, "call": case.call, "M": case.M, "K": case.K, "N": case.N,
+               "k_blocks": c, "t_ref_us": t_ref * 1e3, "t_slice0_us": t0 * 1e3,
+               "t_slice_us": t1 * 1e3, "t_xfer_us": tx * 1e3, "tflops": tf,
+               "pct_bf16_peak": 100.0 * tf / PEAK_BF16_TFLOPS, "exposed_frac": (t1 - t_ref) / tx}
+        res.append(ent)
+        log(f"sweep {case.call} M={case.M} K={case.K} N={case.N}: ref {t_ref*1e3:.0f} us, slice0 "
+            f"{t0*1e3:.0f}, slice {t1*1e3:.0f}, xfer {tx*1e3:.0f} -> {tf:.0f} TFLOP/s "
+            f"({ent['pct_bf16_peak']:.1f}% of peak), exposed {ent['exposed_frac']:.2f}")
+    return res
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -212,8 +289,16 @@ def main():
         """Steady-state duration (ms) of one fn() on the compute stream: `reps` calls enqueued
         back to back, as a training step enqueues them, so that the host's set-up of a call
         (signals, the enqueueing of its copies) runs ahead of the GPU instead of delaying the
-        first copy; median over three such batches."""
-        fn()
+        first copy; median over three such batches. Calls for at least 20 ms first: after a
+        stretch with little to compute (transfers alone, the host) the first few milliseconds of
+        GEMM calls run up to ~50 us per call slower while the clocks come back up."""
+        t_end = time.perf_counter() + 0.02
+        n = 0
+        while n < 3 or time.perf_counter() < t_end:
+            fn()
+            n += 1
+            if n % 4 == 0:
+                torch.cuda.synchronize()
         out = []
         for _ in range(3):
             a, b = ev(), ev()
@@ -421,6 +506,11 @@ def main():
     log(f"timed: {args.steps} steps {total_ms:.2f} ms (host {host_s*1e3:.2f} ms), "
         f"{ms_per_step*1e3:.1f} us/step, {value:.1f} TFLOP/s; AG kernel {mean_ag*1e3:.1f} us, "
         f"RS kernel {mean_rs*1e3:.1f} us")
+
+    # the other workloads after the timed region (their large GEMMs heat the chip)
+    if exposure is not None:
+        exposure["sweep"] = sweep_section(fo, dev, stream, timed, args.exposure_reps, log, kc)
+        fo.check(stream)
 
     cpu = cpu_baseline(ag_case, rs_case, args.cpu_seconds) if args.cpu_seconds > 0 else None
 
