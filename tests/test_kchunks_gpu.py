@@ -125,9 +125,12 @@ def test_kchunks_missed_block_times_out(dev):
     assert rel_frobenius(got, oracle.gemm(x, w)) <= TOL_BF16
 
 
+# the launch configurations the bench times (4 K blocks) on every AG workload, and 2 blocks
 @pytest.mark.parametrize("case,c", [(configs.L70B_AG, 4), (configs.L70B_AG, 2),
-                                    (configs.L405B_AG, 2)],
-                         ids=lambda v: v.name.split(",")[0] if hasattr(v, "name") else str(v))
+                                    (configs.L405B_AG, 4), (configs.L405B_AG, 2),
+                                    (configs.SWEEP_AG[0], 4), (configs.SWEEP_AG[1], 4),
+                                    (configs.SWEEP_AG[3], 4), (configs.SWEEP_AG[4], 4)],
+                         ids=lambda v: f"M{v.M}_K{v.K}_N{v.N}" if hasattr(v, "M") else f"c{v}")
 def test_kchunks_full_size(dev, case, c):
     x, w = case.x(), case.w()
     prob = AGC(x, w, case.P, c, dev)
