@@ -677,7 +677,11 @@ __device__ __forceinline__ void rs_tail_unit(const Plan& p, int u) {
         if (p.recv_slice[i] >= 0) wait_group(p, p.recv_slice[i], g);
   }
   __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
+  // No acquire fence: out and the partials are read with system-coherent loads (sc0 sc1), which
+  // return what the other workgroups' released stores and the copy engines put in memory
+  // whatever this CU's caches hold. (A system-scope acquire invalidates the L2 in every one of
+  // these workgroups; the last group's invalidates serialized into a tail of tens of us.)
+  constexpr int kSys = 1 | 16;  // cache policy sc0 | sc1
   const int64_t N = p.N;
   const int64_t e4 = (r1 - r0) * N / 4;  // 16-byte pieces of the group
   const int64_t lo = e4 * k / p.tail_per_group, hi = e4 * (k + 1) / p.tail_per_group;
@@ -693,7 +697,8 @@ __device__ __forceinline__ void rs_tail_unit(const Plan& p, int u) {
     for (int b = 0; b < TB; ++b) {
       const int64_t j = j0 + b * kThreads;
       off[b] = j < hi ? (uint32_t)(j * 16) : kOOB;
-      x[b] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(out_r, off[b], 0, 0));
+      x[b] = __builtin_bit_cast(float4,
+                                __builtin_amdgcn_raw_buffer_load_b128(out_r, off[b], 0, kSys));
     }
     for (int q0 = 0; q0 < p.n_recv; q0 += 4) {  // four partials' loads in flight, then their adds
       float4 t[4][TB];
@@ -702,9 +707,9 @@ __device__ __forceinline__ void rs_tail_unit(const Plan& p, int u) {
         if (q0 + q < p.n_recv) {
           const __amdgpu_buffer_rsrc_t rr = buffer_res(p.recv[q0 + q] + r0 * N, bytes);
 #pragma unroll
-          for (int b = 0; b < TB; ++b)  // streaming: the partials are read once
-            t[q][b] = __builtin_bit_cast(float4,
-                                         __builtin_amdgcn_raw_buffer_load_b128(rr, off[b], 0, 2));
+          for (int b = 0; b < TB; ++b)  // streaming (nt): the partials are read once
+            t[q][b] = __builtin_bit_cast(
+                float4, __builtin_amdgcn_raw_buffer_load_b128(rr, off[b], 0, kSys | 2));
         }
       }
 #pragma unroll
