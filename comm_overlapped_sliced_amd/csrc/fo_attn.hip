@@ -233,37 +233,59 @@ __device__ __forceinline__ void attn_tile(const AttnPlan& p, const int u, uint8_
         }
       }
 
-      // online softmax in base 2; value v of fragment f is key 32 f + 8 (v / 4) + 4 lh + v % 4
+      // online softmax in base 2 on the raw scores (the running max mrow in raw units, the scale
+      // folded into the exponent's fma); value v of fragment f is key 32 f + 8 (v / 4) + 4 lh +
+      // v % 4. Only a tile that runs past the slice's keys or, under causal masking, past this
+      // wave's first query (the diagonal of the own slice) needs the mask (wave-uniform test).
       const int kb = t * kAK;
+      const bool full = uni((kb + kAK <= m) &&
+                            (!p.causal || j < s || kb + kAK - 1 <= q0 + 32 * wave) ? 1 : 0) != 0;
       float mx = kNegBig;
       float sv[2][16];
+      if (full) {
 #pragma unroll
-      for (int f = 0; f < 2; ++f)
+        for (int f = 0; f < 2; ++f)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int kj = kb + 32 * f + 8 * (v >> 2) + 4 * lh + (v & 3);
-          const bool ok = kj < m && (!p.causal || kpos0 + kj <= qpos);
-          sv[f][v] = ok ? sacc[f][v] * p.scale_log2 : kNegBig;
-          mx = fmaxf(mx, sv[f][v]);
-        }
+          for (int v = 0; v < 16; ++v) {
+            sv[f][v] = sacc[f][v];
+            mx = fmaxf(mx, sv[f][v]);
+          }
+      } else {
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int kj = kb + 32 * f + 8 * (v >> 2) + 4 * lh + (v & 3);
+            const bool ok = kj < m && (!p.causal || kpos0 + kj <= qpos);
+            sv[f][v] = ok ? sacc[f][v] : kNegBig;
+            mx = fmaxf(mx, sv[f][v]);
+          }
+      }
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float mnew = fmaxf(mrow, mx);
-      const float alpha = __builtin_amdgcn_exp2f(mrow - mnew);
+      const float sc = p.scale_log2;
+      const float alpha = __builtin_amdgcn_exp2f((mrow - mnew) * sc);
+      const float mns = -mnew * sc;
       float psum = 0.f;
 #pragma unroll
       for (int f = 0; f < 2; ++f)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const float e = sv[f][v] > kNegBig ? __builtin_amdgcn_exp2f(sv[f][v] - mnew) : 0.f;
+          // a masked score (kNegBig) gives exp2 of about -1e29: exactly 0
+          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[f][v], sc, mns));
           sv[f][v] = e;
           psum += e;
         }
       lrow = lrow * alpha + psum;
+      // the output rows are rescaled only when some running max of the wave grew (alpha = 1
+      // exactly otherwise, so skipping the multiplies changes no bit)
+      if (__ballot(mnew > mrow) != 0) {
+#pragma unroll
+        for (int i = 0; i < kAD / 32; ++i)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) oacc[i][v] *= alpha;
+      }
       mrow = mnew;
-#pragma unroll
-      for (int i = 0; i < kAD / 32; ++i)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) oacc[i][v] *= alpha;
       // P^T as B operands: 16-key step kk takes values 8 (kk % 2) .. 8 (kk % 2) + 7 of fragment
       // kk / 2, i.e. keys 16 kk + 8 (e / 4) + 4 lh + e % 4 for e = 0..7
       bf16x8 pb[4];
