@@ -37,17 +37,19 @@ __device__ __forceinline__ void wait_group(const Plan& p, int slice, int grp) {
   fo::wait_group(p.comp_tab, p.lead, p.ready, p.gen, p.spin_limit, p.err, slice, grp);
 }
 
-// Thread 0 waits for group `grp` of each listed slice (negative ids are skipped); then the whole
-// workgroup acquires at system scope so that data the copy engine wrote before the signal is
-// seen (no stale cache lines).
+// Thread 0 waits for group `grp` of each listed slice (negative ids are skipped) and then
+// acquires at system scope, so that data the copy engine wrote before the signal is seen (the
+// CU's L1 and its XCD's L2 hold no stale line); the barrier holds the other waves until then,
+// so their loads come after the invalidation. One wave's acquire is enough: with every wave
+// acquiring, the four invalidations per workgroup cost ~10 us per Flash-AG call.
 __device__ __forceinline__ void wait_groups_wg(const Plan& p, const int32_t* slices, int n,
                                                int grp) {
   if (threadIdx.x == 0 && p.comp_tab != nullptr) {
     for (int i = 0; i < n; ++i)
       if (slices[i] >= 0) wait_group(p, slices[i], grp);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
   }
   __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
 }
 
 // After a tile of (position, group) is stored: count it; the last tile of that group stores 0
