@@ -471,6 +471,8 @@ fo_status fo_ag_gemm(const void* x_local, const void* const* x_peer, void* x_rec
   if (s != FO_OK) return s;
   set_layout(0, o, p);
   p.chunks = chunks;
+  // transfers on cache-line (128-byte) boundaries: no acquire needed after the arrival waits
+  p.acq = (aligned(x_recv, 128) && ((size_t)(K / chunks) * es) % 128 == 0) ? 0 : 1;
   // ceil(2^32 / steps per chunk): umulhi(step, magic) = step / steps per chunk (steps < 2^16)
   p.chunk_magic = chunks > 1 ? (uint32_t)((((uint64_t)1 << 32) + K / chunks / 32 - 1) /
                                           (uint64_t)(K / chunks / 32)) : 0u;
@@ -627,6 +629,8 @@ fo_status fo_gemm_rs(const void* x_shard, const void* w, float* send_buf, float*
   p.N = N;
   p.grid.npos = P;
   p.out_f32 = 1;
+  // partials' transfers on cache-line (128-byte) boundaries: no acquire after the arrival waits
+  p.acq = (aligned(recv_buf, 128) && ((size_t)N * 4) % 128 == 0) ? 0 : 1;
   // Flash-RS tail: the own chunk's tiles store their sums and workgroups appended to the grid add
   // the partials (same order, same bits), spread over the CUs the other chunks have freed. Needs
   // 16-byte aligned out and partials (else the own tiles add them in their epilogue).

@@ -37,17 +37,23 @@ __device__ __forceinline__ void wait_group(const Plan& p, int slice, int grp) {
   fo::wait_group(p.comp_tab, p.lead, p.ready, p.gen, p.spin_limit, p.err, slice, grp);
 }
 
-// Thread 0 waits for group `grp` of each listed slice (negative ids are skipped) and then
-// acquires at system scope, so that data the copy engine wrote before the signal is seen (the
-// CU's L1 and its XCD's L2 hold no stale line); the barrier holds the other waves until then,
-// so their loads come after the invalidation. One wave's acquire is enough: with every wave
-// acquiring, the four invalidations per workgroup cost ~10 us per Flash-AG call.
+// Thread 0 waits for group `grp` of each listed slice (negative ids are skipped); the barrier
+// holds the other waves until then, so every load of the group's rows is issued after the copy
+// engine's data has landed in memory.
+// With p.acq = 0 no cache invalidation follows, because the caches can hold no stale line of
+// these rows: the kernel's launch invalidates the L1s and L2s of what earlier kernels (earlier
+// calls on the same buffers) cached, inside the launch no workgroup reads a row before its
+// transfer has landed, and the host sets p.acq = 0 only when every transfer starts and ends on
+// a 128-byte cache-line boundary (so no line holds data of two transfers, or of a transfer and
+// another buffer). Otherwise thread 0 acquires at system scope before the barrier. An acquire
+// per waiting workgroup invalidates the XCD's L2 under the other tiles: 15-23 us per Flash-AG
+// call.
 __device__ __forceinline__ void wait_groups_wg(const Plan& p, const int32_t* slices, int n,
                                                int grp) {
   if (threadIdx.x == 0 && p.comp_tab != nullptr) {
     for (int i = 0; i < n; ++i)
       if (slices[i] >= 0) wait_group(p, slices[i], grp);
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
+    if (p.acq) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
   }
   __syncthreads();
 }
@@ -463,8 +469,8 @@ __device__ __forceinline__ void bf16_tile(const Plan& p, const int tile, uint8_t
   };
   // A received slice that travels in K blocks: the first loads of block j (step j * spc) are
   // issued after the barrier of step j * spc - S, so before that barrier thread 0 waits for
-  // block j of the tile's row group to have landed (and acquires, like the wait at the start);
-  // the barrier holds the other waves until then. gate_kt = -1: nothing left to wait for.
+  // block j of the tile's row group to have landed (acquiring only with p.acq, as at the wait
+  // at the start); the barrier holds the other waves until then. gate_kt = -1: nothing left.
   const int spc = (int)(Kc / kBK);
   int gate_kt = (gslice >= 0 && chunks > 1) ? spc - S : -1;
   int gate_j = 1;
@@ -472,7 +478,7 @@ __device__ __forceinline__ void bf16_tile(const Plan& p, const int tile, uint8_t
     if (kt == gate_kt) {
       if (tid == 0) {
         wait_group(p, gslice, grp * chunks + gate_j);
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
+        if (p.acq) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
       }
       ++gate_j;
       gate_kt = gate_j < chunks ? gate_kt + spc : -1;

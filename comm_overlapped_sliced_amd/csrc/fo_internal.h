@@ -62,6 +62,9 @@ struct Plan {
   // and its partials have landed, in the same order as the fused epilogue.
   int32_t tail_units, tail_per_group, tail_bm;
   uint32_t* own_done;
+  // 1: acquire (invalidate the caches) after each arrival wait, because a transfer may share a
+  // cache line with data read before it landed; 0: every transfer is cache-line aligned.
+  int32_t acq;
 };
 
 // A plan with nothing to wait for: no gates, no awaited partials, no tables, no release.
@@ -80,6 +83,7 @@ inline Plan empty_plan() {
   p.tail_per_group = 0;
   p.tail_bm = 0;
   p.own_done = nullptr;
+  p.acq = 1;
   return p;
 }
 

@@ -116,3 +116,40 @@ def test_missed_arrival_times_out(dev):
     fo.check(torch.cuda.current_stream())
     got = prob.run(1)
     assert rel_frobenius(got, oracle.gemm(x, w)) <= TOL_BF16
+
+
+@pytest.mark.parametrize("chunks", [0, 4])
+def test_back_to_back_calls_see_new_arrivals(dev, chunks):
+    """Calls enqueued back to back with no other kernel between them, the peers' data
+    alternating between two sets and landing in the same receive buffer: each call's kernel
+    reads the rows the previous call read, so a cached line of the previous data would show.
+    Each result must equal the unsliced product of its own data bit for bit. (With 16-byte
+    aligned rows, K a multiple of 64, the arrival waits take no cache invalidation.)"""
+    P, m, K, N = 8, 512, 4096, 512
+    xs = [inputs.normal(7950 + i, (P * m, K), 1.0, "bf16") for i in range(2)]
+    w = inputs.normal(7952, (K, N), 0.02, "bf16")
+    w_d = to_dev(w, dev)
+    refs = []
+    for x in xs:
+        y = torch.empty((P * m, N), dtype=torch.bfloat16, device=dev)
+        fo.gemm_ref(to_dev(x, dev), w_d, y, stream=torch.cuda.current_stream())
+        refs.append(y)
+
+    def layout(t):
+        if not chunks:
+            return t.contiguous()
+        return t.reshape(m, chunks, K // chunks).permute(1, 0, 2).contiguous().reshape(m, K)
+
+    peers = [[layout(to_dev(x[s * m:(s + 1) * m], dev)) for s in range(P)] for x in xs]
+    x_recv = torch.empty((P * m, K), dtype=torch.bfloat16, device=dev)
+    ys = [torch.empty((P * m, N), dtype=torch.bfloat16, device=dev) for _ in range(8)]
+    stream = torch.cuda.current_stream()
+    for links in (0, 1):
+        for it in range(8):
+            i, r = it % 2, (3 * it) % P
+            fo.ag_gemm(peers[i][r], peers[i], x_recv, w_d, ys[it], P, r, compute_stream=stream,
+                       o=fo.opts(links=links, k_chunks=chunks))
+        fo.check(stream)
+        for it in range(8):
+            assert torch.equal(ys[it].view(torch.int16), refs[it % 2].view(torch.int16)), \
+                f"call {it} links {links}"

@@ -96,3 +96,38 @@ def test_tail_l70b_down(dev):
         ref = oracle.gemm(xr, w) + sum(parts[q][rows].astype(np.float64)
                                        for q in range(c.P) if q != r)
         assert rel_frobenius(a[rows], ref) <= TOL_BF16, f"rank {r}"
+
+
+def test_back_to_back_calls_see_new_partials(dev):
+    """Flash-RS calls enqueued back to back, the peers' partials alternating between two sets
+    and landing in the same receive buffer: each call reads the rows the previous call read.
+    Both forms of the adds (the tail workgroups, and the own tiles' epilogue with an output
+    that is not 16-byte aligned) must give each set's result, bit for bit the same every time."""
+    P, m, K, N = 8, 256, 512, 1024
+    x = inputs.normal(8700, (P * m, K), 1.0, "bf16")
+    w = inputs.normal(8701, (K, N), 0.02, "bf16")
+    sets = [[inputs.normal(8710 + 10 * i + q, (m, N), 1.0, "f32") for q in range(P)]
+            for i in range(2)]
+    x_d, w_d = to_dev(x, dev), to_dev(w, dev)
+    peers = [[to_dev(p, dev) for p in ps] for ps in sets]
+    send = torch.empty((P * m, N), dtype=torch.float32, device=dev)
+    recv = torch.empty((P * m, N), dtype=torch.float32, device=dev)
+    n = 8
+    buf = torch.empty(n * (m * N + 4), dtype=torch.float32, device=dev)
+    stream = _stream()
+    r = 3
+    for aligned in (True, False):
+        outs = []
+        for it in range(n):
+            base = it * (m * N + 4) + (0 if aligned else 1)
+            out = buf[base:base + m * N].view(m, N)
+            assert (out.data_ptr() % 16 == 0) == aligned
+            fo.gemm_rs(x_d, w_d, send, out, peers[it % 2], recv, P, r, compute_stream=stream)
+            outs.append(out)
+        fo.check(stream)
+        got = [from_dev(o) for o in outs]
+        for i in range(2):
+            ref = oracle.rs(x, w, sets[i], P, r)
+            assert rel_frobenius(got[i], ref) <= TOL_BF16, f"set {i} aligned {aligned}"
+            for it in range(i + 2, n, 2):
+                assert np.array_equal(got[it], got[i]), f"call {it} aligned {aligned}"
