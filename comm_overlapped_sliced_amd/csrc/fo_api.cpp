@@ -863,6 +863,9 @@ fo_status fo_attn(const void* qkv_local, const void* const* qkv_peer, void* qkv_
   p.causal = causal;
   p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
   p.pair_half = attn_pair_half(P, m, hq, causal, st->n_cu);
+  // transfers on cache-line (128-byte) boundaries: no acquire needed after the arrival waits
+  const size_t row_bytes = (size_t)(hq + 2 * hkv) * head_dim * 2;
+  p.acq = (aligned(qkv_recv, 128) && row_bytes % 128 == 0) ? 0 : 1;
 
   hipStream_t cs = (hipStream_t)compute_stream;
   if (arrivals) p.start = call.start;

@@ -109,14 +109,18 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
-// Thread 0 waits until row groups g0..g1 of slice j have landed; then the workgroup acquires at
-// system scope so that the copy engine's data is seen.
+// Thread 0 waits until row groups g0..g1 of slice j have landed; the barrier holds the other
+// waves until then. With p.acq thread 0 also acquires at system scope (invalidating this CU's L1
+// and its XCD's L2) before the barrier; without it (every transfer on 128-byte cache-line
+// boundaries) no cache can hold a stale line of the rows: the launch invalidated what earlier
+// kernels cached, and nothing reads a row before its transfer has landed.
 __device__ __forceinline__ void wait_groups(const AttnPlan& p, int j, int g0, int g1) {
-  if (threadIdx.x == 0 && p.comp_tab != nullptr)
+  if (threadIdx.x == 0 && p.comp_tab != nullptr) {
     for (int g = g0; g <= g1; ++g)
       wait_group(p.comp_tab, p.lead, p.ready, p.gen, p.spin_limit, p.err, j, g);
+    if (p.acq) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
+  }
   __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
 }
 
 __device__ __forceinline__ void attn_tile(const AttnPlan& p, const int u, uint8_t* const lds) {

@@ -176,6 +176,7 @@ struct AttnPlan {
   // workgroups that shares a CU has a balanced amount of work (causal, one workgroup per slot)
   int32_t pair_half;
   float scale_log2;                  // log2(e) / sqrt(128)
+  int32_t acq;                       // 1: acquire after each arrival wait (see Plan::acq)
 };
 bool attn_plan_ok(const AttnPlan& p);
 hipError_t launch_attn(const AttnPlan& p, hipStream_t stream);

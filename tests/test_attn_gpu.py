@@ -144,3 +144,31 @@ def test_attn_l70b_sampled_rows(dev, rank):
                                      for s in range(c.P)] + [rng.integers(0, c.S, 24)]))
     got = from_dev(out[torch.from_numpy(rows).to(dev)])
     _check(got, qkv, c.hq, c.hkv, c.causal, f"L70B rank {rank}", rows=rows)
+
+
+def test_attn_back_to_back_calls_see_new_arrivals(dev):
+    """Calls enqueued back to back with no other kernel between them, the peers' rows
+    alternating between two sets and landing in the same receive buffer (rows of 2560 bytes,
+    cache-line aligned, so the arrival waits take no cache invalidation): each call must equal
+    the resident attention of its own set, bit for bit (index order walks the keys as the
+    resident call does)."""
+    P, m, hq, hkv = 4, 256, 8, 1
+    row = (hq + 2 * hkv) * D
+    sets = [inputs.normal(8400 + i, (P * m, row), 1.0, "bf16") for i in range(2)]
+    st = torch.cuda.current_stream()
+    refs, slices = [], []
+    for q in sets:
+        qd = to_dev(q, dev)
+        ref = torch.empty((P * m, hq * D), dtype=torch.bfloat16, device=dev)
+        fo.attn_ref(qd, ref, hq, hkv, True, stream=st)
+        refs.append(ref)
+        slices.append([qd[s * m:(s + 1) * m].contiguous() for s in range(P)])
+    recv = torch.empty((P * m, row), dtype=torch.bfloat16, device=dev)
+    outs = [torch.empty((P * m, hq * D), dtype=torch.bfloat16, device=dev) for _ in range(6)]
+    for it in range(6):
+        i, rank = it % 2, (it * 3) % P
+        fo.attn(slices[i][rank], slices[i], recv, outs[it], P, rank, hq, hkv, True,
+                compute_stream=st, o=fo.opts(order=fo.ORDER_NATURAL))
+    fo.check(st)
+    for it in range(6):
+        assert torch.equal(outs[it], refs[it % 2]), f"call {it}"
