@@ -123,8 +123,9 @@ def test_back_to_back_calls_see_new_arrivals(dev, chunks):
     """Calls enqueued back to back with no other kernel between them, the peers' data
     alternating between two sets and landing in the same receive buffer: each call's kernel
     reads the rows the previous call read, so a cached line of the previous data would show.
-    Each result must equal the unsliced product of its own data bit for bit. (With 16-byte
-    aligned rows, K a multiple of 64, the arrival waits take no cache invalidation.)"""
+    Each result must equal the unsliced product of its own data bit for bit. (Rows of 8 KB and
+    K blocks of 2 KB lie on 128-byte cache lines, so the arrival waits take no cache
+    invalidation.)"""
     P, m, K, N = 8, 512, 4096, 512
     xs = [inputs.normal(7950 + i, (P * m, K), 1.0, "bf16") for i in range(2)]
     w = inputs.normal(7952, (K, N), 0.02, "bf16")

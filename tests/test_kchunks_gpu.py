@@ -71,7 +71,8 @@ class AGC:
 
 @pytest.mark.parametrize("shape,c", [((8, 512, 2048, 1024), 2), ((8, 512, 2048, 1024), 4),
                                      ((8, 512, 2048, 1024), 8), ((4, 200, 1024, 392), 2),
-                                     ((4, 200, 1024, 392), 4), ((3, 300, 512, 136), 2)],
+                                     ((4, 200, 1024, 392), 4), ((3, 300, 512, 136), 2),
+                                     ((1, 300, 512, 136), 2)],
                          ids=lambda v: str(v))
 @pytest.mark.parametrize("tile", [fo.TILE_AUTO, fo.TILE_128x256, fo.TILE_128x128, fo.TILE_64x64])
 def test_kchunks_equal_row_major(dev, shape, c, tile):

@@ -131,3 +131,23 @@ def test_back_to_back_calls_see_new_partials(dev):
             assert rel_frobenius(got[i], ref) <= TOL_BF16, f"set {i} aligned {aligned}"
             for it in range(i + 2, n, 2):
                 assert np.array_equal(got[it], got[i]), f"call {it} aligned {aligned}"
+
+
+def test_tail_missed_partial_times_out(dev):
+    """A 1 us bound on the in-kernel waits against partials that take a millisecond over one
+    link: the tail workgroups give up, the call reports FO_ERR_TIMEOUT, every kernel finishes,
+    and the next call is correct again."""
+    P, m, K, N = 8, 512, 64, 4096
+    x = inputs.normal(8800, (P * m, K), 1.0, "bf16")
+    w = inputs.normal(8801, (K, N), 0.02, "bf16")
+    parts = [inputs.normal(8810 + q, (m, N), 1.0, "f32") for q in range(P)]
+    prob = RSPair(x, w, parts, P, dev)
+    st = fo.gemm_rs(prob.x_d, prob.w_d, prob.send, prob.out_a, prob.peer, prob.recv, P, 2,
+                    compute_stream=_stream(), o=fo.opts(spin_timeout_us=1, links=1), raw=True)
+    assert st == fo.FO_OK
+    with pytest.raises(fo.FoError) as ei:
+        fo.check(_stream())
+    assert ei.value.status == fo.FO_ERR_TIMEOUT
+    fo.check(_stream())
+    got = prob.run(2, prob.out_a, fo.opts(links=1))
+    assert rel_frobenius(got, oracle.rs(x, w, parts, P, 2)) <= TOL_BF16
