@@ -492,7 +492,7 @@ def main():
         "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
         "traffic": traffic_for(dom),
         "kernel": f"gemm_bf16_kernel<{bm},{bn}> ({'fo_ag_gemm' if dom == 'ag' else 'fo_gemm_rs'})",
-        "kernel_us": round(dom_ms * 1e3, 1), "workgroups": wg,
+        "kernel_us": round(dom_ms * 1e3, 1), "tiles": wg,
         "ag_kernel_us": round(mean_ag * 1e3, 1), "rs_kernel_us": round(mean_rs * 1e3, 1),
         # both launches of the step against the same peak; each launch's time includes its
         # in-kernel waits for the emulated transfers (the RS one waits for 117 MB of partials)
