@@ -155,8 +155,10 @@ def _ptr_array(ptrs):
 def ag_gemm(x_local, x_peer, x_recv, w, y, P: int, rank: int, compute_stream=None,
             o: Opts | None = None, raw: bool = False):
     """Flash-AG (fo_ag_gemm). x_local [m, K], x_peer list of P tensors (or None), x_recv
-    [P*m, K], w [K, N], y [P*m, N] ([P*m, N/2] with the SwiGLU epilogue). Returns the status
-    when raw=True, else raises on error."""
+    [P*m, K], w [K, N], y [P*m, N] ([P*m, N/2] with the SwiGLU epilogue). With o.k_chunks = c > 1
+    every X slice holds its m*K values in the K-block layout (c blocks [m, K/c] one after
+    another; the shapes passed stay [m, K]). Returns the status when raw=True, else raises on
+    error."""
     m, K = x_local.shape
     N = w.shape[1]
     peers = None if x_peer is None else _ptr_array(x_peer)

@@ -50,6 +50,10 @@ def test_opts_defaults():
     assert list(o.kernel_events) == [None, None]
     assert o.row_groups == 0 and o.epilogue == fo.EPI_NONE and o.k_chunks == 0
     assert ctypes.sizeof(fo.Opts) == 48
+    # the C layout: k_chunks is the last 32-bit field, after the events and the epilogue
+    assert fo.Opts.kernel_events.offset == 24 and fo.Opts.epilogue.offset == 40
+    assert fo.Opts.k_chunks.offset == 44
+    assert fo.opts(k_chunks=4).k_chunks == 4
 
 
 @pytest.mark.parametrize("P", list(range(1, 33)))
