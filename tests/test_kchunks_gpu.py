@@ -13,7 +13,8 @@ import pytest
 
 import oracle
 from comm_overlapped_sliced_amd import configs, flashovl as fo, inputs
-from tests.gpu_helpers import TOL_BF16, from_dev, rel_frobenius, sample_indices, to_dev
+from tests.gpu_helpers import (TOL_BF16, ag_oracle_blocks, check_ag_blocks, from_dev,
+                               rel_frobenius, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -133,18 +134,19 @@ def test_kchunks_missed_block_times_out(dev):
                                     (configs.SWEEP_AG[3], 4), (configs.SWEEP_AG[4], 4)],
                          ids=lambda v: f"M{v.M}_K{v.K}_N{v.N}" if hasattr(v, "M") else f"c{v}")
 def test_kchunks_full_size(dev, case, c):
+    """Every output entry (70B, 1K-8K tokens) or whole rows and columns of every tile (16K
+    tokens, 405B) against the oracle, and bit for bit against the unsliced fo_gemm_ref."""
     x, w = case.x(), case.w()
     prob = AGC(x, w, case.P, c, dev)
     y_ref = torch.empty_like(prob.y)
     fo.gemm_ref(to_dev(x, dev), prob.w_d, y_ref, stream=_stream())
     torch.cuda.synchronize()
     mono = from_dev(y_ref)
-    rows, cols = sample_indices(case.M, case.N, 1500, seed=case.M + c, block_rows=case.m)
-    slices = [x[s * case.m:(s + 1) * case.m] for s in range(case.P)]
-    ref = oracle.ag_sampled(slices, w, rows, cols)
+    blocks = ag_oracle_blocks(case)
+    tile = fo.tile_info(case.P, case.m, case.K, case.N)[:2]
     for r in (0, 5):
         got = prob.run(r)
-        assert rel_frobenius(got[rows, cols], ref) <= TOL_BF16, f"rank {r}"
+        check_ag_blocks(got, blocks, tile, f"{case.name}, {c} K blocks: rank {r}")
         assert np.array_equal(got, mono), f"rank {r}: chunk-major sliced != unsliced"
 
 

@@ -13,7 +13,8 @@ import pytest
 
 import oracle
 from comm_overlapped_sliced_amd import configs, flashovl as fo, inputs
-from tests.gpu_helpers import TOL_BF16, from_dev, rel_frobenius, to_dev
+from tests.gpu_helpers import (TOL_BF16, ag_oracle_blocks, assert_parity, from_dev,
+                               rel_frobenius, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -97,18 +98,21 @@ def test_mlp_block_against_oracle(dev):
 
 def test_mlp_block_l70b(dev):
     """The Llama-3.1-70B block (gate+up of config 2, down of config 3, seven fp32 partials), rank
-    0: every entry of the rank's output chunk against the oracle, which needs only slice 0 of X
-    (the rows of H that the own chunk reads)."""
+    0: every entry of the rank's output chunk against the oracle's block.
+
+    Per-element bound 2^-8 (|ref| + rms(ref)): Y and H are rounded to bf16 between the kernels,
+    and where the GPU's fp32 sum and the oracle's exact sum fall on two sides of a rounding tie
+    one entry of H differs by a bf16 ulp (2^-7 of it); the down projection weighs each such
+    entry by a weight of about 0.02, so an output entry moves by a small fraction of rms(ref)
+    (at most about 2e-3 of it measured), not by the 2^-14 of a single fp32 chain."""
     ag, rs = configs.L70B_AG, configs.L70B_RS
-    P, m, inter = ag.P, ag.m, rs.K
+    P, m = ag.P, ag.m
     x, w_gu, w_d = ag.x(), ag.w(), rs.w()
     parts = [rs.partial(q) for q in range(P)]
     r = 0
     got = _block(dev, x, w_gu, w_d, parts, P, r)
-    y0 = oracle.round_bf16(oracle.gemm(x[r * m:(r + 1) * m], w_gu))
-    h0 = oracle.round_bf16(oracle.swiglu(y0))
-    ref = oracle.gemm(h0, w_d) + sum(parts[q].astype(np.float64) for q in range(P) if q != r)
-    assert rel_frobenius(got, ref) <= TOL_BF16
+    ref = oracle.mlp_block([x[q * m:(q + 1) * m] for q in range(P)], w_gu, w_d, parts, P, r)
+    assert_parity(got, ref, "f32", what="70B MLP block, rank 0", bound=(2.0 ** -8, 2.0 ** -8))
 
 
 def _ag_swiglu(dev, x, w_gu, P, r, o):
@@ -168,16 +172,16 @@ def test_swiglu_epilogue_beats_the_two_kernel_path(dev):
     assert e_fused < e_two, (e_fused, e_two)
 
 
-def test_swiglu_epilogue_l70b_sampled_rows(dev):
-    """The Llama-3.1-70B gate+up projection (8 slices of 4096 x 8192, W 8192 x 7168) with the
-    SwiGLU epilogue, rank 3: whole rows of H (every column tile) at the first, a middle and the
-    last row of each slice, against the oracle's fp64 projection of those rows."""
+def test_swiglu_epilogue_l70b(dev):
+    """The Llama-3.1-70B gate+up projection (8 slices of 512 x 8192, W 8192 x 7168) with the
+    SwiGLU epilogue, rank 3: every entry of H against silu(gate) * up of the oracle's fp64
+    projection."""
     ag = configs.L70B_AG
     P, m = ag.P, ag.m
     x, w_gu = ag.x(), ag.w()
     r = 3
     h = _ag_swiglu(dev, x, w_gu, P, r, fo.opts())
-    rows = np.array([q * m + o for q in range(P) for o in (0, m // 2 + 5, m - 1)])
-    got = from_dev(h[torch.from_numpy(rows).to(dev)])
-    ref = oracle.swiglu(oracle.gemm(x[rows], w_gu))
-    assert rel_frobenius(got, ref) <= TOL_BF16
+    (_, _, y), = ag_oracle_blocks(ag)
+    ref = oracle.swiglu(y)
+    bm, bn, _ = fo.tile_info(P, m, ag.K, ag.N)
+    assert_parity(from_dev(h), ref, "bf16", (bm, bn // 2), what="70B gate+up SwiGLU, rank 3")
