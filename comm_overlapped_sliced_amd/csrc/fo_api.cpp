@@ -85,7 +85,8 @@ struct DevState {
   int dev = 0;
   int n_cu = 0;
   int wall_khz = 100000;     // wall-clock counter rate read by the kernels' bounded waits
-  uint32_t* err = nullptr;   // wait record: 1 timeout, 2 failed copy (uncached memory)
+  uint32_t* err = nullptr;   // wait record, two words: what failed (1 timeout, 2 failed copy)
+                             // and the number of the last call that failed (uncached memory)
   uint32_t* go = nullptr;    // the tail reduce's start word (same uncached block)
   uint32_t* own_done = nullptr;  // Flash-RS tail: own-chunk row groups stored [group] (same block)
   uint32_t go_value = 0;
@@ -670,6 +671,7 @@ fo_status fo_gemm_rs(const void* x_shard, const void* w, float* send_buf, float*
     ra.count = m * N;
     ra.spin_limit = p.spin_limit;
     ra.err = st->err;
+    ra.gen = p.gen;
     ra.max_blocks = 2 * st->n_cu;
     ra.go = st->go;
     if (++st->go_value == 0) ++st->go_value;
@@ -959,7 +961,8 @@ fo_status fo_transfer_ref(int32_t kind, const void* const* src, void* dst, int32
   s = order_after_last(st, ks);
   if (s != FO_OK) return s;
   FO_HIP(fo::launch_release(call.start, ks));
-  FO_HIP(fo::launch_wait(call.comp_tab, seq, n, G, spin_ticks(*st, o.spin_timeout_us), st->err, ks));
+  FO_HIP(fo::launch_wait(call.comp_tab, seq, n, G, spin_ticks(*st, o.spin_timeout_us), st->err,
+                         ++st->gen, ks));
   hipEvent_t slot_ev = nullptr;
   FO_DMA(fo::dma::end(st->dev, call, ks, &e_, &slot_ev));
   s = mark_last(st, ks, slot_ev);

@@ -869,11 +869,11 @@ struct SliceList {
 
 // Waits until every group of every listed slice has landed (the transfers alone, without a GEMM).
 __global__ __launch_bounds__(64) void wait_kernel(const int64_t* const* comp_tab, SliceList l,
-                                                  uint64_t limit, uint32_t* err) {
+                                                  uint64_t limit, uint32_t* err, uint32_t gen) {
   if (threadIdx.x == 0)
     for (int i = 0; i < l.n; ++i)
       for (int g = 0; g < l.groups; ++g)
-        wait_signal(comp_tab[l.s[i] * kMaxGroups + g], limit, err);
+        wait_signal(comp_tab[l.s[i] * kMaxGroups + g], limit, err, gen);
   __syncthreads();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
 }
@@ -895,14 +895,14 @@ __device__ __forceinline__ float ld_sys1(const float* p) {
 }
 __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Bounded wait until a device word holds `v` (or a wait of the call has failed).
+// Bounded wait of call `gen` until a device word holds `v` (or a wait of the call has failed).
 __device__ __forceinline__ void wait_word(const uint32_t* w, uint32_t v, uint64_t limit,
-                                          uint32_t* err) {
+                                          uint32_t* err, uint32_t gen) {
   const uint64_t t0 = wall_clock64();
   while (__hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != v) {
-    if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != 0u) return;
+    if (wait_failed(err, gen)) return;
     if (wall_clock64() - t0 > limit) {
-      __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      wait_fail(err, 1u, gen);
       return;
     }
     __builtin_amdgcn_s_sleep(2);
@@ -921,10 +921,10 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
       for (int i = 0; i < a.n_recv; ++i)
         if (a.recv_slice[i] >= 0)
           for (int g = 0; g < a.groups; ++g)
-            wait_signal(a.comp_tab[a.recv_slice[i] * kMaxGroups + g], a.spin_limit, a.err);
+            wait_signal(a.comp_tab[a.recv_slice[i] * kMaxGroups + g], a.spin_limit, a.err, a.gen);
       __hip_atomic_store(a.go, a.go_value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     } else {
-      wait_word(a.go, a.go_value, a.spin_limit, a.err);
+      wait_word(a.go, a.go_value, a.spin_limit, a.err, a.gen);
     }
   }
   __syncthreads();
@@ -973,13 +973,13 @@ hipError_t launch_release(int64_t* v, hipStream_t s) {
 }
 
 hipError_t launch_wait(const int64_t* const* comp_tab, const int32_t* slices, int n, int groups,
-                       uint64_t spin_limit, uint32_t* err, hipStream_t s) {
+                       uint64_t spin_limit, uint32_t* err, uint32_t gen, hipStream_t s) {
   if (n < 0 || n > FO_MAX_P || groups < 1 || groups > kMaxGroups) return hipErrorInvalidValue;
   SliceList l{};
   for (int i = 0; i < n; ++i) l.s[i] = slices[i];
   l.n = n;
   l.groups = groups;
-  hipLaunchKernelGGL(wait_kernel, dim3(1), dim3(64), 0, s, comp_tab, l, spin_limit, err);
+  hipLaunchKernelGGL(wait_kernel, dim3(1), dim3(64), 0, s, comp_tab, l, spin_limit, err, gen);
   return hipGetLastError();
 }
 

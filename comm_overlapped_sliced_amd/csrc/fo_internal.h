@@ -38,7 +38,9 @@ struct Plan {
   int64_t* const* rel_tab;           // release-signal values [position][group] (null: no release)
   const void* b;                     // W [K, N], row stride N
   uint32_t* done;                    // completed-tile counters [position][group] (zero between calls)
-  uint32_t* err;                     // 1: a wait ran past spin_limit; 2: a copy reported failure
+  uint32_t* err;                     // wait record, two words: [0] what failed (1: a wait ran past
+                                     // spin_limit, 2: a copy reported failure), [1] the number
+                                     // of the last call that failed
   uint32_t* lead;                    // [slice][group]: the last call whose poller is elected
   uint32_t* ready;                   // [slice][group]: the last call whose group has landed
   uint32_t gen;                      // this call's number (> 0, grows by one per call)
@@ -109,9 +111,9 @@ hipError_t launch_release(int64_t* v, hipStream_t stream);
 
 // One-workgroup kernel that waits (bounded by spin_limit ticks) until the completion signals of
 // groups 0..groups-1 of each listed slice have dropped to zero (comp_tab as in Plan), recording a
-// timeout or a failed copy in *err like the GEMM's waits.
+// timeout or a failed copy of call `gen` in the wait record err like the GEMM's waits.
 hipError_t launch_wait(const int64_t* const* comp_tab, const int32_t* slices, int n, int groups,
-                       uint64_t spin_limit, uint32_t* err, hipStream_t stream);
+                       uint64_t spin_limit, uint32_t* err, uint32_t gen, hipStream_t stream);
 
 // The received partials added onto `out` after the GEMM (Flash-RS in the data-slicing order,
 // where the own chunk is not the last one computed): out[i] += recv[0][i] + recv[1][i] + ... in
@@ -126,7 +128,8 @@ struct ReduceArgs {
   int32_t vec4;                    // every pointer 16-byte aligned and count % 4 == 0
   int64_t count;
   uint64_t spin_limit;
-  uint32_t* err;
+  uint32_t* err;                   // the wait record (two words, as in Plan)
+  uint32_t gen;                    // the call's number
   int32_t max_blocks;              // persistent grid size
   uint32_t* go;                    // device word (uncached) block 0 sets to go_value once every
   uint32_t go_value;               // partial has landed; the other blocks wait on it

@@ -9,36 +9,48 @@
 
 namespace fo {
 
-// Bounded wait until a signal value has dropped to zero (the copy engine decrements it from 1
-// when its transfer has landed; a negative value reports a failed copy, recorded as err = 2).
-// Once any wait of the call has run past the bound (err set), later waits give up at once, so a
-// missing arrival costs one bound, not one per workgroup.
-__device__ __forceinline__ void wait_signal(const int64_t* v, uint64_t limit, uint32_t* err) {
+// The wait record of the device: err[0] accumulates what went wrong (1: a wait ran past its
+// bound, 2: a copy engine reported a failed transfer) until fo_check reads and clears it;
+// err[1] is the number of the last call that failed. A call's waits give up at once only when
+// that call itself has already failed (a missing arrival costs one bound, not one per
+// workgroup); the calls after it wait as usual.
+__device__ __forceinline__ void wait_fail(uint32_t* err, uint32_t kind, uint32_t gen) {
+  __hip_atomic_fetch_or(err, kind, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  __hip_atomic_fetch_max(err + 1, gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ bool wait_failed(const uint32_t* err, uint32_t gen) {
+  return __hip_atomic_load(err + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == gen;
+}
+
+// Bounded wait of call `gen` until a signal value has dropped to zero (the copy engine
+// decrements it from 1 when its transfer has landed; a negative value reports a failed copy).
+__device__ __forceinline__ void wait_signal(const int64_t* v, uint64_t limit, uint32_t* err,
+                                            uint32_t gen) {
   const uint64_t t0 = wall_clock64();
   for (;;) {
     const int64_t x = __hip_atomic_load(v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     if (x <= 0) {
-      if (x < 0) __hip_atomic_store(err, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      if (x < 0) wait_fail(err, 2u, gen);
       return;
     }
-    if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != 0u) return;
+    if (wait_failed(err, gen)) return;
     if (wall_clock64() - t0 > limit) {
-      __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      wait_fail(err, 1u, gen);
       return;
     }
     __builtin_amdgcn_s_sleep(2);
   }
 }
 
-// Bounded wait until a device word has reached `gen` (or a wait of the call has failed). The
-// word is uncached device memory, so every read sees the latest store from any XCD.
+// Bounded wait of call `gen` until a device word has reached `gen` (or a wait of the call has
+// failed). The word is uncached device memory, so every read sees the latest store from any XCD.
 __device__ __forceinline__ void wait_gen(const uint32_t* w, uint32_t gen, uint64_t limit,
                                          uint32_t* err) {
   const uint64_t t0 = wall_clock64();
   while (__hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < gen) {
-    if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != 0u) return;
+    if (wait_failed(err, gen)) return;
     if (wall_clock64() - t0 > limit) {
-      __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      wait_fail(err, 1u, gen);
       return;
     }
     __builtin_amdgcn_s_sleep(8);
@@ -58,7 +70,7 @@ __device__ __forceinline__ void wait_group(const int64_t* const* comp_tab, uint3
   const uint32_t prev =
       __hip_atomic_fetch_max(lead + k, gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (prev < gen) {
-    wait_signal(comp_tab[k], spin_limit, err);
+    wait_signal(comp_tab[k], spin_limit, err, gen);
     __hip_atomic_store(ready + k, gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   } else {
     wait_gen(ready + k, gen, spin_limit, err);

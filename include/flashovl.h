@@ -35,8 +35,9 @@
  *     call's kernel, whichever stream that was on.
  *   - Errors are return codes; nothing is enqueued when an argument is rejected. An in-kernel
  *     wait that exceeds opts->spin_timeout_us is recorded on the device and reported as
- *     FO_ERR_TIMEOUT by fo_check(); the kernel still runs to completion (no hang), but its
- *     results are then unspecified.
+ *     FO_ERR_TIMEOUT by fo_check(); the kernel still runs to completion (no hang), but that
+ *     call's results are then unspecified. The record names the call: its other waits give up
+ *     at once, while the calls enqueued after it wait as usual and are unaffected.
  *   - Thread safety: entry points may be called from several host threads; each call holds a
  *     per-device lock while it enqueues.
  */
