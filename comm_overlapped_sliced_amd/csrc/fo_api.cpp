@@ -307,6 +307,207 @@ fo_status launch_with_events(const fo::Plan& p, int in_dt, int tile, hipStream_t
   return FO_OK;
 }
 
+// What a Flash-RS call takes from its device: the words its kernels count, wait and record in,
+// the call's number, and the device's CU count and wait bound. fo_gemm_rs takes them from the
+// library-allocated state, fo_gemm_rs_noalloc from the static scratch array.
+struct Words {
+  uint32_t* done = nullptr;
+  uint32_t* own_done = nullptr;
+  uint32_t* err = nullptr;
+  uint32_t* lead = nullptr;
+  uint32_t* ready = nullptr;
+  uint32_t* go = nullptr;
+  uint32_t gen = 0, go_value = 0;
+  int n_cu = 0;
+  uint64_t spin_limit = 0;
+};
+
+// Argument checks of fo_gemm_rs (and of fo_gemm_rs_noalloc, with no peer partials); *o
+// receives the options with defaults filled in. Nothing is enqueued.
+fo_status rs_check(const void* x_shard, const void* w, const float* send_buf, const float* out,
+                   const float* const* peer_partial, const float* recv_buf, int P, int rank,
+                   int64_t m, int64_t K, int64_t N, int in_dt, const fo_opts* opts, fo_opts* o) {
+  fo_status s = check_opts(opts, o);
+  if (s != FO_OK) return s;
+  s = check_common(P, rank, m, K, N, in_dt);
+  if (s != FO_OK) return s;
+  if (o->epilogue != FO_EPI_NONE) return invalid("opts.epilogue applies to fo_ag_gemm only");
+  if (o->k_chunks > 1) return invalid("opts.k_chunks applies to fo_ag_gemm only");
+  const int arrival = o->arrival == FO_ARR_DEFAULT ? FO_ARR_LOCKSTEP : o->arrival;
+  const bool arrivals = peer_partial != nullptr && arrival != FO_ARR_NONE && P > 1;
+  const size_t es = dt_size(in_dt);
+  const size_t align = in_dt == FO_DT_BF16 ? 16 : 4;
+  if (!x_shard || !w || !out || (P > 1 && (!send_buf || !recv_buf))) return invalid("NULL buffer");
+  if (!aligned(x_shard, align) || !aligned(w, align) || !aligned(out, 4) ||
+      (send_buf && !aligned(send_buf, 4)) || (recv_buf && !aligned(recv_buf, 4)))
+    return invalid("misaligned buffer (inputs need %zu-byte alignment)", align);
+  const size_t chunk_b = (size_t)m * N * 4;
+  const Range r_x = rng(x_shard, (size_t)P * m * K * es), r_w = rng(w, (size_t)K * N * es);
+  const Range r_out = rng(out, chunk_b);
+  const Range r_send = rng(send_buf, send_buf ? (size_t)P * chunk_b : 0);
+  const Range r_recv = rng(recv_buf, recv_buf ? (size_t)P * chunk_b : 0);
+  for (Range o1 : {r_out, r_send}) {
+    if (overlap(o1, r_x) || overlap(o1, r_w) || overlap(o1, r_recv))
+      return invalid("an output overlaps an input");
+  }
+  if (overlap(r_out, r_send)) return invalid("out overlaps send_buf");
+  if (arrivals) {
+    for (int q = 0; q < P; ++q) {
+      if (q == rank) continue;
+      if (!peer_partial[q]) return invalid("peer_partial[%d] is NULL", q);
+      if (!aligned(peer_partial[q], 4)) return invalid("peer_partial[%d] misaligned", q);
+      const Range rp = rng(peer_partial[q], chunk_b);
+      if (overlap(rp, r_recv) || overlap(rp, r_out) || overlap(rp, r_send))
+        return invalid("peer_partial[%d] overlaps recv_buf or an output", q);
+    }
+  }
+  return FO_OK;
+}
+
+// The launch plan of a Flash-RS call (no transfer tables: the caller adds them). `arrivals`
+// only decides the acquire after arrival waits. *bm, *tile and *own_pos receive the tile height,
+// the tile shape and the position of the own chunk.
+fo_status rs_plan(const void* x_shard, const void* w, float* send_buf, float* out, float* recv_buf,
+                  int P, int rank, int64_t m, int64_t K, int64_t N, int in_dt, const fo_opts& o,
+                  const Words& wd, bool arrivals, fo::Plan* pp, int* bm, int* tile,
+                  int* own_pos) {
+  fo::Plan& p = *pp;
+  const size_t es = dt_size(in_dt), chunk_b = (size_t)m * N * 4;
+  *tile = resolve_tile(o, in_dt, FO_DT_F32, P, m, K, N, wd.n_cu);
+  const fo_status s = tiles_for(in_dt, *tile, m, N, P, p, bm);
+  if (s != FO_OK) return s;
+  set_layout(1, o, p);
+  // NATURAL (data slicing): chunks in index order, the own chunk written plainly where it falls,
+  // and the partials added after the GEMM by a separate kernel
+  const bool natural = o.order == FO_ORDER_NATURAL;
+  int32_t order[FO_MAX_P];
+  fo::slice_order(1, o.order, P, rank, order);
+  for (int pos = 0; pos < P; ++pos) {
+    const int d = order[pos];
+    p.a_pos[pos] = (const uint8_t*)x_shard + (size_t)d * m * K * es;
+    p.c_pos[pos] = d == rank ? (void*)out : (void*)((uint8_t*)send_buf + (size_t)d * chunk_b);
+    p.gate_slice[pos] = -1;
+    if (d == rank) *own_pos = pos;
+  }
+  if (!natural) p.accum_pos = *own_pos;
+  // partials arrive from rank-1, rank-2, ... (mod P) and are added in that order
+  for (int i = 1; i < P; ++i) {
+    const int q = ((rank - i) % P + P) % P;
+    p.recv[i - 1] = (const float*)((const uint8_t*)recv_buf + (size_t)q * chunk_b);
+    p.recv_slice[i - 1] = -1;
+  }
+  p.n_recv = P - 1;
+  p.b = w;
+  p.done = wd.done;
+  p.lead = wd.lead;
+  p.ready = wd.ready;
+  p.gen = wd.gen;
+  p.err = wd.err;
+  p.spin_limit = wd.spin_limit;
+  p.m = m;
+  p.K = K;
+  p.N = N;
+  p.grid.npos = P;
+  p.out_f32 = 1;
+  // partials' transfers on cache-line (128-byte) boundaries: no acquire after the arrival waits
+  p.acq = (!arrivals || (aligned(recv_buf, 128) && ((size_t)N * 4) % 128 == 0)) ? 0 : 1;
+  // Flash-RS tail: the own chunk's tiles store their sums and workgroups appended to the grid add
+  // the partials (same order, same bits), spread over the CUs the other chunks have freed. Needs
+  // 16-byte aligned out and partials (else the own tiles add them in their epilogue).
+  if (!natural && P > 1 && in_dt == FO_DT_BF16 && aligned(out, 16) &&
+      (double)m * N * 4 < (double)(1u << 31)) {
+    bool al = true;
+    for (int i = 0; i < P - 1; ++i) al = al && aligned(p.recv[i], 16);
+    if (al) {
+      const int64_t rows_g = (int64_t)p.grid.group_rows * *bm;
+      const int64_t pieces = rows_g * N / 4;  // 16-byte pieces of a full group
+      p.tail_per_group = (int32_t)std::max<int64_t>(1, std::min<int64_t>(128, pieces / 2048));
+      p.tail_units = p.grid.groups * p.tail_per_group;
+      p.tail_bm = *bm;
+      p.own_done = wd.own_done;
+    }
+  }
+  return FO_OK;
+}
+
+// The separate pass of Flash-RS in the data-slicing order: out += the partials in arrival order
+// once they have landed (comp_tab null: resident).
+fo_status launch_rs_reduce(const fo::Plan& p, float* out, int64_t m, int64_t N, const Words& wd,
+                           const int64_t* const* comp_tab, hipStream_t cs) {
+  fo::ReduceArgs ra{};
+  ra.out = out;
+  ra.n_recv = p.n_recv;
+  bool al = aligned(out, 16) && ((size_t)m * N) % 4 == 0;
+  for (int i = 0; i < p.n_recv; ++i) {
+    ra.recv[i] = p.recv[i];
+    ra.recv_slice[i] = p.recv_slice[i];
+    al = al && aligned(p.recv[i], 16);
+  }
+  ra.comp_tab = comp_tab;
+  ra.groups = p.grid.groups;
+  ra.vec4 = al ? 1 : 0;
+  ra.count = m * N;
+  ra.spin_limit = p.spin_limit;
+  ra.err = wd.err;
+  ra.gen = wd.gen;
+  ra.max_blocks = 2 * wd.n_cu;
+  ra.go = wd.go;
+  ra.go_value = wd.go_value;
+  FO_HIP(fo::launch_reduce(ra, cs));
+  return FO_OK;
+}
+
+// ---- the scratch of fo_gemm_rs_noalloc -------------------------------------------------------
+// A static device array instead of library-allocated memory, 32-bit words: [0, kNaOwn) the tile
+// counters [position][row group], [kNaOwn, kNaErr) the own chunk's row-group words, [kNaErr,
+// kNaErr + 2) the wait record, kNaGo the start word of the data-slicing reduce. Each device holds
+// its own copy of the array until the process ends; host code reaches it only through the
+// address hipGetSymbolAddress returns on that device (the array's name is a host-side stand-in).
+constexpr int kNaCounters = 0;
+constexpr int kNaOwn = FO_MAX_P * fo::kMaxGroups;
+constexpr int kNaErr = kNaOwn + fo::kMaxGroups;
+constexpr int kNaGo = kNaErr + 8;
+static_assert((kNaGo + 1) * 4 <= FO_NOALLOC_SCRATCH_BYTES, "scratch layout");
+__device__ __align__(256) static uint32_t scratch[FO_NOALLOC_SCRATCH_BYTES / 4];
+
+struct NoAllocDev {
+  std::mutex mu;
+  uint32_t* ptr = nullptr;  // device address of `scratch` on this device
+  int n_cu = 0;
+  int wall_khz = 100000;
+  uint32_t gen = 0;         // number of the device's last fo_gemm_rs_noalloc call
+};
+NoAllocDev g_na[kMaxDevices];
+
+// The current device's scratch, set up on its first call (the symbol's address and two device
+// attributes; nothing is allocated), with its lock held by `lk`.
+fo_status noalloc_state(NoAllocDev** out, std::unique_lock<std::mutex>* lk) {
+  int dev = 0;
+  FO_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) {
+    set_error("device %d beyond the library's limit of %d", dev, kMaxDevices);
+    return FO_ERR_UNSUPPORTED;
+  }
+  NoAllocDev& na = g_na[dev];
+  *lk = std::unique_lock<std::mutex>(na.mu);
+  if (na.ptr == nullptr) {
+    void* ptr = nullptr;
+    FO_HIP(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+    if (ptr == nullptr || !aligned(ptr, 256)) {
+      set_error("hipGetSymbolAddress returned no usable address for the scratch array");
+      return FO_ERR_HIP;
+    }
+    int n_cu = 0, khz = 0;
+    FO_HIP(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev));
+    FO_HIP(hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev));
+    na.n_cu = n_cu;
+    if (khz > 0) na.wall_khz = khz;
+    na.ptr = (uint32_t*)ptr;
+  }
+  *out = &na;
+  return FO_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -545,138 +746,54 @@ fo_status fo_gemm_rs(const void* x_shard, const void* w, float* send_buf, float*
                      int64_t m, int64_t K, int64_t N, int32_t in_dt, void* compute_stream,
                      const fo_opts* opts) {
   fo_opts o;
-  fo_status s = check_opts(opts, &o);
-  if (s != FO_OK) return s;
-  s = check_common(P, rank, m, K, N, in_dt);
-  if (s != FO_OK) return s;
-  if (o.epilogue != FO_EPI_NONE) return invalid("opts.epilogue applies to fo_ag_gemm only");
-  if (o.k_chunks > 1) return invalid("opts.k_chunks applies to fo_ag_gemm only");
+  fo_status s = rs_check(x_shard, w, send_buf, out, peer_partial, recv_buf, P, rank, m, K, N,
+                         in_dt, opts, &o);
+  if (s != FO_OK || m == 0 || N == 0) return s;
   const int arrival = o.arrival == FO_ARR_DEFAULT ? FO_ARR_LOCKSTEP : o.arrival;
   const bool arrivals = peer_partial != nullptr && arrival != FO_ARR_NONE && P > 1;
-  const size_t es = dt_size(in_dt);
-  const size_t align = in_dt == FO_DT_BF16 ? 16 : 4;
-  if (!x_shard || !w || !out || (P > 1 && (!send_buf || !recv_buf))) return invalid("NULL buffer");
-  if (!aligned(x_shard, align) || !aligned(w, align) || !aligned(out, 4) ||
-      (send_buf && !aligned(send_buf, 4)) || (recv_buf && !aligned(recv_buf, 4)))
-    return invalid("misaligned buffer (inputs need %zu-byte alignment)", align);
-  const size_t chunk_b = (size_t)m * N * 4;
-  const Range r_x = rng(x_shard, (size_t)P * m * K * es), r_w = rng(w, (size_t)K * N * es);
-  const Range r_out = rng(out, chunk_b);
-  const Range r_send = rng(send_buf, send_buf ? (size_t)P * chunk_b : 0);
-  const Range r_recv = rng(recv_buf, recv_buf ? (size_t)P * chunk_b : 0);
-  for (Range o1 : {r_out, r_send}) {
-    if (overlap(o1, r_x) || overlap(o1, r_w) || overlap(o1, r_recv))
-      return invalid("an output overlaps an input");
-  }
-  if (overlap(r_out, r_send)) return invalid("out overlaps send_buf");
-  if (arrivals) {
-    for (int q = 0; q < P; ++q) {
-      if (q == rank) continue;
-      if (!peer_partial[q]) return invalid("peer_partial[%d] is NULL", q);
-      if (!aligned(peer_partial[q], 4)) return invalid("peer_partial[%d] misaligned", q);
-      const Range rp = rng(peer_partial[q], chunk_b);
-      if (overlap(rp, r_recv) || overlap(rp, r_out) || overlap(rp, r_send))
-        return invalid("peer_partial[%d] overlaps recv_buf or an output", q);
-    }
-  }
-  if (m == 0 || N == 0) return FO_OK;
 
   DevState* st = nullptr;
   std::unique_lock<std::mutex> lk;
   s = current_state(&st, &lk);
   if (s != FO_OK) return s;
 
-  const int tile = resolve_tile(o, in_dt, FO_DT_F32, P, m, K, N, st->n_cu);
+  Words wd{};
+  wd.done = st->done;
+  wd.own_done = st->own_done;
+  wd.err = st->err;
+  wd.lead = st->arr_lead;
+  wd.ready = st->arr_ready;
+  wd.go = st->go;
+  wd.gen = ++st->gen;
+  if (++st->go_value == 0) ++st->go_value;
+  wd.go_value = st->go_value;
+  wd.n_cu = st->n_cu;
+  wd.spin_limit = spin_ticks(*st, o.spin_timeout_us);
   fo::Plan p = fo::empty_plan();
-  int bm = 0;
-  s = tiles_for(in_dt, tile, m, N, P, p, &bm);
+  int bm = 0, tile = 0, own_pos = 0;
+  s = rs_plan(x_shard, w, send_buf, out, recv_buf, P, rank, m, K, N, in_dt, o, wd, arrivals, &p,
+              &bm, &tile, &own_pos);
   if (s != FO_OK) return s;
-  set_layout(1, o, p);
   const bool lockstep = arrivals && arrival == FO_ARR_LOCKSTEP;
-  // NATURAL (data slicing): chunks in index order, the own chunk written plainly where it falls,
-  // and the partials added after the GEMM by a separate kernel
   const bool natural = o.order == FO_ORDER_NATURAL;
   fo::dma::Call call{};
   if (arrivals) FO_DMA(fo::dma::begin(st->dev, P, p.grid.groups, &call, &e_));
-  int32_t order[FO_MAX_P];
-  fo::slice_order(1, o.order, P, rank, order);
-  int own_pos = 0;
-  for (int pos = 0; pos < P; ++pos) {
-    const int d = order[pos];
-    p.a_pos[pos] = (const uint8_t*)x_shard + (size_t)d * m * K * es;
-    p.c_pos[pos] = d == rank ? (void*)out : (void*)((uint8_t*)send_buf + (size_t)d * chunk_b);
-    p.gate_slice[pos] = -1;
-    if (d == rank) own_pos = pos;
-  }
-  if (!natural) p.accum_pos = own_pos;
   p.comp_tab = call.comp_tab;
   p.rel_tab = lockstep ? call.rel_tab : nullptr;
-  // partials arrive from rank-1, rank-2, ... (mod P) and are added in that order
-  for (int i = 1; i < P; ++i) {
-    const int q = ((rank - i) % P + P) % P;
-    p.recv[i - 1] = (const float*)((const uint8_t*)recv_buf + (size_t)q * chunk_b);
-    p.recv_slice[i - 1] = arrivals ? q : -1;
-  }
-  p.n_recv = P - 1;
-  p.b = w;
-  p.done = st->done;
-  p.lead = st->arr_lead;
-  p.ready = st->arr_ready;
-  p.gen = ++st->gen;
-  p.err = st->err;
-  p.spin_limit = spin_ticks(*st, o.spin_timeout_us);
-  p.m = m;
-  p.K = K;
-  p.N = N;
-  p.grid.npos = P;
-  p.out_f32 = 1;
-  // partials' transfers on cache-line (128-byte) boundaries: no acquire after the arrival waits
-  p.acq = (aligned(recv_buf, 128) && ((size_t)N * 4) % 128 == 0) ? 0 : 1;
-  // Flash-RS tail: the own chunk's tiles store their sums and workgroups appended to the grid add
-  // the partials (same order, same bits), spread over the CUs the other chunks have freed. Needs
-  // 16-byte aligned out and partials (else the own tiles add them in their epilogue).
-  if (!natural && P > 1 && in_dt == FO_DT_BF16 && aligned(out, 16) &&
-      (double)m * N * 4 < (double)(1u << 31)) {
-    bool al = true;
-    for (int i = 0; i < P - 1; ++i) al = al && aligned(p.recv[i], 16);
-    if (al) {
-      const int64_t rows_g = (int64_t)p.grid.group_rows * bm;
-      const int64_t pieces = rows_g * N / 4;  // 16-byte pieces of a full group
-      p.tail_per_group = (int32_t)std::max<int64_t>(1, std::min<int64_t>(128, pieces / 2048));
-      p.tail_units = p.grid.groups * p.tail_per_group;
-      p.tail_bm = bm;
-      p.own_done = st->own_done;
-    }
+  if (arrivals) p.start = call.start;
+  for (int i = 0; i < P - 1; ++i) {
+    const int q = ((rank - 1 - i) % P + P) % P;
+    p.recv_slice[i] = arrivals ? q : -1;
   }
 
   hipStream_t cs = (hipStream_t)compute_stream;
-  if (arrivals) p.start = call.start;
   s = order_after_last(st, cs);
   if (s != FO_OK) return s;
   s = launch_with_events(p, in_dt, tile, cs, o);
   if (s != FO_OK) return s;
   if (natural && P > 1) {
-    fo::ReduceArgs ra{};
-    ra.out = out;
-    ra.n_recv = P - 1;
-    bool al = aligned(out, 16) && ((size_t)m * N) % 4 == 0;
-    for (int i = 0; i < P - 1; ++i) {
-      ra.recv[i] = p.recv[i];
-      ra.recv_slice[i] = p.recv_slice[i];
-      al = al && aligned(p.recv[i], 16);
-    }
-    ra.comp_tab = call.comp_tab;
-    ra.groups = p.grid.groups;
-    ra.vec4 = al ? 1 : 0;
-    ra.count = m * N;
-    ra.spin_limit = p.spin_limit;
-    ra.err = st->err;
-    ra.gen = p.gen;
-    ra.max_blocks = 2 * st->n_cu;
-    ra.go = st->go;
-    if (++st->go_value == 0) ++st->go_value;
-    ra.go_value = st->go_value;
-    FO_HIP(fo::launch_reduce(ra, cs));
+    s = launch_rs_reduce(p, out, m, N, wd, call.comp_tab, cs);
+    if (s != FO_OK) return s;
   }
   hipEvent_t slot_ev = nullptr;
   if (arrivals) FO_DMA(fo::dma::end(st->dev, call, cs, &e_, &slot_ev));
@@ -691,7 +808,7 @@ fo_status fo_gemm_rs(const void* x_shard, const void* w, float* send_buf, float*
     int seq[FO_MAX_P];
     const int n = arrival_sequence(1, FO_ORDER_FLASH, P, rank, seq);
     const int L = links_for(o, P);
-    const size_t row_b = (size_t)N * 4;
+    const size_t row_b = (size_t)N * 4, chunk_b = (size_t)m * N * 4;
     for (int g = 0; g < p.grid.groups; ++g) {
       int64_t r0, r1;
       group_span(p, bm, m, g, &r0, &r1);
@@ -706,6 +823,53 @@ fo_status fo_gemm_rs(const void* x_shard, const void* w, float* send_buf, float*
       }
     }
   }
+  return FO_OK;
+}
+
+fo_status fo_gemm_rs_noalloc(const void* x_shard, const void* w, float* send_buf, float* out,
+                             float* recv_buf, int32_t P, int32_t rank, int64_t m, int64_t K,
+                             int64_t N, int32_t in_dt, void* compute_stream, const fo_opts* opts) {
+  fo_opts o;
+  fo_status s = rs_check(x_shard, w, send_buf, out, nullptr, recv_buf, P, rank, m, K, N, in_dt,
+                         opts, &o);
+  if (s != FO_OK) return s;
+  if (o.arrival != FO_ARR_DEFAULT && o.arrival != FO_ARR_NONE)
+    return invalid("fo_gemm_rs_noalloc takes resident partials: opts.arrival must be DEFAULT or "
+                   "NONE");
+  // what the call keeps in the static array: the tile counters of P positions, the own chunk's
+  // row-group words, the wait record and the start word of the tail reduce
+  const int need = kNaGo + 1;
+  if (P > FO_MAX_P || need * 4 > FO_NOALLOC_SCRATCH_BYTES)
+    return unsupported("fo_gemm_rs_noalloc: P = %d needs more than the %d-byte scratch array", P,
+                       FO_NOALLOC_SCRATCH_BYTES);
+  if (m == 0 || N == 0) return FO_OK;
+  NoAllocDev* na = nullptr;
+  std::unique_lock<std::mutex> lk;
+  s = noalloc_state(&na, &lk);
+  if (s != FO_OK) return s;
+
+  Words wd{};
+  wd.done = na->ptr + kNaCounters;
+  wd.own_done = na->ptr + kNaOwn;
+  wd.err = na->ptr + kNaErr;
+  wd.go = na->ptr + kNaGo;
+  if (++na->gen == 0) ++na->gen;
+  wd.gen = na->gen;
+  wd.go_value = na->gen;
+  wd.n_cu = na->n_cu;
+  wd.spin_limit = (uint64_t)o.spin_timeout_us * na->wall_khz / 1000u;
+  fo::Plan p = fo::empty_plan();
+  int bm = 0, tile = 0, own_pos = 0;
+  s = rs_plan(x_shard, w, send_buf, out, recv_buf, P, rank, m, K, N, in_dt, o, wd, false, &p, &bm,
+              &tile, &own_pos);
+  if (s != FO_OK) return s;
+  hipStream_t cs = (hipStream_t)compute_stream;
+  // the counters and the own chunk's words start at zero in every call (a kernel, so that the
+  // call can be captured in a HIP graph)
+  FO_HIP(fo::launch_zero(na->ptr + kNaCounters, kNaErr - kNaCounters, cs));
+  s = launch_with_events(p, in_dt, tile, cs, o);
+  if (s != FO_OK) return s;
+  if (o.order == FO_ORDER_NATURAL && P > 1) return launch_rs_reduce(p, out, m, N, wd, nullptr, cs);
   return FO_OK;
 }
 
@@ -987,26 +1151,46 @@ fo_status fo_check(void* stream) {
   int dev = 0;
   FO_HIP(hipGetDevice(&dev));
   if (dev < 0 || dev >= kMaxDevices) return FO_OK;
-  DevState& st = g_dev[dev];
-  std::lock_guard<std::mutex> lk(st.mu);
-  if (!st.ready) return FO_OK;
+  // the wait records: the library's (fo_ag_gemm, fo_gemm_rs, fo_attn, fo_transfer_ref) and the
+  // scratch array's (fo_gemm_rs_noalloc); each is read, then its "what failed" word cleared
+  uint32_t kinds = 0;
   {
-    std::string e;
-    bool timed_out = false;
-    if (!fo::dma::drain(dev, 30000, &e, &timed_out)) {
-      set_error("%s", e.c_str());
-      return timed_out ? FO_ERR_TIMEOUT : FO_ERR_HIP;
+    DevState& st = g_dev[dev];
+    std::lock_guard<std::mutex> lk(st.mu);
+    if (st.ready) {
+      std::string e;
+      bool timed_out = false;
+      if (!fo::dma::drain(dev, 30000, &e, &timed_out)) {
+        set_error("%s", e.c_str());
+        return timed_out ? FO_ERR_TIMEOUT : FO_ERR_HIP;
+      }
+      uint32_t w = 0;
+      FO_HIP(hipMemcpy(&w, st.err, sizeof w, hipMemcpyDeviceToHost));
+      if (w) {
+        const uint32_t zero = 0;
+        FO_HIP(hipMemcpy(st.err, &zero, sizeof zero, hipMemcpyHostToDevice));
+      }
+      kinds |= w;
     }
   }
-  uint32_t e = 0;
-  FO_HIP(hipMemcpy(&e, st.err, sizeof e, hipMemcpyDeviceToHost));
-  if (e) {
-    const uint32_t zero = 0;
-    FO_HIP(hipMemcpy(st.err, &zero, sizeof zero, hipMemcpyHostToDevice));
-    if (e == 2) {
-      set_error("a DMA transfer reported failure");
-      return FO_ERR_HIP;
+  {
+    NoAllocDev& na = g_na[dev];
+    std::lock_guard<std::mutex> lk(na.mu);
+    if (na.ptr != nullptr) {
+      uint32_t w = 0;
+      FO_HIP(hipMemcpy(&w, na.ptr + kNaErr, sizeof w, hipMemcpyDeviceToHost));
+      if (w) {
+        const uint32_t zero = 0;
+        FO_HIP(hipMemcpy(na.ptr + kNaErr, &zero, sizeof zero, hipMemcpyHostToDevice));
+      }
+      kinds |= w;
     }
+  }
+  if (kinds & 2u) {
+    set_error("a DMA transfer reported failure");
+    return FO_ERR_HIP;
+  }
+  if (kinds) {
     set_error("an in-kernel arrival wait ran past its bound");
     return FO_ERR_TIMEOUT;
   }

@@ -965,7 +965,22 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
   }
 }
 
+// Zeroes `words` 32-bit words with vector stores (a kernel, not hipMemsetAsync, so that a caller
+// may capture it in a HIP graph).
+__global__ __launch_bounds__(256) void zero_kernel(uint32_t* p, int words) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < words; i += gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
 }  // namespace
+
+hipError_t launch_zero(uint32_t* p, int words, hipStream_t s) {
+  if (p == nullptr || words < 0) return hipErrorInvalidValue;
+  if (words == 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)std::min(64, (words + 255) / 256)), dim3(256), 0,
+                     s, p, words);
+  return hipGetLastError();
+}
 
 hipError_t launch_release(int64_t* v, hipStream_t s) {
   hipLaunchKernelGGL(release_kernel, dim3(1), dim3(64), 0, s, v);

@@ -104,6 +104,10 @@ int choose_tile(int P, int64_t m, int64_t K, int64_t N, bool out_f32, int n_cu);
 // anything is launched.
 hipError_t launch_gemm(const Plan& plan, int in_dt, int tile, hipStream_t stream);
 
+// Zeroes `words` 32-bit words at p from a small kernel on `stream` (no hipMemsetAsync, so the
+// work can be captured in a HIP graph).
+hipError_t launch_zero(uint32_t* p, int words, hipStream_t stream);
+
 // Stores 0 into the signal value `v` from a one-thread kernel (stream-ordered), after a
 // system-scope release: every copy that depends on the signal starts after the work enqueued
 // before it on `stream`.

@@ -22,7 +22,8 @@ EPI_NONE, EPI_SWIGLU = 0, 1
 MAX_P = 32
 MAX_GROUPS = 8
 
-EXPORTS = ("fo_opts_init", "fo_ag_gemm", "fo_gemm_rs", "fo_gemm_ref", "fo_swiglu", "fo_attn",
+EXPORTS = ("fo_opts_init", "fo_ag_gemm", "fo_gemm_rs", "fo_gemm_rs_noalloc", "fo_gemm_ref",
+           "fo_swiglu", "fo_attn",
            "fo_attn_ref",
            "fo_transfer_ref", "fo_check", "fo_slice_order", "fo_tile_info", "fo_tile_order",
            "fo_status_str", "fo_last_error", "fo_version")
@@ -63,6 +64,7 @@ def load():
     lib.fo_opts_init.restype = None
     lib.fo_ag_gemm.argtypes = [vp, vp, vp, vp, vp, i32, i32, i64, i64, i64, i32, i32, vp, op]
     lib.fo_gemm_rs.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i64, i64, i64, i32, vp, op]
+    lib.fo_gemm_rs_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i32, i64, i64, i64, i32, vp, op]
     lib.fo_gemm_ref.argtypes = [vp, vp, vp, i64, i64, i64, i32, i32, i32, vp]
     lib.fo_swiglu.argtypes = [vp, vp, i64, i64, vp]
     lib.fo_attn.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32, i32, i32, vp, op]
@@ -79,7 +81,8 @@ def load():
     lib.fo_last_error.argtypes = []
     lib.fo_last_error.restype = ctypes.c_char_p
     lib.fo_version.argtypes = []
-    for f in ("fo_ag_gemm", "fo_gemm_rs", "fo_gemm_ref", "fo_swiglu", "fo_attn", "fo_attn_ref",
+    for f in ("fo_ag_gemm", "fo_gemm_rs", "fo_gemm_rs_noalloc", "fo_gemm_ref", "fo_swiglu",
+              "fo_attn", "fo_attn_ref",
               "fo_transfer_ref", "fo_check",
               "fo_slice_order", "fo_tile_info", "fo_tile_order", "fo_version"):
         getattr(lib, f).restype = ctypes.c_int32
@@ -188,6 +191,23 @@ def gemm_rs(x_shard, w, send_buf, out, peer_partial, recv_buf, P: int, rank: int
     if raw:
         return st
     _raise_on(st, "fo_gemm_rs")
+    return st
+
+
+def gemm_rs_noalloc(x_shard, w, send_buf, out, recv_buf, P: int, rank: int, compute_stream=None,
+                    o: Opts | None = None, raw: bool = False):
+    """Flash-RS with the partials resident in recv_buf, allocating nothing (fo_gemm_rs_noalloc);
+    the tensors as for gemm_rs."""
+    M, K = x_shard.shape
+    N = w.shape[1]
+    m = M // P
+    st = load().fo_gemm_rs_noalloc(_ptr(x_shard), _ptr(w), _ptr(send_buf), _ptr(out),
+                                   _ptr(recv_buf), P, rank, m, K, N, _dt(x_shard),
+                                   _stream(compute_stream),
+                                   ctypes.byref(o) if o is not None else None)
+    if raw:
+        return st
+    _raise_on(st, "fo_gemm_rs_noalloc")
     return st
 
 

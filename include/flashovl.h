@@ -53,6 +53,7 @@ extern "C" {
 #define FO_VERSION 1
 #define FO_MAX_P 32     /* largest tensor-parallel degree (number of slices) */
 #define FO_MAX_GROUPS 8 /* most row groups per slice (fo_opts.row_groups) */
+#define FO_NOALLOC_SCRATCH_BYTES 4096 /* per-device static scratch of fo_gemm_rs_noalloc */
 
 typedef enum fo_status {
   FO_OK = 0,
@@ -190,6 +191,27 @@ fo_status fo_gemm_rs(const void* x_shard, const void* w, float* send_buf, float*
                      const fo_opts* opts);
 
 /*
+ * fo_gemm_rs with every incoming partial already in recv_buf, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. The result is that of fo_gemm_rs with peer_partial = NULL (the same kernels, the
+ * same bits). The tile counters, the own chunk's row-group words and the wait record live in a
+ * static device array of FO_NOALLOC_SCRATCH_BYTES that every device holds until the process
+ * ends, instead of in memory the library allocates; the call allocates nothing and calls no
+ * allocating routine (its first call on a device looks the array up and reads two device
+ * attributes). Arguments as for fo_gemm_rs; opts: order, tile, row_groups, spin_timeout_us and
+ * kernel_events are used, arrival must be DEFAULT or NONE (else FO_ERR_INVALID_ARG). Each call
+ * first clears the counters and words it uses with a small kernel on compute_stream (no
+ * hipMemsetAsync), then launches the GEMM there. All calls on a device share its array: calls
+ * that overlap on one device (on two streams with no ordering between them) race on it and give
+ * unspecified results; order them on one stream or with events. A call needing more scratch
+ * than the array holds returns FO_ERR_UNSUPPORTED (P <= FO_MAX_P always fits). Waits that run
+ * past their bound are reported by fo_check() like those of the other calls.
+ */
+fo_status fo_gemm_rs_noalloc(const void* x_shard, const void* w, float* send_buf, float* out,
+                             float* recv_buf, int32_t P, int32_t rank, int64_t m, int64_t K,
+                             int64_t N, int32_t in_dt, void* compute_stream, const fo_opts* opts);
+
+/*
  * Plain monolithic GEMM C[M, N] = A[M, K] . B[K, N] with the same kernels (no slices, no waits):
  * the "pure GEMM" latency the overlap is measured against, and the unsliced product that the
  * page's exactness claim compares to. tile: a fo_tile value (AUTO = the choice fo_ag_gemm would
@@ -276,8 +298,9 @@ fo_status fo_transfer_ref(int32_t kind, const void* const* src, void* dst, int32
 
 /* Synchronizes `stream` (hipStream_t), waits (on the host, at most 30 s) until every transfer the
    library issued on the current device has landed, and reports what happened since the previous
-   fo_check: FO_ERR_TIMEOUT if an in-kernel wait ran past its bound or a transfer did not land in
-   time, FO_ERR_HIP if a DMA engine reported a failed copy. The record is then cleared. */
+   fo_check in any call on the device (fo_gemm_rs_noalloc's included): FO_ERR_TIMEOUT if an
+   in-kernel wait ran past its bound or a transfer did not land in time, FO_ERR_HIP if a DMA
+   engine reported a failed copy. The record is then cleared. */
 fo_status fo_check(void* stream);
 
 /* Host-side slice scheduler. kind 0 = AG, 1 = RS; order a fo_order. Writes P slice/chunk ids in

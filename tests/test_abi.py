@@ -294,3 +294,24 @@ def test_attn_empty_is_a_no_op(lib):
     assert _attn(lib, m=0) == fo.FO_OK
     assert lib.fo_attn_ref(A, C, 0, 8, 2, 128, 1, None) == fo.FO_OK
     assert lib.fo_attn_ref(A, A + 16, 4, 8, 2, 128, 1, None) == fo.FO_ERR_INVALID_ARG
+
+
+def test_rs_noalloc_rejects(lib):
+    """fo_gemm_rs_noalloc checks its arguments like fo_gemm_rs, before touching the device, and
+    takes resident partials only."""
+    def call(**kw):
+        a = dict(x=A, w=B, send=C, out=D, recv=0x50000000, P=4, rank=1, m=64, K=256, N=512,
+                 in_dt=fo.BF16, opts=None)
+        a.update(kw)
+        return lib.fo_gemm_rs_noalloc(a["x"], a["w"], a["send"], a["out"], a["recv"], a["P"],
+                                      a["rank"], a["m"], a["K"], a["N"], a["in_dt"], None,
+                                      a["opts"])
+    for kw in (dict(P=0), dict(P=33), dict(rank=4), dict(N=12), dict(x=None), dict(recv=None),
+               dict(out=A), dict(send=D - 4), dict(x=A + 4)):
+        assert call(**kw) == fo.FO_ERR_INVALID_ARG, kw
+    for arrival in (fo.ARR_EAGER, fo.ARR_LOCKSTEP):
+        o = fo.opts(arrival=arrival)
+        assert call(opts=ctypes.byref(o)) == fo.FO_ERR_INVALID_ARG
+    o = fo.opts(epilogue=fo.EPI_SWIGLU)
+    assert call(opts=ctypes.byref(o)) == fo.FO_ERR_INVALID_ARG
+    assert call(m=0) == fo.FO_OK and call(N=0) == fo.FO_OK  # nothing to do, nothing touched
