@@ -179,6 +179,9 @@ fo_status check_opts(const fo_opts* o, fo_opts* out) {
     return invalid("opts.epilogue %d is not a fo_epilogue", o->epilogue);
   if (o->k_chunks < 0 || o->k_chunks > fo::kMaxGroups)
     return invalid("opts.k_chunks %d outside [0, %d]", o->k_chunks, fo::kMaxGroups);
+  if (o->engines_per_link < 0 || o->engines_per_link > 3)
+    return invalid("opts.engines_per_link %d outside [0, 3]", o->engines_per_link);
+  if (o->reserved != 0) return invalid("opts.reserved must be 0");
   *out = *o;
   if (out->spin_timeout_us == 0) out->spin_timeout_us = kDefaultTimeoutUs;
   return FO_OK;
@@ -276,6 +279,20 @@ int arrival_sequence(int kind, int order, int P, int rank, int* seq) {
   }
   return n;
 }
+
+// The engines of one link (opts.engines_per_link): 1 one engine; 2 an engine pair taking the
+// link's copies in turn; 3 the same, the pair's second engine starting once the link's first
+// copy has landed.
+void set_engines(const fo_opts& o, int dflt, fo::dma::Call* call) {
+  const int e = o.engines_per_link ? o.engines_per_link : dflt;
+  call->pairs = e >= 2;
+  call->first_alone = e == 3;
+}
+
+// Default engines per link: Flash-RS moves the most bytes per link and waits on their total
+// (pairs: its 70B call 416 -> 352 us); Flash-AG and the attention wait first on the latency of
+// a slice's first transfer, which a busy partner engine would halve the bandwidth of.
+constexpr int kEnginesAG = 1, kEnginesRS = 2, kEnginesAttn = 1;
 
 // Every call on a device is ordered after the previous one (they share the device's signals,
 // counters and words): a call on another stream first waits for the previous call's event; on
@@ -680,6 +697,7 @@ fo_status fo_ag_gemm(const void* x_local, const void* const* x_peer, void* x_rec
                                           (uint64_t)(K / chunks / 32)) : 0u;
   fo::dma::Call call{};
   if (arrivals) FO_DMA(fo::dma::begin(st->dev, P, p.grid.groups * chunks, &call, &e_));
+  set_engines(o, kEnginesAG, &call);
   int32_t order[FO_MAX_P];
   fo::slice_order(0, o.order, P, rank, order);
   for (int pos = 0; pos < P; ++pos) {
@@ -778,6 +796,7 @@ fo_status fo_gemm_rs(const void* x_shard, const void* w, float* send_buf, float*
   const bool natural = o.order == FO_ORDER_NATURAL;
   fo::dma::Call call{};
   if (arrivals) FO_DMA(fo::dma::begin(st->dev, P, p.grid.groups, &call, &e_));
+  set_engines(o, kEnginesRS, &call);
   p.comp_tab = call.comp_tab;
   p.rel_tab = lockstep ? call.rel_tab : nullptr;
   if (arrivals) p.start = call.start;
@@ -963,8 +982,9 @@ static fo_status launch_attn_events(const fo::AttnPlan& p, hipStream_t cs, const
 }
 
 fo_status fo_attn(const void* qkv_local, const void* const* qkv_peer, void* qkv_recv, void* out,
-                  int32_t P, int32_t rank, int64_t m, int32_t hq, int32_t hkv, int32_t head_dim,
-                  int32_t causal, void* compute_stream, const fo_opts* opts) {
+                  void* const* out_peer, int32_t P, int32_t rank, int64_t m, int32_t hq,
+                  int32_t hkv, int32_t head_dim, int32_t causal, void* compute_stream,
+                  const fo_opts* opts) {
   fo_opts o;
   fo_status s = check_opts(opts, &o);
   if (s != FO_OK) return s;
@@ -975,14 +995,18 @@ fo_status fo_attn(const void* qkv_local, const void* const* qkv_peer, void* qkv_
   if (o.epilogue != FO_EPI_NONE) return invalid("opts.epilogue applies to fo_ag_gemm only");
   if (o.k_chunks > 1) return invalid("opts.k_chunks applies to fo_ag_gemm only");
   const bool arrivals = qkv_peer != nullptr && o.arrival != FO_ARR_NONE && P > 1;
+  const bool sends = out_peer != nullptr && P > 1;
+  if (sends && 2 * P > FO_MAX_P)
+    return unsupported("the return exchange needs P <= %d (P = %d)", FO_MAX_P / 2, P);
   const size_t W = (size_t)(hq + 2 * hkv) * 256, slice_b = (size_t)m * W;
+  const size_t ow = (size_t)hq * 256, oslice_b = (size_t)m * ow;
   if (!qkv_local || !out || (P > 1 && !qkv_recv)) return invalid("NULL buffer");
   if (!aligned(qkv_local, 16) || !aligned(out, 16) || (qkv_recv && !aligned(qkv_recv, 16)))
     return invalid("misaligned buffer (16-byte alignment)");
-  const Range r_out = rng(out, (size_t)P * m * hq * 256);
+  const Range r_out = rng(out, (size_t)P * oslice_b);
   const Range r_recv = rng(qkv_recv, qkv_recv ? (size_t)P * slice_b : 0);
-  if (overlap(r_out, rng(qkv_local, slice_b)) || overlap(r_out, r_recv))
-    return invalid("out overlaps an input");
+  const Range r_local = rng(qkv_local, slice_b);
+  if (overlap(r_out, r_local) || overlap(r_out, r_recv)) return invalid("out overlaps an input");
   if (arrivals) {
     for (int q = 0; q < P; ++q) {
       if (q == rank) continue;
@@ -990,6 +1014,19 @@ fo_status fo_attn(const void* qkv_local, const void* const* qkv_peer, void* qkv_
       if (!aligned(qkv_peer[q], 16)) return invalid("qkv_peer[%d] misaligned", q);
       const Range rp = rng(qkv_peer[q], slice_b);
       if (overlap(rp, r_recv) || overlap(rp, r_out)) return invalid("qkv_peer[%d] overlaps qkv_recv or out", q);
+    }
+  }
+  if (sends) {
+    for (int q = 0; q < P; ++q) {
+      if (q == rank) continue;
+      if (!out_peer[q]) return invalid("out_peer[%d] is NULL", q);
+      if (!aligned(out_peer[q], 16)) return invalid("out_peer[%d] misaligned", q);
+      const Range rp = rng(out_peer[q], oslice_b);
+      if (overlap(rp, r_out) || overlap(rp, r_recv) || overlap(rp, r_local))
+        return invalid("out_peer[%d] overlaps out or an input", q);
+      for (int q2 = 0; q2 < q; ++q2)
+        if (q2 != rank && overlap(rp, rng(out_peer[q2], oslice_b)))
+          return invalid("out_peer[%d] overlaps out_peer[%d]", q, q2);
     }
   }
   if (m == 0) return FO_OK;
@@ -1007,16 +1044,30 @@ fo_status fo_attn(const void* qkv_local, const void* const* qkv_peer, void* qkv_
   p.group_rows = gr;
   p.groups = (int32_t)((m + gr - 1) / gr);
   fo::dma::Call call{};
-  if (arrivals) FO_DMA(fo::dma::begin(st->dev, P, p.groups, &call, &e_));
+  if (arrivals || sends)
+    FO_DMA(fo::dma::begin(st->dev, sends ? 2 * P : P, p.groups, &call, &e_));
+  set_engines(o, kEnginesAttn, &call);
   int32_t order[FO_MAX_P];
   fo::slice_order(0, o.order, P, rank, order);
   for (int i = 0; i < P; ++i) {
     p.order[i] = order[i];
     p.slice[i] = i == rank ? qkv_local : (const uint8_t*)qkv_recv + (size_t)i * slice_b;
     p.gated[i] = (arrivals && i != rank) ? 1 : 0;
+    p.send[i] = (sends && i != rank) ? 1 : 0;
   }
+  // dispatch: the arrival order; with the return exchange in the FLASH order the own slice goes
+  // last (its rows stay on the rank, so the slice computed last has nothing left to send), the
+  // Flash-RS order of the page's rank-adaptive schedule applied to the outgoing exchange; the
+  // data-slicing (NATURAL) order keeps index order
+  const bool own_last = sends && o.order == FO_ORDER_FLASH;
+  int n_disp = 0;
+  for (int i = 0; i < P; ++i)
+    if (!(own_last && order[i] == rank)) p.dispatch[n_disp++] = order[i];
+  if (own_last) p.dispatch[n_disp++] = rank;
   p.out = out;
   p.comp_tab = call.comp_tab;
+  p.rel_tab = sends ? call.rel_tab : nullptr;
+  p.done = st->done;
   p.lead = st->arr_lead;
   p.ready = st->arr_ready;
   p.gen = ++st->gen;
@@ -1034,19 +1085,26 @@ fo_status fo_attn(const void* qkv_local, const void* const* qkv_peer, void* qkv_
   p.acq = (aligned(qkv_recv, 128) && row_bytes % 128 == 0) ? 0 : 1;
 
   hipStream_t cs = (hipStream_t)compute_stream;
-  if (arrivals) p.start = call.start;
+  if (arrivals || sends) p.start = call.start;
   s = order_after_last(st, cs);
   if (s != FO_OK) return s;
   s = launch_attn_events(p, cs, o);
   if (s != FO_OK) return s;
+  int seq[FO_MAX_P];
+  const int n = arrival_sequence(0, o.order, P, rank, seq);
+  if (sends) {
+    // the call ends when its outgoing rows have landed: a one-workgroup kernel after the
+    // attention waits for the completion of every send
+    int out_ids[FO_MAX_P];
+    for (int t = 0; t < n; ++t) out_ids[t] = P + seq[t];
+    FO_HIP(fo::launch_wait(call.comp_tab, out_ids, n, p.groups, p.spin_limit, st->err, p.gen, cs));
+  }
   hipEvent_t slot_ev = nullptr;
-  if (arrivals) FO_DMA(fo::dma::end(st->dev, call, cs, &e_, &slot_ev));
+  if (arrivals || sends) FO_DMA(fo::dma::end(st->dev, call, cs, &e_, &slot_ev));
   s = mark_last(st, cs, slot_ev);
   if (s != FO_OK) return s;
+  const int L = links_for(o, P);
   if (arrivals) {
-    int seq[FO_MAX_P];
-    const int n = arrival_sequence(0, o.order, P, rank, seq);
-    const int L = links_for(o, P);
     for (int g = 0; g < p.groups; ++g) {
       const int64_t r0 = g * gr, r1 = std::min<int64_t>(m, r0 + gr);
       for (int t = 0; t < n; ++t) {
@@ -1054,6 +1112,22 @@ fo_status fo_attn(const void* qkv_local, const void* const* qkv_peer, void* qkv_
         FO_DMA(fo::dma::copy(st->dev, call, t % L, sl, g, -1,
                              (uint8_t*)qkv_recv + (size_t)sl * slice_b + (size_t)r0 * W,
                              (const uint8_t*)qkv_peer[sl] + (size_t)r0 * W, (size_t)(r1 - r0) * W, &e_));
+      }
+    }
+  }
+  if (sends) {
+    // slice s's output rows to rank s, group by group once released; the link to peer s is the
+    // one its slice arrived on, in the other direction (the partner engine of that link's pair:
+    // the two directions of a link are separate queues)
+    const int half = std::max(1, fo::dma::n_engines(st->dev) / 2);
+    for (int g = 0; g < p.groups; ++g) {
+      const int64_t r0 = g * gr, r1 = std::min<int64_t>(m, r0 + gr);
+      for (int t = 0; t < n; ++t) {
+        const int sl = seq[t];
+        FO_DMA(fo::dma::copy(st->dev, call, (t % L) + half, P + sl, g, sl,
+                             (uint8_t*)out_peer[sl] + (size_t)r0 * ow,
+                             (const uint8_t*)out + ((size_t)sl * m + (size_t)r0) * ow,
+                             (size_t)(r1 - r0) * ow, &e_));
       }
     }
   }
@@ -1077,6 +1151,7 @@ fo_status fo_attn_ref(const void* qkv, void* out, int64_t S, int32_t hq, int32_t
   p.group_rows = (S + 127) / 128 * 128;
   p.groups = 1;
   p.order[0] = 0;
+  p.dispatch[0] = 0;
   p.slice[0] = qkv;
   p.gated[0] = 0;
   p.out = out;
@@ -1119,6 +1194,7 @@ fo_status fo_transfer_ref(int32_t kind, const void* const* src, void* dst, int32
   const int G = std::max(1, o.row_groups);
   fo::dma::Call call{};
   FO_DMA(fo::dma::begin(st->dev, P, G, &call, &e_));
+  set_engines(o, kind == 1 ? kEnginesRS : kEnginesAG, &call);
   int seq[FO_MAX_P];
   const int n = arrival_sequence(kind, o.order, P, rank, seq);
   hipStream_t ks = (hipStream_t)stream;

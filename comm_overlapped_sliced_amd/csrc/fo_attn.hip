@@ -149,7 +149,7 @@ __device__ __forceinline__ void attn_tile(const AttnPlan& p, const int u, uint8_
     // are dispatched first
     qt = uni(qtiles - 1 - rr / hq);
     h = uni(rr % hq);
-    s = uni(p.order[pos]);
+    s = uni(p.dispatch[pos]);
   }
   const int kvh = h / (hq / p.hkv);
   const int W = (hq + 2 * p.hkv) * kRowB;  // bytes of one token's Q, K and V rows
@@ -346,6 +346,25 @@ __device__ __forceinline__ void attn_tile(const AttnPlan& p, const int u, uint8_
     const uint32_t off = (uint32_t)(q0 + 32 * wave + row) * (uint32_t)ow + h * kRowB + ch * 16;
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, x), ores, off, 0, 0);
   }
+  if (p.rel_tab != nullptr && p.send[s]) {
+    // the return exchange: every wave's stores of this item are complete before the barrier;
+    // the last item of (slice, row group) then releases the copy of its rows to rank s
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();
+    if (tid == 0) {
+      const int g = q0 / gr;
+      const int r1 = (g + 1) * gr < m ? (g + 1) * gr : m;
+      const uint32_t items = (uint32_t)(((r1 - g * gr + kAQ - 1) / kAQ) * hq);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
+      uint32_t* cnt = p.done + s * kMaxGroups + g;
+      const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      if (old + 1 == items) {
+        __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(p.rel_tab[s * kMaxGroups + g], (int64_t)0, __ATOMIC_RELEASE,
+                           __HIP_MEMORY_SCOPE_SYSTEM);
+      }
+    }
+  }
   lds_barrier();  // the next tile's loads overwrite the staging rows
 }
 
@@ -369,6 +388,12 @@ bool attn_plan_ok(const AttnPlan& p) {
   const int64_t W = (int64_t)(p.hq + 2 * p.hkv) * kRowB;
   if ((p.m + kAQ) * W >= ((int64_t)1 << 31) || (p.m + kAQ) * p.hq * kRowB >= ((int64_t)1 << 31))
     return false;
+  if (p.rel_tab != nullptr && p.done == nullptr) return false;
+  bool seen[FO_MAX_P] = {};
+  for (int i = 0; i < p.P; ++i) {
+    if (p.dispatch[i] < 0 || p.dispatch[i] >= p.P || seen[p.dispatch[i]]) return false;
+    seen[p.dispatch[i]] = true;
+  }
   for (int i = 0; i < p.P; ++i) {
     if (p.order[i] < 0 || p.order[i] >= p.P || p.slice[i] == nullptr) return false;
     if (p.gated[i] && (p.comp_tab == nullptr || p.lead == nullptr || p.ready == nullptr || p.gen == 0))

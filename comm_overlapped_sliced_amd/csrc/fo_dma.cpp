@@ -111,6 +111,8 @@ struct Slot {
   bool pending = false;     // used by a call that may not be complete yet
   std::bitset<kSignals> issued;  // completion signals a copy will decrement
   uint32_t started = 0;          // engines that already hold a copy of the call waiting on start
+  uint8_t turn[32] = {};         // per engine pair: copies the call has issued on it
+  int16_t first[32] = {};        // per engine pair: completion signal of the call's first copy
 };
 
 struct Dev {
@@ -118,6 +120,7 @@ struct Dev {
   hsa_agent_t agent{};
   int n_eng = 0;
   uint32_t eng[32] = {};
+  int n_pairs = 0;  // eng[i] and eng[i + n_pairs] form a pair (engines 2k and 2k+1), i < n_pairs
   Slot slot[kSlots];
   int next = 0;
 };
@@ -261,6 +264,12 @@ bool init(int dev, void* scratch, std::string* err) {
   std::stable_partition(d.eng, d.eng + d.n_eng, [](uint32_t bit) {
     return (__builtin_ctz(bit) & 1) == 0;
   });
+  // engine pairs for links of two engines: the even engine i and its odd partner i + n_pairs,
+  // when every even engine has its partner in place
+  const int half = d.n_eng / 2;
+  bool paired = d.n_eng % 2 == 0 && half > 0;
+  for (int i = 0; paired && i < half; ++i) paired = d.eng[i + half] == (d.eng[i] << 1);
+  d.n_pairs = paired ? half : 0;
   w.issued.reset();
   d.ready = true;
   return true;
@@ -296,6 +305,7 @@ bool begin(int dev, int P, int groups, Call* call, std::string* err) {
     }
   sl.issued.reset();
   sl.started = 0;
+  memset(sl.turn, 0, sizeof sl.turn);
   sl.pending = true;
   d.next = (k + 1) % kSlots;
   call->slot = k;
@@ -317,9 +327,19 @@ bool copy(int dev, const Call& call, int link, int slice, int group, int rel_pos
   // An engine runs its copies one after the other in issue order, so only the call's first copy
   // on an engine waits for the start signal; a copy gated on a release signal needs no start
   // signal at all (the kernel stores the release after it has started).
-  const int ei = (link % d.n_eng + d.n_eng) % d.n_eng;
+  int ei = (link % d.n_eng + d.n_eng) % d.n_eng;
+  int after = -1;  // completion signal the copy waits for (the pair's first copy, see below)
+  if (call.pairs && d.n_pairs > 0) {
+    const int pr = (link % d.n_pairs + d.n_pairs) % d.n_pairs;
+    const int k = sl.turn[pr]++;
+    ei = pr + (k & 1) * d.n_pairs;
+    if (k == 0) sl.first[pr] = (int16_t)ci;
+    // first alone: the partner engine's first copy starts once the link's first copy has
+    // landed, so that copy has the pair's whole bandwidth
+    if (call.first_alone && k == 1) after = sl.first[pr];
+  }
   const uint32_t eng = d.eng[ei];
-  hsa_signal_t deps[1];
+  hsa_signal_t deps[2];
   uint32_t n = 0;
   if (rel_pos >= 0) {
     deps[n++] = sl.rel[rel_pos * kMaxGroups + group];
@@ -327,6 +347,7 @@ bool copy(int dev, const Call& call, int link, int slice, int group, int rel_pos
     deps[n++] = sl.start;
     sl.started |= 1u << ei;
   }
+  if (after >= 0) deps[n++] = sl.comp[after];
   // (the runtime rejects a dependency array with a count of zero: pass none then)
   const hsa_status_t s = g_hsa.copy(dst, d.agent, src, d.agent, bytes, n, n ? deps : nullptr,
                                     sl.comp[ci], (hsa_amd_sdma_engine_id_t)eng, true);

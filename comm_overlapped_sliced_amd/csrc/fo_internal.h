@@ -184,6 +184,16 @@ struct AttnPlan {
   int32_t pair_half;
   float scale_log2;                  // log2(e) / sqrt(128)
   int32_t acq;                       // 1: acquire after each arrival wait (see Plan::acq)
+  // Dispatch order of the query slices (position -> slice id) when pair_half is 0; the key walk
+  // follows `order`. With the return exchange the own slice is dispatched last.
+  int32_t dispatch[FO_MAX_P];
+  // The return exchange (the second All-to-All of Ulysses parallelism): when every work item of
+  // (slice s, row group g) with send[s] set has stored its output rows, the last one to finish
+  // stores 0 into the release signal rel_tab[s][g]; the copy engine that sends those rows to
+  // rank s waits for it. rel_tab null: no return exchange.
+  int64_t* const* rel_tab;
+  uint32_t* done;                    // finished work items [slice][group] (zero between calls)
+  int32_t send[FO_MAX_P];            // by slice id: 1 = its output rows are sent back
 };
 bool attn_plan_ok(const AttnPlan& p);
 hipError_t launch_attn(const AttnPlan& p, hipStream_t stream);
@@ -208,6 +218,10 @@ struct Call {
   int64_t* start;
   const int64_t* const* comp_tab;
   int64_t* const* rel_tab;
+  // a link is an engine pair whose two engines take the link's copies in turn (else one engine);
+  // with first_alone the second engine's first copy waits until the link's first copy has landed
+  bool pairs = false;
+  bool first_alone = false;
 };
 
 // Per-device setup (called once, under the device lock, with the device current): finds the
@@ -221,8 +235,9 @@ int n_engines(int dev);
 // used it last is complete: its event done and its copies landed), re-arms the start signal and
 // the release and completion signals of P slices x `groups` groups to 1, and returns them.
 bool begin(int dev, int P, int groups, Call* call, std::string* err);
-// Copy `bytes` from src to dst on link `link` (engine link mod n_engines), starting once the
-// call's start signal and, when rel_pos >= 0, the release signal of (rel_pos, group) are zero.
+// Copy `bytes` from src to dst on link `link` (engine link mod n_engines, or with call.pairs the
+// next engine in turn of pair link mod n_pairs), starting once the call's start signal and,
+// when rel_pos >= 0, the release signal of (rel_pos, group) are zero.
 // The completion signal of (slice, group) is decremented when the copy has landed.
 bool copy(int dev, const Call& call, int link, int slice, int group, int rel_pos, void* dst,
           const void* src, size_t bytes, std::string* err);

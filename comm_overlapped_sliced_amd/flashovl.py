@@ -40,7 +40,8 @@ class Opts(ctypes.Structure):
                 ("tile", ctypes.c_int32), ("spin_timeout_us", ctypes.c_uint32),
                 ("links", ctypes.c_int32), ("row_groups", ctypes.c_int32),
                 ("kernel_events", ctypes.c_void_p * 2), ("epilogue", ctypes.c_int32),
-                ("k_chunks", ctypes.c_int32)]
+                ("k_chunks", ctypes.c_int32), ("engines_per_link", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 _lib = None
@@ -67,7 +68,7 @@ def load():
     lib.fo_gemm_rs_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i32, i64, i64, i64, i32, vp, op]
     lib.fo_gemm_ref.argtypes = [vp, vp, vp, i64, i64, i64, i32, i32, i32, vp]
     lib.fo_swiglu.argtypes = [vp, vp, i64, i64, vp]
-    lib.fo_attn.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32, i32, i32, vp, op]
+    lib.fo_attn.argtypes = [vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, i32, i32, vp, op]
     lib.fo_attn_ref.argtypes = [vp, vp, i64, i32, i32, i32, i32, vp]
     lib.fo_transfer_ref.argtypes = [i32, vp, vp, i32, i32, i64, vp, op]
     lib.fo_check.argtypes = [vp]
@@ -102,12 +103,24 @@ def _raise_on(status: int, where: str) -> None:
         raise FoError(status, where, load().fo_last_error().decode())
 
 
+_default_engines_per_link = 0
+
+
+def set_default_engines_per_link(n: int) -> None:
+    """The engines_per_link that opts() fills in when none is given (0: the library's)."""
+    global _default_engines_per_link
+    _default_engines_per_link = int(n)
+
+
 def opts(order=ORDER_FLASH, arrival=ARR_DEFAULT, tile=TILE_AUTO, spin_timeout_us=0, links=0,
-         row_groups=0, kernel_events=None, epilogue=EPI_NONE, k_chunks=0) -> Opts:
+         row_groups=0, kernel_events=None, epilogue=EPI_NONE, k_chunks=0,
+         engines_per_link=None) -> Opts:
     o = Opts()
     load().fo_opts_init(ctypes.byref(o))
     o.order, o.arrival, o.tile, o.links = order, arrival, tile, links
     o.row_groups, o.epilogue, o.k_chunks = row_groups, epilogue, k_chunks
+    o.engines_per_link = (_default_engines_per_link if engines_per_link is None
+                          else engines_per_link)
     if spin_timeout_us:
         o.spin_timeout_us = spin_timeout_us
     if kernel_events is not None:
@@ -304,15 +317,21 @@ def runtimes_mapped(name: str = "libamdhip64") -> set:
 
 
 def attn(qkv_local, qkv_peer, qkv_recv, out, P: int, rank: int, hq: int, hkv: int,
-         causal: bool = True, compute_stream=None, o: Opts | None = None, raw: bool = False):
-    """Query-split attention after a Flash All-to-All (fo_attn). qkv_local [m, (hq+2hkv)*128]
-    bf16, qkv_peer list of P tensors (or None), qkv_recv [P*m, same], out [P*m, hq*128] bf16."""
+         causal: bool = True, compute_stream=None, o: Opts | None = None, raw: bool = False,
+         out_peer=None):
+    """Query-split attention between the two Flash All-to-Alls (fo_attn). qkv_local
+    [m, (hq+2hkv)*128] bf16, qkv_peer list of P tensors (or None), qkv_recv [P*m, same], out
+    [P*m, hq*128] bf16, out_peer list of P [m, hq*128] bf16 tensors receiving each slice's rows
+    (entry [rank] unused; None: no return exchange)."""
     m, row = qkv_local.shape
     d = row // (hq + 2 * hkv)
     peers = None if qkv_peer is None else _ptr_array(qkv_peer)
+    outs = None if out_peer is None else _ptr_array(out_peer)
     st = load().fo_attn(_ptr(qkv_local), ctypes.cast(peers, ctypes.c_void_p) if peers else None,
-                        _ptr(qkv_recv), _ptr(out), P, rank, m, hq, hkv, d, int(causal),
-                        _stream(compute_stream), ctypes.byref(o) if o is not None else None)
+                        _ptr(qkv_recv), _ptr(out),
+                        ctypes.cast(outs, ctypes.c_void_p) if outs else None, P, rank, m, hq, hkv,
+                        d, int(causal), _stream(compute_stream),
+                        ctypes.byref(o) if o is not None else None)
     if raw:
         return st
     _raise_on(st, "fo_attn")

@@ -136,6 +136,16 @@ typedef struct fo_opts {
                                block j only before they read its columns. Needs bf16 operands,
                                K a multiple of 256*c and m*K*2 <= 2^30 bytes (else
                                FO_ERR_UNSUPPORTED); row groups are capped at FO_MAX_GROUPS / c */
+  int32_t engines_per_link; /* DMA engines that carry one emulated link: 1 = one engine, the
+                               link's transfers one after the other; 2 = the two engines of a
+                               pair (which share one bandwidth) taking the link's transfers in
+                               turn, so that one copy's start-up overlaps the other's data (a
+                               link's transfers may then land out of issue order; every wait is
+                               per transfer, so results do not change); 3 = as 2, the pair's
+                               second engine starting once the link's first transfer has landed
+                               (that one has the whole bandwidth); 0 = the default: 2 for
+                               fo_gemm_rs and fo_transfer_ref kind 1, else 1 */
+  int32_t reserved;         /* must be 0 */
 } fo_opts;
 
 /* Fills *o with the defaults (FLASH order, DEFAULT arrival, AUTO tile, 2 s bound, one link per
@@ -236,39 +246,52 @@ fo_status fo_gemm_ref(const void* a, const void* b, void* c, int64_t M, int64_t 
 fo_status fo_swiglu(const void* y, void* h, int64_t rows, int64_t inter, void* stream);
 
 /*
- * Query-split attention after a Flash All-to-All: one rank's share of Ulysses (sequence)
- * parallelism. The FlashOverlap page (gist.science paper 2604.24013, technical summary section
- * 2 "Methodology") applies its sliced overlap to attention by query slices and to the
- * All-to-All of Ulysses parallelism. After the All-to-All, rank `rank` holds, for its own hq
- * query heads and hkv key/value heads, the rows of every peer's sequence chunk: slice s is the
- * m tokens at sequence positions s*m .. s*m+m-1. Slice `rank` is local; slice s != rank is
- * copied from qkv_peer[s] into qkv_recv (emulated arrival, one copy per slice, in the Flash-AG
- * arrival order). The attention runs by query slices: the work for the queries of slice s
- * starts once slice s has landed and reads key slices in arrival order as each one lands (with
- * causal masking only slices j <= s). Per head h (key head h / (hq / hkv)) and query position i:
+ * Query-split attention between the two All-to-Alls of Ulysses (sequence) parallelism, both
+ * decomposed into point-to-point transfers: one rank's share. The FlashOverlap page (gist.science
+ * paper 2604.24013, technical summary section 2 "Methodology") applies its sliced overlap to
+ * attention by query slices and to the All-to-All of Ulysses parallelism. After the first
+ * All-to-All, rank `rank` holds, for its own hq query heads and hkv key/value heads, the rows of
+ * every peer's sequence chunk: slice s is the m tokens at sequence positions s*m .. s*m+m-1.
+ * Slice `rank` is local; slice s != rank is copied from qkv_peer[s] into qkv_recv (emulated
+ * arrival, in the Flash-AG arrival order). The attention runs by query slices: the work for the
+ * queries of slice s starts once slice s has landed and reads key slices in arrival order as
+ * each one lands (with causal masking only slices j <= s). Per head h (key head h / (hq / hkv))
+ * and query position i:
  *     out[i, h] = sum_j softmax_j(q_i . k_j / sqrt(head_dim)) v_j, over key positions j (j <= i
  *     when causal).
+ * The second All-to-All returns each query slice's output rows (this rank's heads) to the rank
+ * that owns those positions: with out_peer given, the rows of slice s != rank are copied to
+ * out_peer[s] as soon as every work item of a row group of slice s has stored them, while the
+ * later slices compute; in the FLASH order the own slice, whose rows stay, is dispatched last
+ * (the Flash-RS order applied to the outgoing exchange). The call ends when every sent row has
+ * landed.
  *   qkv_local  device [m, (hq + 2*hkv) * head_dim] bf16: one row per token, [hq query heads |
  *              hkv key heads | hkv value heads], each head_dim values.
  *   qkv_peer   host array of P device pointers (entry [rank] ignored), each [m, row] like
  *              qkv_local; NULL = the slices are already in qkv_recv (no arrivals).
  *   qkv_recv   device [P*m, row] bf16; slice s at rows s*m (the rows of slice `rank` unused).
  *   out        device [P*m, hq * head_dim] bf16: row i is query position i, heads side by side.
+ *   out_peer   host array of P device pointers (entry [rank] ignored), each [m, hq * head_dim]
+ *              bf16, not overlapping out, the inputs or one another: out_peer[s] stands for
+ *              rank s's receive buffer and gets out's rows s*m .. s*m+m-1. NULL = no return
+ *              exchange. Needs 2*P <= FO_MAX_P (else FO_ERR_UNSUPPORTED).
  * Computed in fp32 (bf16 MFMA products, fp32 sums, fp32 softmax in base 2); the probabilities
  * enter the value product as bf16; one round to nearest even of the output.
  * head_dim must be 128 (else FO_ERR_UNSUPPORTED); hq a multiple of hkv; causal 0 or 1; every
  * pointer 16-byte aligned; out must not overlap an input (else FO_ERR_INVALID_ARG, nothing
  * enqueued). opts: order (FLASH: local slice first, then rank-1, rank-2, ...; NATURAL: index
- * order), arrival (NONE, EAGER or DEFAULT = EAGER), links, row_groups (each slice sent in that
- * many row groups, group by group, of a whole number of 128-row query tiles; 0 = whole
- * slices), spin_timeout_us and kernel_events are used: a query tile waits for the group holding
- * its rows, and the walk over a key slice for the groups holding the keys it reads. tile must be AUTO,
- * epilogue NONE. Enqueued on compute_stream
- * like fo_ag_gemm, with the same ordering, timeout and error reporting through fo_check.
+ * order, own slice included, for the data-slicing baseline), arrival (NONE, EAGER or DEFAULT =
+ * EAGER), links, row_groups (each slice sent in that many row groups, group by group, of a
+ * whole number of 128-row query tiles, both ways; 0 = whole slices), spin_timeout_us and
+ * kernel_events are used: a query tile waits for the group holding its rows, and the walk over a
+ * key slice for the groups holding the keys it reads. tile must be AUTO, epilogue NONE.
+ * Enqueued on compute_stream like fo_ag_gemm, with the same ordering, timeout and error
+ * reporting through fo_check.
  */
 fo_status fo_attn(const void* qkv_local, const void* const* qkv_peer, void* qkv_recv, void* out,
-                  int32_t P, int32_t rank, int64_t m, int32_t hq, int32_t hkv, int32_t head_dim,
-                  int32_t causal, void* compute_stream, const fo_opts* opts);
+                  void* const* out_peer, int32_t P, int32_t rank, int64_t m, int32_t hq,
+                  int32_t hkv, int32_t head_dim, int32_t causal, void* compute_stream,
+                  const fo_opts* opts);
 
 /*
  * The same attention with every slice resident (one sequence of S tokens, no transfers): the

@@ -49,10 +49,11 @@ def test_opts_defaults():
     assert o.spin_timeout_us == 2_000_000
     assert list(o.kernel_events) == [None, None]
     assert o.row_groups == 0 and o.epilogue == fo.EPI_NONE and o.k_chunks == 0
-    assert ctypes.sizeof(fo.Opts) == 48
-    # the C layout: k_chunks is the last 32-bit field, after the events and the epilogue
+    assert ctypes.sizeof(fo.Opts) == 56
+    # the C layout: after the events, the epilogue, k_chunks, engines_per_link and a reserved word
     assert fo.Opts.kernel_events.offset == 24 and fo.Opts.epilogue.offset == 40
-    assert fo.Opts.k_chunks.offset == 44
+    assert fo.Opts.k_chunks.offset == 44 and fo.Opts.engines_per_link.offset == 48
+    assert fo.Opts.reserved.offset == 52 and o.engines_per_link == 0 and o.reserved == 0
     assert fo.opts(k_chunks=4).k_chunks == 4
 
 
@@ -134,6 +135,15 @@ def _ag(lib, **kw):
 def test_ag_rejects(lib, kw):
     assert _ag(lib, **kw) == fo.FO_ERR_INVALID_ARG
     assert lib.fo_last_error().decode() != ""
+
+
+def test_bad_engines_per_link_and_reserved_rejected(lib):
+    for kw in (dict(engines_per_link=4), dict(engines_per_link=-1), dict(reserved=1)):
+        o = fo.opts()
+        for k, v in kw.items():
+            setattr(o, k, v)
+        assert _rs(lib, opts=ctypes.byref(o)) == fo.FO_ERR_INVALID_ARG, kw
+        assert _attn(lib, opts=ctypes.byref(o)) == fo.FO_ERR_INVALID_ARG, kw
 
 
 def test_ag_rejects_bad_opts(lib):
@@ -251,16 +261,19 @@ def test_swiglu_rejects(lib):
 
 
 def _attn(lib, **kw):
-    args = dict(local=A, peers=None, recv=B, out=C, P=4, rank=0, m=64, hq=8, hkv=2, d=128,
-                causal=1, opts=None)
+    args = dict(local=A, peers=None, recv=B, out=C, out_peer=None, P=4, rank=0, m=64, hq=8,
+                hkv=2, d=128, causal=1, opts=None)
     args.update(kw)
-    peers = args["peers"]
-    if peers is not None:
-        arr = (ctypes.c_void_p * len(peers))(*peers)
-        peers = ctypes.cast(arr, ctypes.c_void_p)
-    return lib.fo_attn(args["local"], peers, args["recv"], args["out"], args["P"], args["rank"],
-                       args["m"], args["hq"], args["hkv"], args["d"], args["causal"], None,
-                       args["opts"])
+
+    def arr(ptrs):
+        if ptrs is None:
+            return None
+        a = (ctypes.c_void_p * len(ptrs))(*ptrs)
+        return ctypes.cast(a, ctypes.c_void_p)
+
+    return lib.fo_attn(args["local"], arr(args["peers"]), args["recv"], args["out"],
+                       arr(args["out_peer"]), args["P"], args["rank"], args["m"], args["hq"],
+                       args["hkv"], args["d"], args["causal"], None, args["opts"])
 
 
 @pytest.mark.parametrize("kw", [dict(hq=6, hkv=4), dict(hq=0), dict(hkv=0), dict(causal=2),
@@ -288,6 +301,19 @@ def test_attn_rejects_bad_opts(lib):
         assert _attn(lib, opts=ctypes.byref(o)) == fo.FO_ERR_INVALID_ARG, kw
     peers = [0x50000000, 0, 0x60000000, 0x70000000]   # a NULL peer with arrivals on
     assert _attn(lib, peers=peers) == fo.FO_ERR_INVALID_ARG
+
+
+def test_attn_return_exchange_rejects(lib):
+    """out_peer (the return All-to-All): every entry but the rank's present, 16-byte aligned, and
+    clear of out, of the inputs and of the other entries; 2P slots of signals needed."""
+    E, F, G = 0x60000000, 0x68000000, 0x70000000   # out slices are 64 x 8 x 256 B = 128 KiB
+    ok = [0, E, F, G]
+    for bad in ([0, 0, F, G], [0, E + 8, F, G], [0, C, F, G], [0, E, E + 4096, G],
+                [0, E, F, A]):
+        assert _attn(lib, out_peer=bad) == fo.FO_ERR_INVALID_ARG, bad
+    assert _attn(lib, out_peer=ok, m=0) == fo.FO_OK
+    big = [0] + [0x60000000 + i * (1 << 20) for i in range(16)]
+    assert _attn(lib, out_peer=big, P=17, m=64) == fo.FO_ERR_UNSUPPORTED
 
 
 def test_attn_empty_is_a_no_op(lib):

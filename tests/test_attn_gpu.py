@@ -62,7 +62,10 @@ def test_attn_ref_against_oracle(dev, S, hq, hkv, causal):
     _check(from_dev(out), qkv, hq, hkv, causal, f"S{S} hq{hq} hkv{hkv} causal{causal}")
 
 
-def _sliced(dev, qkv, P, rank, hq, hkv, causal, o=None, arrivals=True):
+def _sliced(dev, qkv, P, rank, hq, hkv, causal, o=None, arrivals=True, send=True):
+    """fo_attn with both exchanges (send=True: the output rows of every slice but the rank's own
+    go back to their owner): checks that every sent slice equals the rank's output rows bit for
+    bit and that the own slice's buffer is untouched, and returns the output."""
     S, row = qkv.shape
     m = S // P
     slices = [to_dev(qkv[s * m:(s + 1) * m], dev) for s in range(P)]
@@ -71,14 +74,22 @@ def _sliced(dev, qkv, P, rank, hq, hkv, causal, o=None, arrivals=True):
         for s in range(P):
             recv[s * m:(s + 1) * m] = slices[s]
     out = torch.full((S, hq * D), float("nan"), dtype=torch.bfloat16, device=dev)
+    back = [torch.full((m, hq * D), float("nan"), dtype=torch.bfloat16, device=dev)
+            for _ in range(P)] if send else None
     st = torch.cuda.current_stream()
     o = o or fo.opts()
     if not arrivals:
         o.arrival = fo.ARR_NONE
     fo.attn(slices[rank], slices if arrivals else None, recv, out, P, rank, hq, hkv, causal,
-            compute_stream=st, o=o)
+            compute_stream=st, o=o, out_peer=back)
     fo.check(st)
     assert not torch.isnan(out).any().item()
+    if send:
+        for s in range(P):
+            if s == rank:
+                assert torch.isnan(back[s]).all().item(), "the own slice is not sent"
+            else:
+                assert torch.equal(back[s], out[s * m:(s + 1) * m]), f"slice {s} sent to rank {s}"
     return out
 
 
@@ -109,6 +120,25 @@ def test_attn_row_group_arrivals(dev, groups):
                    f"groups {groups} rank {rank}", rows=rows)
 
 
+@pytest.mark.parametrize("epl", [1, 2], ids=["one_engine", "engine_pair"])
+@pytest.mark.parametrize("groups", [1, 2])
+@pytest.mark.parametrize("order", [fo.ORDER_FLASH, fo.ORDER_NATURAL], ids=["flash", "natural"])
+def test_attn_return_exchange_every_rank(dev, groups, order, epl):
+    """The return All-to-All at every rank, whole slices and two row groups per slice (the second
+    one short: m = 200 rows), against the oracle: each slice's rows reach its owner (checked in
+    _sliced), and the output, including the own slice computed last, is the attention."""
+    P, m, hq, hkv = 4, 200, 2, 1
+    qkv = inputs.normal(8170 + groups, (P * m, (hq + 2 * hkv) * D), 1.0, "bf16")
+    for rank in range(P):
+        out = _sliced(dev, qkv, P, rank, hq, hkv, True,
+                      fo.opts(row_groups=groups, order=order, engines_per_link=epl))
+        _check(from_dev(out), qkv, hq, hkv, True, f"return exchange rank {rank} groups {groups}")
+    # without the return exchange the output is the same, bit for bit
+    a = _sliced(dev, qkv, P, 1, hq, hkv, True, fo.opts(row_groups=groups, order=order))
+    b = _sliced(dev, qkv, P, 1, hq, hkv, True, fo.opts(row_groups=groups, order=order), send=False)
+    assert torch.equal(a, b)
+
+
 def test_attn_arrivals_match_resident_slices(dev):
     """Gating changes when a key slice is read, not what is computed: the call with arrivals
     equals the same call on slices already in place, bit for bit."""
@@ -135,8 +165,8 @@ def test_attn_sliced_equals_resident_in_natural_order(dev):
 @pytest.mark.parametrize("rank", [0, 7])
 def test_attn_l70b(dev, rank):
     """The Llama-3.1-70B Ulysses share (8 slices of 1024 tokens, 8 query heads, 1 key/value head,
-    causal) with arrivals: every query row and head against the oracle (the result does not
-    depend on the rank, so the oracle runs once)."""
+    causal) with both exchanges: every query row and head against the oracle (the result does
+    not depend on the rank, so the oracle runs once), and every sent slice equal to those rows."""
     c = configs.L70B_ATTN
     qkv = c.qkv()
     out = _sliced(dev, qkv, c.P, rank, c.hq, c.hkv, c.causal)
@@ -165,10 +195,18 @@ def test_attn_back_to_back_calls_see_new_arrivals(dev):
         slices.append([qd[s * m:(s + 1) * m].contiguous() for s in range(P)])
     recv = torch.empty((P * m, row), dtype=torch.bfloat16, device=dev)
     outs = [torch.empty((P * m, hq * D), dtype=torch.bfloat16, device=dev) for _ in range(6)]
+    # the return exchange into the same receive buffers every call: each call's sent rows must
+    # be its own (calls in a row, one kernel after the other)
+    backs = [[torch.empty((m, hq * D), dtype=torch.bfloat16, device=dev) for _ in range(P)]
+             for _ in range(6)]
     for it in range(6):
         i, rank = it % 2, (it * 3) % P
         fo.attn(slices[i][rank], slices[i], recv, outs[it], P, rank, hq, hkv, True,
-                compute_stream=st, o=fo.opts(order=fo.ORDER_NATURAL))
+                compute_stream=st, o=fo.opts(order=fo.ORDER_NATURAL), out_peer=backs[it])
     fo.check(st)
     for it in range(6):
+        rank = (it * 3) % P
         assert torch.equal(outs[it], refs[it % 2]), f"call {it}"
+        for s in range(P):
+            if s != rank:
+                assert torch.equal(backs[it][s], refs[it % 2][s * m:(s + 1) * m]), f"call {it} slice {s}"

@@ -118,8 +118,9 @@ def test_missed_arrival_times_out(dev):
     assert rel_frobenius(got, oracle.gemm(x, w)) <= TOL_BF16
 
 
+@pytest.mark.parametrize("epl", [1, 2, 3], ids=["one_engine", "engine_pair", "pair_first_alone"])
 @pytest.mark.parametrize("chunks", [0, 4])
-def test_back_to_back_calls_see_new_arrivals(dev, chunks):
+def test_back_to_back_calls_see_new_arrivals(dev, chunks, epl):
     """Calls enqueued back to back with no other kernel between them, the peers' data
     alternating between two sets and landing in the same receive buffer: each call's kernel
     reads the rows the previous call read, so a cached line of the previous data would show.
@@ -149,8 +150,8 @@ def test_back_to_back_calls_see_new_arrivals(dev, chunks):
         for it in range(8):
             i, r = it % 2, (3 * it) % P
             fo.ag_gemm(peers[i][r], peers[i], x_recv, w_d, ys[it], P, r, compute_stream=stream,
-                       o=fo.opts(links=links, k_chunks=chunks))
+                       o=fo.opts(links=links, k_chunks=chunks, engines_per_link=epl))
         fo.check(stream)
         for it in range(8):
             assert torch.equal(ys[it].view(torch.int16), refs[it % 2].view(torch.int16)), \
-                f"call {it} links {links}"
+                f"call {it} links {links} engines per link {epl}"

@@ -70,9 +70,12 @@ def test_tail_equals_fused_epilogue(dev, shape, tile):
     assert prob.out_u.data_ptr() % 16 == 4
     for r in sorted({0, P - 1, 1 % P}):
         ref = oracle.rs(x, w, parts, P, r)
-        for arrival, groups, resident in ((fo.ARR_LOCKSTEP, 0, False), (fo.ARR_EAGER, 1, False),
-                                          (fo.ARR_NONE, 0, True), (fo.ARR_LOCKSTEP, 2, False)):
-            o = fo.opts(tile=tile, arrival=arrival, row_groups=groups)
+        for arrival, groups, resident, epl in ((fo.ARR_LOCKSTEP, 0, False, 1),
+                                               (fo.ARR_EAGER, 1, False, 1),
+                                               (fo.ARR_NONE, 0, True, 1),
+                                               (fo.ARR_LOCKSTEP, 2, False, 1),
+                                               (fo.ARR_LOCKSTEP, 0, False, 2)):
+            o = fo.opts(tile=tile, arrival=arrival, row_groups=groups, engines_per_link=epl)
             a = prob.run(r, prob.out_a, o, resident)
             u = prob.run(r, prob.out_u, o, resident)
             assert not np.isnan(a).any()
