@@ -114,3 +114,7 @@ class AttnCase:
 # Llama-3.1-70B attention (64 query heads, 8 key/value heads, head_dim 128) under Ulysses
 # parallelism over 8 ranks: 8 query heads and 1 key/value head per rank, causal, 8K tokens
 L70B_ATTN = AttnCase(6, 8, 8192, 8, 1, name="Llama-3.1-70B attention, Ulysses 8 rank share, seq 8192")
+
+# the same share at 2K to 16K tokens: the attention gain against sequence length
+SWEEP_ATTN = tuple(AttnCase(6, 8, S, 8, 1, name=f"Llama-3.1-70B attention, Ulysses 8 rank share, seq {S}")
+                   for S in (2048, 4096, 8192, 16384))

@@ -40,14 +40,24 @@ int slice_order(int kind, int order, int P, int rank, int32_t* out) {
 //   - a sliced call with fp32 output and K <= 4096 (Flash-RS at Llama-70B down-projection
 //     shapes): 128x256. Such a call waits on its transfers more than on its GEMM, and the
 //     smaller tiles finish the first outgoing row groups sooner (450 vs 493 us);
+//   - fewer 256x256 tiles than CUs while the 128x256 tiles still fit in as many rounds over the
+//     CUs: 128x256, which fills the CUs the larger tiles leave idle (the monolithic GEMM of the
+//     Llama-70B gate+up at 1K tokens: 112 tiles of 256x256 on 256 CUs took 142-147 us, the
+//     same product in 224 tiles of 128x256 111 us);
 //   - otherwise 256x256 (Llama-70B gate+up, 2K-16K tokens, and both Llama-405B calls).
 // Rows of a tile never cross a slice.
 int choose_tile(int P, int64_t m, int64_t K, int64_t N, bool out_f32, int n_cu) {
-  (void)n_cu;
   if (m <= 64 || N <= 64) return FO_TILE_64x64;
   if (m <= 128) return N >= 256 ? FO_TILE_128x256 : FO_TILE_128x128;
   if (N < 256) return FO_TILE_256x128;
   if (P > 1 && out_f32 && K <= 4096) return FO_TILE_128x256;
+  if (n_cu > 0) {
+    const int64_t tn = (N + 255) / 256;
+    const int64_t t256 = (int64_t)P * ((m + 255) / 256) * tn;
+    const int64_t t128 = (int64_t)P * ((m + 127) / 128) * tn;
+    if (t256 < n_cu && (t128 + n_cu - 1) / n_cu <= (t256 + n_cu - 1) / n_cu)
+      return FO_TILE_128x256;
+  }
   return FO_TILE_256x256;
 }
 

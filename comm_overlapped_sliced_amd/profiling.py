@@ -1,0 +1,314 @@
+"""rocprofv3 harness of the benchmark: the counter passes behind the roofline evidence, and the
+text summaries kept under profiles/.
+
+    python -m comm_overlapped_sliced_amd.profiling run --raw gpurun_out/prof
+    python -m comm_overlapped_sliced_amd.profiling summarize --raw gpurun_out/prof --out profiles
+
+`run` launches, one after the other and each under its own time limit, rocprofv3 on bench.py:
+  1. --kernel-trace --stats: per-kernel durations of the step (no exposure sweep, no oracle);
+  2. --pmc FETCH_SIZE and 3. --pmc WRITE_SIZE (each a run of its own): HBM bytes per dispatch,
+     with a plain copy of known size in the same run to scale the counters;
+  4. --pmc of the MFMA counters: bf16 MFMA operations (x 512 = flops) and MFMA-busy cycles.
+It stops at the first pass that fails. rocprofv3 is the program started, with python after
+`--`; this module itself never touches the GPU.
+
+`summarize` reads those outputs and writes, for the GEMM launches of the step (Flash-AG on the
+Llama-3.1-70B gate+up share, Flash-RS on the down share):
+  - gemm_bf16_kernel_l70b_mlp_step_kernel_trace.md (durations; bench.py's own timing of the
+    same run beside them),
+  - gemm_bf16_kernel_l70b_mlp_step_hbm_counters.md and traffic.json (bytes per launch, the
+    counters' scale from the copy, the algorithmic bytes, and the sha256 of the kernel source
+    they were taken on: bench.py reports them only while the source is unchanged),
+  - gemm_bf16_kernel_l70b_mlp_step_mfma_counters.md (counted MFMA flops against 2MNK, busy
+    cycles per SIMD and the busy share at the nominal and at the sampled shader clock).
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import glob
+import hashlib
+import json
+import os
+import re
+import statistics
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+KERNEL_SRC = os.path.join(HERE, "csrc", "fo_gemm.hip")
+CALIB_BYTES = 268435456
+N_SIMD = 1024  # 256 CUs x 4 SIMDs
+
+BENCH_ARGS = ["bench.py", "--no-exposure", "--cpu-seconds", "0", "--clock-seconds", "0"]
+PASSES = [
+    # (name, rocprofv3 options, bench options, time limit in seconds)
+    ("trace", ["--kernel-trace", "--stats"], ["--steps", "10", "--warmup", "3"], 240),
+    ("fetch", ["--pmc", "FETCH_SIZE", "--kernel-trace"],
+     ["--steps", "3", "--warmup", "1", "--copy-calibration", str(CALIB_BYTES)], 180),
+    ("write", ["--pmc", "WRITE_SIZE", "--kernel-trace"],
+     ["--steps", "3", "--warmup", "1", "--copy-calibration", str(CALIB_BYTES)], 180),
+    ("mfma", ["--pmc", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES",
+              "--kernel-trace"], ["--steps", "3", "--warmup", "1"], 180),
+]
+
+# the step's two GEMM launches: (kind, call, M, K, N, algorithmic read bytes, write bytes)
+STEP = {
+    "ag": ("fo_ag_gemm", 4096, 8192, 7168,
+           4096 * 8192 * 2 + 8192 * 7168 * 2, 4096 * 7168 * 2),
+    "rs": ("fo_gemm_rs", 4096, 3584, 8192,
+           4096 * 3584 * 2 + 3584 * 8192 * 2 + 7 * 512 * 8192 * 4, 4096 * 8192 * 4),
+}
+
+
+def command(name: str, raw: str, python: str = sys.executable) -> list:
+    """The argv of one pass."""
+    for n, opts, bargs, _ in PASSES:
+        if n == name:
+            return (["rocprofv3", *opts, "--output-format", "csv", "-d",
+                     os.path.join(raw, n), "-o", n, "--", python, *BENCH_ARGS, *bargs])
+    raise KeyError(name)
+
+
+def command_text(name: str, raw: str) -> str:
+    return " ".join(command(name, raw, "python3"))
+
+
+def run(raw: str) -> int:
+    os.makedirs(raw, exist_ok=True)
+    env = dict(os.environ, TMPDIR="/tmp")
+    for name, _, _, limit in PASSES:
+        cmd = command(name, raw)
+        print(f"pass {name}: {' '.join(cmd)}", flush=True)
+        with open(os.path.join(raw, f"{name}.log"), "w") as log:
+            try:
+                rc = subprocess.run(cmd, cwd=ROOT, env=env, stdout=log, stderr=subprocess.STDOUT,
+                                    timeout=limit).returncode
+            except subprocess.TimeoutExpired:
+                print(f"pass {name}: time limit {limit} s", flush=True)
+                return 124
+        print(f"pass {name}: rc {rc}", flush=True)
+        if rc != 0:
+            return rc
+    return 0
+
+
+# ---- summaries --------------------------------------------------------------------------
+
+def _one(pattern: str) -> str:
+    hits = sorted(glob.glob(pattern, recursive=True))
+    if not hits:
+        raise FileNotFoundError(pattern)
+    return hits[0]
+
+
+def _short(name: str) -> str:
+    m = re.search(r"gemm_bf16_kernel<(\d+), (\d+), (\w+)>", name)
+    if m:
+        return f"gemm_bf16_kernel<{m.group(1)}, {m.group(2)}, {m.group(3)}>"
+    m = re.search(r"(\w+)\(", name)
+    return m.group(1) if m else name[:60]
+
+
+def _timed_line(log: str) -> str:
+    with open(log) as f:
+        for line in f:
+            if line.startswith("timed:"):
+                return line.strip()[len("timed: "):]
+    return "(no timed line)"
+
+
+def _step_kernels(trace_csv: str):
+    """Names of the step's Flash-AG and Flash-RS launches: bench.py's steps alternate AG and RS,
+    so the kernels are the two GEMM instantiations that run equally often with the most calls."""
+    counts = collections.Counter()
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            if "gemm_bf16_kernel" in r["Kernel_Name"]:
+                counts[r["Kernel_Name"]] += 1
+    names = [n for n, _ in counts.most_common()]
+    ag = next(n for n in names if "<256, 256" in n)
+    rs = next(n for n in names if n != ag)
+    return {"ag": ag, "rs": rs}
+
+
+def _per_dispatch(counter_csv: str):
+    """{dispatch id: (kernel, grid, {counter: value})}."""
+    out = {}
+    with open(counter_csv) as f:
+        for r in csv.DictReader(f):
+            d = int(r["Dispatch_Id"])
+            ent = out.setdefault(d, (r["Kernel_Name"], int(r["Grid_Size"]), {}))
+            ent[2][r["Counter_Name"]] = ent[2].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return out
+
+
+def summarize(raw: str, out_dir: str, sclk_mhz: float | None = None) -> dict:
+    sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    os.makedirs(out_dir, exist_ok=True)
+    trace_dir = os.path.join(raw, "trace")
+    stats_csv = _one(os.path.join(trace_dir, "**", "*kernel_stats.csv"))
+    trace_csv = _one(os.path.join(trace_dir, "**", "*kernel_trace.csv"))
+    names = _step_kernels(trace_csv)
+    timed = _timed_line(os.path.join(raw, "trace.log"))
+
+    # 1. kernel trace
+    rows = ["| kernel | launches | total us | average us | min us | max us |",
+            "|---|---|---|---|---|---|"]
+    avg = {}
+    with open(stats_csv) as f:
+        for r in csv.DictReader(f):
+            if "direct_copy" in r["Name"] or "elementwise" in r["Name"]:
+                continue
+            rows.append(f"| `{_short(r['Name'])}` | {r['Calls']} | "
+                        f"{float(r['TotalDurationNs']) / 1e3:.1f} | {float(r['AverageNs']) / 1e3:.1f} | "
+                        f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
+            for k, n in names.items():
+                if r["Name"] == n:
+                    avg[k] = float(r["AverageNs"]) / 1e3
+    # per-launch durations of the timed steps only (the trace also has the warm-up launches)
+    dur = collections.defaultdict(list)
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            for k, n in names.items():
+                if r["Kernel_Name"] == n:
+                    dur[k].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    timed_avg = {k: statistics.mean(v[-10:]) for k, v in dur.items() if v}
+    cmd = command_text("trace", raw)
+    text = f"""# rocprofv3 kernel trace: Flash-AG + Flash-RS step, Llama-3.1-70B MLP rank share (P=8)
+
+Flash-AG: fo_ag_gemm M=4096 K=8192 N=7168 bf16, `{_short(names['ag'])}`.
+Flash-RS: fo_gemm_rs M=4096 K=3584 N=8192 with seven fp32 partials, `{_short(names['rs'])}`.
+Emulated transfers on SDMA engines, one per peer; each GEMM launch's duration includes its
+in-kernel waits for them.
+
+Command (from the repository root, TMPDIR=/tmp; `python -m comm_overlapped_sliced_amd.profiling run`
+runs it as its first pass):
+
+    {cmd}
+
+Kernel statistics (3 warm-up + 10 timed steps):
+
+{chr(10).join(rows)}
+
+Average of the 10 timed launches in the same trace: Flash-AG {timed_avg.get('ag', float('nan')):.1f} us,
+Flash-RS {timed_avg.get('rs', float('nan')):.1f} us. bench.py's own HIP-event timing of the same run:
+{timed}.
+
+fo_gemm.hip sha256: {sha}
+"""
+    with open(os.path.join(out_dir, "gemm_bf16_kernel_l70b_mlp_step_kernel_trace.md"), "w") as f:
+        f.write(text)
+
+    # 2. HBM traffic
+    fetch = _per_dispatch(_one(os.path.join(raw, "fetch", "**", "*counter_collection.csv")))
+    write = _per_dispatch(_one(os.path.join(raw, "write", "**", "*counter_collection.csv")))
+
+    def calib(d, counter):
+        vals = [c[counter] for (n, _, c) in d.values() if "copyBuffer" in n and counter in c]
+        return max(vals)
+
+    cf, cw = calib(fetch, "FETCH_SIZE"), calib(write, "WRITE_SIZE")
+    fs, ws = CALIB_BYTES / (cf * 1024), CALIB_BYTES / (cw * 1024)
+    traffic, trows = {}, []
+    for kind, name in names.items():
+        fv = [c["FETCH_SIZE"] for d, (n, _, c) in sorted(fetch.items()) if n == name]
+        wv = [c["WRITE_SIZE"] for d, (n, _, c) in sorted(write.items()) if n == name]
+        ft, wt = statistics.mean(fv[1:] or fv), statistics.mean(wv[1:] or wv)
+        b = ft * 1024 * fs + wt * 1024 * ws
+        call, M, K, N, ar, aw = STEP[kind]
+        traffic[kind] = {"kernel": _short(name), "kernel_source_sha256": sha,
+                         "fetch_kib_counter": round(ft, 1), "write_kib_counter": round(wt, 1),
+                         "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
+                         "bytes_per_launch": int(b), "algorithmic_read_bytes": ar,
+                         "algorithmic_write_bytes": aw,
+                         "launches": f"{max(1, len(fv) - 1)} timed (the warm-up launch excluded)"}
+        trows.append(f"| `{_short(name)}` ({call}) | {', '.join(str(round(x)) for x in fv)} | "
+                     f"{', '.join(str(round(x)) for x in wv)} | {b / 1e6:.1f} MB | "
+                     f"{(ar + aw) / 1e6:.1f} MB | {b / (ar + aw):.2f} |")
+    with open(os.path.join(out_dir, "traffic.json"), "w") as f:
+        json.dump(traffic, f, indent=1)
+    text = f"""# HBM traffic of the GEMM kernels (rocprofv3 counters), Llama-3.1-70B MLP rank share
+
+Commands (each a run of its own, from the repository root with TMPDIR=/tmp; passes 2 and 3 of
+`python -m comm_overlapped_sliced_amd.profiling run`):
+
+    {command_text('fetch', raw)}
+    {command_text('write', raw)}
+
+Calibration: the same runs copy {CALIB_BYTES} bytes with one plain copy kernel
+(`__amd_rocclr_copyBuffer`), whose counters read FETCH_SIZE {cf:.0f} KiB and WRITE_SIZE {cw:.0f} KiB;
+scale factors (true bytes / counter bytes): fetch {fs:.4f}, write {ws:.4f}.
+
+| kernel | FETCH_SIZE KiB per launch (warm-up, timed) | WRITE_SIZE KiB per launch | scaled bytes per timed launch | algorithmic read + write bytes | ratio |
+|---|---|---|---|---|---|
+{chr(10).join(trows)}
+
+Algorithmic bytes: X and W read once, the partials read once (Flash-RS), outputs written once.
+
+fo_gemm.hip sha256: {sha}
+"""
+    with open(os.path.join(out_dir, "gemm_bf16_kernel_l70b_mlp_step_hbm_counters.md"), "w") as f:
+        f.write(text)
+
+    # 3. MFMA counters
+    mf_dir = os.path.join(raw, "mfma")
+    mf = _per_dispatch(_one(os.path.join(mf_dir, "**", "*counter_collection.csv")))
+    mdur = {}
+    with open(_one(os.path.join(mf_dir, "**", "*kernel_trace.csv"))) as f:
+        for r in csv.DictReader(f):
+            mdur[int(r["Dispatch_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    lines = []
+    for d, (n, _, c) in sorted(mf.items()):
+        kind = next((k for k, nm in names.items() if nm == n), None)
+        if kind is None:
+            continue
+        call, M, K, N, _, _ = STEP[kind]
+        flops = c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", float("nan")) * 512
+        busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan")) / N_SIMD
+        t = mdur.get(d, float("nan"))
+        at = f"{busy / (t * 1e-6 * sclk_mhz * 1e6):.3f}" if sclk_mhz else "n/a"
+        lines.append(f"| {call} | {d} | {t:.1f} | {flops:.4e} | {2 * M * N * K:.4e} | {busy:.0f} | "
+                     f"{busy / (t * 1e-6 * 2.4e9):.3f} | {at} |")
+    text = f"""# MFMA counters of the GEMM kernels, Llama-3.1-70B MLP rank share (P=8)
+
+Command (from the repository root with TMPDIR=/tmp, a run of its own; pass 4 of
+`python -m comm_overlapped_sliced_amd.profiling run`):
+
+    {command_text('mfma', raw)}
+
+MFMA flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512. Busy cycles per SIMD = SQ_VALU_MFMA_BUSY_CYCLES /
+{N_SIMD} SIMDs. The busy share divides them by the launch's cycles at the nominal 2.4 GHz and at
+{f'{sclk_mhz:.0f} MHz, the shader clock the benchmark sampled from the SMU under this load' if sclk_mhz else 'the sampled clock (none given)'}.
+
+| call | dispatch | duration us | MFMA flops (counter) | 2MNK | MFMA busy cycles / SIMD | busy at 2.4 GHz | busy at sampled clock |
+|---|---|---|---|---|---|---|---|
+{chr(10).join(lines)}
+
+fo_gemm.hip sha256: {sha}
+"""
+    with open(os.path.join(out_dir, "gemm_bf16_kernel_l70b_mlp_step_mfma_counters.md"), "w") as f:
+        f.write(text)
+    return traffic
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(prog="python -m comm_overlapped_sliced_amd.profiling")
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    r = sub.add_parser("run")
+    r.add_argument("--raw", default="gpurun_out/prof")
+    s = sub.add_parser("summarize")
+    s.add_argument("--raw", default="gpurun_out/prof")
+    s.add_argument("--out", default="profiles")
+    s.add_argument("--sclk-mhz", type=float, default=None)
+    a = ap.parse_args(argv)
+    if a.cmd == "run":
+        return run(a.raw)
+    print(json.dumps(summarize(a.raw, a.out, a.sclk_mhz), indent=1))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
