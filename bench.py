@@ -72,9 +72,11 @@ def parse():
                     help="emulated links per call (0: one DMA engine per peer; 1: one link)")
     ap.add_argument("--row-groups", type=int, default=0,
                     help="row groups per slice (0: one per tile row; 1: whole slices)")
-    ap.add_argument("--ag-k-chunks", type=int, default=4,
-                    help="Flash-AG slices stored and sent in this many K blocks (opts.k_chunks; "
-                         "0: row-major slices)")
+    ap.add_argument("--ag-k-chunks", type=int, default=0,
+                    help="Flash-AG slices stored and sent in this many K blocks in the timed step "
+                         "(opts.k_chunks; 0: row-major slices, the activation's own layout); the "
+                         "exposure section measures 4 K blocks beside the row-major call either "
+                         "way")
     ap.add_argument("--engines-per-link", type=int, default=0,
                     help="DMA engines per emulated link (opts.engines_per_link; 0: the library's "
                          "default)")
@@ -194,7 +196,8 @@ def mlp_sweep_section(fo, dev, stream, timed, reps, log, kc):
     """The MLP block of the page's latency experiment (gate+up Flash-AG -> SwiGLU -> down Flash-RS,
     one TP8 rank's share of the Llama-3.1-70B MLP, rank 0) at 1K to 16K tokens: vanilla (each
     projection's transfers, then its GEMM, nothing overlapped, plus the activation kernel), data
-    slicing (index order, whole slices) and Flash (row groups, gate+up slices in kc K blocks),
+    slicing (index order, whole slices) and Flash (row groups; gate+up slices row-major, or in kc
+    K blocks when the timed step uses them),
     with the activation as its own kernel and fused into the gate+up write-back. The pure GEMMs
     of vanilla are the fastest the library has for each product (fo_gemm_ref or the sliced call
     with everything resident)."""
@@ -294,7 +297,8 @@ def mlp_sweep_section(fo, dev, stream, timed, reps, log, kc):
 def sweep_section(fo, dev, stream, timed, reps, log, kc):
     """The other workloads of the measurement, each in the three forms of the metric: the 70B
     gate+up AG-GEMM at 1K to 16K tokens and the 405B AG and RS shares at 8K tokens, rank 0, one
-    DMA engine per peer, row groups (AG slices in kc K blocks where K allows). Per call: T_ref
+    link per peer, row groups (AG slices row-major, or in kc K blocks when the timed step uses
+    them and K allows). Per call: T_ref
     (monolithic GEMM), T_slice0 (slices resident), T_slice (arrivals), T_xfer (the same copies
     alone); TFLOP/s and the share of the bf16 peak from T_slice; exposed = (T_slice - T_ref) /
     T_xfer."""
@@ -411,15 +415,18 @@ def main():
                  for s in range(P)]
     ag_full = dev_of(xa)
     del xa
-    # Flash-AG slices in the K-block layout of opts.k_chunks (block j = columns j*K/c .. of every
-    # row), the form the sending rank keeps them in; the row-major slices stay for the baselines
+    # The timed step's Flash-AG slices: row-major (the activation's layout), or with
+    # --ag-k-chunks c > 1 in the K-block layout of opts.k_chunks (block j = columns j*K/c .. of
+    # every row), which a sender would have to produce. The exposure section measures the K-block
+    # form (kb blocks) beside the row-major one either way.
     kc = args.ag_k_chunks
+    kb = kc if kc > 1 else 4
 
     def k_blocks(t, c):
         m_, k_ = t.shape
         return t.reshape(m_, c, k_ // c).permute(1, 0, 2).contiguous().reshape(m_, k_)
 
-    ag_chunked = [k_blocks(t, kc) for t in ag_slices] if kc > 1 else ag_slices
+    ag_chunked = [k_blocks(t, kb) for t in ag_slices]
     ag_w = dev_of(ag_case.w())
     ag_recv = torch.empty((ag_case.M, ag_case.K), dtype=torch.bfloat16, device=dev)
     ag_y = torch.empty((ag_case.M, ag_case.N), dtype=torch.bfloat16, device=dev)
@@ -508,13 +515,10 @@ def main():
         # one DMA engine per peer (the xGMI mesh) with row-group arrivals (the default), the same
         # with whole slices (the page's granularity), and every transfer over one link (the
         # ring of the page's Flash-AG, where all slices come from one neighbour)
-        # (name, links, row groups, Flash-AG K blocks). With --ag-k-chunks > 1 the K-block
-        # variant is the timed step's configuration; it changes Flash-AG only, so its RS entry
-        # repeats the row-major one.
-        variants = [("mesh_rowgroups", 0, 0, 0), ("mesh_slices", 0, 1, 0),
-                    ("onelink_slices", 1, 1, 0)]
-        if kc > 1:
-            variants.insert(1, ("mesh_rowgroups_kblocks", 0, 0, kc))
+        # (name, links, row groups, Flash-AG K blocks). The K-block variant changes Flash-AG
+        # only, so its RS entry repeats the row-major one.
+        variants = [("mesh_rowgroups", 0, 0, 0), ("mesh_rowgroups_kblocks", 0, 0, kb),
+                    ("mesh_slices", 0, 1, 0), ("onelink_slices", 1, 1, 0)]
 
         def groups_of(kind, case, req, chunks=0):
             order = fo.tile_order(kind, P, case.m, case.K, case.N,
@@ -777,8 +781,10 @@ def main():
         "config": {"workload": "Llama-3.1-70B MLP, one TP8 rank share (rank %d): Flash-AG "
                    "gate+up M=4096 K=8192 N=7168 + Flash-RS down M=4096 K=3584 N=8192, "
                    "P=8 slices" % r,
-                   "transfers": "SDMA engines, %s" % ("one per peer" if args.links == 0
-                                                      else "%d link(s)" % args.links),
+                   "transfers": "SDMA engines, %s, engines per link: %s" % (
+                       "one link per peer" if args.links == 0 else "%d link(s)" % args.links,
+                       args.engines_per_link or "library default (an engine pair, each "
+                                                "transfer split across it)"),
                    "row_groups": "one per tile row" if args.row_groups == 0 else args.row_groups,
                    "ag_k_blocks": kc if kc > 1 else "row-major slices",
                    "ag_arrival": "eager", "rs_arrival": "lockstep",

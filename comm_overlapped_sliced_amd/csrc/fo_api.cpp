@@ -281,18 +281,18 @@ int arrival_sequence(int kind, int order, int P, int rank, int* seq) {
 }
 
 // The engines of one link (opts.engines_per_link): 1 one engine; 2 an engine pair taking the
-// link's copies in turn; 3 the same, the pair's second engine starting once the link's first
-// copy has landed.
+// link's copies in turn; 3 the pair, every copy split in two halves, one on each engine.
 void set_engines(const fo_opts& o, int dflt, fo::dma::Call* call) {
   const int e = o.engines_per_link ? o.engines_per_link : dflt;
   call->pairs = e >= 2;
-  call->first_alone = e == 3;
+  call->split = e == 3;
 }
 
-// Default engines per link: Flash-RS moves the most bytes per link and waits on their total
-// (pairs: its 70B call 416 -> 352 us); Flash-AG and the attention wait first on the latency of
-// a slice's first transfer, which a busy partner engine would halve the bandwidth of.
-constexpr int kEnginesAG = 1, kEnginesRS = 2, kEnginesAttn = 1;
+// Default engines per link: the pair with every transfer split across it. A released Flash-RS
+// group then leaves at the pair's rate, not one engine's (70B call: one engine 416 us, pairs
+// taking copies in turn 352 us, split 323 us), and the first row group of a Flash-AG slice lands
+// sooner (row-major 70B call 456 -> 438 us).
+constexpr int kEnginesAG = 3, kEnginesRS = 3, kEnginesAttn = 3;
 
 // Every call on a device is ordered after the previous one (they share the device's signals,
 // counters and words): a call on another stream first waits for the previous call's event; on

@@ -112,7 +112,6 @@ struct Slot {
   std::bitset<kSignals> issued;  // completion signals a copy will decrement
   uint32_t started = 0;          // engines that already hold a copy of the call waiting on start
   uint8_t turn[32] = {};         // per engine pair: copies the call has issued on it
-  int16_t first[32] = {};        // per engine pair: completion signal of the call's first copy
 };
 
 struct Dev {
@@ -129,6 +128,7 @@ constexpr int kMaxDevices = 64;
 Dev g_dev[kMaxDevices];
 
 constexpr size_t kWarmBytes = 65536;
+constexpr size_t kSplitMin = 65536;  // a transfer is split across a pair only if each half is this big
 
 const char* hsa_msg(hsa_status_t s) {
   switch (s) {
@@ -327,34 +327,45 @@ bool copy(int dev, const Call& call, int link, int slice, int group, int rel_pos
   // An engine runs its copies one after the other in issue order, so only the call's first copy
   // on an engine waits for the start signal; a copy gated on a release signal needs no start
   // signal at all (the kernel stores the release after it has started).
-  int ei = (link % d.n_eng + d.n_eng) % d.n_eng;
-  int after = -1;  // completion signal the copy waits for (the pair's first copy, see below)
+  // the engines of this copy: one; or the pair's next in turn; or (split) both halves of the
+  // transfer, one on each engine of the pair, counted down on the same completion signal
+  int ei[2] = {(link % d.n_eng + d.n_eng) % d.n_eng, -1};
+  size_t part[2] = {bytes, 0};
   if (call.pairs && d.n_pairs > 0) {
     const int pr = (link % d.n_pairs + d.n_pairs) % d.n_pairs;
-    const int k = sl.turn[pr]++;
-    ei = pr + (k & 1) * d.n_pairs;
-    if (k == 0) sl.first[pr] = (int16_t)ci;
-    // first alone: the partner engine's first copy starts once the link's first copy has
-    // landed, so that copy has the pair's whole bandwidth
-    if (call.first_alone && k == 1) after = sl.first[pr];
+    if (call.split && bytes >= 2 * kSplitMin) {
+      ei[0] = pr;
+      ei[1] = pr + d.n_pairs;
+      part[0] = (bytes / 2 + 255) / 256 * 256;  // the first half ends on a 256-byte boundary
+      part[1] = bytes - part[0];
+      g_hsa.store(sl.comp[ci], 2);
+    } else {
+      ei[0] = pr + (sl.turn[pr]++ & 1) * d.n_pairs;
+    }
   }
-  const uint32_t eng = d.eng[ei];
-  hsa_signal_t deps[2];
-  uint32_t n = 0;
-  if (rel_pos >= 0) {
-    deps[n++] = sl.rel[rel_pos * kMaxGroups + group];
-  } else if (!(sl.started & (1u << ei))) {
-    deps[n++] = sl.start;
-    sl.started |= 1u << ei;
-  }
-  if (after >= 0) deps[n++] = sl.comp[after];
-  // (the runtime rejects a dependency array with a count of zero: pass none then)
-  const hsa_status_t s = g_hsa.copy(dst, d.agent, src, d.agent, bytes, n, n ? deps : nullptr,
-                                    sl.comp[ci], (hsa_amd_sdma_engine_id_t)eng, true);
-  if (s != HSA_STATUS_SUCCESS) {
-    // the kernel must not wait for a copy that was never issued: report it as failed
-    g_hsa.store(sl.comp[ci], -1);
-    return fail(err, "hsa_amd_memory_async_copy_on_engine", s);
+  size_t off = 0;
+  for (int k = 0; k < 2 && ei[k] >= 0; ++k) {
+    const uint32_t eng = d.eng[ei[k]];
+    hsa_signal_t deps[1];
+    uint32_t n = 0;
+    if (rel_pos >= 0) {
+      deps[n++] = sl.rel[rel_pos * kMaxGroups + group];
+    } else if (!(sl.started & (1u << ei[k]))) {
+      deps[n++] = sl.start;
+      sl.started |= 1u << ei[k];
+    }
+    // (the runtime rejects a dependency array with a count of zero: pass none then)
+    const hsa_status_t s =
+        g_hsa.copy((uint8_t*)dst + off, d.agent, (const uint8_t*)src + off, d.agent, part[k], n,
+                   n ? deps : nullptr, sl.comp[ci], (hsa_amd_sdma_engine_id_t)eng, true);
+    if (s != HSA_STATUS_SUCCESS) {
+      // the kernel must not wait for a copy that was never issued: report it as failed (a half
+      // already issued still counts the signal down, so it stays negative)
+      g_hsa.store(sl.comp[ci], -(int64_t)16);
+      sl.issued.set(ci);
+      return fail(err, "hsa_amd_memory_async_copy_on_engine", s);
+    }
+    off += part[k];
   }
   sl.issued.set(ci);
   return true;

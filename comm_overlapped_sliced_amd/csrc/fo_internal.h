@@ -219,9 +219,9 @@ struct Call {
   const int64_t* const* comp_tab;
   int64_t* const* rel_tab;
   // a link is an engine pair whose two engines take the link's copies in turn (else one engine);
-  // with first_alone the second engine's first copy waits until the link's first copy has landed
+  // with split each copy is cut in two halves, one on each engine of the pair
   bool pairs = false;
-  bool first_alone = false;
+  bool split = false;
 };
 
 // Per-device setup (called once, under the device lock, with the device current): finds the
@@ -235,9 +235,10 @@ int n_engines(int dev);
 // used it last is complete: its event done and its copies landed), re-arms the start signal and
 // the release and completion signals of P slices x `groups` groups to 1, and returns them.
 bool begin(int dev, int P, int groups, Call* call, std::string* err);
-// Copy `bytes` from src to dst on link `link` (engine link mod n_engines, or with call.pairs the
-// next engine in turn of pair link mod n_pairs), starting once the call's start signal and,
-// when rel_pos >= 0, the release signal of (rel_pos, group) are zero.
+// Copy `bytes` from src to dst on link `link` (engine link mod n_engines; with call.pairs the
+// next engine in turn of pair link mod n_pairs, or with call.split both engines of the pair, a
+// half each), starting once the call's start signal and, when rel_pos >= 0, the release signal
+// of (rel_pos, group) are zero.
 // The completion signal of (slice, group) is decremented when the copy has landed.
 bool copy(int dev, const Call& call, int link, int slice, int group, int rel_pos, void* dst,
           const void* src, size_t bytes, std::string* err);

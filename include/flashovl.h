@@ -141,10 +141,9 @@ typedef struct fo_opts {
                                pair (which share one bandwidth) taking the link's transfers in
                                turn, so that one copy's start-up overlaps the other's data (a
                                link's transfers may then land out of issue order; every wait is
-                               per transfer, so results do not change); 3 = as 2, the pair's
-                               second engine starting once the link's first transfer has landed
-                               (that one has the whole bandwidth); 0 = the default: 2 for
-                               fo_gemm_rs and fo_transfer_ref kind 1, else 1 */
+                               per transfer, so results do not change); 3 = the pair, every
+                               transfer cut in two halves, one on each engine, landing when both
+                               have; 0 = the default (3) */
   int32_t reserved;         /* must be 0 */
 } fo_opts;
 

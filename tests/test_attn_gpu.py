@@ -120,7 +120,7 @@ def test_attn_row_group_arrivals(dev, groups):
                    f"groups {groups} rank {rank}", rows=rows)
 
 
-@pytest.mark.parametrize("epl", [1, 2], ids=["one_engine", "engine_pair"])
+@pytest.mark.parametrize("epl", [1, 2, 3], ids=["one_engine", "engine_pair", "pair_split"])
 @pytest.mark.parametrize("groups", [1, 2])
 @pytest.mark.parametrize("order", [fo.ORDER_FLASH, fo.ORDER_NATURAL], ids=["flash", "natural"])
 def test_attn_return_exchange_every_rank(dev, groups, order, epl):

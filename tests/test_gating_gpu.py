@@ -118,7 +118,7 @@ def test_missed_arrival_times_out(dev):
     assert rel_frobenius(got, oracle.gemm(x, w)) <= TOL_BF16
 
 
-@pytest.mark.parametrize("epl", [1, 2, 3], ids=["one_engine", "engine_pair", "pair_first_alone"])
+@pytest.mark.parametrize("epl", [1, 2, 3], ids=["one_engine", "engine_pair", "pair_split"])
 @pytest.mark.parametrize("chunks", [0, 4])
 def test_back_to_back_calls_see_new_arrivals(dev, chunks, epl):
     """Calls enqueued back to back with no other kernel between them, the peers' data

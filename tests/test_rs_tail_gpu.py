@@ -74,7 +74,8 @@ def test_tail_equals_fused_epilogue(dev, shape, tile):
                                                (fo.ARR_EAGER, 1, False, 1),
                                                (fo.ARR_NONE, 0, True, 1),
                                                (fo.ARR_LOCKSTEP, 2, False, 1),
-                                               (fo.ARR_LOCKSTEP, 0, False, 2)):
+                                               (fo.ARR_LOCKSTEP, 0, False, 2),
+                                               (fo.ARR_LOCKSTEP, 0, False, 3)):
             o = fo.opts(tile=tile, arrival=arrival, row_groups=groups, engines_per_link=epl)
             a = prob.run(r, prob.out_a, o, resident)
             u = prob.run(r, prob.out_u, o, resident)
