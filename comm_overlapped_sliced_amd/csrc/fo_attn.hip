@@ -24,7 +24,9 @@
 // - K and V tiles are filled straight from HBM into a 2-stage LDS ring by LDS-writing buffer
 //   loads (16 bytes per lane); rows past a slice read zeros through the buffer range check and
 //   are masked. K rows are XOR-swizzled by key (the A-operand reads of 32 keys at one offset
-//   spread over the banks), V rows by key mod 4 (the transpose reads).
+//   spread over the banks), V rows by key mod 4 (the transpose reads: chunk XOR (0, 6, 12,
+//   10)[key & 3], which gives the 4 key rows x 4 chunks a 32-lane read covers distinct bank
+//   groups whether the LDS serves 128 or 256 bytes per cycle).
 // - Two workgroups per CU (64 KB of LDS each): one workgroup's softmax overlaps the other's
 //   MFMAs.
 #include <hip/hip_runtime.h>
@@ -104,6 +106,9 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
+
+// chunk swizzle of a V row (256 bytes, 16 chunks) by its key: (0, 6, 12, 10)[key & 3]
+__device__ __forceinline__ int vswz(int key) { return (0xAC60 >> ((key & 3) * 4)) & 15; }
 
 __device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
@@ -199,14 +204,14 @@ __device__ __forceinline__ void attn_tile(const AttnPlan& p, const int u, uint8_
     const i32x4 kvres = rsrc_i(p.slice[j], (uint32_t)m * (uint32_t)W);
     const uint32_t kcol = (uint32_t)(hq + kvh) * kRowB, vcol = (uint32_t)(hq + p.hkv + kvh) * kRowB;
     // key tile t into stage st: K rows with chunk c at position c ^ (key & 15), V rows with
-    // chunk c at c ^ 2 (key & 3)
+    // chunk c at c ^ vswz(key)
     auto issue = [&](int t, int st) {
 #pragma unroll
       for (int i = 0; i < kLoads; ++i) {
         const bool isv = i >= kLoads / 2;
         const int piece = wave * (kLoads / 2) + (i % (kLoads / 2));
         const int row = 4 * piece + prow;
-        const int gch = isv ? (pch ^ (2 * (row & 3))) : (pch ^ (row & 15));
+        const int gch = isv ? (pch ^ vswz(row)) : (pch ^ (row & 15));
         const uint32_t voff =
             (uint32_t)(t * kAK + row) * (uint32_t)W + (isv ? vcol : kcol) + gch * 16;
         load_lds16(kvres, (uint32_t)uni((int)(lds0 + st * kStage + (isv ? kTileB : 0) + piece * 1024)),
@@ -311,7 +316,7 @@ __device__ __forceinline__ void attn_tile(const AttnPlan& p, const int u, uint8_
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           const int kr = 16 * kk + 4 * (g16 >> 1) + (i16 >> 2);
-          const int off = kr * kRowB + (((d >> 3) ^ (2 * (kr & 3))) * 16) + ((d >> 2) & 1) * 8;
+          const int off = kr * kRowB + (((d >> 3) ^ vswz(kr)) * 16) + ((d >> 2) & 1) * 8;
           const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + off));
           const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + off + 8 * kRowB));
           const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);

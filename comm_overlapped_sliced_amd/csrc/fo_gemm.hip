@@ -151,9 +151,21 @@ struct Cfg {
   static_assert(ER % 32 == 0 && BM % ER == 0, "epilogue block");
 };
 
-// swizzle of the 4 chunks of an A row and of the chunks of a W row
+// Swizzles of the 16-byte chunks of an LDS row, conflict-free whether the LDS serves 128 bytes
+// (32 banks) or 256 bytes (64 banks) per cycle.
+// A (64-byte rows, ds_read_b128: 8 or 16 rows at one chunk offset per cycle): the chunk XOR
+// ((row >> 1) ^ (row >> 3)) & 3 puts those rows on distinct 16-byte bank groups.
+// W (rows of B_ROW bytes, ds_read_b64_tr_b16 of 8 bytes per lane: per cycle 16 lanes = 4 k rows
+// x 2 chunks, or 32 lanes = 4 k rows x 4 chunks): a row of 256 or more bytes starts on bank 0,
+// so the chunks of row k are XORed with (0, 6, 12, 10)[k & 3], which gives the 4 rows distinct
+// bank groups under both widths. The earlier XOR with 2 (k & 3) left rows k and k + 1 on the
+// same 32-lane groups: rocprofv3 counted bank-conflict stalls in half of the LDS's busy cycles
+// of the 70B gate+up GEMM. 128-byte rows alternate bank halves by themselves and take 2 (k & 3).
 __device__ __forceinline__ int swz_a(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
-__device__ __forceinline__ int swz_b(int krow) { return (krow & 3) << 1; }
+template <int B_ROW>
+__device__ __forceinline__ int swz_b(int krow) {
+  return B_ROW >= 256 ? ((0xAC60 >> ((krow & 3) * 4)) & 15) : (krow & 3) << 1;
+}
 
 // Values the compiler cannot prove wave-uniform (they come out of VALU integer division) are
 // moved to scalar registers explicitly: buffer descriptors must live in SGPRs.
@@ -281,7 +293,7 @@ __device__ __forceinline__ void bf16_tile(const Plan& p, const int tile, uint8_t
   for (int j = 0; j < C::B_LOADS; ++j) {
     const int P = (wave * C::B_LOADS + j) * 1024 + lane * 16;
     const int kr = P / C::B_ROW;
-    const int n = ((((P % C::B_ROW) >> 4) ^ swz_b(kr))) * 8;
+    const int n = ((((P % C::B_ROW) >> 4) ^ swz_b<C::B_ROW>(kr))) * 8;
     int64_t wc;  // W column of tile column n
     bool ok;
     if constexpr (act) {
@@ -359,7 +371,7 @@ __device__ __forceinline__ void bf16_tile(const Plan& p, const int tile, uint8_t
     const uint8_t* sb = stage + C::A_BYTES;
     const int kr = 16 * kk + 8 * (g16 >> 1) + (i16 >> 2);
     const int n = wn * C::WTN + j * 32 + 16 * (g16 & 1) + 4 * (i16 & 3);
-    const int off = ((n >> 3) ^ swz_b(kr)) * 16 + ((n >> 2) & 1) * 8;
+    const int off = ((n >> 3) ^ swz_b<C::B_ROW>(kr)) * 16 + ((n >> 2) & 1) * 8;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sb + kr * C::B_ROW + off));
     const s16x4 hi =
         __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sb + (kr + 4) * C::B_ROW + off));
