@@ -357,9 +357,10 @@ __device__ __forceinline__ void attn_tile(const AttnPlan& p, const int u, uint8_
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();
     if (tid == 0) {
-      const int g = q0 / gr;
-      const int r1 = (g + 1) * gr < m ? (g + 1) * gr : m;
-      const uint32_t items = (uint32_t)(((r1 - g * gr + kAQ - 1) / kAQ) * hq);
+      const int og = (int)p.out_group_rows;
+      const int g = q0 / og;
+      const int r1 = (g + 1) * og < m ? (g + 1) * og : m;
+      const uint32_t items = (uint32_t)(((r1 - g * og + kAQ - 1) / kAQ) * hq);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
       uint32_t* cnt = p.done + s * kMaxGroups + g;
       const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
@@ -393,7 +394,10 @@ bool attn_plan_ok(const AttnPlan& p) {
   const int64_t W = (int64_t)(p.hq + 2 * p.hkv) * kRowB;
   if ((p.m + kAQ) * W >= ((int64_t)1 << 31) || (p.m + kAQ) * p.hq * kRowB >= ((int64_t)1 << 31))
     return false;
-  if (p.rel_tab != nullptr && p.done == nullptr) return false;
+  if (p.rel_tab != nullptr &&
+      (p.done == nullptr || p.out_groups < 1 || p.out_groups > kMaxGroups ||
+       p.out_group_rows < 1 || p.out_group_rows % kAQ != 0 || p.out_group_rows * p.out_groups < p.m))
+    return false;
   bool seen[FO_MAX_P] = {};
   for (int i = 0; i < p.P; ++i) {
     if (p.dispatch[i] < 0 || p.dispatch[i] >= p.P || seen[p.dispatch[i]]) return false;

@@ -194,6 +194,10 @@ struct AttnPlan {
   int64_t* const* rel_tab;
   uint32_t* done;                    // finished work items [slice][group] (zero between calls)
   int32_t send[FO_MAX_P];            // by slice id: 1 = its output rows are sent back
+  // the outgoing groups: rows of a slice released and sent together (a multiple of the 128-row
+  // query tile, independent of the arriving groups above)
+  int64_t out_group_rows;
+  int32_t out_groups;
 };
 bool attn_plan_ok(const AttnPlan& p);
 hipError_t launch_attn(const AttnPlan& p, hipStream_t stream);

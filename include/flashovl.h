@@ -260,10 +260,10 @@ fo_status fo_swiglu(const void* y, void* h, int64_t rows, int64_t inter, void* s
  *     when causal).
  * The second All-to-All returns each query slice's output rows (this rank's heads) to the rank
  * that owns those positions: with out_peer given, the rows of slice s != rank are copied to
- * out_peer[s] as soon as every work item of a row group of slice s has stored them, while the
- * later slices compute; in the FLASH order the own slice, whose rows stay, is dispatched last
- * (the Flash-RS order applied to the outgoing exchange). The call ends when every sent row has
- * landed.
+ * out_peer[s] as soon as every work item of a row group of slice s (the groups it arrived in)
+ * has stored them, while the later work computes; in the FLASH order the own slice, whose rows
+ * stay, is dispatched last (the Flash-RS order applied to the outgoing exchange). The call ends
+ * when every sent row has landed.
  *   qkv_local  device [m, (hq + 2*hkv) * head_dim] bf16: one row per token, [hq query heads |
  *              hkv key heads | hkv value heads], each head_dim values.
  *   qkv_peer   host array of P device pointers (entry [rank] ignored), each [m, row] like
