@@ -86,9 +86,13 @@ def parse():
     ap.add_argument("--no-exposure", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample (0 disables)")
+    ap.add_argument("--settle-seconds", type=float, default=1.5,
+                    help="right before the warm-up and timed steps, run the step back to back "
+                         "this long, so that the timed steps find the clocks and power at their "
+                         "steady state (the shader clock is sampled meanwhile; 0 disables)")
     ap.add_argument("--clock-seconds", type=float, default=1.5,
-                    help="after the timed region, run the step back to back this long while the "
-                         "shader clock is sampled (0 disables)")
+                    help="sample the SMU's shader clock, and after the timed region run the "
+                         "monolithic gate+up GEMM alone this long (0 disables both)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="also run one plain device copy of BYTES bytes after the warmup: the "
                          "reference that scales the HBM byte counters of a profiled run")
@@ -490,8 +494,8 @@ def main():
             out.append(a.elapsed_time(b) / reps)
         return statistics.median(out)
 
-    for _ in range(args.warmup):
-        step()
+    # one step first: the first call on a device sets up its engines and signals
+    step()
     fo.check(stream)
     if args.copy_calibration:
         n = args.copy_calibration
@@ -657,9 +661,34 @@ def main():
         step()
         fo.check(stream)
 
-    # ---- timed region -------------------------------------------------------------------
+    # ---- sustained window, then the timed region ------------------------------------------
+    # The same step back to back for about args.settle_seconds (the sampler reads the clock the
+    # chip sustains under it), then the W warm-up steps and the K timed steps without a break.
+    # After idling or a change of load (the sections above) the power controller overshoots and
+    # settles over ~40 steps (~35 ms: steps of 843, 1027, then 815 us), so timed steps started
+    # right after the attention sweep measured that transient instead of the steady state a
+    # training loop runs in.
     he = HipEvents()
     kevs = [((he.create(), he.create()), (he.create(), he.create())) for _ in range(args.steps)]
+    sustained = None
+    if args.settle_seconds > 0:
+        t_one = time.perf_counter()
+        step()
+        torch.cuda.synchronize()
+        t_one = time.perf_counter() - t_one
+        n_sus = max(1, int(args.settle_seconds / max(1e-4, t_one)))
+        torch.cuda.synchronize()
+        s0 = time.monotonic_ns()
+        for i in range(n_sus):
+            step()
+            if i % 64 == 63:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        s1 = time.monotonic_ns()
+        sustained = (s0, s1, n_sus)
+
+    for _ in range(args.warmup):
+        step()
     torch.cuda.synchronize()
     g0, g1 = ev(), ev()
     h0 = time.perf_counter()
@@ -672,25 +701,15 @@ def main():
     c1 = time.monotonic_ns()
     host_s = time.perf_counter() - h0
     fo.check(stream)
-    # the same step back to back for about args.clock_seconds, while the sampler reads the
-    # clock the chip sustains under this load (the timed region above is too short for more
-    # than a few samples)
     clock_timed = sampler.window(c0, c1)
     clock_sustained = None
-    if args.clock_seconds > 0:
-        n_sus = max(1, int(args.clock_seconds / max(1e-6, (time.perf_counter() - h0) / args.steps)))
-        torch.cuda.synchronize()
-        s0 = time.monotonic_ns()
-        for i in range(n_sus):
-            step()
-            if i % 64 == 63:
-                torch.cuda.synchronize()
-        torch.cuda.synchronize()
-        s1 = time.monotonic_ns()
-        fo.check(stream)
+    if sustained is not None:
+        s0, s1, n_sus = sustained
         clock_sustained = sampler.window(s0, s1)
         clock_sustained["steps"] = n_sus
         clock_sustained["us_per_step"] = round((s1 - s0) / 1e3 / n_sus, 1)
+        clock_sustained["when"] = "right before the warm-up and timed steps"
+    if args.clock_seconds > 0:
         # the monolithic gate+up GEMM alone, back to back, for the same time: the clock the chip
         # holds under a pure MFMA load, and the fraction of the peak at that clock
         n_g = max(1, int(args.clock_seconds / 0.4e-3))
@@ -713,7 +732,8 @@ def main():
         if clock_gemm.get("sclk_mhz"):
             clock_gemm["frac_at_sclk"] = round(clock_gemm["tflops"] /
                                                clocks.peak_at(clock_gemm["sclk_mhz"]), 4)
-        clock_sustained["gemm_only"] = clock_gemm
+        if clock_sustained is not None:
+            clock_sustained["gemm_only"] = clock_gemm
     sampler.stop()
     log(f"shader clock: timed region {clock_timed}; sustained {clock_sustained}")
     total_ms = g0.elapsed_time(g1)

@@ -318,9 +318,8 @@ fo_status mark_last(DevState* st, hipStream_t cs, hipEvent_t slot_ev) {
 
 fo_status launch_with_events(const fo::Plan& p, int in_dt, int tile, hipStream_t cs,
                              const fo_opts& o) {
-  if (o.kernel_events[0]) FO_HIP(hipEventRecord((hipEvent_t)o.kernel_events[0], cs));
-  FO_HIP(fo::launch_gemm(p, in_dt, tile, cs));
-  if (o.kernel_events[1]) FO_HIP(hipEventRecord((hipEvent_t)o.kernel_events[1], cs));
+  FO_HIP(fo::launch_gemm(p, in_dt, tile, cs, (hipEvent_t)o.kernel_events[0],
+                         (hipEvent_t)o.kernel_events[1]));
   return FO_OK;
 }
 
@@ -975,9 +974,7 @@ static int32_t attn_pair_half(int32_t P, int64_t m, int32_t hq, int32_t causal, 
 }
 
 static fo_status launch_attn_events(const fo::AttnPlan& p, hipStream_t cs, const fo_opts& o) {
-  if (o.kernel_events[0]) FO_HIP(hipEventRecord((hipEvent_t)o.kernel_events[0], cs));
-  FO_HIP(fo::launch_attn(p, cs));
-  if (o.kernel_events[1]) FO_HIP(hipEventRecord((hipEvent_t)o.kernel_events[1], cs));
+  FO_HIP(fo::launch_attn(p, cs, (hipEvent_t)o.kernel_events[0], (hipEvent_t)o.kernel_events[1]));
   return FO_OK;
 }
 

@@ -29,6 +29,7 @@
 //   groups whether the LDS serves 128 or 256 bytes per cycle).
 // - Two workgroups per CU (64 KB of LDS each): one workgroup's softmax overlaps the other's
 //   MFMAs.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -411,10 +412,10 @@ bool attn_plan_ok(const AttnPlan& p) {
   return true;
 }
 
-hipError_t launch_attn(const AttnPlan& p, hipStream_t s) {
+hipError_t launch_attn(const AttnPlan& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   if (!attn_plan_ok(p)) return hipErrorInvalidValue;
   const int64_t total = (int64_t)p.P * ((p.m + kAQ - 1) / kAQ) * p.hq;
-  hipLaunchKernelGGL(attn_kernel, dim3((unsigned)total), dim3(kThreads), 0, s, p);
+  hipExtLaunchKernelGGL(attn_kernel, dim3((unsigned)total), dim3(kThreads), 0, s, e0, e1, 0, p);
   return hipGetLastError();
 }
 

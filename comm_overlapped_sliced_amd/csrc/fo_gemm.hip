@@ -12,6 +12,7 @@
 // row-contiguous 16-byte accesses.
 //
 // fp32 path: a plain LDS-tiled fp32 FMA kernel (exact fp32 products, fp32 sums in k order).
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -854,14 +855,16 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(Plan p) {
   }
 }
 
+// e0 / e1 (may be null): events that take the kernel's own start and end times from its
+// dispatch (hipExtLaunchKernel), with no marker packets around it on the stream
 template <int BM, int BN>
-hipError_t launch_bf16(const Plan& p, int64_t grid, hipStream_t s) {
+hipError_t launch_bf16(const Plan& p, int64_t grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   if (p.act)
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, true>), dim3((unsigned)grid), dim3(kThreads), 0,
-                       s, p);
+    hipExtLaunchKernelGGL((gemm_bf16_kernel<BM, BN, true>), dim3((unsigned)grid), dim3(kThreads),
+                          0, s, e0, e1, 0, p);
   else
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, false>), dim3((unsigned)grid), dim3(kThreads), 0,
-                       s, p);
+    hipExtLaunchKernelGGL((gemm_bf16_kernel<BM, BN, false>), dim3((unsigned)grid), dim3(kThreads),
+                          0, s, e0, e1, 0, p);
   return hipGetLastError();
 }
 
@@ -1066,22 +1069,24 @@ static bool plan_ok(const Plan& p) {
   return true;
 }
 
-hipError_t launch_gemm(const Plan& p, int in_dt, int tile, hipStream_t s) {
+hipError_t launch_gemm(const Plan& p, int in_dt, int tile, hipStream_t s, hipEvent_t e0,
+                       hipEvent_t e1) {
   if (!plan_ok(p)) return hipErrorInvalidValue;
   int64_t grid = (int64_t)p.grid.npos * p.grid.tiles_m * p.grid.tiles_n;
   if (in_dt == FO_DT_F32) {
     // the fp32 kernel has no SwiGLU epilogue and adds its partials itself
     if (p.act || p.tail_units) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(gemm_f32_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+    hipExtLaunchKernelGGL(gemm_f32_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, e0, e1, 0,
+                          p);
     return hipGetLastError();
   }
   grid += p.tail_units;
   switch (tile) {
-    case FO_TILE_256x256: return launch_bf16<256, 256>(p, grid, s);
-    case FO_TILE_256x128: return launch_bf16<256, 128>(p, grid, s);
-    case FO_TILE_128x256: return launch_bf16<128, 256>(p, grid, s);
-    case FO_TILE_128x128: return launch_bf16<128, 128>(p, grid, s);
-    case FO_TILE_64x64: return launch_bf16<64, 64>(p, grid, s);
+    case FO_TILE_256x256: return launch_bf16<256, 256>(p, grid, s, e0, e1);
+    case FO_TILE_256x128: return launch_bf16<256, 128>(p, grid, s, e0, e1);
+    case FO_TILE_128x256: return launch_bf16<128, 256>(p, grid, s, e0, e1);
+    case FO_TILE_128x128: return launch_bf16<128, 128>(p, grid, s, e0, e1);
+    case FO_TILE_64x64: return launch_bf16<64, 64>(p, grid, s, e0, e1);
     default: return hipErrorInvalidValue;
   }
 }

@@ -102,7 +102,9 @@ int choose_tile(int P, int64_t m, int64_t K, int64_t N, bool out_f32, int n_cu);
 // kernel when in_dt is FO_DT_F32). A plan whose waits or releases point at no signal table, or
 // whose grid and row groups do not fit together, is refused (hipErrorInvalidValue) before
 // anything is launched.
-hipError_t launch_gemm(const Plan& plan, int in_dt, int tile, hipStream_t stream);
+// e0 / e1 (optional): events given the kernel's own start and end times
+hipError_t launch_gemm(const Plan& plan, int in_dt, int tile, hipStream_t stream,
+                       hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 
 // Zeroes `words` 32-bit words at p from a small kernel on `stream` (no hipMemsetAsync, so the
 // work can be captured in a HIP graph).
@@ -200,7 +202,8 @@ struct AttnPlan {
   int32_t out_groups;
 };
 bool attn_plan_ok(const AttnPlan& p);
-hipError_t launch_attn(const AttnPlan& p, hipStream_t stream);
+hipError_t launch_attn(const AttnPlan& p, hipStream_t stream, hipEvent_t e0 = nullptr,
+                       hipEvent_t e1 = nullptr);
 
 // Slice schedule: kind 0 = AG, 1 = RS; order = fo_order. Writes P ids.
 int slice_order(int kind, int order, int P, int rank, int32_t* out);

@@ -8,7 +8,10 @@ text summaries kept under profiles/.
   1. --kernel-trace --stats: per-kernel durations of the step (no exposure sweep, no oracle);
   2. --pmc FETCH_SIZE and 3. --pmc WRITE_SIZE (each a run of its own): HBM bytes per dispatch,
      with a plain copy of known size in the same run to scale the counters;
-  4. --pmc of the MFMA counters: bf16 MFMA operations (x 512 = flops) and MFMA-busy cycles.
+  4. --pmc of the MFMA counters: bf16 MFMA operations (x 512 = flops) and MFMA-busy cycles;
+  5. --memory-copy-trace: the emulated transfers (SDMA copies) of the step;
+  6. --kernel-trace --stats of the whole benchmark (every section), for its list of kernels.
+`--passes a,b` runs only those.
 It stops at the first pass that fails. rocprofv3 is the program started, with python after
 `--`; this module itself never touches the GPU.
 
@@ -20,7 +23,9 @@ Llama-3.1-70B gate+up share, Flash-RS on the down share):
     counters' scale from the copy, the algorithmic bytes, and the sha256 of the kernel source
     they were taken on: bench.py reports them only while the source is unchanged),
   - gemm_bf16_kernel_l70b_mlp_step_mfma_counters.md (counted MFMA flops against 2MNK, busy
-    cycles per SIMD and the busy share at the nominal and at the sampled shader clock).
+    cycles per SIMD and the busy share at the nominal and at the sampled shader clock);
+  - sdma_copies_l70b_mlp_step_copy_trace.md and all_kernels_l70b_bench_kernel_trace.md from
+    passes 5 and 6, when their outputs are there.
 """
 from __future__ import annotations
 
@@ -40,18 +45,31 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 KERNEL_SRC = os.path.join(HERE, "csrc", "fo_gemm.hip")
 CALIB_BYTES = 268435456
+COUNTER_STEPS = 3  # timed steps of the counter passes
 N_SIMD = 1024  # 256 CUs x 4 SIMDs
 
-BENCH_ARGS = ["bench.py", "--no-exposure", "--cpu-seconds", "0", "--clock-seconds", "0"]
+# the step alone: no exposure sections, no oracle, no clock sampler; a short back-to-back window
+# before the timed steps where timing matters (trace, copies), none where only counts do
+STEP_ARGS = ["bench.py", "--no-exposure", "--cpu-seconds", "0", "--clock-seconds", "0"]
 PASSES = [
-    # (name, rocprofv3 options, bench options, time limit in seconds)
-    ("trace", ["--kernel-trace", "--stats"], ["--steps", "10", "--warmup", "3"], 240),
+    # (name, rocprofv3 options, bench argv, time limit in seconds)
+    ("trace", ["--kernel-trace", "--stats"],
+     STEP_ARGS + ["--steps", "10", "--warmup", "3", "--settle-seconds", "0.5"], 240),
     ("fetch", ["--pmc", "FETCH_SIZE", "--kernel-trace"],
-     ["--steps", "3", "--warmup", "1", "--copy-calibration", str(CALIB_BYTES)], 180),
+     STEP_ARGS + ["--steps", str(COUNTER_STEPS), "--warmup", "1", "--settle-seconds", "0",
+                  "--copy-calibration", str(CALIB_BYTES)], 180),
     ("write", ["--pmc", "WRITE_SIZE", "--kernel-trace"],
-     ["--steps", "3", "--warmup", "1", "--copy-calibration", str(CALIB_BYTES)], 180),
+     STEP_ARGS + ["--steps", str(COUNTER_STEPS), "--warmup", "1", "--settle-seconds", "0",
+                  "--copy-calibration", str(CALIB_BYTES)], 180),
     ("mfma", ["--pmc", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES",
-              "--kernel-trace"], ["--steps", "3", "--warmup", "1"], 180),
+              "--kernel-trace"],
+     STEP_ARGS + ["--steps", str(COUNTER_STEPS), "--warmup", "1", "--settle-seconds", "0"], 180),
+    ("copies", ["--kernel-trace", "--memory-copy-trace", "--stats"],
+     STEP_ARGS + ["--steps", "10", "--warmup", "3", "--settle-seconds", "0.2"], 240),
+    # the whole benchmark (every section and sweep), for the list of every kernel it launches
+    ("bench", ["--kernel-trace", "--stats"],
+     ["bench.py", "--cpu-seconds", "0", "--clock-seconds", "0", "--steps", "10", "--warmup", "3",
+      "--settle-seconds", "0.5"], 420),
 ]
 
 # the step's two GEMM launches: (kind, call, M, K, N, algorithmic read bytes, write bytes)
@@ -68,7 +86,7 @@ def command(name: str, raw: str, python: str = sys.executable) -> list:
     for n, opts, bargs, _ in PASSES:
         if n == name:
             return (["rocprofv3", *opts, "--output-format", "csv", "-d",
-                     os.path.join(raw, n), "-o", n, "--", python, *BENCH_ARGS, *bargs])
+                     os.path.join(raw, n), "-o", n, "--", python, *bargs])
     raise KeyError(name)
 
 
@@ -76,10 +94,12 @@ def command_text(name: str, raw: str) -> str:
     return " ".join(command(name, raw, "python3"))
 
 
-def run(raw: str) -> int:
+def run(raw: str, only=None) -> int:
     os.makedirs(raw, exist_ok=True)
     env = dict(os.environ, TMPDIR="/tmp")
     for name, _, _, limit in PASSES:
+        if only and name not in only:
+            continue
         cmd = command(name, raw)
         print(f"pass {name}: {' '.join(cmd)}", flush=True)
         with open(os.path.join(raw, f"{name}.log"), "w") as log:
@@ -181,15 +201,15 @@ def summarize(raw: str, out_dir: str, sclk_mhz: float | None = None) -> dict:
 
 Flash-AG: fo_ag_gemm M=4096 K=8192 N=7168 bf16, `{_short(names['ag'])}`.
 Flash-RS: fo_gemm_rs M=4096 K=3584 N=8192 with seven fp32 partials, `{_short(names['rs'])}`.
-Emulated transfers on SDMA engines, one per peer; each GEMM launch's duration includes its
-in-kernel waits for them.
+Emulated transfers on SDMA engines, one link per peer, each link an engine pair with every
+transfer split across it; each GEMM launch's duration includes its in-kernel waits for them.
 
 Command (from the repository root, TMPDIR=/tmp; `python -m comm_overlapped_sliced_amd.profiling run`
 runs it as its first pass):
 
     {cmd}
 
-Kernel statistics (3 warm-up + 10 timed steps):
+Kernel statistics (the 0.5 s back-to-back window, 3 warm-up and 10 timed steps):
 
 {chr(10).join(rows)}
 
@@ -216,7 +236,8 @@ fo_gemm.hip sha256: {sha}
     for kind, name in names.items():
         fv = [c["FETCH_SIZE"] for d, (n, _, c) in sorted(fetch.items()) if n == name]
         wv = [c["WRITE_SIZE"] for d, (n, _, c) in sorted(write.items()) if n == name]
-        ft, wt = statistics.mean(fv[1:] or fv), statistics.mean(wv[1:] or wv)
+        # the timed launches: the last COUNTER_STEPS of the run
+        ft, wt = statistics.mean(fv[-COUNTER_STEPS:]), statistics.mean(wv[-COUNTER_STEPS:])
         b = ft * 1024 * fs + wt * 1024 * ws
         call, M, K, N, ar, aw = STEP[kind]
         traffic[kind] = {"kernel": _short(name), "kernel_source_sha256": sha,
@@ -224,7 +245,7 @@ fo_gemm.hip sha256: {sha}
                          "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
                          "bytes_per_launch": int(b), "algorithmic_read_bytes": ar,
                          "algorithmic_write_bytes": aw,
-                         "launches": f"{max(1, len(fv) - 1)} timed (the warm-up launch excluded)"}
+                         "launches": f"the {COUNTER_STEPS} timed ones of {len(fv)}"}
         trows.append(f"| `{_short(name)}` ({call}) | {', '.join(str(round(x)) for x in fv)} | "
                      f"{', '.join(str(round(x)) for x in wv)} | {b / 1e6:.1f} MB | "
                      f"{(ar + aw) / 1e6:.1f} MB | {b / (ar + aw):.2f} |")
@@ -242,7 +263,7 @@ Calibration: the same runs copy {CALIB_BYTES} bytes with one plain copy kernel
 (`__amd_rocclr_copyBuffer`), whose counters read FETCH_SIZE {cf:.0f} KiB and WRITE_SIZE {cw:.0f} KiB;
 scale factors (true bytes / counter bytes): fetch {fs:.4f}, write {ws:.4f}.
 
-| kernel | FETCH_SIZE KiB per launch (warm-up, timed) | WRITE_SIZE KiB per launch | scaled bytes per timed launch | algorithmic read + write bytes | ratio |
+| kernel | FETCH_SIZE KiB per launch (set-up, warm-up, timed) | WRITE_SIZE KiB per launch | scaled bytes per timed launch | algorithmic read + write bytes | ratio |
 |---|---|---|---|---|---|
 {chr(10).join(trows)}
 
@@ -294,19 +315,116 @@ fo_gemm.hip sha256: {sha}
     return traffic
 
 
+def _col(row: dict, *names):
+    """The first of `names` that the CSV row has (rocprofv3's column names vary by version)."""
+    for n in names:
+        if n in row and row[n] != "":
+            return row[n]
+    return None
+
+
+def summarize_copies(raw: str, out_dir: str) -> None:
+    """sdma_copies_l70b_mlp_step_copy_trace.md: every emulated transfer of the step's calls,
+    grouped by direction and size."""
+    d = os.path.join(raw, "copies")
+    copy_csv = _one(os.path.join(d, "**", "*memory_copy_trace.csv"))
+    groups = collections.defaultdict(list)
+    with open(copy_csv) as f:
+        for r in csv.DictReader(f):
+            size = _col(r, "Size", "Bytes", "Copy_Size", "Memory_Copy_Size")
+            kind = _col(r, "Direction", "Operation", "Kind") or "?"
+            t = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            groups[(kind.replace("MEMORY_COPY_", "").lower(), int(size) if size else -1)].append(t)
+    rows = ["| direction | bytes per copy | copies | median us | p10 / p90 us | median GB/s per copy |",
+            "|---|---|---|---|---|---|"]
+    for (kind, size), ts in sorted(groups.items(), key=lambda kv: (kv[0][0], kv[0][1])):
+        ts = sorted(ts)
+        med = statistics.median(ts)
+        p10, p90 = ts[len(ts) // 10], ts[(9 * len(ts)) // 10]
+        gbs = f"{size / (med * 1e-6) / 1e9:.1f}" if size > 0 and med > 0 else "n/a"
+        rows.append(f"| {kind} | {size if size >= 0 else 'n/a'} | {len(ts)} | {med:.1f} | "
+                    f"{p10:.1f} / {p90:.1f} | {gbs} |")
+    timed = _timed_line(os.path.join(raw, "copies.log"))
+    text = f"""# Emulated transfers: SDMA copy trace, Llama-3.1-70B MLP step (P=8, rank 0)
+
+Command (from the repository root, TMPDIR=/tmp; `python -m comm_overlapped_sliced_amd.profiling
+run --passes copies`):
+
+    {command_text('copies', raw)}
+
+Each link is an engine pair (engines 2k and 2k+1) and every transfer is cut in two halves, one
+per engine, so one row group of one peer is two copies: Flash-AG 7 peers x 2 row groups of 256
+rows x 8192 bf16 (4 MiB, two 2 MiB halves); Flash-RS 7 peers x 4 row groups of 128 rows x 8192
+fp32 (4 MiB, two 2 MiB halves). Host-to-device copies are PyTorch's staging of the inputs; the
+small device copies at start-up are the engines' warm-up. The counts cover every step of the run
+(the back-to-back window, the warm-up and the timed steps).
+
+{chr(10).join(rows)}
+
+Copy tracing slows the run; this run's timed steps: {timed}.
+"""
+    with open(os.path.join(out_dir, "sdma_copies_l70b_mlp_step_copy_trace.md"), "w") as f:
+        f.write(text)
+
+
+def summarize_bench(raw: str, out_dir: str) -> None:
+    """all_kernels_l70b_bench_kernel_trace.md: every kernel the whole benchmark launches."""
+    d = os.path.join(raw, "bench")
+    stats_csv = _one(os.path.join(d, "**", "*kernel_stats.csv"))
+    rows = ["| kernel | launches | total us | average us | min us | max us | % |",
+            "|---|---|---|---|---|---|---|"]
+    with open(stats_csv) as f:
+        for r in csv.DictReader(f):
+            pct = r.get("Percentage")
+            pct = f"{float(pct):.2f}" if pct else "n/a"
+            rows.append(f"| `{_short(r['Name'])}` | {r['Calls']} | "
+                        f"{float(r['TotalDurationNs']) / 1e3:.1f} | {float(r['AverageNs']) / 1e3:.1f} | "
+                        f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {pct} |")
+    timed = _timed_line(os.path.join(raw, "bench.log"))
+    sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    text = f"""# rocprofv3 kernel trace of the whole benchmark run (all sections), Llama-3.1-70B shares
+
+Every kernel bench.py launches: the sliced GEMMs (Flash-AG, Flash-RS, the monolithic reference,
+the SwiGLU-epilogue form), the query-split attention (`attn_kernel`), the SwiGLU activation, the
+data-slicing reduce, and the small wait/release kernels of the transfer-only timings. The GEMM
+rows mix every variant the benchmark times (slices resident or arriving, one engine pair per
+peer or one link, ranks 0 and 7, the 1K-16K-token and 405B workloads), so only the attention and
+activation rows come close to single-configuration figures.
+
+Command (from the repository root, TMPDIR=/tmp; `python -m comm_overlapped_sliced_amd.profiling
+run --passes bench`):
+
+    {command_text('bench', raw)}
+
+{chr(10).join(rows)}
+
+The same run's timed steps: {timed}.
+
+fo_gemm.hip sha256: {sha}
+"""
+    with open(os.path.join(out_dir, "all_kernels_l70b_bench_kernel_trace.md"), "w") as f:
+        f.write(text)
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(prog="python -m comm_overlapped_sliced_amd.profiling")
     sub = ap.add_subparsers(dest="cmd", required=True)
     r = sub.add_parser("run")
     r.add_argument("--raw", default="gpurun_out/prof")
+    r.add_argument("--passes", default="", help="comma-separated pass names (default: all)")
     s = sub.add_parser("summarize")
     s.add_argument("--raw", default="gpurun_out/prof")
     s.add_argument("--out", default="profiles")
     s.add_argument("--sclk-mhz", type=float, default=None)
     a = ap.parse_args(argv)
     if a.cmd == "run":
-        return run(a.raw)
-    print(json.dumps(summarize(a.raw, a.out, a.sclk_mhz), indent=1))
+        return run(a.raw, [p for p in a.passes.split(",") if p])
+    if os.path.isdir(os.path.join(a.raw, "trace")):
+        print(json.dumps(summarize(a.raw, a.out, a.sclk_mhz), indent=1))
+    if os.path.isdir(os.path.join(a.raw, "copies")):
+        summarize_copies(a.raw, a.out)
+    if os.path.isdir(os.path.join(a.raw, "bench")):
+        summarize_bench(a.raw, a.out)
     return 0
 
 

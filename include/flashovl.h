@@ -123,8 +123,10 @@ typedef struct fo_opts {
                                the own chunk (RS) last, each whole. 1 = whole slices, the page's
                                slice-by-slice order; 0 = one group per tile row, at most
                                FO_MAX_GROUPS */
-  void* kernel_events[2];   /* optional hipEvent_t pair recorded on the compute stream right
-                               before and right after the GEMM kernel launch (profiling) */
+  void* kernel_events[2];   /* optional hipEvent_t pair (created by the caller) that the GEMM
+                               kernel's launch gives its own start and end times
+                               (hipExtLaunchKernel; no marker packets on the stream): for
+                               hipEventElapsedTime, not for ordering other work (profiling) */
   int32_t epilogue;         /* fo_epilogue (fo_ag_gemm only; else FO_ERR_INVALID_ARG) */
   int32_t k_chunks;         /* fo_ag_gemm only (else it must be 0 or 1): 0 or 1 = every X slice
                                row-major [m, K]. c in 2..FO_MAX_GROUPS = every X slice (x_local,
