@@ -53,8 +53,7 @@ N_SIMD = 1024  # 256 CUs x 4 SIMDs
 STEP_ARGS = ["bench.py", "--no-exposure", "--cpu-seconds", "0", "--clock-seconds", "0"]
 PASSES = [
     # (name, rocprofv3 options, bench argv, time limit in seconds)
-    ("trace", ["--kernel-trace", "--stats"],
-     STEP_ARGS + ["--steps", "10", "--warmup", "3", "--settle-seconds", "0.5"], 240),
+    ("trace", ["--kernel-trace", "--stats"], STEP_ARGS + ["--steps", "10", "--warmup", "3"], 240),
     ("fetch", ["--pmc", "FETCH_SIZE", "--kernel-trace"],
      STEP_ARGS + ["--steps", str(COUNTER_STEPS), "--warmup", "1", "--settle-seconds", "0",
                   "--copy-calibration", str(CALIB_BYTES)], 180),
@@ -209,7 +208,7 @@ runs it as its first pass):
 
     {cmd}
 
-Kernel statistics (the 0.5 s back-to-back window, 3 warm-up and 10 timed steps):
+Kernel statistics (the back-to-back window, 3 warm-up and 10 timed steps):
 
 {chr(10).join(rows)}
 
@@ -323,27 +322,49 @@ def _col(row: dict, *names):
     return None
 
 
+# the step's device-to-device copies, in issue order: Flash-AG 7 peers x 2 row groups x 2 halves,
+# then Flash-RS 7 peers x 4 row groups x 2 halves (each link an engine pair, every transfer cut
+# in two halves); the engines' warm-up copies come before the first step
+STEP_COPIES = (("Flash-AG row-group half (128 of its 256 rows x 8192 bf16)", 7 * 2 * 2, 2 << 20),
+               ("Flash-RS row-group half (64 of its 128 rows x 8192 fp32)", 7 * 4 * 2, 2 << 20))
+
+
 def summarize_copies(raw: str, out_dir: str) -> None:
-    """sdma_copies_l70b_mlp_step_copy_trace.md: every emulated transfer of the step's calls,
-    grouped by direction and size."""
+    """sdma_copies_l70b_mlp_step_copy_trace.md: the emulated transfers of the step's calls. The
+    trace has no byte counts, so each copy is named by its place in the step's issue order."""
     d = os.path.join(raw, "copies")
     copy_csv = _one(os.path.join(d, "**", "*memory_copy_trace.csv"))
-    groups = collections.defaultdict(list)
+    d2d, h2d = [], []
     with open(copy_csv) as f:
         for r in csv.DictReader(f):
-            size = _col(r, "Size", "Bytes", "Copy_Size", "Memory_Copy_Size")
-            kind = _col(r, "Direction", "Operation", "Kind") or "?"
-            t = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-            groups[(kind.replace("MEMORY_COPY_", "").lower(), int(size) if size else -1)].append(t)
-    rows = ["| direction | bytes per copy | copies | median us | p10 / p90 us | median GB/s per copy |",
+            t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+            kind = _col(r, "Direction", "Operation", "Kind") or ""
+            (d2d if "DEVICE_TO_DEVICE" in kind else h2d).append((t0, t1))
+    d2d.sort()
+    per_step = sum(n for _, n, _ in STEP_COPIES)
+    warm = len(d2d) % per_step
+    classes = collections.defaultdict(list)
+    classes[("engine warm-up at start-up", None)] = [b - a for a, b in d2d[:warm]]
+    for i, (a, b) in enumerate(d2d[warm:]):
+        k = i % per_step
+        for name, n, size in STEP_COPIES:
+            if k < n:
+                classes[(name, size)].append(b - a)
+                break
+            k -= n
+    classes[("host to device (input staging)", None)] = [b - a for a, b in h2d]
+    rows = ["| copy | bytes (by construction) | copies | median us | p10 / p90 us | GB/s per engine at the median |",
             "|---|---|---|---|---|---|"]
-    for (kind, size), ts in sorted(groups.items(), key=lambda kv: (kv[0][0], kv[0][1])):
-        ts = sorted(ts)
+    for (name, size), ts in classes.items():
+        if not ts:
+            continue
+        ts = sorted(t / 1e3 for t in ts)
         med = statistics.median(ts)
         p10, p90 = ts[len(ts) // 10], ts[(9 * len(ts)) // 10]
-        gbs = f"{size / (med * 1e-6) / 1e9:.1f}" if size > 0 and med > 0 else "n/a"
-        rows.append(f"| {kind} | {size if size >= 0 else 'n/a'} | {len(ts)} | {med:.1f} | "
-                    f"{p10:.1f} / {p90:.1f} | {gbs} |")
+        gbs = f"{size / (med * 1e-6) / 1e9:.1f}" if size and med > 0 else "n/a"
+        rows.append(f"| {name} | {size or 'n/a'} | {len(ts)} | {med:.1f} | {p10:.1f} / {p90:.1f} "
+                    f"| {gbs} |")
+    steps = (len(d2d) - warm) / per_step
     timed = _timed_line(os.path.join(raw, "copies.log"))
     text = f"""# Emulated transfers: SDMA copy trace, Llama-3.1-70B MLP step (P=8, rank 0)
 
@@ -352,16 +373,23 @@ run --passes copies`):
 
     {command_text('copies', raw)}
 
-Each link is an engine pair (engines 2k and 2k+1) and every transfer is cut in two halves, one
-per engine, so one row group of one peer is two copies: Flash-AG 7 peers x 2 row groups of 256
-rows x 8192 bf16 (4 MiB, two 2 MiB halves); Flash-RS 7 peers x 4 row groups of 128 rows x 8192
-fp32 (4 MiB, two 2 MiB halves). Host-to-device copies are PyTorch's staging of the inputs; the
-small device copies at start-up are the engines' warm-up. The counts cover every step of the run
-(the back-to-back window, the warm-up and the timed steps).
+Each link is an engine pair (engines 2k and 2k+1, which share one bandwidth) and every transfer
+is cut in two halves, one per engine of the pair, started together. One row group of one peer is
+therefore two ~2 MiB copies: per step, Flash-AG 7 peers x 2 row groups of 256 rows x 8192 bf16
+and Flash-RS 7 peers x 4 row groups of 128 rows x 8192 fp32, {per_step} copies. This rocprofv3
+trace carries no byte counts: each copy is classed by its place in that issue order (the
+warm-up copies come first; {steps:.0f} steps traced: the first call, the back-to-back window,
+the warm-up and the timed steps).
 
 {chr(10).join(rows)}
 
-Copy tracing slows the run; this run's timed steps: {timed}.
+A pair moves one 4 MiB row group in about the time of one half; the two halves of a link share
+its bandwidth, so the rate per link is about twice the per-engine figure.
+
+rocprofv3's copy tracing logs "bad original signal value in async_copy_handler" for these copies:
+the two halves of a transfer count down one completion signal, which its handler does not
+expect. The run completed, and its in-kernel waits reported no error. Copy tracing also slows
+the step; this run's timed steps: {timed}.
 """
     with open(os.path.join(out_dir, "sdma_copies_l70b_mlp_step_copy_trace.md"), "w") as f:
         f.write(text)
