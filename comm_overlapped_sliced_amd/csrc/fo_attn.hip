@@ -228,20 +228,41 @@ __device__ __forceinline__ void attn_tile(const AttnPlan& p, const int u, uint8_
       const uint8_t* kt = lds + st * kStage;
       const uint8_t* vt = kt + kTileB;
 
-      // S^T = K Q^T for 64 keys (two fragments of 32) x this wave's 32 queries
+      // S^T = K Q^T for 64 keys (two fragments of 32) x this wave's 32 queries; the two
+      // fragments' products alternate, so that consecutive MFMAs never wait on each other
       f32x16 sacc[2];
 #pragma unroll
-      for (int f = 0; f < 2; ++f) {
+      for (int f = 0; f < 2; ++f)
 #pragma unroll
         for (int v = 0; v < 16; ++v) sacc[f][v] = 0.f;
+      // K fragments one head-dim step ahead of their MFMAs
+      auto kfrag = [&](int kd, int f) {
         const int key = 32 * f + l32;
+        const int ch = (2 * kd + lh) ^ (key & 15);
+        return __builtin_bit_cast(bf16x8, *(const uint4*)(kt + key * kRowB + ch * 16));
+      };
+      bf16x8 a[2][2];
+      a[0][0] = kfrag(0, 0);
+      a[0][1] = kfrag(0, 1);
 #pragma unroll
-        for (int kd = 0; kd < kAD / 16; ++kd) {
-          const int ch = (2 * kd + lh) ^ (key & 15);
-          const bf16x8 a = __builtin_bit_cast(bf16x8, *(const uint4*)(kt + key * kRowB + ch * 16));
-          sacc[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kd], sacc[f], 0, 0, 0);
+      for (int kd = 0; kd < kAD / 16; ++kd) {
+        if (kd + 1 < kAD / 16) {
+          a[(kd + 1) & 1][0] = kfrag(kd + 1, 0);
+          a[(kd + 1) & 1][1] = kfrag(kd + 1, 1);
         }
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+          sacc[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kd & 1][f], qf[kd], sacc[f], 0, 0, 0);
       }
+      // keep that order: the first two steps' reads, then per step its two MFMAs and the next
+      // step's two reads (the scheduler would otherwise wait for each step's reads in turn)
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int kd = 0; kd + 1 < kAD / 16; ++kd) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
 
       // online softmax in base 2 on the raw scores (the running max mrow in raw units, the scale
       // folded into the exponent's fma); value v of fragment f is key 32 f + 8 (v / 4) + 4 lh +
@@ -310,20 +331,24 @@ __device__ __forceinline__ void attn_tile(const AttnPlan& p, const int u, uint8_
         pb[kk] = __builtin_bit_cast(bf16x8, w);
       }
       // O^T += V^T P^T: A operand row d = 32 i + l32 with the keys of step kk in the same order,
-      // from two transpose reads (keys 16 kk + 4 lh + 0..3, then 8 further)
+      // from two transpose reads (keys 16 kk + 4 lh + 0..3, then 8 further); per key step the
+      // four row blocks' reads are issued together and their MFMAs, on four accumulators, follow
 #pragma unroll
-      for (int i = 0; i < kAD / 32; ++i) {
-        const int d = 32 * i + 16 * (g16 & 1) + 4 * (i16 & 3);
+      for (int kk = 0; kk < 4; ++kk) {
+        const int kr = 16 * kk + 4 * (g16 >> 1) + (i16 >> 2);
+        bf16x8 a[kAD / 32];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const int kr = 16 * kk + 4 * (g16 >> 1) + (i16 >> 2);
+        for (int i = 0; i < kAD / 32; ++i) {
+          const int d = 32 * i + 16 * (g16 & 1) + 4 * (i16 & 3);
           const int off = kr * kRowB + (((d >> 3) ^ vswz(kr)) * 16) + ((d >> 2) & 1) * 8;
           const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + off));
           const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + off + 8 * kRowB));
           const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
-          const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(l2.x, l2.y, h2.x, h2.y));
-          oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kk], oacc[i], 0, 0, 0);
+          a[i] = __builtin_bit_cast(bf16x8, make_uint4(l2.x, l2.y, h2.x, h2.y));
         }
+#pragma unroll
+        for (int i = 0; i < kAD / 32; ++i)
+          oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], pb[kk], oacc[i], 0, 0, 0);
       }
     }
     lds_barrier();  // every wave is done with the stages before the next slice refills them
