@@ -59,6 +59,7 @@ constexpr int kPieces = kTileB / 1024;     // 1 KB loads per tile (16), 4 per wa
 constexpr int kLoads = 2 * kPieces / 4;    // loads per wave per key tile (K and V): 8
 constexpr int kOutStride = kRowB + 16;     // output staging row (bytes): 16-byte aligned, padded
 constexpr float kNegBig = -1.0e30f;        // "minus infinity" that keeps exp2 finite
+constexpr float kLazyLog2 = 8.0f;          // growth of a row max (log2 units) that moves it
 constexpr int kRsrcWord3 = 0x00020000;     // raw buffer, 32-bit data format
 static_assert(4 * 32 * kOutStride <= kStages * kStage, "output staging fits in the ring");
 
@@ -264,38 +265,39 @@ __device__ __forceinline__ void attn_tile(const AttnPlan& p, const int u, uint8_
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
 
-      // online softmax in base 2 on the raw scores (the running max mrow in raw units, the scale
-      // folded into the exponent's fma); value v of fragment f is key 32 f + 8 (v / 4) + 4 lh +
-      // v % 4. Only a tile that runs past the slice's keys or, under causal masking, past this
-      // wave's first query (the diagonal of the own slice) needs the mask (wave-uniform test).
+      // online softmax in base 2 on the raw scores (the reference max mrow in raw units, the
+      // scale folded into the exponent's fma); value v of fragment f is key 32 f + 8 (v / 4) +
+      // 4 lh + v % 4. Only a tile that runs past the slice's keys or, under causal masking, past
+      // this wave's first query (the diagonal of the own slice) needs the mask (wave-uniform
+      // test); masked scores are overwritten in place.
       const int kb = t * kAK;
       const bool full = uni((kb + kAK <= m) &&
                             (!p.causal || j < s || kb + kAK - 1 <= q0 + 32 * wave) ? 1 : 0) != 0;
-      float mx = kNegBig;
-      float sv[2][16];
-      if (full) {
-#pragma unroll
-        for (int f = 0; f < 2; ++f)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            sv[f][v] = sacc[f][v];
-            mx = fmaxf(mx, sv[f][v]);
-          }
-      } else {
+      if (!full) {
 #pragma unroll
         for (int f = 0; f < 2; ++f)
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int kj = kb + 32 * f + 8 * (v >> 2) + 4 * lh + (v & 3);
             const bool ok = kj < m && (!p.causal || kpos0 + kj <= qpos);
-            sv[f][v] = ok ? sacc[f][v] : kNegBig;
-            mx = fmaxf(mx, sv[f][v]);
+            if (!ok) sacc[f][v] = kNegBig;
           }
       }
+      float mx = kNegBig;
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[f][v]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(mrow, mx);
+      // A lane moves its reference max only when the tile's max exceeds it by more than
+      // kLazyLog2 in the exponent: below that its probabilities are at most 2^kLazyLog2, which
+      // fp32 and bf16 hold with their usual relative rounding, and softmax does not depend on
+      // the reference (the sum lrow uses the same one). The output rows then need rescaling
+      // only when some lane of the wave moved it, which after a query's first keys is rare.
       const float sc = p.scale_log2;
-      const float alpha = __builtin_amdgcn_exp2f((mrow - mnew) * sc);
+      const bool grow = (mx - mrow) * sc > kLazyLog2;
+      const float mnew = grow ? mx : mrow;
+      const float alpha = grow ? __builtin_amdgcn_exp2f((mrow - mnew) * sc) : 1.f;
       const float mns = -mnew * sc;
       float psum = 0.f;
 #pragma unroll
@@ -303,14 +305,12 @@ __device__ __forceinline__ void attn_tile(const AttnPlan& p, const int u, uint8_
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           // a masked score (kNegBig) gives exp2 of about -1e29: exactly 0
-          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[f][v], sc, mns));
-          sv[f][v] = e;
+          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[f][v], sc, mns));
+          sacc[f][v] = e;
           psum += e;
         }
       lrow = lrow * alpha + psum;
-      // the output rows are rescaled only when some running max of the wave grew (alpha = 1
-      // exactly otherwise, so skipping the multiplies changes no bit)
-      if (__ballot(mnew > mrow) != 0) {
+      if (__ballot(grow) != 0) {
 #pragma unroll
         for (int i = 0; i < kAD / 32; ++i)
 #pragma unroll
@@ -324,10 +324,10 @@ __device__ __forceinline__ void attn_tile(const AttnPlan& p, const int u, uint8_
       for (int kk = 0; kk < 4; ++kk) {
         const int f = kk >> 1, b = 8 * (kk & 1);
         uint4 w;
-        w.x = cvt_bf16x2(sv[f][b + 0], sv[f][b + 1]);
-        w.y = cvt_bf16x2(sv[f][b + 2], sv[f][b + 3]);
-        w.z = cvt_bf16x2(sv[f][b + 4], sv[f][b + 5]);
-        w.w = cvt_bf16x2(sv[f][b + 6], sv[f][b + 7]);
+        w.x = cvt_bf16x2(sacc[f][b + 0], sacc[f][b + 1]);
+        w.y = cvt_bf16x2(sacc[f][b + 2], sacc[f][b + 3]);
+        w.z = cvt_bf16x2(sacc[f][b + 4], sacc[f][b + 5]);
+        w.w = cvt_bf16x2(sacc[f][b + 6], sacc[f][b + 7]);
         pb[kk] = __builtin_bit_cast(bf16x8, w);
       }
       // O^T += V^T P^T: A operand row d = 32 i + l32 with the keys of step kk in the same order,
