@@ -13,6 +13,7 @@ exposed-transfer decomposition, and the CPU oracle timed on a bounded sample.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -444,6 +445,12 @@ def main():
     ref_y_rs = torch.empty((rs_case.M, rs_case.N), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     log(f"inputs ready in {time.time() - t0:.1f} s")
+    # Python's collector: a full collection of this process's heap takes ~50 ms on the host,
+    # long enough to starve the GPU for dozens of steps; the objects made so far are frozen
+    # out of later collections, and the collector is off from the back-to-back window to the end
+    # of the timed steps
+    gc.collect()
+    gc.freeze()
 
     def ev():
         return torch.cuda.Event(enable_timing=True)
@@ -670,6 +677,8 @@ def main():
     # training loop runs in.
     he = HipEvents()
     kevs = [((he.create(), he.create()), (he.create(), he.create())) for _ in range(args.steps)]
+    gc.collect()
+    gc.disable()
     sustained = None
     if args.settle_seconds > 0:
         t_one = time.perf_counter()
@@ -700,6 +709,7 @@ def main():
     torch.cuda.synchronize()
     c1 = time.monotonic_ns()
     host_s = time.perf_counter() - h0
+    gc.enable()
     fo.check(stream)
     clock_timed = sampler.window(c0, c1)
     clock_sustained = None
