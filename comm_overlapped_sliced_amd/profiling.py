@@ -10,7 +10,8 @@ text summaries kept under profiles/.
      with a plain copy of known size in the same run to scale the counters;
   4. --pmc of the MFMA counters: bf16 MFMA operations (x 512 = flops) and MFMA-busy cycles;
   5. --memory-copy-trace: the emulated transfers (SDMA copies) of the step;
-  6. --kernel-trace --stats of the whole benchmark (every section), for its list of kernels.
+  6. --kernel-trace --stats of the whole benchmark (every section), for its list of kernels;
+  7.-9. the resident attention (`attn_run`): kernel trace, then two SQ counter passes.
 `--passes a,b` runs only those.
 It stops at the first pass that fails. rocprofv3 is the program started, with python after
 `--`; this module itself never touches the GPU.
@@ -25,7 +26,8 @@ Llama-3.1-70B gate+up share, Flash-RS on the down share):
   - gemm_bf16_kernel_l70b_mlp_step_mfma_counters.md (counted MFMA flops against 2MNK, busy
     cycles per SIMD and the busy share at the nominal and at the sampled shader clock);
   - sdma_copies_l70b_mlp_step_copy_trace.md and all_kernels_l70b_bench_kernel_trace.md from
-    passes 5 and 6, when their outputs are there.
+    passes 5 and 6, attn_kernel_l70b_ulysses_s8192.md from passes 7-9, when their outputs are
+    there.
 """
 from __future__ import annotations
 
@@ -48,6 +50,15 @@ CALIB_BYTES = 268435456
 COUNTER_STEPS = 3  # timed steps of the counter passes
 N_SIMD = 1024  # 256 CUs x 4 SIMDs
 
+ATTN_SEQ = 8192
+ATTN_ARGS = ["-m", "comm_overlapped_sliced_amd.attn_run", "--seq", str(ATTN_SEQ)]
+# two passes of at most 8 SQ counters each
+ATTN_PMC = (["SQ_WAVES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES",
+             "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_INSTS_VALU", "SQ_INSTS_LDS"],
+            ["SQ_WAIT_INST_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_ANY", "SQ_WAIT_INST_ANY",
+             "SQ_INSTS_MFMA", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_VALU_TRANS_F32", "SQ_WAIT_ANY"])
+N_SE = 32  # shader engines (SQ_BUSY_CYCLES sums one count per engine)
+
 # the step alone: no exposure sections, no oracle, no clock sampler; a short back-to-back window
 # before the timed steps where timing matters (trace, copies), none where only counts do
 STEP_ARGS = ["bench.py", "--no-exposure", "--cpu-seconds", "0", "--clock-seconds", "0"]
@@ -69,6 +80,10 @@ PASSES = [
     ("bench", ["--kernel-trace", "--stats"],
      ["bench.py", "--cpu-seconds", "0", "--clock-seconds", "0", "--steps", "10", "--warmup", "3",
       "--settle-seconds", "0.5"], 420),
+    # the resident attention on the 70B Ulysses share: its durations, then two counter passes
+    ("attn", ["--kernel-trace", "--stats"], ATTN_ARGS + ["--calls", "50"], 180),
+    ("attn_pmc1", ["--pmc", *ATTN_PMC[0], "--kernel-trace"], ATTN_ARGS + ["--calls", "3"], 120),
+    ("attn_pmc2", ["--pmc", *ATTN_PMC[1], "--kernel-trace"], ATTN_ARGS + ["--calls", "3"], 120),
 ]
 
 # the step's two GEMM launches: (kind, call, M, K, N, algorithmic read bytes, write bytes)
@@ -434,6 +449,93 @@ fo_gemm.hip sha256: {sha}
         f.write(text)
 
 
+def _attn_timed(log: str) -> str:
+    with open(log) as f:
+        for line in f:
+            if line.startswith("attn timed:"):
+                return line.strip()[len("attn timed: "):]
+    return "(no timed line)"
+
+
+def summarize_attn(raw: str, out_dir: str) -> None:
+    """attn_kernel_l70b_ulysses_s8192.md: durations and counters of the resident attention."""
+    src = os.path.join(HERE, "csrc", "fo_attn.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    stats_csv = _one(os.path.join(raw, "attn", "**", "*kernel_stats.csv"))
+    row = None
+    with open(stats_csv) as f:
+        for r in csv.DictReader(f):
+            if "attn_kernel" in r["Name"]:
+                row = r
+    cnt, dur = {}, []
+    for name in ("attn_pmc1", "attn_pmc2"):
+        disp = _per_dispatch(_one(os.path.join(raw, name, "**", "*counter_collection.csv")))
+        ids = sorted(d for d, (n, _, _) in disp.items() if "attn_kernel" in n)[-3:]
+        for c in ATTN_PMC[0 if name == "attn_pmc1" else 1]:
+            cnt[c] = statistics.mean(disp[d][2].get(c, float("nan")) for d in ids)
+        with open(_one(os.path.join(raw, name, "**", "*kernel_trace.csv"))) as f:
+            t = {int(r["Dispatch_Id"]): (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                 for r in csv.DictReader(f)}
+        dur += [t[d] for d in ids if d in t]
+    us = statistics.mean(dur)
+    cycles = cnt["SQ_BUSY_CYCLES"] / N_SE
+    mfma = cnt["SQ_INSTS_MFMA"]
+    lines = [
+        f"| counted MFMA instructions (32x32x16 bf16) | {mfma:.4g} |",
+        f"| kernel cycles: SQ_BUSY_CYCLES / {N_SE} shader engines | {cycles:.4g} "
+        f"({cycles / us:.0f} MHz over the {us:.1f} us launches) |",
+        f"| MFMA busy share: SQ_VALU_MFMA_BUSY_CYCLES / {N_SIMD} SIMDs / kernel cycles | "
+        f"{cnt['SQ_VALU_MFMA_BUSY_CYCLES'] / N_SIMD / cycles:.3f} |",
+        f"| VALU instructions other than MFMA, per MFMA | "
+        f"{(cnt['SQ_INSTS_VALU'] - mfma) / mfma:.2f} |",
+        f"| transcendental (exp2) instructions per MFMA | {cnt['SQ_INSTS_VALU_TRANS_F32'] / mfma:.2f} |",
+        f"| VALU issue: SQ_ACTIVE_INST_VALU / SQ_WAVE_CYCLES | "
+        f"{cnt['SQ_ACTIVE_INST_VALU'] / cnt['SQ_WAVE_CYCLES']:.3f} |",
+        f"| LDS issue: SQ_ACTIVE_INST_LDS / SQ_WAVE_CYCLES | "
+        f"{cnt['SQ_ACTIVE_INST_LDS'] / cnt['SQ_WAVE_CYCLES']:.3f} |",
+        f"| LDS bank conflicts: SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE | "
+        f"{cnt['SQ_LDS_BANK_CONFLICT'] / cnt['SQ_LDS_IDX_ACTIVE']:.4f} |",
+        f"| waiting to issue: SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES (second pass / first) | "
+        f"{cnt['SQ_WAIT_INST_ANY'] / cnt['SQ_WAVE_CYCLES']:.3f} |",
+        f"| waiting on LDS: SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES (second pass / first) | "
+        f"{cnt['SQ_WAIT_INST_LDS'] / cnt['SQ_WAVE_CYCLES']:.3f} |",
+    ]
+    raw_rows = "\n".join(f"| {c} | {cnt[c]:.4e} |" for c in ATTN_PMC[0] + ATTN_PMC[1])
+    stat = (f"{row['Calls']} launches, average {float(row['AverageNs']) / 1e3:.1f} us, min "
+            f"{float(row['MinNs']) / 1e3:.1f}, max {float(row['MaxNs']) / 1e3:.1f}" if row else "n/a")
+    text = f"""# rocprofv3: query-split attention (`attn_kernel`), Llama-3.1-70B Ulysses share, S = {ATTN_SEQ}
+
+Resident attention (`fo_attn_ref`): 8 query heads, 1 key/value head of dimension 128, causal,
+{ATTN_SEQ} tokens; seeded inputs of the bench's attention workload. Algorithmic work 4 d hq
+(pairs attended) = 137.5 GFLOP.
+
+Commands (from the repository root, TMPDIR=/tmp; `python -m comm_overlapped_sliced_amd.profiling
+run --passes attn,attn_pmc1,attn_pmc2`):
+
+    {command_text('attn', raw)}
+    {command_text('attn_pmc1', raw)}
+    {command_text('attn_pmc2', raw)}
+
+Kernel trace: {stat}. The driver's own timing of the same run: {_attn_timed(os.path.join(raw, 'attn.log'))}.
+
+Counters (mean over the three timed launches of each counter run):
+
+| quantity | value |
+|---|---|
+{chr(10).join(lines)}
+
+Raw counter sums per launch:
+
+| counter | value |
+|---|---|
+{raw_rows}
+
+fo_attn.hip sha256: {sha}
+"""
+    with open(os.path.join(out_dir, f"attn_kernel_l70b_ulysses_s{ATTN_SEQ}.md"), "w") as f:
+        f.write(text)
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(prog="python -m comm_overlapped_sliced_amd.profiling")
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -453,6 +555,8 @@ def main(argv=None) -> int:
         summarize_copies(a.raw, a.out)
     if os.path.isdir(os.path.join(a.raw, "bench")):
         summarize_bench(a.raw, a.out)
+    if all(os.path.isdir(os.path.join(a.raw, n)) for n in ("attn", "attn_pmc1", "attn_pmc2")):
+        summarize_attn(a.raw, a.out)
     return 0
 
 

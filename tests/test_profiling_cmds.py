@@ -1,5 +1,5 @@
 """The rocprofv3 harness builds commands that the profiler can run: the program after `--` is
-python itself (no launcher in between), counter passes trace kernels only (no copy, HIP, HSA,
+python itself (no launcher in between) on bench.py or the attention driver, counter passes trace kernels only (no copy, HIP, HSA,
 marker or system traces beside --pmc) and ask for at most 8 SQ and 4 TCC counters, and every pass
 writes under its own directory."""
 from __future__ import annotations
@@ -18,7 +18,9 @@ def test_pass_command(name):
     argv = profiling.command(name, "out", python="python3")
     assert argv[0] == "rocprofv3"
     sep = argv.index("--")
-    assert argv[sep + 1] == "python3" and argv[sep + 2] == "bench.py"
+    assert argv[sep + 1] == "python3"
+    assert argv[sep + 2] == "bench.py" or argv[sep + 2:sep + 4] == [
+        "-m", "comm_overlapped_sliced_amd.attn_run"]
     opts = argv[1:sep]
     assert opts[opts.index("-d") + 1] == f"out/{name}"
     if "--pmc" in opts:
