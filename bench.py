@@ -385,9 +385,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: every box of this setup has a single MI355X, so "
-              "--gpus must be 1 (the multi-GPU sharding is described in DESIGN.md)",
-              file=sys.stderr)
+        print("bench.py measures one GPU (one rank's share of the tensor-parallel layer); "
+              "--gpus must be 1", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

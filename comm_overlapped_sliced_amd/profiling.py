@@ -516,7 +516,7 @@ run --passes attn,attn_pmc1,attn_pmc2`):
     {command_text('attn_pmc1', raw)}
     {command_text('attn_pmc2', raw)}
 
-Kernel trace: {stat}. The driver's own timing of the same run: {_attn_timed(os.path.join(raw, 'attn.log'))}.
+Kernel trace: {stat}. attn_run's own timing of the same run: {_attn_timed(os.path.join(raw, 'attn.log'))}.
 
 Counters (mean over the three timed launches of each counter run):
 

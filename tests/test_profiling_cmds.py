@@ -1,7 +1,7 @@
 """The rocprofv3 harness builds commands that the profiler can run: the program after `--` is
-python itself (no launcher in between) on bench.py or the attention driver, counter passes trace kernels only (no copy, HIP, HSA,
-marker or system traces beside --pmc) and ask for at most 8 SQ and 4 TCC counters, and every pass
-writes under its own directory."""
+python itself (no launcher in between) on bench.py or the attention module (attn_run), counter
+passes trace kernels only (no copy, HIP, HSA, marker or system traces beside --pmc) and ask for
+at most 8 SQ and 4 TCC counters, and every pass writes under its own directory."""
 from __future__ import annotations
 
 import pytest
