@@ -870,8 +870,15 @@ def cpu_baseline(ag_case, rs_case, target_s: float):
             batch *= 2
         parts.append(f"first {done} of {case.M} rows of the {case.call.upper()} product "
                      f"(K={case.K}, N={case.N})")
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(fl / secs / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle", "sample": "; ".join(parts) + f"; fp64, {secs:.1f} s"}
+            "kind": "oracle", "sample": "; ".join(parts) + f"; fp64, {secs:.1f} s",
+            "host": {"nproc": os.cpu_count(), "cpu_model": model}}
 
 
 if __name__ == "__main__":
