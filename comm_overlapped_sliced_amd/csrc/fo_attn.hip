@@ -27,8 +27,9 @@
 //   spread over the banks), V rows by key mod 4 (the transpose reads: chunk XOR (0, 6, 12,
 //   10)[key & 3], which gives the 4 key rows x 4 chunks a 32-lane read covers distinct bank
 //   groups whether the LDS serves 128 or 256 bytes per cycle).
-// - Two workgroups per CU (64 KB of LDS each): one workgroup's softmax overlaps the other's
-//   MFMAs.
+// - Two workgroups per CU (64 KB of LDS each), two waves per SIMD, so that a wave's softmax can
+//   run while the other wave of its SIMD issues MFMAs (they fill each other's gaps only in
+//   part: the kernel stays latency-bound).
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
