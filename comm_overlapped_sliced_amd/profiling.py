@@ -510,7 +510,7 @@ Resident attention (`fo_attn_ref`): 8 query heads, 1 key/value head of dimension
 (pairs attended) = 137.5 GFLOP.
 
 Commands (from the repository root, TMPDIR=/tmp; `python -m comm_overlapped_sliced_amd.profiling
-run --passes attn,attn_pmc1,attn_pmc2`):
+run --raw {raw} --passes attn,attn_pmc1,attn_pmc2`):
 
     {command_text('attn', raw)}
     {command_text('attn_pmc1', raw)}
