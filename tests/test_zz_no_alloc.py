@@ -91,3 +91,41 @@ def test_noalloc_rejects_arrivals_and_bad_args(dev):
     st = lib.fo_gemm_rs_noalloc(xd.data_ptr(), wd.data_ptr(), t[0].data_ptr(), t[0].data_ptr(),
                                 t[2].data_ptr(), P, 0, m, K, N, fo.BF16, None, None)
     assert st == fo.FO_ERR_INVALID_ARG  # out overlaps send_buf
+
+
+@pytest.mark.parametrize("order", [fo.ORDER_FLASH, fo.ORDER_NATURAL], ids=["flash", "natural"])
+def test_noalloc_captured_in_a_graph(dev, order):
+    """The call captured in a HIP graph (torch.cuda.graph) and replayed four times, with eager
+    work between the replays (the outputs poisoned, another problem run eagerly through the same
+    static array): every replay equals the eager call bit for bit."""
+    P, m, K, N, r, seed = 4, 200, 520, 392, 1, 9400
+    print(f"noalloc graph P={P} m={m} K={K} N={N} rank={r} order={order}", flush=True)
+    x, w, parts, xd, wd, recv = _problem(dev, P, m, K, N, seed)
+    o = fo.opts(order=order)
+    out_e, send_e = _run(_noalloc, dev, xd, wd, recv, P, r, m, N, o)
+    other = _problem(dev, 3, 64, 256, 136, seed + 50)
+
+    send = torch.full((P * m, N), float("nan"), dtype=torch.float32, device=dev)
+    out = torch.full((m, N), float("nan"), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st = fo.gemm_rs_noalloc(xd, wd, send, out, recv, P, r,
+                                compute_stream=torch.cuda.current_stream(), o=o, raw=True)
+    assert st == fo.FO_OK, fo.load().fo_last_error().decode()
+    for rep in range(4):
+        out.fill_(float("nan"))
+        send.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        fo.check(torch.cuda.current_stream())
+        assert np.array_equal(from_dev(out), out_e), f"replay {rep}: own chunk"
+        got = from_dev(send)
+        for d in range(P):
+            if d != r:
+                assert np.array_equal(got[d * m:(d + 1) * m], send_e[d * m:(d + 1) * m]), \
+                    f"replay {rep}: send chunk {d}"
+        # eager work on the same static array between replays
+        _, _, _, oxd, owd, orecv = other
+        _run(_noalloc, dev, oxd, owd, orecv, 3, 2, 64, 136, fo.opts(order=order))
+    del g
