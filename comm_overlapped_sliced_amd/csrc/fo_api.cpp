@@ -18,7 +18,9 @@
 #include <cstdio>
 #include <cstring>
 #include <mutex>
+#include <queue>
 #include <string>
+#include <vector>
 
 #include "fo_internal.h"
 
@@ -99,6 +101,19 @@ struct DevState {
   hipEvent_t last_ev = nullptr;     // the event recorded after the device's last call
   hipStream_t last_stream = nullptr;
   bool have_last = false;
+  // the attention's work tables, by shape (built once per shape, kept until the process ends),
+  // and the partial outputs and counters of its split items (grown to the largest call)
+  struct AttnTable {
+    int32_t P, hq, causal;
+    int64_t m;
+    int4* table;
+    int32_t* bins;
+    int32_t n_items, n_bins, n_pairs;
+  };
+  std::vector<AttnTable> attn_tables;
+  float* attn_part = nullptr;
+  uint32_t* attn_cnt = nullptr;
+  int64_t attn_pairs_cap = 0;
 };
 
 DevState g_dev[kMaxDevices];
@@ -973,6 +988,161 @@ static int32_t attn_pair_half(int32_t P, int64_t m, int32_t hq, int32_t causal, 
   return (causal && total % 2 == 0 && total > n_cu && total <= 2 * (int64_t)n_cu) ? (int32_t)(total / 2) : 0;
 }
 
+// The attention's work table for causal calls. Under causal masking the items' key walks run
+// from 1 to P * m / 64 tiles, and with one workgroup per item the longest ones set the kernel's
+// time (70B share, 8K tokens: a CU running a 128-tile item next to a 2-tile one ended at 183 us,
+// CUs with two 65-tile items at 128 us). Instead each CU's two workgroups (b and b + CUs, all
+// resident at once) take lists of items that give every CU the same work:
+//   - items longer than a workgroup slot's share are cut in two along their key walk;
+//   - the items go longest first to the least loaded CU, each counted with a fixed cost for its
+//     query load, pipeline fill and epilogue;
+//   - a CU's items are divided between its two workgroups so that the first one dispatched takes
+//     about 60% of the cost: of two workgroups sharing a CU the older one ran a key tile in ~1.7
+//     us and the younger in ~2.5 (16K tokens), so both then end together.
+// Measured and not kept: assigning each item to the list that would end it first (the same for
+// resident calls, slower behind the transfers: 8K, both exchanges, 260 against 246 us), taking
+// the slices one after another in arrival order (under causal masking the slice that arrives
+// first may need every other slice's keys: 194 -> 231 us inbound), and the own slice's items
+// last with the return exchange (246 -> 259 us).
+constexpr int kAttnItemCost = 4;        // per item, in key tiles
+constexpr double kAttnFirstShare = 0.6;
+static fo_status attn_schedule(DevState* st, fo::AttnPlan& p) {
+  p.table = nullptr;
+  p.bins = nullptr;
+  if (!p.causal) return FO_OK;
+  const int64_t qtiles = (p.m + 127) / 128;
+  const int64_t base = (int64_t)p.P * qtiles * p.hq;
+  const int64_t n_cu = st->n_cu, slots = 2 * n_cu;
+  if (base > ((int64_t)1 << 22)) return FO_OK;
+  const DevState::AttnTable* t = nullptr;
+  for (const auto& e : st->attn_tables)
+    if (e.P == p.P && e.m == p.m && e.hq == p.hq && e.causal == p.causal) t = &e;
+  if (t == nullptr) {
+    const int64_t mt = (p.m + 63) / 64;
+    struct Item {
+      int64_t cost;
+      int4 e;
+    };
+    std::vector<Item> items;
+    int64_t sum = 0;
+    for (int s = 0; s < p.P; ++s)
+      for (int64_t qt = 0; qt < qtiles; ++qt) {
+        const int64_t q1 = std::min<int64_t>(p.m, (qt + 1) * 128);
+        sum += p.hq * (s * mt + (q1 + 63) / 64 + kAttnItemCost);
+      }
+    const int64_t share = (sum + slots - 1) / slots;
+    int32_t pairs = 0;
+    for (int s = 0; s < p.P; ++s)
+      for (int64_t qt = 0; qt < qtiles; ++qt) {
+        const int64_t q1 = std::min<int64_t>(p.m, (qt + 1) * 128);
+        const int32_t w = (int32_t)(s * mt + (q1 + 63) / 64);
+        for (int h = 0; h < p.hq; ++h) {
+          if (w >= 2 && w + kAttnItemCost > share) {
+            const int32_t cut = (w + 1) / 2;
+            items.push_back({cut + kAttnItemCost, make_int4(s, (int)qt, h, 2 * pairs)});
+            items.push_back({w - cut + kAttnItemCost, make_int4(s, (int)qt, h, 2 * pairs + 1)});
+            ++pairs;
+          } else {
+            items.push_back({w + kAttnItemCost, make_int4(s, (int)qt, h, -1)});
+          }
+        }
+      }
+    // longest first (equal costs keep their table order: the schedule is a function of the shape)
+    std::stable_sort(items.begin(), items.end(),
+                     [](const Item& a, const Item& b) { return a.cost > b.cost; });
+    const int64_t E = (int64_t)items.size();
+    std::vector<std::vector<int4>> lists;
+    if (E <= n_cu) {
+      // one item per workgroup, each on a CU of its own
+      for (const Item& it : items) lists.push_back({it.e});
+    } else {
+      using Load = std::pair<int64_t, int>;
+      std::priority_queue<Load, std::vector<Load>, std::greater<Load>> heap;
+      for (int c = 0; c < n_cu; ++c) heap.push({0, c});
+      std::vector<std::vector<const Item*>> cu(n_cu);
+      for (const Item& it : items) {
+        Load l = heap.top();
+        heap.pop();
+        cu[l.second].push_back(&it);
+        l.first += it.cost;
+        heap.push(l);
+      }
+      lists.assign(slots, {});
+      for (int c = 0; c < n_cu; ++c) {
+        // the first workgroup's items: the subset whose cost is closest to its share (every
+        // subset while there are few items, else longest first up to the share)
+        const auto& v = cu[c];
+        int64_t tot = 0;
+        for (const Item* it : v) tot += it->cost;
+        const double want = kAttnFirstShare * (double)tot;
+        std::vector<char> first(v.size(), 0);
+        if (v.size() <= 10) {
+          double best = 1e300;
+          uint32_t pick = 0;
+          for (uint32_t mask = 0; mask < (1u << v.size()); ++mask) {
+            int64_t a = 0;
+            for (size_t i = 0; i < v.size(); ++i)
+              if (mask >> i & 1) a += v[i]->cost;
+            const double d = std::fabs((double)a - want);
+            if (d < best) {
+              best = d;
+              pick = mask;
+            }
+          }
+          for (size_t i = 0; i < v.size(); ++i) first[i] = (char)(pick >> i & 1);
+        } else {
+          int64_t a = 0;
+          for (size_t i = 0; i < v.size(); ++i)
+            if ((double)(a + v[i]->cost) <= want) {
+              a += v[i]->cost;
+              first[i] = 1;
+            }
+        }
+        for (size_t i = 0; i < v.size(); ++i) lists[first[i] ? c : n_cu + c].push_back(v[i]->e);
+      }
+    }
+    const int nb = (int)lists.size();
+    std::vector<int4> host;
+    std::vector<int32_t> bins(nb + 1, 0);
+    for (int b = 0; b < nb; ++b) {
+      bins[b] = (int32_t)host.size();
+      host.insert(host.end(), lists[b].begin(), lists[b].end());
+    }
+    bins[nb] = (int32_t)host.size();
+    const size_t tb = host.size() * sizeof(int4), bb = bins.size() * sizeof(int32_t);
+    void* d = nullptr;
+    FO_HIP(hipMalloc(&d, tb + bb));
+    FO_HIP(hipMemcpy(d, host.data(), tb, hipMemcpyHostToDevice));
+    FO_HIP(hipMemcpy((uint8_t*)d + tb, bins.data(), bb, hipMemcpyHostToDevice));
+    st->attn_tables.push_back({p.P, p.hq, p.causal, p.m, (int4*)d,
+                               (int32_t*)((uint8_t*)d + tb), (int32_t)host.size(), nb, pairs});
+    t = &st->attn_tables.back();
+  }
+  if (t->n_pairs > st->attn_pairs_cap) {
+    // grown to the largest call so far; the previous buffers may still be in use by an earlier
+    // call's kernel
+    FO_HIP(hipDeviceSynchronize());
+    if (st->attn_part) FO_HIP(hipFree(st->attn_part));
+    if (st->attn_cnt) FO_HIP(hipFree(st->attn_cnt));
+    st->attn_part = nullptr;
+    st->attn_cnt = nullptr;
+    st->attn_pairs_cap = 0;
+    const size_t n = (size_t)t->n_pairs;
+    FO_HIP(hipMalloc((void**)&st->attn_part, n * 2 * fo::kAttnPartFloats * sizeof(float)));
+    FO_HIP(hipMalloc((void**)&st->attn_cnt, n * sizeof(uint32_t)));
+    FO_HIP(hipMemset(st->attn_cnt, 0, n * sizeof(uint32_t)));
+    st->attn_pairs_cap = t->n_pairs;
+  }
+  p.table = t->table;
+  p.bins = t->bins;
+  p.n_items = t->n_items;
+  p.n_bins = t->n_bins;
+  p.part_buf = st->attn_part;
+  p.pair_cnt = st->attn_cnt;
+  if (t->n_pairs > 0 && (p.part_buf == nullptr || p.pair_cnt == nullptr)) return FO_ERR_HIP;
+  return FO_OK;
+}
+
 static fo_status launch_attn_events(const fo::AttnPlan& p, hipStream_t cs, const fo_opts& o) {
   FO_HIP(fo::launch_attn(p, cs, (hipEvent_t)o.kernel_events[0], (hipEvent_t)o.kernel_events[1]));
   return FO_OK;
@@ -1084,6 +1254,8 @@ fo_status fo_attn(const void* qkv_local, const void* const* qkv_peer, void* qkv_
   p.causal = causal;
   p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
   p.pair_half = attn_pair_half(P, m, hq, causal, st->n_cu);
+  s = attn_schedule(st, p);
+  if (s != FO_OK) return s;
   // transfers on cache-line (128-byte) boundaries: no acquire needed after the arrival waits
   const size_t row_bytes = (size_t)(hq + 2 * hkv) * head_dim * 2;
   p.acq = (aligned(qkv_recv, 128) && row_bytes % 128 == 0) ? 0 : 1;
@@ -1169,7 +1341,16 @@ fo_status fo_attn_ref(const void* qkv, void* out, int64_t S, int32_t hq, int32_t
   p.causal = causal;
   p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
   p.pair_half = attn_pair_half(1, S, hq, causal, st->n_cu);
-  FO_HIP(fo::launch_attn(p, (hipStream_t)stream));
+  s = attn_schedule(st, p);
+  if (s != FO_OK) return s;
+  hipStream_t cs = (hipStream_t)stream;
+  if (p.table != nullptr) {
+    // split items share the device's partial buffers: ordered after the device's last call
+    s = order_after_last(st, cs);
+    if (s != FO_OK) return s;
+  }
+  FO_HIP(fo::launch_attn(p, cs));
+  if (p.table != nullptr) return mark_last(st, cs, nullptr);
   return FO_OK;
 }
 

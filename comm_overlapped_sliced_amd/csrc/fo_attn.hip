@@ -131,7 +131,8 @@ __device__ __forceinline__ void wait_groups(const AttnPlan& p, int j, int g0, in
   __syncthreads();
 }
 
-__device__ __forceinline__ void attn_tile(const AttnPlan& p, const int u, uint8_t* const lds) {
+__device__ __forceinline__ void attn_tile(const AttnPlan& p, const int u, uint8_t* const lds,
+                                          uint32_t* const bcast) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uni(tid >> 6);
@@ -139,8 +140,14 @@ __device__ __forceinline__ void attn_tile(const AttnPlan& p, const int u, uint8_
   const int m = (int)p.m;
   const int hq = p.hq;
   const int qtiles = (m + kAQ - 1) / kAQ;
-  int s, qt, h;
-  if (p.pair_half > 0) {
+  int s, qt, h, wpart = -1;
+  if (p.table != nullptr) {
+    const int4 e = p.table[u];
+    s = uni(e.x);
+    qt = uni(e.y);
+    h = uni(e.z);
+    wpart = uni(e.w);
+  } else if (p.pair_half > 0) {
     // items by global query tile, most keys first; the second half of the grid in reverse, so
     // that workgroup b and workgroup b + pair_half (which share a CU) sum to about the same work
     const int total = p.P * qtiles * hq;
@@ -193,6 +200,21 @@ __device__ __forceinline__ void attn_tile(const AttnPlan& p, const int u, uint8_
   // per-lane LDS offsets of the loads: a 1 KB piece covers 4 key rows, lane -> (row, chunk)
   const int prow = lane >> 4, pch = lane & 15;
 
+  // the key tiles of the item's walk (every slice, or under causal masking the slices j < s and
+  // the diagonal slice up to the tile's last query), numbered in walk order; a part of a split
+  // item visits walk tiles [w_lo, w_hi) only
+  const int mt = (m + kAK - 1) / kAK;
+  const int wtot = p.causal ? s * mt + (q0 + qrows + kAK - 1) / kAK : p.P * mt;
+  int w_lo = 0, w_hi = wtot;
+  if (wpart >= 0) {
+    const int cut = (wtot + 1) / 2;
+    if (wpart & 1)
+      w_lo = cut;
+    else
+      w_hi = cut;
+  }
+  int wt = 0;  // walk tiles before slice j
+
   for (int jp = 0; jp < p.P; ++jp) {
     const int j = uni(p.order[jp]);
     if (p.causal && j > s) continue;
@@ -200,9 +222,14 @@ __device__ __forceinline__ void attn_tile(const AttnPlan& p, const int u, uint8_
     // last query
     const int nk = (p.causal && j == s) ? (q0 + qrows) : m;
     const int nt = (nk + kAK - 1) / kAK;
+    // this item's tiles of slice j: [lo, hi)
+    const int lo = w_lo - wt > 0 ? w_lo - wt : 0;
+    const int hi = w_hi - wt < nt ? w_hi - wt : nt;
+    wt += nt;
+    if (lo >= hi) continue;
     // the row groups holding those keys, all before the walk (a wait inside the tile loop slows
     // its code down more than an earlier start of a slice's first groups gains)
-    if (p.gated[j]) wait_groups(p, j, 0, (nk - 1) / gr);
+    if (p.gated[j]) wait_groups(p, j, lo * kAK / gr, ((hi * kAK < nk ? hi * kAK : nk) - 1) / gr);
     const int64_t kpos0 = (int64_t)j * m;
     const i32x4 kvres = rsrc_i(p.slice[j], (uint32_t)m * (uint32_t)W);
     const uint32_t kcol = (uint32_t)(hq + kvh) * kRowB, vcol = (uint32_t)(hq + p.hkv + kvh) * kRowB;
@@ -221,12 +248,12 @@ __device__ __forceinline__ void attn_tile(const AttnPlan& p, const int u, uint8_
                    voff);
       }
     };
-    issue(0, 0);
-    for (int t = 0; t < nt; ++t) {
-      const int st = t & 1;
+    issue(lo, 0);
+    for (int t = lo; t < hi; ++t) {
+      const int st = (t - lo) & 1;
       wait_vmcnt<0>();  // tile t has landed (this wave's loads)
       lds_barrier();    // every wave's loads of tile t landed; tile t-1's stage is free
-      if (t + 1 < nt) issue(t + 1, st ^ 1);
+      if (t + 1 < hi) issue(t + 1, st ^ 1);
       const uint8_t* kt = lds + st * kStage;
       const uint8_t* vt = kt + kTileB;
 
@@ -355,6 +382,60 @@ __device__ __forceinline__ void attn_tile(const AttnPlan& p, const int u, uint8_
     lds_barrier();  // every wave is done with the stages before the next slice refills them
   }
 
+  if (wpart >= 0) {
+    // ---- a part of a split item: store this part's output, max and sum; the second part to
+    // finish combines the two. The partials are written through to memory and read back with
+    // system-coherent loads (sc0 sc1), so neither side needs a cache invalidate.
+    constexpr int kSys = 1 | 16;  // cache policy sc0 | sc1
+    const int pair = wpart >> 1, part = wpart & 1;
+    const uint32_t wbase = (uint32_t)(wave * 66 * 64 + lane) * 4u;
+    const __amdgpu_buffer_rsrc_t mine =
+        rsrc_b(p.part_buf + ((size_t)pair * 2 + part) * kAttnPartFloats, kAttnPartFloats * 4);
+#pragma unroll
+    for (int i = 0; i < kAD / 32; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        // through a scalar: a bit cast of the vector element itself reads element 0
+        const float x = oacc[i][v];
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, x), mine,
+                                              wbase + (uint32_t)((i * 16 + v) * 64 * 4), 0, kSys);
+      }
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, mrow), mine, wbase + 64 * 64 * 4, 0,
+                                          kSys);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, lrow), mine, wbase + 65 * 64 * 4, 0,
+                                          kSys);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();  // every wave's partial is stored
+    if (tid == 0)
+      *bcast = __hip_atomic_fetch_add(p.pair_cnt + pair, 1u, __ATOMIC_RELEASE,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (*bcast == 0) return;  // the other part combines (every wave leaves here together)
+    if (tid == 0) __hip_atomic_store(p.pair_cnt + pair, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const __amdgpu_buffer_rsrc_t other =
+        rsrc_b(p.part_buf + ((size_t)pair * 2 + (part ^ 1)) * kAttnPartFloats, kAttnPartFloats * 4);
+    const float om = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(other, wbase + 64 * 64 * 4, 0, kSys));
+    const float ol = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(other, wbase + 65 * 64 * 4, 0, kSys));
+    // both parts relative to the larger reference max; the sums are formed in part order (part
+    // 0's term through the fma), so the result does not depend on which part finished last
+    const float mm = fmaxf(mrow, om);
+    const float fm = __builtin_amdgcn_exp2f((mrow - mm) * p.scale_log2);
+    const float fo = __builtin_amdgcn_exp2f((om - mm) * p.scale_log2);
+    lrow = part == 0 ? __builtin_fmaf(lrow, fm, ol * fo) : __builtin_fmaf(ol, fo, lrow * fm);
+#pragma unroll
+    for (int i = 0; i < kAD / 32; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float ov = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(other, wbase + (uint32_t)((i * 16 + v) * 64 * 4),
+                                                        0, kSys));
+        oacc[i][v] = part == 0 ? __builtin_fmaf(oacc[i][v], fm, ov * fo)
+                               : __builtin_fmaf(ov, fo, oacc[i][v] * fm);
+      }
+  }
+
   // ---- epilogue: O = O^T / l, staged per wave as [query][d] bf16, stored row-contiguous -----
   const float ltot = lrow + __shfl_xor(lrow, 32);
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
@@ -403,10 +484,16 @@ __device__ __forceinline__ void attn_tile(const AttnPlan& p, const int u, uint8_
 
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnPlan p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * kStage];
+  __shared__ uint32_t bcast;
   release_start(p.start);
   const int qtiles = (int)((p.m + kAQ - 1) / kAQ);
+  if (p.table != nullptr) {
+    const int u1 = p.bins[blockIdx.x + 1];
+    for (int u = p.bins[blockIdx.x]; u < u1; ++u) attn_tile(p, u, lds, &bcast);
+    return;
+  }
   const int total = p.P * qtiles * p.hq;
-  for (int u = blockIdx.x; u < total; u += gridDim.x) attn_tile(p, u, lds);
+  for (int u = blockIdx.x; u < total; u += gridDim.x) attn_tile(p, u, lds, &bcast);
 }
 
 }  // namespace
@@ -425,6 +512,7 @@ bool attn_plan_ok(const AttnPlan& p) {
       (p.done == nullptr || p.out_groups < 1 || p.out_groups > kMaxGroups ||
        p.out_group_rows < 1 || p.out_group_rows % kAQ != 0 || p.out_group_rows * p.out_groups < p.m))
     return false;
+  if (p.table != nullptr && (p.bins == nullptr || p.n_items < 1 || p.n_bins < 1)) return false;
   bool seen[FO_MAX_P] = {};
   for (int i = 0; i < p.P; ++i) {
     if (p.dispatch[i] < 0 || p.dispatch[i] >= p.P || seen[p.dispatch[i]]) return false;
@@ -440,7 +528,8 @@ bool attn_plan_ok(const AttnPlan& p) {
 
 hipError_t launch_attn(const AttnPlan& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   if (!attn_plan_ok(p)) return hipErrorInvalidValue;
-  const int64_t total = (int64_t)p.P * ((p.m + kAQ - 1) / kAQ) * p.hq;
+  const int64_t total =
+      p.table != nullptr ? p.n_bins : (int64_t)p.P * ((p.m + kAQ - 1) / kAQ) * p.hq;
   hipExtLaunchKernelGGL(attn_kernel, dim3((unsigned)total), dim3(kThreads), 0, s, e0, e1, 0, p);
   return hipGetLastError();
 }

@@ -200,7 +200,22 @@ struct AttnPlan {
   // query tile, independent of the arriving groups above)
   int64_t out_group_rows;
   int32_t out_groups;
+  // Work table (null: one item per (slice, query tile, head) in the order above). Entry u is the
+  // workgroup's item: {slice, query tile, head, w}; w < 0 covers every key of the item, else the
+  // item's key walk is cut in two at ceil(tiles / 2) and entry w covers part w & 1 of pair w >> 1.
+  // The two parts of a pair each store their unnormalized output, running max and sum in
+  // part_buf; the second to finish (pair_cnt counts them, zero between calls) combines them and
+  // stores the item's output.
+  // Workgroup b takes entries bins[b] .. bins[b + 1] - 1 of the table, one after the other
+  // (n_bins workgroups, all resident at once: two per CU).
+  const int4* table;
+  const int32_t* bins;
+  int32_t n_items, n_bins;
+  float* part_buf;                   // [pair][part][kAttnPartFloats] (null: no pair)
+  uint32_t* pair_cnt;                // [pair]
 };
+// floats of one part's partial output: 4 waves x (64 output values + running max + sum) x 64 lanes
+constexpr int kAttnPartFloats = 4 * 66 * 64;
 bool attn_plan_ok(const AttnPlan& p);
 hipError_t launch_attn(const AttnPlan& p, hipStream_t stream, hipEvent_t e0 = nullptr,
                        hipEvent_t e1 = nullptr);

@@ -265,7 +265,11 @@ fo_status fo_swiglu(const void* y, void* h, int64_t rows, int64_t inter, void* s
  * out_peer[s] as soon as every work item of a row group of slice s (the groups it arrived in)
  * has stored them, while the later work computes; in the FLASH order the own slice, whose rows
  * stay, is dispatched last (the Flash-RS order applied to the outgoing exchange). The call ends
- * when every sent row has landed.
+ * when every sent row has landed. Under causal masking the work items (slice, 128-query tile,
+ * head) differ in length up to P*m/64 key tiles; the workgroups (two per CU) then take lists
+ * that give every CU the same work, the longest items cut in two along their keys and the two
+ * halves combined in a fixed order (the same bits whichever half ends last), and the dispatch
+ * order above no longer applies.
  *   qkv_local  device [m, (hq + 2*hkv) * head_dim] bf16: one row per token, [hq query heads |
  *              hkv key heads | hkv value heads], each head_dim values.
  *   qkv_peer   host array of P device pointers (entry [rank] ignored), each [m, row] like
@@ -298,7 +302,9 @@ fo_status fo_attn(const void* qkv_local, const void* const* qkv_peer, void* qkv_
  * The same attention with every slice resident (one sequence of S tokens, no transfers): the
  * pure-attention latency of the exposed-transfer fraction and the unsliced result of the
  * exactness check. qkv [S, (hq + 2*hkv) * head_dim] bf16, out [S, hq * head_dim] bf16; the
- * checks of fo_attn apply. Enqueued on `stream`.
+ * checks of fo_attn apply. Enqueued on `stream`; a causal call cuts long items in two like
+ * fo_attn and keeps their halves in the device's buffers, so it is also ordered after the
+ * device's previous call as fo_attn is.
  */
 fo_status fo_attn_ref(const void* qkv, void* out, int64_t S, int32_t hq, int32_t hkv,
                       int32_t head_dim, int32_t causal, void* stream);

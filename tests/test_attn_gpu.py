@@ -210,3 +210,27 @@ def test_attn_back_to_back_calls_see_new_arrivals(dev):
         for s in range(P):
             if s != rank:
                 assert torch.equal(backs[it][s], refs[it % 2][s * m:(s + 1) * m]), f"call {it} slice {s}"
+
+
+def test_attn_split_items_same_bits_every_call(dev):
+    """Causal items longer than a workgroup's share are cut in two along their keys and the two
+    halves combined in a fixed order: whichever half ends last, every call gives the same bits
+    (resident form and the sliced call with both exchanges), within the tolerance of the oracle."""
+    S, hq, hkv = 2048, 8, 1
+    qkv = inputs.normal(8190, (S, (hq + 2 * hkv) * D), 1.0, "bf16")
+    qd = to_dev(qkv, dev)
+    st = torch.cuda.current_stream()
+    outs = []
+    for _ in range(4):
+        out = torch.full((S, hq * D), float("nan"), dtype=torch.bfloat16, device=dev)
+        fo.attn_ref(qd, out, hq, hkv, True, stream=st)
+        fo.check(st)
+        outs.append(out)
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+    _check(from_dev(outs[0]), qkv, hq, hkv, True, "split items, resident")
+    P = 8
+    a = _sliced(dev, qkv, P, 5, hq, hkv, True)
+    b = _sliced(dev, qkv, P, 5, hq, hkv, True)
+    assert torch.equal(a, b)
+    _check(from_dev(a), qkv, hq, hkv, True, "split items, sliced")
