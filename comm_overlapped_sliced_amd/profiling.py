@@ -384,7 +384,7 @@ def summarize_copies(raw: str, out_dir: str) -> None:
     text = f"""# Emulated transfers: SDMA copy trace, Llama-3.1-70B MLP step (P=8, rank 0)
 
 Command (from the repository root, TMPDIR=/tmp; `python -m comm_overlapped_sliced_amd.profiling
-run --passes copies`):
+run --raw {raw} --passes copies`):
 
     {command_text('copies', raw)}
 
@@ -435,7 +435,7 @@ peer or one link, ranks 0 and 7, the 1K-16K-token and 405B workloads), so only t
 activation rows come close to single-configuration figures.
 
 Command (from the repository root, TMPDIR=/tmp; `python -m comm_overlapped_sliced_amd.profiling
-run --passes bench`):
+run --raw {raw} --passes bench`):
 
     {command_text('bench', raw)}
 
