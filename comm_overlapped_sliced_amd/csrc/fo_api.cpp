@@ -539,6 +539,113 @@ fo_status noalloc_state(NoAllocDev** out, std::unique_lock<std::mutex>* lk) {
   return FO_OK;
 }
 
+constexpr int kAttnItemCost = 4;        // per item, in key tiles
+constexpr double kAttnFirstShare = 0.6;
+
+// The lists of one causal attention shape for n_cu CUs (host only): entries {slice, query tile,
+// head, w} list by list, bins[b] .. bins[b + 1] - 1 the entries of workgroup b; returns the
+// number of split pairs. False when the shape is too large for a table.
+bool attn_lists(int32_t P, int64_t m, int32_t hq, int64_t n_cu, std::vector<int4>* entries,
+                std::vector<int32_t>* bins_out, int32_t* n_pairs) {
+  const int64_t qtiles = (m + 127) / 128;
+  const int64_t base = (int64_t)P * qtiles * hq;
+  const int64_t slots = 2 * n_cu;
+  if (base < 1 || base > ((int64_t)1 << 22) || n_cu < 1) return false;
+  const int64_t mt = (m + 63) / 64;
+  struct Item {
+    int64_t cost;
+    int4 e;
+  };
+  std::vector<Item> items;
+  int64_t sum = 0;
+  for (int s = 0; s < P; ++s)
+    for (int64_t qt = 0; qt < qtiles; ++qt) {
+      const int64_t q1 = std::min<int64_t>(m, (qt + 1) * 128);
+      sum += hq * (s * mt + (q1 + 63) / 64 + kAttnItemCost);
+    }
+  const int64_t share = (sum + slots - 1) / slots;
+  int32_t pairs = 0;
+  for (int s = 0; s < P; ++s)
+    for (int64_t qt = 0; qt < qtiles; ++qt) {
+      const int64_t q1 = std::min<int64_t>(m, (qt + 1) * 128);
+      const int32_t w = (int32_t)(s * mt + (q1 + 63) / 64);
+      for (int h = 0; h < hq; ++h) {
+        if (w >= 2 && w + kAttnItemCost > share) {
+          const int32_t cut = (w + 1) / 2;
+          items.push_back({cut + kAttnItemCost, make_int4(s, (int)qt, h, 2 * pairs)});
+          items.push_back({w - cut + kAttnItemCost, make_int4(s, (int)qt, h, 2 * pairs + 1)});
+          ++pairs;
+        } else {
+          items.push_back({w + kAttnItemCost, make_int4(s, (int)qt, h, -1)});
+        }
+      }
+    }
+  // longest first (equal costs keep their table order: the schedule is a function of the shape)
+  std::stable_sort(items.begin(), items.end(),
+                   [](const Item& a, const Item& b) { return a.cost > b.cost; });
+  const int64_t E = (int64_t)items.size();
+  std::vector<std::vector<int4>> lists;
+  if (E <= n_cu) {
+    // one item per workgroup, each on a CU of its own
+    for (const Item& it : items) lists.push_back({it.e});
+  } else {
+    using Load = std::pair<int64_t, int>;
+    std::priority_queue<Load, std::vector<Load>, std::greater<Load>> heap;
+    for (int c = 0; c < n_cu; ++c) heap.push({0, c});
+    std::vector<std::vector<const Item*>> cu(n_cu);
+    for (const Item& it : items) {
+      Load l = heap.top();
+      heap.pop();
+      cu[l.second].push_back(&it);
+      l.first += it.cost;
+      heap.push(l);
+    }
+    lists.assign(slots, {});
+    for (int c = 0; c < n_cu; ++c) {
+      // the first workgroup's items: the subset whose cost is closest to its share (every
+      // subset while there are few items, else longest first up to the share)
+      const auto& v = cu[c];
+      int64_t tot = 0;
+      for (const Item* it : v) tot += it->cost;
+      const double want = kAttnFirstShare * (double)tot;
+      std::vector<char> first(v.size(), 0);
+      if (v.size() <= 10) {
+        double best = 1e300;
+        uint32_t pick = 0;
+        for (uint32_t mask = 0; mask < (1u << v.size()); ++mask) {
+          int64_t a = 0;
+          for (size_t i = 0; i < v.size(); ++i)
+            if (mask >> i & 1) a += v[i]->cost;
+          const double d = std::fabs((double)a - want);
+          if (d < best) {
+            best = d;
+            pick = mask;
+          }
+        }
+        for (size_t i = 0; i < v.size(); ++i) first[i] = (char)(pick >> i & 1);
+      } else {
+        int64_t a = 0;
+        for (size_t i = 0; i < v.size(); ++i)
+          if ((double)(a + v[i]->cost) <= want) {
+            a += v[i]->cost;
+            first[i] = 1;
+          }
+      }
+      for (size_t i = 0; i < v.size(); ++i) lists[first[i] ? c : n_cu + c].push_back(v[i]->e);
+    }
+  }
+  const int nb = (int)lists.size();
+  entries->clear();
+  bins_out->assign(nb + 1, 0);
+  for (int b = 0; b < nb; ++b) {
+    (*bins_out)[b] = (int32_t)entries->size();
+    entries->insert(entries->end(), lists[b].begin(), lists[b].end());
+  }
+  (*bins_out)[nb] = (int32_t)entries->size();
+  *n_pairs = pairs;
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -644,6 +751,33 @@ fo_status fo_tile_order(int32_t kind, int32_t P, int64_t m, int64_t K, int64_t N
     out[4 * u + 2] = tm;
     out[4 * u + 3] = tn;
   }
+  return FO_OK;
+}
+
+fo_status fo_attn_schedule(int32_t P, int64_t m, int32_t hq, int32_t n_cu, int32_t* out,
+                           int64_t capacity, int64_t* count, int32_t* workgroups) {
+  if (P < 1 || P > FO_MAX_P || m < 1 || hq < 1 || n_cu < 1) return invalid("bad shape");
+  if (count == nullptr || workgroups == nullptr || (capacity > 0 && out == nullptr))
+    return invalid("NULL output");
+  std::vector<int4> entries;
+  std::vector<int32_t> bins;
+  int32_t pairs = 0;
+  if (!attn_lists(P, m, hq, n_cu, &entries, &bins, &pairs)) {
+    *count = 0;
+    *workgroups = 0;
+    return FO_OK;
+  }
+  *count = (int64_t)entries.size();
+  *workgroups = (int32_t)bins.size() - 1;
+  int64_t k = 0;
+  for (int b = 0; b + 1 < (int)bins.size(); ++b)
+    for (int u = bins[b]; u < bins[b + 1] && k < capacity; ++u, ++k) {
+      out[5 * k + 0] = b;
+      out[5 * k + 1] = entries[u].x;
+      out[5 * k + 2] = entries[u].y;
+      out[5 * k + 3] = entries[u].z;
+      out[5 * k + 4] = entries[u].w;
+    }
   return FO_OK;
 }
 
@@ -1004,111 +1138,19 @@ static int32_t attn_pair_half(int32_t P, int64_t m, int32_t hq, int32_t causal, 
 // the slices one after another in arrival order (under causal masking the slice that arrives
 // first may need every other slice's keys: 194 -> 231 us inbound), and the own slice's items
 // last with the return exchange (246 -> 259 us).
-constexpr int kAttnItemCost = 4;        // per item, in key tiles
-constexpr double kAttnFirstShare = 0.6;
 static fo_status attn_schedule(DevState* st, fo::AttnPlan& p) {
   p.table = nullptr;
   p.bins = nullptr;
   if (!p.causal) return FO_OK;
-  const int64_t qtiles = (p.m + 127) / 128;
-  const int64_t base = (int64_t)p.P * qtiles * p.hq;
-  const int64_t n_cu = st->n_cu, slots = 2 * n_cu;
-  if (base > ((int64_t)1 << 22)) return FO_OK;
   const DevState::AttnTable* t = nullptr;
   for (const auto& e : st->attn_tables)
     if (e.P == p.P && e.m == p.m && e.hq == p.hq && e.causal == p.causal) t = &e;
   if (t == nullptr) {
-    const int64_t mt = (p.m + 63) / 64;
-    struct Item {
-      int64_t cost;
-      int4 e;
-    };
-    std::vector<Item> items;
-    int64_t sum = 0;
-    for (int s = 0; s < p.P; ++s)
-      for (int64_t qt = 0; qt < qtiles; ++qt) {
-        const int64_t q1 = std::min<int64_t>(p.m, (qt + 1) * 128);
-        sum += p.hq * (s * mt + (q1 + 63) / 64 + kAttnItemCost);
-      }
-    const int64_t share = (sum + slots - 1) / slots;
-    int32_t pairs = 0;
-    for (int s = 0; s < p.P; ++s)
-      for (int64_t qt = 0; qt < qtiles; ++qt) {
-        const int64_t q1 = std::min<int64_t>(p.m, (qt + 1) * 128);
-        const int32_t w = (int32_t)(s * mt + (q1 + 63) / 64);
-        for (int h = 0; h < p.hq; ++h) {
-          if (w >= 2 && w + kAttnItemCost > share) {
-            const int32_t cut = (w + 1) / 2;
-            items.push_back({cut + kAttnItemCost, make_int4(s, (int)qt, h, 2 * pairs)});
-            items.push_back({w - cut + kAttnItemCost, make_int4(s, (int)qt, h, 2 * pairs + 1)});
-            ++pairs;
-          } else {
-            items.push_back({w + kAttnItemCost, make_int4(s, (int)qt, h, -1)});
-          }
-        }
-      }
-    // longest first (equal costs keep their table order: the schedule is a function of the shape)
-    std::stable_sort(items.begin(), items.end(),
-                     [](const Item& a, const Item& b) { return a.cost > b.cost; });
-    const int64_t E = (int64_t)items.size();
-    std::vector<std::vector<int4>> lists;
-    if (E <= n_cu) {
-      // one item per workgroup, each on a CU of its own
-      for (const Item& it : items) lists.push_back({it.e});
-    } else {
-      using Load = std::pair<int64_t, int>;
-      std::priority_queue<Load, std::vector<Load>, std::greater<Load>> heap;
-      for (int c = 0; c < n_cu; ++c) heap.push({0, c});
-      std::vector<std::vector<const Item*>> cu(n_cu);
-      for (const Item& it : items) {
-        Load l = heap.top();
-        heap.pop();
-        cu[l.second].push_back(&it);
-        l.first += it.cost;
-        heap.push(l);
-      }
-      lists.assign(slots, {});
-      for (int c = 0; c < n_cu; ++c) {
-        // the first workgroup's items: the subset whose cost is closest to its share (every
-        // subset while there are few items, else longest first up to the share)
-        const auto& v = cu[c];
-        int64_t tot = 0;
-        for (const Item* it : v) tot += it->cost;
-        const double want = kAttnFirstShare * (double)tot;
-        std::vector<char> first(v.size(), 0);
-        if (v.size() <= 10) {
-          double best = 1e300;
-          uint32_t pick = 0;
-          for (uint32_t mask = 0; mask < (1u << v.size()); ++mask) {
-            int64_t a = 0;
-            for (size_t i = 0; i < v.size(); ++i)
-              if (mask >> i & 1) a += v[i]->cost;
-            const double d = std::fabs((double)a - want);
-            if (d < best) {
-              best = d;
-              pick = mask;
-            }
-          }
-          for (size_t i = 0; i < v.size(); ++i) first[i] = (char)(pick >> i & 1);
-        } else {
-          int64_t a = 0;
-          for (size_t i = 0; i < v.size(); ++i)
-            if ((double)(a + v[i]->cost) <= want) {
-              a += v[i]->cost;
-              first[i] = 1;
-            }
-        }
-        for (size_t i = 0; i < v.size(); ++i) lists[first[i] ? c : n_cu + c].push_back(v[i]->e);
-      }
-    }
-    const int nb = (int)lists.size();
     std::vector<int4> host;
-    std::vector<int32_t> bins(nb + 1, 0);
-    for (int b = 0; b < nb; ++b) {
-      bins[b] = (int32_t)host.size();
-      host.insert(host.end(), lists[b].begin(), lists[b].end());
-    }
-    bins[nb] = (int32_t)host.size();
+    std::vector<int32_t> bins;
+    int32_t pairs = 0;
+    if (!attn_lists(p.P, p.m, p.hq, st->n_cu, &host, &bins, &pairs)) return FO_OK;
+    const int nb = (int)bins.size() - 1;
     const size_t tb = host.size() * sizeof(int4), bb = bins.size() * sizeof(int32_t);
     void* d = nullptr;
     FO_HIP(hipMalloc(&d, tb + bb));

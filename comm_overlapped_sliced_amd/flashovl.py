@@ -26,6 +26,7 @@ EXPORTS = ("fo_opts_init", "fo_ag_gemm", "fo_gemm_rs", "fo_gemm_rs_noalloc", "fo
            "fo_swiglu", "fo_attn",
            "fo_attn_ref",
            "fo_transfer_ref", "fo_check", "fo_slice_order", "fo_tile_info", "fo_tile_order",
+           "fo_attn_schedule",
            "fo_status_str", "fo_last_error", "fo_version")
 
 
@@ -75,6 +76,8 @@ def load():
     lib.fo_slice_order.argtypes = [i32, i32, i32, i32, ctypes.POINTER(i32)]
     lib.fo_tile_info.argtypes = [i32, i64, i64, i64, i32, i32, i32, ctypes.POINTER(i32),
                                  ctypes.POINTER(i32), ctypes.POINTER(i64)]
+    lib.fo_attn_schedule.argtypes = [i32, i64, i32, i32, ctypes.POINTER(i32), i64,
+                                     ctypes.POINTER(i64), ctypes.POINTER(i32)]
     lib.fo_tile_order.argtypes = [i32, i32, i64, i64, i64, i32, i32, op, ctypes.POINTER(i32), i64,
                                   ctypes.POINTER(i64)]
     lib.fo_status_str.argtypes = [i32]
@@ -85,7 +88,8 @@ def load():
     for f in ("fo_ag_gemm", "fo_gemm_rs", "fo_gemm_rs_noalloc", "fo_gemm_ref", "fo_swiglu",
               "fo_attn", "fo_attn_ref",
               "fo_transfer_ref", "fo_check",
-              "fo_slice_order", "fo_tile_info", "fo_tile_order", "fo_version"):
+              "fo_slice_order", "fo_tile_info", "fo_tile_order", "fo_attn_schedule",
+              "fo_version"):
         getattr(lib, f).restype = ctypes.c_int32
     _lib = lib
     return lib
@@ -283,6 +287,19 @@ def tile_info(P: int, m: int, K: int, N: int, in_dt: int = BF16, tile: int = TIL
                              ctypes.byref(wg))
     _raise_on(st, "fo_tile_info")
     return bm.value, bn.value, wg.value
+
+
+def attn_schedule(P: int, m: int, hq: int, n_cu: int):
+    """Work lists of a causal attention launch (fo_attn_schedule): a list of (workgroup, slice,
+    query tile, head, w) entries in launch order, and the number of workgroups."""
+    lib = load()
+    cnt, wgs = ctypes.c_int64(), ctypes.c_int32()
+    _raise_on(lib.fo_attn_schedule(P, m, hq, n_cu, None, 0, ctypes.byref(cnt), ctypes.byref(wgs)),
+              "fo_attn_schedule")
+    buf = (ctypes.c_int32 * max(1, 5 * cnt.value))()
+    _raise_on(lib.fo_attn_schedule(P, m, hq, n_cu, buf, cnt.value, ctypes.byref(cnt),
+                                   ctypes.byref(wgs)), "fo_attn_schedule")
+    return [tuple(buf[5 * i:5 * i + 5]) for i in range(cnt.value)], wgs.value
 
 
 def tile_order(kind: str, P: int, m: int, K: int, N: int, in_dt: int = BF16,

@@ -353,6 +353,17 @@ fo_status fo_tile_order(int32_t kind, int32_t P, int64_t m, int64_t K, int64_t N
                         int32_t out_dt, const fo_opts* opts, int32_t* out, int64_t capacity,
                         int64_t* count);
 
+/* The work lists of a causal fo_attn / fo_attn_ref launch for P slices of m tokens, hq query heads
+   and n_cu CUs (host only, no device needed): entry k (in launch order) is out[5k] = the
+   workgroup that takes it, out[5k+1] = slice, out[5k+2] = 128-query tile, out[5k+3] = head and
+   out[5k+4] = -1 for a whole item, else 2 * pair + part for one of the two halves (the first or
+   the second half of its key walk) of a split item. Workgroup b takes its entries in order;
+   workgroups b and b + n_cu share a CU. Writes the first min(capacity, count) entries; *count
+   receives the number of entries, *workgroups the number of workgroups (0 and 0: the shape has
+   no table and the launch takes one workgroup per item). */
+fo_status fo_attn_schedule(int32_t P, int64_t m, int32_t hq, int32_t n_cu, int32_t* out,
+                           int64_t capacity, int64_t* count, int32_t* workgroups);
+
 const char* fo_status_str(fo_status s);
 /* Detail of the last failure on the calling thread (empty string if none). */
 const char* fo_last_error(void);
