@@ -540,6 +540,7 @@ fo_status noalloc_state(NoAllocDev** out, std::unique_lock<std::mutex>* lk) {
 }
 
 constexpr int kAttnItemCost = 4;        // per item, in key tiles
+constexpr size_t kAttnTablesMax = 64;   // attention shapes whose tables a device keeps
 constexpr double kAttnFirstShare = 0.6;
 
 // The lists of one causal attention shape for n_cu CUs (host only): entries {slice, query tile,
@@ -1150,6 +1151,13 @@ static fo_status attn_schedule(DevState* st, fo::AttnPlan& p) {
     std::vector<int32_t> bins;
     int32_t pairs = 0;
     if (!attn_lists(p.P, p.m, p.hq, st->n_cu, &host, &bins, &pairs)) return FO_OK;
+    if (st->attn_tables.size() >= kAttnTablesMax) {
+      // a bounded cache: past this many shapes the tables are dropped (after every earlier
+      // launch that may read one has ended) and built again as shapes come back
+      FO_HIP(hipDeviceSynchronize());
+      for (const auto& e : st->attn_tables) FO_HIP(hipFree(e.table));
+      st->attn_tables.clear();
+    }
     const int nb = (int)bins.size() - 1;
     const size_t tb = host.size() * sizeof(int4), bb = bins.size() * sizeof(int32_t);
     void* d = nullptr;

@@ -234,3 +234,27 @@ def test_attn_split_items_same_bits_every_call(dev):
     b = _sliced(dev, qkv, P, 5, hq, hkv, True)
     assert torch.equal(a, b)
     _check(from_dev(a), qkv, hq, hkv, True, "split items, sliced")
+
+
+def test_attn_many_shapes_rebuild_tables(dev):
+    """More causal shapes than the device keeps tables for: the tables are dropped and built
+    again, and a shape seen before gives the same bits after the rebuild."""
+    hq, hkv = 2, 1
+    st = torch.cuda.current_stream()
+    sizes = [64 + 8 * k for k in range(70)]
+    qkvs = {S: inputs.normal(8300 + S, (S, (hq + 2 * hkv) * D), 1.0, "bf16") for S in (sizes[0], sizes[-1])}
+    first = None
+    for S in sizes + [sizes[0]]:
+        qkv = qkvs.get(S)
+        if qkv is None:
+            qkv = inputs.normal(8300 + S, (S, (hq + 2 * hkv) * D), 1.0, "bf16")
+        out = torch.full((S, hq * D), float("nan"), dtype=torch.bfloat16, device=dev)
+        fo.attn_ref(to_dev(qkv, dev), out, hq, hkv, True, stream=st)
+        fo.check(st)
+        assert not torch.isnan(out).any().item(), f"S={S}"
+        if S == sizes[0]:
+            if first is None:
+                first = out
+            else:
+                assert torch.equal(out, first)
+    _check(from_dev(first), qkvs[sizes[0]], hq, hkv, True, "after the table rebuild")
