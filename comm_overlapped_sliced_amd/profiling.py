@@ -1,8 +1,8 @@
 """rocprofv3 harness of the benchmark: the counter passes behind the roofline evidence, and the
 text summaries kept under profiles/.
 
-    python -m comm_overlapped_sliced_amd.profiling run --raw gpurun_out/prof
-    python -m comm_overlapped_sliced_amd.profiling summarize --raw gpurun_out/prof --out profiles
+    python -m comm_overlapped_sliced_amd.profiling run --raw rocprof_raw
+    python -m comm_overlapped_sliced_amd.profiling summarize --raw rocprof_raw --out profiles
 
 `run` launches, one after the other and each under its own time limit, rocprofv3 on bench.py:
   1. --kernel-trace --stats: per-kernel durations of the step (no exposure sweep, no oracle);
@@ -540,10 +540,10 @@ def main(argv=None) -> int:
     ap = argparse.ArgumentParser(prog="python -m comm_overlapped_sliced_amd.profiling")
     sub = ap.add_subparsers(dest="cmd", required=True)
     r = sub.add_parser("run")
-    r.add_argument("--raw", default="gpurun_out/prof")
+    r.add_argument("--raw", default="rocprof_raw")
     r.add_argument("--passes", default="", help="comma-separated pass names (default: all)")
     s = sub.add_parser("summarize")
-    s.add_argument("--raw", default="gpurun_out/prof")
+    s.add_argument("--raw", default="rocprof_raw")
     s.add_argument("--out", default="profiles")
     s.add_argument("--sclk-mhz", type=float, default=None)
     a = ap.parse_args(argv)
