@@ -258,3 +258,21 @@ def test_attn_many_shapes_rebuild_tables(dev):
             else:
                 assert torch.equal(out, first)
     _check(from_dev(first), qkvs[sizes[0]], hq, hkv, True, "after the table rebuild")
+
+
+@pytest.mark.parametrize("std", [3.0, 0.05], ids=["peaked", "flat"])
+def test_attn_split_items_extreme_softmax(dev, std):
+    """Split items under a peaked softmax (queries and keys with standard deviation 3: scores of
+    several hundred, so the two halves' maxima differ widely and one half's weight underflows)
+    and a flat one (std 0.05: every key nearly equal), resident and sliced, against the oracle."""
+    S, hq, hkv, P = 2048, 8, 1, 8
+    qkv = inputs.normal(8400 + int(std * 100), (S, (hq + 2 * hkv) * D), 1.0, "bf16")
+    scaled = inputs.normal(8401 + int(std * 100), (S, (hq + hkv) * D), std, "bf16")
+    qkv[:, :(hq + hkv) * D] = scaled  # queries and keys at `std`, values at 1
+    st = torch.cuda.current_stream()
+    out = torch.full((S, hq * D), float("nan"), dtype=torch.bfloat16, device=dev)
+    fo.attn_ref(to_dev(qkv, dev), out, hq, hkv, True, stream=st)
+    fo.check(st)
+    _check(from_dev(out), qkv, hq, hkv, True, f"split items, std {std}, resident")
+    a = _sliced(dev, qkv, P, 3, hq, hkv, True)
+    _check(from_dev(a), qkv, hq, hkv, True, f"split items, std {std}, sliced")
