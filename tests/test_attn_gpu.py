@@ -276,3 +276,27 @@ def test_attn_split_items_extreme_softmax(dev, std):
     _check(from_dev(out), qkv, hq, hkv, True, f"split items, std {std}, resident")
     a = _sliced(dev, qkv, P, 3, hq, hkv, True)
     _check(from_dev(a), qkv, hq, hkv, True, f"split items, std {std}, sliced")
+
+
+def test_attn_missed_arrival_times_out_then_recovers(dev):
+    """Causal attention with split items whose arrival waits have a 1 us bound against transfers
+    over one link: the call reports FO_ERR_TIMEOUT and every kernel still finishes (both halves of
+    every pair reach their combine), and the next calls, with split items again, are correct and
+    give the same bits as before the timeout."""
+    P, m, hq, hkv = 8, 256, 8, 1
+    qkv = inputs.normal(8500, (P * m, (hq + 2 * hkv) * D), 1.0, "bf16")
+    before = _sliced(dev, qkv, P, 2, hq, hkv, True)
+    slices = [to_dev(qkv[s * m:(s + 1) * m], dev) for s in range(P)]
+    recv = torch.empty((P * m, qkv.shape[1]), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((P * m, hq * D), dtype=torch.bfloat16, device=dev)
+    st = torch.cuda.current_stream()
+    s = fo.attn(slices[2], slices, recv, out, P, 2, hq, hkv, True, compute_stream=st,
+                o=fo.opts(spin_timeout_us=1, links=1), raw=True)
+    assert s == fo.FO_OK
+    with pytest.raises(fo.FoError) as ei:
+        fo.check(st)
+    assert ei.value.status == fo.FO_ERR_TIMEOUT
+    fo.check(st)
+    after = _sliced(dev, qkv, P, 2, hq, hkv, True)
+    assert torch.equal(after, before)
+    _check(from_dev(after), qkv, hq, hkv, True, "after a timed-out call")
