@@ -13,7 +13,11 @@
 // online softmax makes the order of the keys irrelevant up to rounding.
 //
 // Kernel design (CDNA4):
-// - One workgroup per (slice, 128-query tile, head): 4 waves of 32 queries; key tiles of 64.
+// - One work item per (slice, 128-query tile, head): 4 waves of 32 queries; key tiles of 64.
+//   Causal calls run from a table built on the host: each workgroup (two per CU, all resident)
+//   walks its own list of items, and an item longer than a workgroup's share of the key tiles
+//   is cut in two along its key walk, each half storing its unnormalized output, running max
+//   and sum, the second to finish combining them in a fixed order (attn_tile's end).
 // - Scores are computed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16, K from LDS as the A
 //   operand, Q in registers as the B operand), so that each lane owns one query: the softmax
 //   row state (running max and sum) is per lane, and a row reduction needs one cross-lane swap.
@@ -421,9 +425,9 @@ __device__ __forceinline__ void attn_tile(const AttnPlan& p, const int u, uint8_
     // both parts relative to the larger reference max; the sums are formed in part order (part
     // 0's term through the fma), so the result does not depend on which part finished last
     const float mm = fmaxf(mrow, om);
-    const float fm = __builtin_amdgcn_exp2f((mrow - mm) * p.scale_log2);
-    const float fo = __builtin_amdgcn_exp2f((om - mm) * p.scale_log2);
-    lrow = part == 0 ? __builtin_fmaf(lrow, fm, ol * fo) : __builtin_fmaf(ol, fo, lrow * fm);
+    const float f_own = __builtin_amdgcn_exp2f((mrow - mm) * p.scale_log2);
+    const float f_oth = __builtin_amdgcn_exp2f((om - mm) * p.scale_log2);
+    lrow = part == 0 ? __builtin_fmaf(lrow, f_own, ol * f_oth) : __builtin_fmaf(ol, f_oth, lrow * f_own);
 #pragma unroll
     for (int i = 0; i < kAD / 32; ++i)
 #pragma unroll
@@ -431,8 +435,8 @@ __device__ __forceinline__ void attn_tile(const AttnPlan& p, const int u, uint8_
         const float ov = __builtin_bit_cast(
             float, __builtin_amdgcn_raw_buffer_load_b32(other, wbase + (uint32_t)((i * 16 + v) * 64 * 4),
                                                         0, kSys));
-        oacc[i][v] = part == 0 ? __builtin_fmaf(oacc[i][v], fm, ov * fo)
-                               : __builtin_fmaf(ov, fo, oacc[i][v] * fm);
+        oacc[i][v] = part == 0 ? __builtin_fmaf(oacc[i][v], f_own, ov * f_oth)
+                               : __builtin_fmaf(ov, f_oth, oacc[i][v] * f_own);
       }
   }
 
