@@ -278,6 +278,37 @@ def test_attn_split_items_extreme_softmax(dev, std):
     _check(from_dev(a), qkv, hq, hkv, True, f"split items, std {std}, sliced")
 
 
+@pytest.mark.parametrize("P,m", [(1, 8000), (8, 1000)], ids=["resident_8000", "sliced_8x1000"])
+def test_attn_split_items_ragged_length(dev, P, m):
+    """Split items at lengths that are not a multiple of the 128-query tile or the 64-key tile
+    (the last query tile of a slice holds 64 or 104 rows, the last key tile of the diagonal is
+    partly past the slice): the resident call (P = 1, 8000 tokens) or the sliced one with both
+    exchanges (P = 8, m = 1000, rank 6), twice with the same bits, against the oracle on rows at
+    the start, around a split item of the middle and at the ragged end of every slice."""
+    hq, hkv = 8, 1
+    S = P * m
+    sched, _ = fo.attn_schedule(P, m, hq, torch.cuda.get_device_properties(dev).multi_processor_count)
+    assert sum(1 for e in sched if e[4] >= 0) > 0, "the shape has split items"
+    qkv = inputs.normal(8600 + m, (S, (hq + 2 * hkv) * D), 1.0, "bf16")
+    st = torch.cuda.current_stream()
+    if P == 1:
+        qd = to_dev(qkv, dev)
+        outs = []
+        for _ in range(2):
+            out = torch.full((S, hq * D), float("nan"), dtype=torch.bfloat16, device=dev)
+            fo.attn_ref(qd, out, hq, hkv, True, stream=st)
+            fo.check(st)
+            outs.append(out)
+    else:
+        outs = [_sliced(dev, qkv, P, 6, hq, hkv, True) for _ in range(2)]
+    assert torch.equal(outs[0], outs[1])
+    rows = sorted({r for s in range(P) for r in
+                   [*range(s * m, s * m + 16), *range(s * m + m // 2 - 8, s * m + m // 2 + 8),
+                    *range(s * m + m - 40, s * m + m)]})
+    _check(from_dev(outs[0])[rows], qkv, hq, hkv, True, f"split items, ragged, P={P} m={m}",
+           rows=rows)
+
+
 def test_attn_missed_arrival_times_out_then_recovers(dev):
     """Causal attention with split items whose arrival waits have a 1 us bound against transfers
     over one link: the call reports FO_ERR_TIMEOUT and every kernel still finishes (both halves of
